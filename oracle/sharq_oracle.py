@@ -1,0 +1,320 @@
+"""CPU oracle for the SharQ linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline leg
+may import this module.  The HIP library never calls it and shares no code
+with it; the two meet only through the seeded inputs of
+``fp4_sparse_dense_amd.synth``.
+
+What is computed (SharQ paper page, "SharQ: Bridging Activation Sparsity and
+FP4 Quantization for LLM Inference", Abstract):
+
+  per activation row: RMSNorm -> N:M mask keeping the largest magnitudes
+  (the sparse backbone S) -> FP4 quantisation of S -> residual R = X - deq(Q(S))
+  taken against the *quantised* backbone -> FP4 quantisation of R; then
+  Y = deq(Q(S)) deq(W)^T + deq(Q(R)) deq(W)^T over one FP4 weight payload.
+
+The pages print no formulas.  Readings used here (each listed in the design doc):
+
+* RMSNorm is evaluated in IEEE binary32 with the sum of squares taken as a
+  balanced pairwise tree in index order over the row zero-padded to a power of
+  two; 1/sqrt and the division by K are correctly rounded.
+* Mask ties go to the lower index; +0 and -0 have equal magnitude.
+* MXFP4 follows the OCP Microscaling v1.0 definition: 32-element blocks, E8M0
+  shared exponent e = floor(log2 amax) - 2, E2M1 elements rounded to nearest
+  with ties to the even code, saturating at 6.
+* The residual is r = v - d in binary32 (exact: shown and tested).
+* GEMM outputs are accumulated in float64.
+
+Parity status of each function is given in its docstring ("pinned by" lists
+the independent checks in tests/test_oracle_*.py).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+
+# E2M1 magnitudes by 3-bit code (sign is bit 3 of the nibble).
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+MX_BLOCK = 32
+E8M0_BIAS = 127
+E2M1_EMAX = 2          # largest E2M1 value is 1.5 * 2^2
+
+
+# --------------------------------------------------------------------------
+# bf16 widening
+# --------------------------------------------------------------------------
+def widen_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns -> float32 (exact: bf16 is the upper half of binary32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# RMSNorm  (SharQ abstract: the preparation operator absorbs the normalisation;
+# SharQ README, Evaluation/Benchmarks: the fused normalisation is RMSNorm)
+# --------------------------------------------------------------------------
+def pairwise_tree_sum_f32(q: np.ndarray) -> np.ndarray:
+    """Balanced pairwise sum along the last axis, binary32, in index order.
+
+    The row is zero-padded to the next power of two P and summed as
+    T[lo,hi) = T[lo,mid) + T[mid,hi), mid = (lo+hi)/2, leaves = elements.
+    Pinned by: exact integer sums, fp64 comparison, explicit recursive tree.
+    """
+    q = np.asarray(q, dtype=F32)
+    K = q.shape[-1]
+    P = 1
+    while P < K:
+        P *= 2
+    if P != K:
+        pad = np.zeros(q.shape[:-1] + (P - K,), dtype=F32)
+        q = np.concatenate([q, pad], axis=-1)
+    while q.shape[-1] > 1:
+        q = q[..., 0::2] + q[..., 1::2]
+    return q[..., 0]
+
+
+def rmsnorm(x_bits, gamma_bits, eps: float) -> np.ndarray:
+    """v = x * (1/sqrt(mean(x^2) + eps)) * gamma in binary32; gamma None -> v = x.
+
+    Steps: x widened exactly; q = x*x (exact: 8-bit significands);
+    ss = pairwise tree of q; mean = ss / K; inv = 1 / sqrt(mean + eps);
+    v = (x * inv) * gamma, every operation rounded once to binary32.
+    Pinned by: constant-row closed form, fp64 formula within 4 ulp,
+    the identity path.
+    """
+    x = widen_bf16(x_bits)
+    if gamma_bits is None:
+        return x.copy()
+    K = x.shape[-1]
+    ss = pairwise_tree_sum_f32(x * x)
+    mean = ss / F32(K)
+    inv = F32(1.0) / np.sqrt(mean + F32(eps))
+    g = widen_bf16(gamma_bits)
+    return (x * inv[..., None]) * g
+
+
+# --------------------------------------------------------------------------
+# N:M input-adaptive mask  (SharQ abstract: an input-dependent N:M mask keeps
+# the outlier-dominated entries as the sparse backbone)
+# --------------------------------------------------------------------------
+def nm_mask(v: np.ndarray, n: int = 2, m: int = 4) -> np.ndarray:
+    """Boolean keep-mask: in each aligned group of m along the last axis keep n.
+
+    Element k of a group is kept iff fewer than n members beat it, where i
+    beats k when |v_i| > |v_k|, or |v_i| == |v_k| and i < k.
+    Pinned by: brute force over every 4-tuple of a 7-value set with ties and
+    signed zeros; exactly-n and ordering invariants.
+    """
+    v = np.asarray(v, dtype=F32)
+    K = v.shape[-1]
+    if K % m:
+        raise ValueError("K must be a multiple of m")
+    a = np.abs(v).reshape(v.shape[:-1] + (K // m, m))
+    rank = np.zeros(a.shape, dtype=np.int32)
+    for k in range(m):
+        for i in range(m):
+            if i == k:
+                continue
+            beats = a[..., i] > a[..., k]
+            if i < k:
+                beats = beats | (a[..., i] == a[..., k])
+            rank[..., k] += beats
+    return (rank < n).reshape(v.shape)
+
+
+def pack_meta_24(kept: np.ndarray) -> np.ndarray:
+    """2:4 metadata: per group the two kept offsets i0 < i1 as nibble i0 | i1<<2;
+    group j goes to byte j//2, low nibble for even j.  Shape [..., K/8] uint8."""
+    K = kept.shape[-1]
+    g = kept.reshape(kept.shape[:-1] + (K // 4, 4))
+    if not np.all(g.sum(-1) == 2):
+        raise ValueError("2:4 metadata needs exactly two kept per group")
+    off = np.argsort(~g, axis=-1, kind="stable")[..., :2]   # kept offsets, ascending
+    nib = (off[..., 0] | (off[..., 1] << 2)).astype(np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_meta_24(meta: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of pack_meta_24: boolean keep-mask [..., K]."""
+    meta = np.asarray(meta, dtype=np.uint8)
+    nib = np.stack([meta & 0xF, meta >> 4], axis=-1).reshape(meta.shape[:-1] + (K // 4,))
+    i0, i1 = nib & 3, nib >> 2
+    pos = np.arange(4)
+    kept = (pos == i0[..., None]) | (pos == i1[..., None])
+    return kept.reshape(meta.shape[:-1] + (K,))
+
+
+# --------------------------------------------------------------------------
+# MXFP4 (OCP Microscaling v1.0: E2M1 elements, E8M0 scale per 32 elements)
+# --------------------------------------------------------------------------
+def floor_log2(a: np.ndarray) -> np.ndarray:
+    """Exact floor(log2 a) for positive finite a (frexp: a = f 2^x, f in [0.5,1))."""
+    _, x = np.frexp(np.asarray(a, dtype=np.float64))
+    return x.astype(np.int32) - 1
+
+
+def mx_exponent(amax: np.ndarray) -> np.ndarray:
+    """Shared exponent e = clamp(floor(log2 amax) - 2, -127, 127); amax == 0 -> -127."""
+    amax = np.asarray(amax, dtype=np.float64)
+    e = np.full(amax.shape, -E8M0_BIAS, dtype=np.int32)
+    nz = amax > 0
+    e[nz] = floor_log2(amax[nz]) - E2M1_EMAX
+    return np.clip(e, -E8M0_BIAS, E8M0_BIAS)
+
+
+def e2m1_nearest(t) -> np.ndarray:
+    """E2M1 nibble of real t: nearest grid magnitude, ties to the even code,
+    magnitudes beyond 6 saturate to 6 (6 is the nearest grid point there);
+    nibble = sign(t)<<3 | code, the sign taken from t's sign bit (-0 -> 0x8).
+
+    Each midpoint between neighbouring grid values is a decision threshold:
+    crossing it moves up one code; landing exactly on it moves up only when
+    the upper code is even.  Comparisons are exact (t is binary32, compared in
+    float64).  Pinned by: exact-rational argmin over the whole grid.
+    """
+    t = np.asarray(t, dtype=np.float64)
+    a = np.abs(t)
+    code = np.zeros(a.shape, dtype=np.uint8)
+    for i in range(7):
+        mid = 0.5 * (E2M1_GRID[i] + E2M1_GRID[i + 1])
+        up_even = (i + 1) % 2 == 0
+        code += (a > mid) | ((a == mid) & up_even)
+    return code | (np.signbit(t).astype(np.uint8) << 3)
+
+
+def e2m1_value(nib) -> np.ndarray:
+    """Signed value of an E2M1 nibble (float64; -0.0 for 0x8)."""
+    nib = np.asarray(nib, dtype=np.uint8)
+    mag = E2M1_GRID[nib & 7]
+    return np.where(nib & 8, -mag, mag)
+
+
+def quantize_mx(u: np.ndarray):
+    """MXFP4 quantisation along the last axis (length a multiple of 32).
+
+    Returns (E8M0 scale bytes [..., K/32], nibbles [..., K]).  Element code =
+    e2m1_nearest(u / 2^e) with e the block's shared exponent; the division is
+    exact in float64.  Pinned by: amax/2^e in [4,8), codes on the grid,
+    brute force of the element rounding, closed-form blocks.
+    """
+    u = np.asarray(u, dtype=F32)
+    K = u.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blocks = u.reshape(u.shape[:-1] + (K // MX_BLOCK, MX_BLOCK)).astype(np.float64)
+    amax = np.abs(blocks).max(axis=-1)
+    e = mx_exponent(amax)
+    t = blocks / np.exp2(e.astype(np.float64))[..., None]
+    nib = e2m1_nearest(t).reshape(u.shape)
+    return (e + E8M0_BIAS).astype(np.uint8), nib
+
+
+def dequant_mx(scales: np.ndarray, nib: np.ndarray) -> np.ndarray:
+    """val(code) * 2^(E-127), float64, exact."""
+    K = nib.shape[-1]
+    e = np.asarray(scales, dtype=np.int64) - E8M0_BIAS
+    val = e2m1_value(nib).reshape(nib.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    return (val * np.exp2(e.astype(np.float64))[..., None]).reshape(nib.shape)
+
+
+def pack_nibbles(nib: np.ndarray) -> np.ndarray:
+    """Two codes per byte, the lower index in the low nibble."""
+    nib = np.asarray(nib, dtype=np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint8)
+    return np.stack([b & 0xF, b >> 4], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+
+
+# --------------------------------------------------------------------------
+# Preparation  (SharQ abstract: mask generation, residual construction and
+# normalisation form one preparation operator)
+# --------------------------------------------------------------------------
+def prepare(x_bits, gamma_bits=None, eps: float = 1e-5, n: int = 2, m: int = 4):
+    """Sparse-dense decomposition of activation rows (MXFP4, 2:4 outputs).
+
+    Returns a dict with the canonical byte outputs
+      s_codes  [M, K/4]  kept S codes in k order, 2 per byte (low nibble first)
+      s_meta   [M, K/8]  2:4 metadata (pack_meta_24)
+      s_scales [M, K/32] E8M0 of S over 32 logical positions
+      r_codes  [M, K/2]  all R codes, 2 per byte
+      r_scales [M, K/32] E8M0 of R
+    and intermediates v, kept, s_nib (dense S nibbles), d (deq S, binary32),
+    r (binary32).
+    Pinned by: v == d + r exactly; S scale == scale of the unmasked block;
+    exactly two kept per group; special cases that make R vanish.
+    """
+    if (n, m) != (2, 4):
+        raise ValueError("byte outputs are defined for 2:4")
+    v = rmsnorm(x_bits, gamma_bits, eps)
+    kept = nm_mask(v, n, m)
+    s = np.where(kept, v, F32(0.0))
+    s_scales, s_nib = quantize_mx(s)
+    d = dequant_mx(s_scales, s_nib)
+    d = np.where(kept, d, 0.0).astype(F32)       # exact: at most 3 significant bits
+    r = v - d                                      # binary32 subtraction
+    r_scales, r_nib = quantize_mx(r)
+    M, K = v.shape
+    s_kept_nib = s_nib[kept].reshape(M, K // 2)
+    return dict(
+        s_codes=pack_nibbles(s_kept_nib),
+        s_meta=pack_meta_24(kept),
+        s_scales=s_scales,
+        r_codes=pack_nibbles(r_nib),
+        r_scales=r_scales,
+        v=v, kept=kept, s_nib=s_nib, d=d, r=r,
+    )
+
+
+def pack_weight(w_bits):
+    """Single FP4 weight payload (SharQ abstract: both paths read one FP4 weight
+    payload): MXFP4 over each 32-block of a row of W[N,K] (bf16 bits), no mask,
+    no norm.  Returns (codes [N, K/2], E8M0 scales [N, K/32])."""
+    scales, nib = quantize_mx(widen_bf16(w_bits))
+    return pack_nibbles(nib), scales
+
+
+# --------------------------------------------------------------------------
+# Dequantised operands and the dual GEMM
+# --------------------------------------------------------------------------
+def deq_sparse(s_codes, s_meta, s_scales, K: int) -> np.ndarray:
+    """Dense float64 D^S [M,K] from the compressed 2:4 operand."""
+    s_codes = np.asarray(s_codes)
+    M = s_codes.shape[0]
+    kept = unpack_meta_24(s_meta, K)
+    nib = np.zeros((M, K), dtype=np.uint8)
+    nib[kept] = unpack_nibbles(s_codes).reshape(-1)
+    val = dequant_mx(s_scales, nib)
+    return np.where(kept, val, 0.0)
+
+
+def deq_dense(codes, scales) -> np.ndarray:
+    return dequant_mx(scales, unpack_nibbles(codes))
+
+
+def linear(act: dict, w_codes, w_scales, rows=None):
+    """y = D^S D^W^T + D^R D^W^T in float64, plus the bound B = sum|terms|.
+
+    (SharQ abstract: a sparse FP4 GEMM on the backbone and a dense FP4 GEMM on
+    the residual; the README's epilogue fusion sums the two.)
+    ``rows`` restricts the output to a subset of rows.  Returns (y, B).
+    Pinned by: exact rational tiny GEMMs, the R == 0 special case,
+    the path split y = y_S + y_R.
+    """
+    K = 2 * np.asarray(w_codes).shape[1]
+    sl = slice(None) if rows is None else rows
+    ds = deq_sparse(act["s_codes"][sl], act["s_meta"][sl], act["s_scales"][sl], K)
+    dr = deq_dense(act["r_codes"][sl], act["r_scales"][sl])
+    dw = deq_dense(w_codes, w_scales)
+    y = ds @ dw.T + dr @ dw.T
+    b = np.abs(ds) @ np.abs(dw).T + np.abs(dr) @ np.abs(dw).T
+    return y, b
+
+
+def within_tolerance(y_gpu, y_ref, bound, rel: float = 1e-5, abs_: float = 1e-6):
+    """Elementwise |y_gpu - y_ref| <= rel * sum|terms| + abs."""
+    err = np.abs(np.asarray(y_gpu, dtype=np.float64) - y_ref)
+    lim = rel * bound + abs_
+    return err <= lim
