@@ -1,0 +1,133 @@
+"""SharQ sparse-dense FP4 linear layer on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over libsharq.so (include/sharq.h).  Functions take torch
+tensors only as device memory: every step of the layer runs in the HIP
+kernels behind the C ABI.  The names follow the C entry points:
+
+    w = sharq_pack_weight(w_bf16)                 # one FP4 weight payload
+    a = sharq_prepare(x_bf16, gamma, eps)         # fused RMSNorm + 2:4 + MXFP4(S) + R + MXFP4(R)
+    y = sharq_linear(a, w)                        # sparse + dense FP4 GEMMs, one epilogue
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+from . import _lib
+from ._lib import FMT_HIF4, FMT_MXFP4, FMT_NVFP4, OUT_BF16, OUT_F32, SharqError
+
+__all__ = [
+    "SharqWeight", "SharqAct", "SharqError",
+    "sharq_pack_weight", "sharq_prepare", "sharq_linear",
+    "weight_bytes", "act_bytes",
+    "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+def weight_bytes(N: int, K: int, fmt: int = FMT_MXFP4):
+    lib = _lib.load()
+    cb, sb = C.c_size_t(), C.c_size_t()
+    _lib.check(lib.sharq_weight_bytes(N, K, fmt, C.byref(cb), C.byref(sb)), "sharq_weight_bytes")
+    return cb.value, sb.value
+
+
+def act_bytes(M: int, K: int, n: int = 2, m: int = 4, fmt: int = FMT_MXFP4):
+    lib = _lib.load()
+    sizes = (C.c_size_t * 5)()
+    _lib.check(lib.sharq_act_bytes(M, K, n, m, fmt, sizes), "sharq_act_bytes")
+    return list(sizes)
+
+
+class SharqWeight:
+    """Packed weight: device tensors codes [N, K/2] and scales [N, K/32] plus the descriptor."""
+
+    def __init__(self, N: int, K: int, device, fmt: int = FMT_MXFP4):
+        torch = _torch()
+        cb, sb = weight_bytes(N, K, fmt)
+        self.codes = torch.empty(cb, dtype=torch.uint8, device=device).view(N, K // 2)
+        self.scales = torch.empty(sb, dtype=torch.uint8, device=device).view(N, K // 32)
+        self.desc = _lib.WeightDesc()
+        self.desc.struct_size = C.sizeof(_lib.WeightDesc)
+        self.desc.codes = self.codes.data_ptr()
+        self.desc.scales = self.scales.data_ptr()
+        self.N, self.K, self.fmt = N, K, fmt
+
+
+class SharqAct:
+    """Prepared activation: five device byte tensors plus the descriptor."""
+
+    FIELDS = ("s_codes", "s_meta", "s_scales", "r_codes", "r_scales")
+
+    def __init__(self, M: int, K: int, device, n: int = 2, m: int = 4, fmt: int = FMT_MXFP4):
+        torch = _torch()
+        sizes = act_bytes(M, K, n, m, fmt)
+        widths = (K // 4, K // 8, K // 32, K // 2, K // 32)
+        self.desc = _lib.ActDesc()
+        self.desc.struct_size = C.sizeof(_lib.ActDesc)
+        for name, size, wdt in zip(self.FIELDS, sizes, widths):
+            # keep every buffer 256-byte aligned even when empty
+            t = torch.empty(max(size, 1), dtype=torch.uint8, device=device)[:size].view(M, wdt)
+            setattr(self, name, t)
+            setattr(self.desc, name, t.data_ptr())
+        self.M, self.K, self.n, self.m, self.fmt = M, K, n, m, fmt
+
+    def host(self) -> dict:
+        """Copies of the five byte arrays as numpy (for checks)."""
+        return {f: getattr(self, f).cpu().numpy() for f in self.FIELDS}
+
+
+def sharq_pack_weight(w, fmt: int = FMT_MXFP4, out: SharqWeight | None = None, stream=None) -> SharqWeight:
+    """Pack a bf16 device weight [N, K] (row stride w.stride(0)) into the FP4 payload."""
+    torch = _torch()
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D bf16 tensor with unit inner stride")
+    N, K = w.shape
+    out = out or SharqWeight(N, K, w.device, fmt)
+    lib = _lib.load()
+    _lib.check(lib.sharq_pack_weight(_ptr(w), N, K, w.stride(0), fmt, C.byref(out.desc), _stream_ptr(stream)),
+               "sharq_pack_weight")
+    return out
+
+
+def sharq_prepare(x, gamma=None, eps: float = 1e-5, n: int = 2, m: int = 4, fmt: int = FMT_MXFP4,
+                  out: SharqAct | None = None, stream=None) -> SharqAct:
+    """Fused preparation of bf16 device activations x [M, K]; gamma [K] bf16 or None (no RMSNorm)."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit inner stride")
+    if gamma is not None and (gamma.dtype != torch.bfloat16 or not gamma.is_contiguous()):
+        raise ValueError("gamma must be a contiguous bf16 tensor")
+    M, K = x.shape
+    out = out or SharqAct(M, K, x.device, n, m, fmt)
+    lib = _lib.load()
+    _lib.check(lib.sharq_prepare(_ptr(x), M, K, x.stride(0), _ptr(gamma), eps, n, m, fmt, C.byref(out.desc),
+                                 _stream_ptr(stream)), "sharq_prepare")
+    return out
+
+
+def sharq_linear(act: SharqAct, weight: SharqWeight, out=None, out_dtype: int = OUT_F32, stream=None):
+    """Y [M, N] = sparse FP4 GEMM + dense FP4 GEMM over the shared payload, one epilogue."""
+    torch = _torch()
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty(act.M, weight.N, dtype=dt, device=act.s_codes.device)
+    if out.dtype != dt or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be 2-D with unit inner stride and the requested dtype")
+    lib = _lib.load()
+    _lib.check(lib.sharq_linear(C.byref(act.desc), C.byref(weight.desc), _ptr(out), out.stride(0), out_dtype,
+                                _stream_ptr(stream)), "sharq_linear")
+    return out

@@ -1,0 +1,229 @@
+// C ABI of the SharQ hot path: argument checks, size queries, dispatch.
+// Every check runs on the host before any HIP call, so invalid requests
+// launch nothing and leave outputs untouched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/sharq.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sharq_status fail(sharq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+sharq_status hip_fail(hipError_t e, const char* what) {
+  return fail(SHARQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// gfx950 check, once per device id (the only state the library keeps).
+constexpr int kMaxDev = 64;
+int g_arch_ok[kMaxDev];  // 0 unknown, 1 gfx950, -1 other
+std::mutex g_arch_mu;
+
+sharq_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDev) return fail(SHARQ_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    g_arch_ok[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  if (g_arch_ok[dev] != 1) return fail(SHARQ_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return SHARQ_OK;
+}
+
+sharq_status check_fmt(int32_t fmt) {
+  if (fmt == SHARQ_FMT_MXFP4) return SHARQ_OK;
+  if (fmt == SHARQ_FMT_NVFP4) return fail(SHARQ_ERR_UNSUPPORTED, "NVFP4 is not built in this library");
+  if (fmt == SHARQ_FMT_HIF4) return fail(SHARQ_ERR_UNSUPPORTED, "HiF4 is not defined on the SharQ pages");
+  return fail(SHARQ_ERR_INVALID_ARG, "unknown format %d", (int)fmt);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sharq_abi_version(void) { return SHARQ_ABI_VERSION; }
+
+const char* sharq_status_str(sharq_status s) {
+  switch (s) {
+    case SHARQ_OK: return "ok";
+    case SHARQ_ERR_INVALID_ARG: return "invalid argument";
+    case SHARQ_ERR_UNSUPPORTED: return "unsupported";
+    case SHARQ_ERR_WORKSPACE: return "workspace too small";
+    case SHARQ_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* sharq_last_error(void) { return g_err; }
+
+sharq_status sharq_weight_bytes(int64_t N, int64_t K, int32_t fmt, size_t* codes_bytes,
+                                size_t* scales_bytes) {
+  g_err[0] = 0;
+  if (!codes_bytes || !scales_bytes) return fail(SHARQ_ERR_INVALID_ARG, "null output pointer");
+  if (N <= 0 || K <= 0) return fail(SHARQ_ERR_INVALID_ARG, "N and K must be positive (N=%lld K=%lld)", (long long)N, (long long)K);
+  if (K % 32) return fail(SHARQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 32", (long long)K);
+  sharq_status s = check_fmt(fmt);
+  if (s) return s;
+  *codes_bytes = (size_t)N * (size_t)(K / 2);
+  *scales_bytes = (size_t)N * (size_t)(K / 32);
+  return SHARQ_OK;
+}
+
+sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t fmt, size_t sizes[5]) {
+  g_err[0] = 0;
+  if (!sizes) return fail(SHARQ_ERR_INVALID_ARG, "null output pointer");
+  if (M < 0 || K <= 0) return fail(SHARQ_ERR_INVALID_ARG, "bad shape M=%lld K=%lld", (long long)M, (long long)K);
+  if (K % 32) return fail(SHARQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 32", (long long)K);
+  if (n != 2 || m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built (got %d:%d)", (int)n, (int)m);
+  sharq_status s = check_fmt(fmt);
+  if (s) return s;
+  sizes[0] = (size_t)M * (size_t)(K / 4);
+  sizes[1] = (size_t)M * (size_t)(K / 8);
+  sizes[2] = (size_t)M * (size_t)(K / 32);
+  sizes[3] = (size_t)M * (size_t)(K / 2);
+  sizes[4] = (size_t)M * (size_t)(K / 32);
+  return SHARQ_OK;
+}
+
+sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int64_t ldw, int32_t fmt,
+                               sharq_weight* out, void* stream) {
+  g_err[0] = 0;
+  if (!w_bf16_dev || !out) return fail(SHARQ_ERR_INVALID_ARG, "null pointer");
+  if (out->struct_size != sizeof(sharq_weight))
+    return fail(SHARQ_ERR_INVALID_ARG, "sharq_weight.struct_size %u != %zu", out->struct_size, sizeof(sharq_weight));
+  if (!out->codes || !out->scales) return fail(SHARQ_ERR_INVALID_ARG, "weight buffers not set");
+  if (N <= 0 || K <= 0 || K % 32) return fail(SHARQ_ERR_INVALID_ARG, "bad shape N=%lld K=%lld (K%%32 must be 0)", (long long)N, (long long)K);
+  if (K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "K too large");
+  if (ldw < K || ldw % 8) return fail(SHARQ_ERR_INVALID_ARG, "ldw=%lld must be >= K and a multiple of 8", (long long)ldw);
+  if (!aligned(w_bf16_dev, 16)) return fail(SHARQ_ERR_INVALID_ARG, "weight not 16-byte aligned");
+  if (!aligned(out->codes, 16)) return fail(SHARQ_ERR_INVALID_ARG, "codes buffer not 16-byte aligned");
+  sharq_status s = check_fmt(fmt);
+  if (s) return s;
+  s = check_device();
+  if (s) return s;
+  hipError_t e = sharq::launch_pack_weight(static_cast<const uint16_t*>(w_bf16_dev), N, (int)K, ldw, out->codes,
+                                           out->scales, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack_weight launch");
+  out->layout_version = SHARQ_ABI_VERSION;
+  out->N = N;
+  out->K = K;
+  out->fmt = fmt;
+  for (int p = 0; p < 2; ++p) {
+    out->view[p].base = out->scales;
+    out->view[p].ld = K / 32;
+    out->view[p].block = 32;
+    out->view[p].reserved = 0;
+  }
+  return SHARQ_OK;
+}
+
+sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx, const void* gamma_bf16_dev,
+                           float eps, int32_t n, int32_t m, int32_t fmt, sharq_act* out, void* stream) {
+  g_err[0] = 0;
+  if (!out) return fail(SHARQ_ERR_INVALID_ARG, "null output descriptor");
+  if (out->struct_size != sizeof(sharq_act))
+    return fail(SHARQ_ERR_INVALID_ARG, "sharq_act.struct_size %u != %zu", out->struct_size, sizeof(sharq_act));
+  if (M < 0 || K <= 0 || K % 32) return fail(SHARQ_ERR_INVALID_ARG, "bad shape M=%lld K=%lld (K%%32 must be 0)", (long long)M, (long long)K);
+  if (K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "K too large");
+  if (gamma_bf16_dev && K > 32768) return fail(SHARQ_ERR_INVALID_ARG, "RMSNorm rows are limited to K <= 32768");
+  if (n != 2 || m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built (got %d:%d)", (int)n, (int)m);
+  sharq_status s = check_fmt(fmt);
+  if (s) return s;
+  if (M > 0) {
+    if (!x_bf16_dev) return fail(SHARQ_ERR_INVALID_ARG, "null activation pointer");
+    if (!out->s_codes || !out->s_meta || !out->s_scales || !out->r_codes || !out->r_scales)
+      return fail(SHARQ_ERR_INVALID_ARG, "activation output buffers not set");
+    if (ldx < K || ldx % 8) return fail(SHARQ_ERR_INVALID_ARG, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
+    if (!aligned(x_bf16_dev, 16)) return fail(SHARQ_ERR_INVALID_ARG, "activation not 16-byte aligned");
+    if (gamma_bf16_dev && !aligned(gamma_bf16_dev, 16)) return fail(SHARQ_ERR_INVALID_ARG, "gamma not 16-byte aligned");
+    if (!aligned(out->s_codes, 16) || !aligned(out->s_meta, 16) || !aligned(out->r_codes, 16))
+      return fail(SHARQ_ERR_INVALID_ARG, "activation output buffers must be 16-byte aligned");
+    s = check_device();
+    if (s) return s;
+    sharq::PrepOut po{out->s_codes, out->s_meta, out->s_scales, out->r_codes, out->r_scales};
+    hipError_t e = sharq::launch_prepare(static_cast<const uint16_t*>(x_bf16_dev), M, (int)K, ldx,
+                                         static_cast<const uint16_t*>(gamma_bf16_dev), eps, po,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prepare launch");
+  }
+  out->layout_version = SHARQ_ABI_VERSION;
+  out->M = M;
+  out->K = K;
+  out->n = n;
+  out->m = m;
+  out->fmt = fmt;
+  return SHARQ_OK;
+}
+
+sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev, int64_t ldy, int32_t out_dtype,
+                          void* stream) {
+  g_err[0] = 0;
+  if (!a || !w) return fail(SHARQ_ERR_INVALID_ARG, "null descriptor");
+  if (a->struct_size != sizeof(sharq_act) || w->struct_size != sizeof(sharq_weight))
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor struct_size mismatch");
+  if (a->layout_version != SHARQ_ABI_VERSION || w->layout_version != SHARQ_ABI_VERSION)
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor layout_version mismatch (not produced by this library?)");
+  if (a->K != w->K) return fail(SHARQ_ERR_INVALID_ARG, "K mismatch: activation %lld, weight %lld", (long long)a->K, (long long)w->K);
+  if (a->M < 0 || w->N <= 0 || a->K <= 0 || a->K % 32) return fail(SHARQ_ERR_INVALID_ARG, "bad shapes");
+  if (a->K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "K too large");
+  if (out_dtype != SHARQ_OUT_F32 && out_dtype != SHARQ_OUT_BF16) return fail(SHARQ_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
+  if (a->n != 2 || a->m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built");
+  if (a->fmt != w->fmt) return fail(SHARQ_ERR_INVALID_ARG, "activation and weight formats differ");
+  sharq_status s = check_fmt(a->fmt);
+  if (s) return s;
+  if (a->M == 0) return SHARQ_OK;
+  if (!y_dev) return fail(SHARQ_ERR_INVALID_ARG, "null output pointer");
+  if (ldy < w->N) return fail(SHARQ_ERR_INVALID_ARG, "ldy=%lld < N=%lld", (long long)ldy, (long long)w->N);
+  if (!aligned(y_dev, out_dtype == SHARQ_OUT_F32 ? 4 : 2)) return fail(SHARQ_ERR_INVALID_ARG, "output misaligned");
+  if (!a->s_codes || !a->s_meta || !a->s_scales || !a->r_codes || !a->r_scales || !w->codes)
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor buffers not set");
+  if (!aligned(a->s_codes, 16) || !aligned(a->s_meta, 16) || !aligned(a->r_codes, 16) || !aligned(w->codes, 16))
+    return fail(SHARQ_ERR_INVALID_ARG, "code buffers must be 16-byte aligned");
+  const sharq_scale_view& vs = w->view[SHARQ_PATH_SPARSE];
+  const sharq_scale_view& vd = w->view[SHARQ_PATH_DENSE];
+  if (!vs.base || !vd.base || vs.block != 32 || vd.block != 32 || vs.ld != vd.ld || vs.ld < w->K / 32)
+    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be MX (block 32) with one row stride >= K/32");
+  s = check_device();
+  if (s) return s;
+  sharq::GemmArgs g;
+  g.s_codes = a->s_codes;
+  g.s_meta = a->s_meta;
+  g.s_scales = a->s_scales;
+  g.r_codes = a->r_codes;
+  g.r_scales = a->r_scales;
+  g.w_codes = w->codes;
+  g.w_scales_sparse = vs.base;
+  g.w_scales_dense = vd.base;
+  g.w_scales_ld = vs.ld;
+  g.y = y_dev;
+  g.ldy = ldy;
+  g.M = a->M;
+  g.N = w->N;
+  g.K = (int)a->K;
+  g.out_bf16 = out_dtype == SHARQ_OUT_BF16;
+  hipError_t e = sharq::launch_linear(g, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  return SHARQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Device helpers shared by the SharQ kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sharq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------- DPP lane exchange
+// Row-local permutes; every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over the 64 lanes whose partial results equal a balanced pairwise tree
+// in lane order: at every step each lane adds the sum of the neighbouring
+// aligned lane group of the same size (x + y == y + x bit for bit, so the
+// mirrors used once groups are uniform give exactly T[left] + T[right]).
+__device__ __forceinline__ float wave_tree_sum(float s) {
+  s = s + dpp_f32<kQuadXor1>(s);
+  s = s + dpp_f32<kQuadXor2>(s);
+  s = s + dpp_f32<kRowHalfMirror>(s);
+  s = s + dpp_f32<kRowMirror>(s);
+  s = s + __shfl_xor(s, 16, kWave);
+  s = s + __shfl_xor(s, 32, kWave);
+  return s;
+}
+
+// max over the 4 lanes of an aligned quad
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kQuadXor1>(v));
+  v = max(v, dpp_u32<kQuadXor2>(v));
+  return v;
+}
+
+// ---------------------------------------------------------------- MXFP4 scale
+// Shared exponent of a block with largest magnitude `amax_bits` (binary32 bits,
+// sign cleared): e = clamp(floor(log2 amax) - 2, -127, 127); 0 -> -127.
+// floor(log2) comes from the bit pattern: biased exponent - 127 for normals,
+// top mantissa bit position - 149 for subnormals.
+__device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits) {
+  int fl;
+  uint32_t ex = amax_bits >> 23;
+  if (ex != 0) fl = (int)ex - 127;
+  else fl = (31 - __clz((int)amax_bits)) - 149;   // amax_bits == 0 -> very negative
+  int e = fl - 2;
+  e = e < -127 ? -127 : e;
+  return e;   // finite inputs give e <= 125
+}
+// 2^-e as binary32 (normal for every e in [-127, 125])
+__device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+// 2^e as binary32 (subnormal 2^-127 for e == -127)
+__device__ __forceinline__ float pow2(int e) {
+  return e >= -126 ? __uint_as_float((uint32_t)(127 + e) << 23) : __uint_as_float(0x00400000u);
+}
+
+// ---------------------------------------------------------------- E2M1
+// Two binary32 values -> two E2M1 nibbles placed in byte SEL of `old`.
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to nearest, ties to even,
+// saturates at 6 and keeps the sign of zero; it was checked equal to that rule
+// on every finite binary32 input.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pack2(uint32_t old, float lo, float hi) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, 1.0f, SEL);
+}
+// E2M1 nibbles of byte SEL of `packed` -> two binary32 values (exact).
+template <int SEL>
+__device__ __forceinline__ void fp4_unpack2(uint32_t packed, float& lo, float& hi) {
+  auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, SEL);
+  lo = v[0];
+  hi = v[1];
+}
+
+}  // namespace sharq

@@ -1,0 +1,179 @@
+/*
+ * sharq.h -- C ABI of the SharQ linear-layer hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The method (SharQ paper page, "SharQ: Bridging Activation Sparsity and FP4
+ * Quantization for LLM Inference", Abstract): each activation row is split online
+ * into an N:M-masked sparse backbone S, quantised to FP4, and a dense residual R
+ * taken against the *quantised* backbone, also quantised to FP4.  A sparse FP4
+ * GEMM on Q(S) and a dense FP4 GEMM on Q(R) read one shared FP4 weight payload,
+ * and one epilogue sums them.  The preparation (normalisation, mask, residual,
+ * both quantisations) is one fused operator.  The README page of the SharQ
+ * repository (section "Evaluation") names the fused normalisation RMSNorm.
+ *
+ * Conventions for every entry point:
+ *  - Ownership: the caller allocates every buffer (sizes from the *_bytes
+ *    queries).  The library never allocates, frees or keeps device memory and
+ *    holds no mutable global state other than a thread-local error string and
+ *    a per-device architecture check, so it is reentrant.
+ *  - Pointers named *_dev are device pointers; struct fields are device
+ *    pointers unless stated.  `stream` is a hipStream_t (NULL = the null stream).
+ *  - Ordering: every call is asynchronous on `stream`; nothing synchronises
+ *    the host.
+ *  - Errors: arguments are checked on the host before anything is launched; on
+ *    any error nothing is launched and outputs are untouched.  No C++ exception
+ *    crosses this ABI.  sharq_last_error() gives a thread-local detail string.
+ *  - Inputs must be finite (NaN/Inf give unspecified codes).
+ *  - Layouts are row-major with the K (reduction) index fastest.  FP4 codes
+ *    are E2M1 nibbles, two per byte, the lower k in the low nibble; the sign
+ *    is nibble bit 3.  E8M0 scale bytes encode 2^(byte-127).
+ */
+#ifndef SHARQ_H
+#define SHARQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SHARQ_ABI_VERSION 1
+
+typedef enum {
+  SHARQ_OK = 0,
+  SHARQ_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad enum */
+  SHARQ_ERR_UNSUPPORTED = 2, /* valid request this build does not run (e.g. HiF4, N:M != 2:4, not gfx950) */
+  SHARQ_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  SHARQ_ERR_HIP = 4          /* a HIP runtime call or launch failed; detail in sharq_last_error() */
+} sharq_status;
+
+/* FP4 formats named by the SharQ abstract (it reports results in NVFP4, HiF4
+ * and MXFP4).  MXFP4 = OCP Microscaling v1.0: 32-element blocks, E8M0 scale.
+ * NVFP4 and HiF4 are declared for the format slot; this build returns
+ * SHARQ_ERR_UNSUPPORTED for them (HiF4 is not defined on the pages). */
+typedef enum { SHARQ_FMT_MXFP4 = 0, SHARQ_FMT_NVFP4 = 1, SHARQ_FMT_HIF4 = 2 } sharq_format;
+
+typedef enum { SHARQ_OUT_F32 = 0, SHARQ_OUT_BF16 = 1 } sharq_out_dtype;
+
+/* Which GEMM path a weight scale view serves (SharQ abstract: the two paths
+ * share one FP4 weight payload through path-specific scale views). */
+typedef enum { SHARQ_PATH_SPARSE = 0, SHARQ_PATH_DENSE = 1 } sharq_path;
+
+/* A scale view: how one GEMM path reads the weight's block scales.
+ * base: device pointer to E8M0 bytes; ld: bytes between rows n; block: K
+ * elements per scale byte.  On gfx950 both paths run the same block-scaled
+ * MFMA on dense 4-bit operands (the sparse operand is expanded on chip), so
+ * sharq_pack_weight sets both views to the same array and layout. */
+typedef struct {
+  const uint8_t* base;
+  int64_t ld;
+  int32_t block;
+  int32_t reserved;
+} sharq_scale_view;
+
+/* Packed weight W[N,K] (nn.Linear orientation: out x in; Y = X W^T).
+ * The caller sets codes/scales to buffers of the queried sizes; sharq_pack_weight
+ * fills them and every other field. */
+typedef struct {
+  uint32_t struct_size;     /* sizeof(sharq_weight) */
+  uint32_t layout_version;  /* SHARQ_ABI_VERSION */
+  int64_t N, K;
+  int32_t fmt;              /* sharq_format */
+  int32_t reserved;
+  uint8_t* codes;           /* [N][K/2] E2M1, the single FP4 payload both paths read */
+  uint8_t* scales;          /* [N][K/32] E8M0 */
+  sharq_scale_view view[2]; /* indexed by sharq_path */
+} sharq_weight;
+
+/* Prepared activation (output of sharq_prepare).  For 2:4 and MXFP4:
+ *   s_codes  [M][K/4]   E2M1 of the kept S entries in k order
+ *   s_meta   [M][K/8]   per group of 4 the kept offsets i0<i1 as nibble i0|i1<<2,
+ *                       group j in byte j/2 (low nibble for even j)
+ *   s_scales [M][K/32]  E8M0 of S per 32 logical positions
+ *   r_codes  [M][K/2]   E2M1 of R
+ *   r_scales [M][K/32]  E8M0 of R
+ * Row strides are the packed widths above (rows are contiguous). */
+typedef struct {
+  uint32_t struct_size;     /* sizeof(sharq_act) */
+  uint32_t layout_version;  /* SHARQ_ABI_VERSION */
+  int64_t M, K;
+  int32_t n, m;             /* N:M pattern of the backbone mask */
+  int32_t fmt;              /* sharq_format */
+  int32_t reserved;
+  uint8_t* s_codes;
+  uint8_t* s_meta;
+  uint8_t* s_scales;
+  uint8_t* r_codes;
+  uint8_t* r_scales;
+} sharq_act;
+
+/* ABI version of the loaded library (SHARQ_ABI_VERSION). */
+int sharq_abi_version(void);
+
+/* Text of a status code (static storage). */
+const char* sharq_status_str(sharq_status s);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* sharq_last_error(void);
+
+/* Byte sizes of the packed weight buffers for W[N,K] in `fmt`.
+ * Errors: INVALID_ARG for N<=0, K<=0, K%32, null outputs; UNSUPPORTED for NVFP4/HiF4. */
+sharq_status sharq_weight_bytes(int64_t N, int64_t K, int32_t fmt,
+                                size_t* codes_bytes, size_t* scales_bytes);
+
+/* Byte sizes of the five prepared-activation buffers, in the order
+ * s_codes, s_meta, s_scales, r_codes, r_scales.  M == 0 gives zeros.
+ * Errors: INVALID_ARG for M<0, K<=0, K%32, null output; UNSUPPORTED unless
+ * (n,m) == (2,4) and fmt == MXFP4. */
+sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t fmt,
+                             size_t sizes[5]);
+
+/* Pack W[N,K] (bf16, row stride ldw elements) into the single FP4 weight
+ * payload: per row n and 32-block b, E = floor(log2 amax)-2 (E8M0, clamped)
+ * and E2M1 codes of w/2^E (round to nearest, ties to even, saturating at 6).
+ * SharQ abstract: both GEMM paths read this one payload.
+ * `out` must have struct_size set and codes/scales pointing at buffers of the
+ * sizes given by sharq_weight_bytes; N, K, fmt and both views are filled in.
+ * Errors: INVALID_ARG (null, N<=0, K<=0, K%32, ldw<K, w not 16-B aligned or
+ * ldw%8), UNSUPPORTED (fmt != MXFP4, device not gfx950), HIP. */
+sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int64_t ldw,
+                               int32_t fmt, sharq_weight* out, void* stream);
+
+/* Fused preparation of X[M,K] (bf16, row stride ldx elements), one pass:
+ *   v = RMSNorm(x) * gamma (binary32; skipped when gamma_bf16_dev is NULL):
+ *       ss = pairwise tree sum of x^2 in index order over the row zero-padded
+ *       to a power of two; inv = 1/sqrt(ss/K + eps), each op correctly rounded;
+ *       v = (x*inv)*gamma;
+ *   mask: in each group of 4 along K keep the 2 largest |v| (ties: lower index);
+ *   S = v on kept entries, 0 elsewhere; Q(S) = MXFP4 over 32 logical positions;
+ *   R = v - deq(Q(S)) (exact in binary32); Q(R) = MXFP4.
+ * SharQ abstract: one fused operator absorbs mask generation, residual
+ * construction and the normalisation; the residual is relative to the
+ * quantised backbone.
+ * `out` must have struct_size set and the five buffers allocated per
+ * sharq_act_bytes; M, K, n, m, fmt are filled in.  M == 0 launches nothing.
+ * Errors: INVALID_ARG (null, K<=0, K%32, K>32768 with gamma, ldx<K, x not
+ * 16-B aligned or ldx%8, gamma misaligned), UNSUPPORTED ((n,m) != (2,4),
+ * fmt != MXFP4, not gfx950), HIP. */
+sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx,
+                           const void* gamma_bf16_dev, float eps,
+                           int32_t n, int32_t m, int32_t fmt,
+                           sharq_act* out, void* stream);
+
+/* Y[M,N] = deq(Q(S)) deq(W)^T + deq(Q(R)) deq(W)^T with one epilogue store.
+ * SharQ abstract: a sparse FP4 GEMM on the backbone and a dense FP4 GEMM on
+ * the residual; README "Benchmarks": the epilogue fusion sums them.
+ * On gfx950 the compressed 2:4 operand is expanded to dense 4-bit codes on
+ * chip and both paths run block-scaled MXFP4 MFMA into one fp32 accumulator,
+ * reading each weight tile once for both paths.
+ * y: device, fp32 or bf16 per out_dtype, row stride ldy elements (>= N).
+ * Errors: INVALID_ARG (null, K mismatch, ldy<N, misaligned y),
+ * UNSUPPORTED (fmt, pattern, not gfx950), HIP. */
+sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w,
+                          void* y_dev, int64_t ldy, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHARQ_H */

@@ -86,9 +86,10 @@ def rmsnorm(x_bits, gamma_bits, eps: float) -> np.ndarray:
     if gamma_bits is None:
         return x.copy()
     K = x.shape[-1]
-    ss = pairwise_tree_sum_f32(x * x)
-    mean = ss / F32(K)
-    inv = F32(1.0) / np.sqrt(mean + F32(eps))
+    with np.errstate(over="ignore", divide="ignore"):    # IEEE overflow to inf is part of the definition
+        ss = pairwise_tree_sum_f32(x * x)
+        mean = ss / F32(K)
+        inv = F32(1.0) / np.sqrt(mean + F32(eps))
     g = widen_bf16(gamma_bits)
     return (x * inv[..., None]) * g
 

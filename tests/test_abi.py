@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every function include/sharq.h declares,
+answers size queries, and rejects invalid requests on the host before any HIP
+call (CPU only: no compute call is made)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp4_sparse_dense_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sharq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sharq_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libsharq.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_exports_match_header(lib):
+    decl = declared_functions()
+    assert "sharq_prepare" in decl and "sharq_linear" in decl and "sharq_pack_weight" in decl
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sharq_[a-z_0-9]+)", out))
+    assert set(decl) <= exported, set(decl) - exported
+    assert set(_lib.PROTOTYPES) == set(decl)
+    for name in decl:
+        getattr(lib, name)
+
+
+def test_struct_sizes_match_c_layout():
+    # sharq_scale_view: ptr + i64 + 2*i32 ; weight: 2*u32 + 2*i64 + 2*i32 + 2 ptr + 2 views
+    assert C.sizeof(_lib.ScaleView) == 24
+    assert C.sizeof(_lib.WeightDesc) == 8 + 16 + 8 + 16 + 48
+    assert C.sizeof(_lib.ActDesc) == 8 + 16 + 8 + 8 + 40
+
+
+def test_status_strings(lib):
+    assert lib.sharq_abi_version() == _lib.SHARQ_ABI_VERSION
+    assert lib.sharq_status_str(0) == b"ok"
+    assert lib.sharq_status_str(2) == b"unsupported"
+
+
+def test_size_queries(lib):
+    cb, sb = C.c_size_t(), C.c_size_t()
+    assert lib.sharq_weight_bytes(6144, 4096, 0, C.byref(cb), C.byref(sb)) == 0
+    assert (cb.value, sb.value) == (6144 * 2048, 6144 * 128)
+    sizes = (C.c_size_t * 5)()
+    assert lib.sharq_act_bytes(2048, 4096, 2, 4, 0, sizes) == 0
+    assert list(sizes) == [2048 * 1024, 2048 * 512, 2048 * 128, 2048 * 2048, 2048 * 128]
+    # prep writes 0.9375 B per element
+    assert sum(sizes) == int(2048 * 4096 * 0.9375)
+    assert lib.sharq_act_bytes(0, 4096, 2, 4, 0, sizes) == 0 and sum(sizes) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((2048, 4008, 2, 4, 0), _lib.ERR_INVALID_ARG),   # K % 32
+    ((2048, 0, 2, 4, 0), _lib.ERR_INVALID_ARG),
+    ((-1, 4096, 2, 4, 0), _lib.ERR_INVALID_ARG),
+    ((16, 4096, 1, 4, 0), _lib.ERR_UNSUPPORTED),     # only 2:4
+    ((16, 4096, 2, 4, 1), _lib.ERR_UNSUPPORTED),     # NVFP4 not built
+    ((16, 4096, 2, 4, 2), _lib.ERR_UNSUPPORTED),     # HiF4 undefined
+    ((16, 4096, 2, 4, 7), _lib.ERR_INVALID_ARG),
+])
+def test_act_bytes_errors(lib, args, status):
+    sizes = (C.c_size_t * 5)(*([123] * 5))
+    assert lib.sharq_act_bytes(*args, sizes) == status
+    assert list(sizes) == [123] * 5            # outputs untouched
+    assert lib.sharq_last_error() != b""
+
+
+def _act(M=16, K=256, **over):
+    a = _lib.ActDesc()
+    a.struct_size = C.sizeof(_lib.ActDesc)
+    for i, f in enumerate(("s_codes", "s_meta", "s_scales", "r_codes", "r_scales")):
+        setattr(a, f, 0x10000 * (i + 1))
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_prepare_rejects_before_launch(lib):
+    x = C.c_void_p(0x100000)
+    # bad struct size
+    a = _act(struct_size=3)
+    assert lib.sharq_prepare(x, 16, 256, 256, None, 1e-5, 2, 4, 0, C.byref(a), None) == _lib.ERR_INVALID_ARG
+    a = _act()
+    assert lib.sharq_prepare(x, 16, 250, 256, None, 1e-5, 2, 4, 0, C.byref(a), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_prepare(x, 16, 256, 200, None, 1e-5, 2, 4, 0, C.byref(a), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_prepare(C.c_void_p(0x100002), 16, 256, 256, None, 1e-5, 2, 4, 0, C.byref(a), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_prepare(x, 16, 256, 256, None, 1e-5, 3, 4, 0, C.byref(a), None) == _lib.ERR_UNSUPPORTED
+    assert lib.sharq_prepare(x, 16, 256, 256, None, 1e-5, 2, 4, 2, C.byref(a), None) == _lib.ERR_UNSUPPORTED
+    assert lib.sharq_prepare(x, 16, 65536, 65536, C.c_void_p(0x200000), 1e-5, 2, 4, 0, C.byref(a), None) == _lib.ERR_INVALID_ARG
+    b = _act(s_meta=0)
+    assert lib.sharq_prepare(x, 16, 256, 256, None, 1e-5, 2, 4, 0, C.byref(b), None) == _lib.ERR_INVALID_ARG
+    assert b.M == 0 and b.layout_version == 0     # descriptor untouched on error
+    # M == 0 is a valid no-op: no device is touched
+    z = _act()
+    assert lib.sharq_prepare(None, 0, 256, 256, None, 1e-5, 2, 4, 0, C.byref(z), None) == _lib.OK
+    assert z.M == 0 and z.K == 256 and z.layout_version == _lib.SHARQ_ABI_VERSION
+
+
+def test_pack_and_linear_reject_before_launch(lib):
+    w = _lib.WeightDesc()
+    w.struct_size = C.sizeof(_lib.WeightDesc)
+    w.codes, w.scales = 0x100000, 0x200000
+    src = C.c_void_p(0x300000)
+    assert lib.sharq_pack_weight(src, 16, 250, 256, 0, C.byref(w), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_pack_weight(src, 0, 256, 256, 0, C.byref(w), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_pack_weight(src, 16, 256, 100, 0, C.byref(w), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_pack_weight(src, 16, 256, 256, 1, C.byref(w), None) == _lib.ERR_UNSUPPORTED
+    # linear: descriptors that were never filled by the library are refused
+    a = _act()
+    assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 16, 0, None) == _lib.ERR_INVALID_ARG
+    a.layout_version = w.layout_version = _lib.SHARQ_ABI_VERSION
+    a.M, a.K, a.n, a.m, w.N, w.K = 16, 256, 2, 4, 32, 512
+    assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 0, None) == _lib.ERR_INVALID_ARG
+    w.K = 256
+    assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 16, 0, None) == _lib.ERR_INVALID_ARG  # ldy < N
+    assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 5, None) == _lib.ERR_INVALID_ARG
+    # scale views must describe the MX payload
+    assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 0, None) == _lib.ERR_INVALID_ARG
+    a.M = 0
+    assert lib.sharq_linear(C.byref(a), C.byref(w), None, 32, 0, None) == _lib.OK

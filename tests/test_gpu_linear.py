@@ -1,0 +1,94 @@
+"""GPU parity of the dual FP4 GEMM: |y_gpu - y_ref| <= 1e-5 * sum|terms| + 1e-6
+elementwise against the float64 oracle, on full outputs for small shapes and on
+sampled rows/columns of the full-size workloads."""
+import numpy as np
+import pytest
+
+import fp4_sparse_dense_amd as sq
+from fp4_sparse_dense_amd import synth
+from oracle import sharq_oracle as O
+from tests.gpu_helpers import assert_linear_close, assert_prep_equal, dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_layer(x, gamma, w, eps=1e-5, out_dtype=sq.OUT_F32):
+    import torch
+    act = sq.sharq_prepare(dev_bf16(x), dev_bf16(gamma) if gamma is not None else None, eps)
+    wt = sq.sharq_pack_weight(dev_bf16(w))
+    y = sq.sharq_linear(act, wt, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return act, wt, y
+
+
+def test_linear_tiny_full():
+    print("linear tiny", flush=True)
+    inp = synth.layer_inputs("tiny", seed=0)
+    act, wt, y = gpu_layer(inp["x"], inp["gamma"], inp["w"])
+    ref = O.prepare(inp["x"], inp["gamma"], inp["eps"])
+    assert_prep_equal(act.host(), ref, "tiny")
+    wc, ws = O.pack_weight(inp["w"])
+    yr, b = O.linear(ref, wc, ws)
+    assert_linear_close(y.cpu().numpy(), yr, b, "tiny")
+
+
+@pytest.mark.parametrize("M,K,N,norm", [(37, 96, 53, True), (1, 4096, 4096, False), (130, 768, 200, False),
+                                        (64, 4096, 4096, False), (17, 2048, 1536, False), (256, 256, 272, True)])
+def test_linear_ragged_full(M, K, N, norm):
+    print(f"linear M={M} K={K} N={N}", flush=True)
+    rng = np.random.default_rng(M + K + N)
+    x = synth.outlier_activations(rng, M, K)
+    g = synth.norm_weight(rng, K) if norm else None
+    w = synth.linear_weight(rng, N, K)
+    act, wt, y = gpu_layer(x, g, w)
+    ref = O.prepare(x, g, 1e-5)
+    wc, ws = O.pack_weight(w)
+    yr, b = O.linear(ref, wc, ws)
+    assert_linear_close(y.cpu().numpy(), yr, b, f"M={M} K={K} N={N}")
+
+
+def _sample_rows(M, rng, n=24):
+    return np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), rng.choice(M, n, replace=False)]))
+
+
+@pytest.mark.parametrize("name,ncols", [("qkv", None), ("down", None), ("gateup", 2048)])
+def test_linear_workloads_sampled(name, ncols):
+    """Full-size GEMM on the GPU; the oracle recomputes sampled rows (and, for the
+    widest layer, sampled columns) one by one."""
+    print(f"linear {name}", flush=True)
+    inp = synth.layer_inputs(name, seed=0)
+    act, wt, y = gpu_layer(inp["x"], inp["gamma"], inp["w"])
+    rng = np.random.default_rng(1)
+    rows = _sample_rows(inp["M"], rng)
+    cols = np.arange(inp["N"]) if ncols is None else np.unique(np.concatenate(
+        [np.arange(16), np.arange(inp["N"] - 16, inp["N"]), rng.choice(inp["N"], ncols, replace=False)]))
+    ref = O.prepare(inp["x"][rows], inp["gamma"], inp["eps"])
+    wc, ws = O.pack_weight(inp["w"][cols])
+    yr, b = O.linear(ref, wc, ws)
+    yg = y.cpu().numpy()[np.ix_(rows, cols)]
+    assert_linear_close(yg, yr, b, name)
+
+
+def test_linear_bf16_output():
+    inp = synth.layer_inputs("tiny", seed=0)
+    _, _, y = gpu_layer(inp["x"], inp["gamma"], inp["w"], out_dtype=sq.OUT_BF16)
+    ref = O.prepare(inp["x"], inp["gamma"], inp["eps"])
+    wc, ws = O.pack_weight(inp["w"])
+    yr, b = O.linear(ref, wc, ws)
+    import torch
+    yg = y.float().cpu().numpy()
+    half_ulp = np.abs(yr) * 2.0 ** -8
+    assert_linear_close(yg, yr, b, "bf16 out", extra=half_ulp)
+
+
+def test_linear_deterministic_and_strided_output():
+    import torch
+    inp = synth.layer_inputs("qkv", seed=1, M=256)
+    act = sq.sharq_prepare(dev_bf16(inp["x"]), dev_bf16(inp["gamma"]))
+    wt = sq.sharq_pack_weight(dev_bf16(inp["w"]))
+    y1 = sq.sharq_linear(act, wt)
+    big = torch.full((256, inp["N"] + 64), 7.0, device="cuda")
+    y2 = sq.sharq_linear(act, wt, out=big[:, 32:32 + inp["N"]])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.all(big[:, :32] == 7.0) and torch.all(big[:, 32 + inp["N"]:] == 7.0)
