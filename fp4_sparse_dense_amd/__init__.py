@@ -53,13 +53,14 @@ def act_bytes(M: int, K: int, n: int = 2, m: int = 4, fmt: int = FMT_MXFP4):
 
 
 class SharqWeight:
-    """Packed weight: device tensors codes [N, K/2] and scales [N, K/32] plus the descriptor."""
+    """Packed weight: flat device byte tensors `codes` and `scales` in the tiled
+    layout of include/sharq.h, plus the descriptor."""
 
     def __init__(self, N: int, K: int, device, fmt: int = FMT_MXFP4):
         torch = _torch()
         cb, sb = weight_bytes(N, K, fmt)
-        self.codes = torch.empty(cb, dtype=torch.uint8, device=device).view(N, K // 2)
-        self.scales = torch.empty(sb, dtype=torch.uint8, device=device).view(N, K // 32)
+        self.codes = torch.empty(cb, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(sb, dtype=torch.uint8, device=device)
         self.desc = _lib.WeightDesc()
         self.desc.struct_size = C.sizeof(_lib.WeightDesc)
         self.desc.codes = self.codes.data_ptr()
@@ -68,25 +69,25 @@ class SharqWeight:
 
 
 class SharqAct:
-    """Prepared activation: five device byte tensors plus the descriptor."""
+    """Prepared activation: five flat device byte tensors in the tiled layout of
+    include/sharq.h, plus the descriptor."""
 
     FIELDS = ("s_codes", "s_meta", "s_scales", "r_codes", "r_scales")
 
     def __init__(self, M: int, K: int, device, n: int = 2, m: int = 4, fmt: int = FMT_MXFP4):
         torch = _torch()
         sizes = act_bytes(M, K, n, m, fmt)
-        widths = (K // 4, K // 8, K // 32, K // 2, K // 32)
         self.desc = _lib.ActDesc()
         self.desc.struct_size = C.sizeof(_lib.ActDesc)
-        for name, size, wdt in zip(self.FIELDS, sizes, widths):
+        for name, size in zip(self.FIELDS, sizes):
             # keep every buffer 256-byte aligned even when empty
-            t = torch.empty(max(size, 1), dtype=torch.uint8, device=device)[:size].view(M, wdt)
+            t = torch.empty(max(size, 1), dtype=torch.uint8, device=device)[:size]
             setattr(self, name, t)
             setattr(self.desc, name, t.data_ptr())
         self.M, self.K, self.n, self.m, self.fmt = M, K, n, m, fmt
 
     def host(self) -> dict:
-        """Copies of the five byte arrays as numpy (for checks)."""
+        """Copies of the five tiled byte arrays as numpy."""
         return {f: getattr(self, f).cpu().numpy() for f in self.FIELDS}
 
 

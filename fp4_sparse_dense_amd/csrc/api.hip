@@ -84,8 +84,9 @@ sharq_status sharq_weight_bytes(int64_t N, int64_t K, int32_t fmt, size_t* codes
   if (K % 32) return fail(SHARQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 32", (long long)K);
   sharq_status s = check_fmt(fmt);
   if (s) return s;
-  *codes_bytes = (size_t)N * (size_t)(K / 2);
-  *scales_bytes = (size_t)N * (size_t)(K / 32);
+  const size_t nb = (size_t)((N + 15) / 16), kb = (size_t)((K + 127) / 128);
+  *codes_bytes = nb * kb * 1024;
+  *scales_bytes = nb * kb * 64;
   return SHARQ_OK;
 }
 
@@ -97,11 +98,12 @@ sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t
   if (n != 2 || m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built (got %d:%d)", (int)n, (int)m);
   sharq_status s = check_fmt(fmt);
   if (s) return s;
-  sizes[0] = (size_t)M * (size_t)(K / 4);
-  sizes[1] = (size_t)M * (size_t)(K / 8);
-  sizes[2] = (size_t)M * (size_t)(K / 32);
-  sizes[3] = (size_t)M * (size_t)(K / 2);
-  sizes[4] = (size_t)M * (size_t)(K / 32);
+  const size_t tiles = (size_t)((M + 15) / 16) * (size_t)((K + 127) / 128);
+  sizes[0] = tiles * 512;
+  sizes[1] = tiles * 256;
+  sizes[2] = tiles * 64;
+  sizes[3] = tiles * 1024;
+  sizes[4] = tiles * 64;
   return SHARQ_OK;
 }
 
@@ -116,7 +118,8 @@ sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int
   if (K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "K too large");
   if (ldw < K || ldw % 8) return fail(SHARQ_ERR_INVALID_ARG, "ldw=%lld must be >= K and a multiple of 8", (long long)ldw);
   if (!aligned(w_bf16_dev, 16)) return fail(SHARQ_ERR_INVALID_ARG, "weight not 16-byte aligned");
-  if (!aligned(out->codes, 16)) return fail(SHARQ_ERR_INVALID_ARG, "codes buffer not 16-byte aligned");
+  if (!aligned(out->codes, 16) || !aligned(out->scales, 16))
+    return fail(SHARQ_ERR_INVALID_ARG, "weight buffers must be 16-byte aligned");
   sharq_status s = check_fmt(fmt);
   if (s) return s;
   s = check_device();
@@ -130,7 +133,7 @@ sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int
   out->fmt = fmt;
   for (int p = 0; p < 2; ++p) {
     out->view[p].base = out->scales;
-    out->view[p].ld = K / 32;
+    out->view[p].ld = (N + 15) / 16 * 64;   // bytes between K tiles of the [KB][NB][64] scale array
     out->view[p].block = 32;
     out->view[p].reserved = 0;
   }
@@ -156,7 +159,8 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
     if (ldx < K || ldx % 8) return fail(SHARQ_ERR_INVALID_ARG, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
     if (!aligned(x_bf16_dev, 16)) return fail(SHARQ_ERR_INVALID_ARG, "activation not 16-byte aligned");
     if (gamma_bf16_dev && !aligned(gamma_bf16_dev, 16)) return fail(SHARQ_ERR_INVALID_ARG, "gamma not 16-byte aligned");
-    if (!aligned(out->s_codes, 16) || !aligned(out->s_meta, 16) || !aligned(out->r_codes, 16))
+    if (!aligned(out->s_codes, 16) || !aligned(out->s_meta, 16) || !aligned(out->r_codes, 16) ||
+        !aligned(out->s_scales, 16) || !aligned(out->r_scales, 16))
       return fail(SHARQ_ERR_INVALID_ARG, "activation output buffers must be 16-byte aligned");
     s = check_device();
     if (s) return s;
@@ -197,12 +201,15 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   if (!aligned(y_dev, out_dtype == SHARQ_OUT_F32 ? 4 : 2)) return fail(SHARQ_ERR_INVALID_ARG, "output misaligned");
   if (!a->s_codes || !a->s_meta || !a->s_scales || !a->r_codes || !a->r_scales || !w->codes)
     return fail(SHARQ_ERR_INVALID_ARG, "descriptor buffers not set");
-  if (!aligned(a->s_codes, 16) || !aligned(a->s_meta, 16) || !aligned(a->r_codes, 16) || !aligned(w->codes, 16))
-    return fail(SHARQ_ERR_INVALID_ARG, "code buffers must be 16-byte aligned");
+  if (!aligned(a->s_codes, 16) || !aligned(a->s_meta, 16) || !aligned(a->r_codes, 16) || !aligned(w->codes, 16) ||
+      !aligned(a->s_scales, 16) || !aligned(a->r_scales, 16))
+    return fail(SHARQ_ERR_INVALID_ARG, "operand buffers must be 16-byte aligned");
   const sharq_scale_view& vs = w->view[SHARQ_PATH_SPARSE];
   const sharq_scale_view& vd = w->view[SHARQ_PATH_DENSE];
-  if (!vs.base || !vd.base || vs.block != 32 || vd.block != 32 || vs.ld != vd.ld || vs.ld < w->K / 32)
-    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be MX (block 32) with one row stride >= K/32");
+  const int64_t nb64 = (w->N + 15) / 16 * 64;
+  if (!vs.base || !vd.base || vs.block != 32 || vd.block != 32 || vs.ld != nb64 || vd.ld != nb64 ||
+      !aligned(vs.base, 16) || !aligned(vd.base, 16))
+    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be tiled MX views (block 32, K-tile stride NB*64)");
   s = check_device();
   if (s) return s;
   sharq::GemmArgs g;

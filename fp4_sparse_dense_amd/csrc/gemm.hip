@@ -21,26 +21,6 @@
 
 namespace sharq {
 
-// Expand the compressed 2:4 operand of 32 logical K positions (8 groups):
-// codes = 16 kept nibbles (8 bytes, group g in byte g, lower offset in the low
-// nibble), meta = 8 nibbles (group g: i0 | i1<<2 at nibble g).  Result: 32
-// dense nibbles with zero codes at dropped positions.
-__device__ __forceinline__ uint32_t expand_pair(uint32_t cbytes, uint32_t mbyte) {
-  uint32_t b0 = cbytes & 0xFFu, b1 = (cbytes >> 8) & 0xFFu;
-  uint32_t m0 = mbyte & 0xFu, m1 = (mbyte >> 4) & 0xFu;
-  uint32_t o = ((b0 & 0xFu) << ((m0 & 3u) * 4u)) | ((b0 >> 4) << ((m0 >> 2) * 4u));
-  o |= (((b1 & 0xFu) << ((m1 & 3u) * 4u)) | ((b1 >> 4) << ((m1 >> 2) * 4u))) << 16;
-  return o;
-}
-__device__ __forceinline__ uint4 expand32(uint2 codes, uint32_t meta) {
-  uint4 d;
-  d.x = expand_pair(codes.x & 0xFFFFu, meta & 0xFFu);
-  d.y = expand_pair(codes.x >> 16, (meta >> 8) & 0xFFu);
-  d.z = expand_pair(codes.y & 0xFFFFu, (meta >> 16) & 0xFFu);
-  d.w = expand_pair(codes.y >> 16, meta >> 24);
-  return d;
-}
-
 __device__ __forceinline__ v8i as_operand(uint4 q) {
   v8i r;
   r[0] = (int)q.x; r[1] = (int)q.y; r[2] = (int)q.z; r[3] = (int)q.w;
@@ -52,15 +32,64 @@ __device__ __forceinline__ v4f mfma_fp4(v8i a, v8i b, v4f c, uint32_t sa, uint32
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
-// Reference-simple tiling: each wave owns WM x WN MFMA tiles (16x16 each) and
-// reads its fragments straight from global memory.  Block = 4 waves as 2x2.
+// ---------------------------------------------------------------------------
+// 2:4 expansion.  The compressed operand of 32 logical K positions (8 groups)
+// is 16 kept nibbles (group g in byte g, lower offset in the low nibble) plus
+// 8 metadata nibbles (group g: i0 | i1<<2 in nibble g).  The result is 32
+// dense nibbles with zero codes at dropped positions.  Two groups are handled
+// per dword, one in each 16-bit half, with byte permutes and packed shifts.
+// ---------------------------------------------------------------------------
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+template <int H>
+__device__ __forceinline__ uint32_t expand_dword(uint32_t cw, uint32_t mb4, int j) {
+  // code bytes 2H and 2H+1 of cw -> low byte of half 0 and half 1
+  constexpr uint32_t sel = H == 0 ? 0x0C010C00u : 0x0C030C02u;
+  const uint32_t d = __builtin_amdgcn_perm(0u, cw, sel);
+  const uint32_t lo = d & 0x000F000Fu, hi = d & 0x00F000F0u;
+  // metadata byte j -> both halves; the second half keeps the upper nibble
+  const uint32_t msel = 0x0C000C00u | (uint32_t)j | ((uint32_t)j << 16);
+  u16x2 tv = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(0u, mb4, msel));
+  tv = tv >> (u16x2){0, 4};
+  const uint32_t t = __builtin_bit_cast(uint32_t, tv);
+  const uint32_t sl = (t << 2) & 0x000C000Cu;            // 4*i0 per half
+  const uint32_t sh = (t & 0x000C000Cu) - 0x00040004u;   // 4*i1 - 4 per half (i1 >= 1)
+  const u16x2 los = __builtin_bit_cast(u16x2, lo) << __builtin_bit_cast(u16x2, sl);
+  const u16x2 his = __builtin_bit_cast(u16x2, hi) << __builtin_bit_cast(u16x2, sh);
+  return __builtin_bit_cast(uint32_t, los) | __builtin_bit_cast(uint32_t, his);
+}
+
+__device__ __forceinline__ uint4 expand_chunk(uint32_t codes_lo, uint32_t codes_hi, uint32_t meta) {
+  uint4 d;
+  d.x = expand_dword<0>(codes_lo, meta, 0);
+  d.y = expand_dword<1>(codes_lo, meta, 1);
+  d.z = expand_dword<0>(codes_hi, meta, 2);
+  d.w = expand_dword<1>(codes_hi, meta, 3);
+  return d;
+}
+
+__device__ __forceinline__ void store_out(const GemmArgs& g, int64_t row, int64_t col, float v) {
+  if (g.out_bf16) {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    reinterpret_cast<uint16_t*>(g.y)[row * g.ldy + col] = (uint16_t)(u >> 16);
+  } else {
+    reinterpret_cast<float*>(g.y)[row * g.ldy + col] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Direct kernel (small M): each wave owns WM x WN MFMA tiles (16 x 16) and
+// reads its fragments straight from global memory.  In the tiled layout a
+// fragment is 64 contiguous lanes, so these reads are contiguous too.
+// ---------------------------------------------------------------------------
 template <int WM, int WN>
 __global__ __launch_bounds__(256) void dual_gemm_direct(GemmArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m_base = (int64_t)blockIdx.y * (2 * WM * 16) + (wave >> 1) * WM * 16;
-  const int64_t n_base = (int64_t)blockIdx.x * (2 * WN * 16) + (wave & 1) * WN * 16;
-  const int K = g.K;
-  const int64_t K2 = K / 2, K4 = K / 4, K8 = K / 8, K32 = K / 32;
+  const int64_t RB = (g.M + 15) / 16, NB = (g.N + 15) / 16;
+  const int KB = (g.K + 127) / 128;
+  const int64_t rb_base = (int64_t)blockIdx.y * (2 * WM) + (wave >> 1) * WM;
+  const int64_t nb_base = (int64_t)blockIdx.x * (2 * WN) + (wave & 1) * WN;
   const int r16 = lane & 15, chunk = lane >> 4;
 
   v4f acc[WM][WN];
@@ -69,39 +98,40 @@ __global__ __launch_bounds__(256) void dual_gemm_direct(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < K; k0 += 128) {
-    const int kk = k0 + 32 * chunk;
-    const bool kin = kk < K;
+  for (int ks = 0; ks < KB; ++ks) {
     v8i as[WM], ar[WM], b[WN];
     uint32_t ss[WM], sr[WM], sw_s[WN], sw_d[WN];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      const int64_t row = m_base + 16 * i + r16;
-      const bool ok = kin && row < g.M;
-      uint4 rq = ok ? *reinterpret_cast<const uint4*>(g.r_codes + row * K2 + kk / 2) : make_uint4(0, 0, 0, 0);
-      uint2 sq = ok ? *reinterpret_cast<const uint2*>(g.s_codes + row * K4 + kk / 4) : make_uint2(0, 0);
-      uint32_t mq = ok ? *reinterpret_cast<const uint32_t*>(g.s_meta + row * K8 + kk / 8) : 0u;
+      const int64_t rb = rb_base + i;
+      const bool ok = rb < RB;
+      const int64_t tile = rb * KB + ks;
+      uint4 rq = ok ? *reinterpret_cast<const uint4*>(g.r_codes + tile * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
+      uint32_t lo = ok ? *reinterpret_cast<const uint32_t*>(g.s_codes + tile * 512 + lane * 4) : 0u;
+      uint32_t hi = ok ? *reinterpret_cast<const uint32_t*>(g.s_codes + tile * 512 + 256 + lane * 4) : 0u;
+      uint32_t mq = ok ? *reinterpret_cast<const uint32_t*>(g.s_meta + tile * 256 + lane * 4) : 0x44444444u;
       ar[i] = as_operand(rq);
-      as[i] = as_operand(expand32(sq, mq));
-      ss[i] = ok ? g.s_scales[row * K32 + kk / 32] : 0u;
-      sr[i] = ok ? g.r_scales[row * K32 + kk / 32] : 0u;
+      as[i] = as_operand(expand_chunk(lo, hi, mq));
+      ss[i] = ok ? g.s_scales[((int64_t)ks * RB + rb) * 64 + lane] : 0u;
+      sr[i] = ok ? g.r_scales[((int64_t)ks * RB + rb) * 64 + lane] : 0u;
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      const int64_t col = n_base + 16 * j + r16;
-      const bool ok = kin && col < g.N;
-      uint4 wq = ok ? *reinterpret_cast<const uint4*>(g.w_codes + col * K2 + kk / 2) : make_uint4(0, 0, 0, 0);
+      const int64_t nb = nb_base + j;
+      const bool ok = nb < NB;
+      uint4 wq = ok ? *reinterpret_cast<const uint4*>(g.w_codes + (nb * KB + ks) * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
       b[j] = as_operand(wq);
-      sw_s[j] = ok ? g.w_scales_sparse[col * g.w_scales_ld + kk / 32] : 0u;
-      sw_d[j] = ok ? g.w_scales_dense[col * g.w_scales_ld + kk / 32] : 0u;
+      sw_s[j] = ok ? g.w_scales_sparse[(int64_t)ks * g.w_scales_ld + nb * 64 + lane] : 0u;
+      sw_d[j] = ok ? g.w_scales_dense[(int64_t)ks * g.w_scales_ld + nb * 64 + lane] : 0u;
     }
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        acc[i][j] = mfma_fp4(as[i], b[j], acc[i][j], ss[i], sw_s[j]);
-        acc[i][j] = mfma_fp4(ar[i], b[j], acc[i][j], sr[i], sw_d[j]);
-      }
+      for (int j = 0; j < WN; ++j) acc[i][j] = mfma_fp4(as[i], b[j], acc[i][j], ss[i], sw_s[j]);
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[i][j] = mfma_fp4(ar[i], b[j], acc[i][j], sr[i], sw_d[j]);
   }
 
   // single epilogue store of Y_S + Y_R
@@ -109,217 +139,182 @@ __global__ __launch_bounds__(256) void dual_gemm_direct(GemmArgs g) {
   for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      const int64_t col = n_base + 16 * j + r16;
+      const int64_t col = (nb_base + j) * 16 + r16;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int64_t row = m_base + 16 * i + 4 * chunk + t;
-        if (row < g.M && col < g.N) {
-          if (g.out_bf16) {
-            float f = acc[i][j][t];
-            uint32_t u = __float_as_uint(f);
-            u += 0x7FFFu + ((u >> 16) & 1u);
-            reinterpret_cast<uint16_t*>(g.y)[row * g.ldy + col] = (uint16_t)(u >> 16);
-          } else {
-            reinterpret_cast<float*>(g.y)[row * g.ldy + col] = acc[i][j][t];
-          }
-        }
+        const int64_t row = (rb_base + i) * 16 + 4 * chunk + t;
+        if (row < g.M && col < g.N) store_out(g, row, col, acc[i][j][t]);
       }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Tiled dual GEMM (M > 64, K % 128 == 0).
+// Tiled kernel (M > 64).
 //
-// LDS holds each 16-row x 128-K operand block as 1 KiB in MFMA lane order
-// (16 bytes for lane l = row l%16, K chunk l/16), so every fragment read is a
-// contiguous 16-byte-per-lane read.  The dense residual codes, the weight
-// codes and all scale dwords are copied global -> LDS by buffer loads with the
-// LDS destination (no register staging); a lane fetches exactly the 16 bytes
-// its LDS slot needs.  The compressed backbone is loaded to registers,
-// expanded to dense 4-bit codes and written in the same layout.  Rows past M
-// or N are given an out-of-range buffer offset, which the hardware turns into
-// zeros.  Each weight fragment feeds the sparse and the dense MFMA of the same
-// output tile; all products accumulate in one register tile.
+// Operands arrive in the MFMA-tiled layout (16 rows x 128 K per tile, lane
+// order), so every global -> LDS copy is a contiguous run: one 1 KiB dense
+// tile per instruction, the 512-byte compressed tile and its 256-byte
+// metadata, and the scale bytes of a whole tile edge in one go.  Copies are
+// buffer loads with an LDS destination (no register staging).  Tiles past the
+// padded row count get an out-of-range buffer offset, which reads as zero.
+// The compressed backbone of a tile lands in the first 768 bytes of the 1 KiB
+// slot it will become, and the wave that copied it expands it in place.  Each
+// weight fragment feeds the sparse and the dense MFMA of the same output tile.
 // ---------------------------------------------------------------------------
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Expand two 2:4 groups (code bytes at bits [8h, 8h+16) of cw, metadata byte
-// mb) into one dword of 8 dense nibbles, using 16-bit halves for the groups.
-template <int H>
-__device__ __forceinline__ uint32_t expand_dword(uint32_t cw, uint32_t mb4, int j) {
-  // codes: group 2j' byte to half 0, next byte to half 1 (zero-extended)
-  constexpr uint32_t sel = H == 0 ? 0x0C010C00u : 0x0C030C02u;
-  const uint32_t d = __builtin_amdgcn_perm(0u, cw, sel);
-  const uint32_t lo = d & 0x000F000Fu, hi = d & 0x00F000F0u;
-  // metadata byte j of mb4 to both halves, then the second half's nibble down
-  const uint32_t msel = 0x0C000C00u | (uint32_t)j | ((uint32_t)j << 16);
-  uint32_t t = __builtin_amdgcn_perm(0u, mb4, msel);
-  t = t >> (uint32_t)0 ;  // keep as dword; halves: (mb, mb)
-  u16x2 tv = __builtin_bit_cast(u16x2, t);
-  tv = tv >> (u16x2){0, 4};
-  t = __builtin_bit_cast(uint32_t, tv);
-  const uint32_t sl = (t << 2) & 0x000C000Cu;            // 4*i0 per half
-  const uint32_t sh = (t & 0x000C000Cu) - 0x00040004u;   // 4*i1 - 4 per half (i1 >= 1)
-  const u16x2 los = __builtin_bit_cast(u16x2, lo) << __builtin_bit_cast(u16x2, sl);
-  const u16x2 his = __builtin_bit_cast(u16x2, hi) << __builtin_bit_cast(u16x2, sh);
-  return __builtin_bit_cast(uint32_t, los) | __builtin_bit_cast(uint32_t, his);
+// Buffer resource for a raw byte buffer (stride 0, offsets checked against
+// num_records: reads past the end return zero).
+__device__ __forceinline__ u32x4 make_desc(const void* p, uint64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t n = bytes >= 0x7FFFFFFFull ? 0x7FFFFFFFu : (uint32_t)bytes;
+  return (u32x4){(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, n, 0x00020000u};
 }
 
-__device__ __forceinline__ uint4 expand_chunk(uint2 codes, uint32_t meta) {
-  uint4 d;
-  d.x = expand_dword<0>(codes.x, meta, 0);
-  d.y = expand_dword<1>(codes.x, meta, 1);
-  d.z = expand_dword<0>(codes.y, meta, 2);
-  d.w = expand_dword<1>(codes.y, meta, 3);
-  return d;
+// Global -> LDS copies (buffer_load ... lds): lane l's bytes land at
+// lds_off + l*size.  They are issued from inline asm so that the compiler does
+// not make every later LDS access wait for them; the kernel waits for them
+// itself (vmcnt) before the barrier that publishes a stage.  They have no
+// register results.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_off, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+__device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t lds_off, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
-__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every buffer: reads as zero
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
-  const int n = bytes >= 0x7FFFFFFFull ? 0x7FFFFFFF : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+// s_waitcnt with vmcnt <= VM and lgkmcnt <= LG (expcnt not waited); gfx9 encoding
+template <int VM, int LG>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | ((LG & 15) << 8));
 }
 
-template <int BM, int BN, int NWM, int NWN>
+template <int BM, int BN, int NWM, int NWN, int NST>
 struct TileCfg {
   static constexpr int kWaves = NWM * NWN;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kMB = BM / 16, kNB = BN / 16;     // 16-row blocks
-  static constexpr int kWMT = kMB / NWM, kWNT = kNB / NWN; // MFMA tiles per wave
+  static constexpr int kMB = BM / 16, kNB = BN / 16;       // 16-row blocks
+  static constexpr int kWMT = kMB / NWM, kWNT = kNB / NWN;  // MFMA tiles per wave
   static constexpr int kOffAS = 0;
   static constexpr int kOffAR = kMB * 1024;
   static constexpr int kOffB = 2 * kMB * 1024;
-  static constexpr int kOffSS = kOffB + kNB * 1024;       // scale dword per row (4 K-blocks)
-  static constexpr int kOffSR = kOffSS + BM * 4;
-  static constexpr int kOffSW = kOffSR + BM * 4;
-  static constexpr int kStage = kOffSW + ((BN + 63) / 64) * 256;  // W scale groups of 64 rows
-  static_assert(BM % 64 == 0 && BN % 16 == 0, "tile");
+  static constexpr int kOffSS = kOffB + kNB * 1024;         // scale bytes, 64 per 16-row block (lane order)
+  static constexpr int kOffSR = kOffSS + kMB * 64;
+  static constexpr int kOffSW = kOffSR + kMB * 64;
+  static constexpr int kStage = kOffSW + kNB * 64;
+  static constexpr int kStages = NST;                // LDS ring depth; copies run NST-1 steps ahead
+  static_assert(BM % 16 == 0 && BN % 16 == 0 && BM <= 256 && BN <= 256, "tile (scale edge copied by one instruction)");
   static_assert(kMB % NWM == 0 && kNB % NWN == 0, "wave split");
 };
 
-template <int BM, int BN, int NWM, int NWN>
+template <int BM, int BN, int NWM, int NWN, int NST>
 __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
-  using C = TileCfg<BM, BN, NWM, NWN>;
+  using C = TileCfg<BM, BN, NWM, NWN, NST>;
   extern __shared__ __align__(1024) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets go to M0
-  const int K = g.K;
-  const uint32_t K2 = K / 2, K4 = K / 4, K8 = K / 8, K32 = K / 32;
-  const int KT = K / 128;
+  const int KT = (g.K + 127) / 128;                       // K tiles (zero padded)
+  const int64_t RB = (g.M + 15) / 16, NB = (g.N + 15) / 16; // padded 16-row blocks
 
-  // ---- tile selection: blocks on one XCD (block id mod 8) take a contiguous
+  // tile selection: blocks on one XCD (block id mod 8) take a contiguous
   // range of tiles, walked M-fastest, so they share weight and activation rows in L2
   const int tiles_m = (int)((g.M + BM - 1) / BM);
   const int tiles_n = (int)((g.N + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
   int t = blockIdx.x;
   if (T % 8 == 0) t = (t % 8) * (T / 8) + t / 8;
-  const int64_t m0 = (int64_t)(t % tiles_m) * BM;
-  const int64_t n0 = (int64_t)(t / tiles_m) * BN;
+  const int64_t rb0 = (int64_t)(t % tiles_m) * C::kMB;      // first 16-row block of the tile
+  const int64_t nb0 = (int64_t)(t / tiles_m) * C::kNB;
 
-  const __amdgpu_buffer_rsrc_t rs_sc = make_rsrc(g.s_codes, (uint64_t)g.M * K4);
-  const __amdgpu_buffer_rsrc_t rs_sm = make_rsrc(g.s_meta, (uint64_t)g.M * K8);
-  const __amdgpu_buffer_rsrc_t rs_ss = make_rsrc(g.s_scales, (uint64_t)g.M * K32);
-  const __amdgpu_buffer_rsrc_t rs_rc = make_rsrc(g.r_codes, (uint64_t)g.M * K2);
-  const __amdgpu_buffer_rsrc_t rs_rs = make_rsrc(g.r_scales, (uint64_t)g.M * K32);
-  const __amdgpu_buffer_rsrc_t rs_wc = make_rsrc(g.w_codes, (uint64_t)g.N * K2);
-  const __amdgpu_buffer_rsrc_t rs_ws = make_rsrc(g.w_scales_dense, (uint64_t)g.N * (uint64_t)g.w_scales_ld);
-
+  const u32x4 rs_sc = make_desc(g.s_codes, (uint64_t)RB * KT * 512);
+  const u32x4 rs_sm = make_desc(g.s_meta, (uint64_t)RB * KT * 256);
+  const u32x4 rs_ss = make_desc(g.s_scales, (uint64_t)RB * KT * 64);
+  const u32x4 rs_rc = make_desc(g.r_codes, (uint64_t)RB * KT * 1024);
+  const u32x4 rs_rs = make_desc(g.r_scales, (uint64_t)RB * KT * 64);
+  const u32x4 rs_wc = make_desc(g.w_codes, (uint64_t)NB * KT * 1024);
+  const u32x4 rs_ws = make_desc(g.w_scales_dense, (uint64_t)KT * (uint64_t)g.w_scales_ld);
+  const uint32_t lds0 = lds_addr(smem);
   const int r16 = lane & 15, c4 = lane >> 4;
 
-  // ---- per-lane buffer offsets at K step 0 (invalid rows -> kOOB), hoisted out of the K loop
-  // S/R blocks and W blocks are dealt to waves round-robin; scale rows go in
-  // groups of 64 (one lane per row): S groups, then R groups, then W groups.
+  // ---- per-lane buffer offsets at K tile 0 (blocks past the padding -> kOOB),
+  // hoisted out of the K loop.  A-side blocks and W blocks are dealt to waves
+  // round-robin; waves 0, 1, 2 copy the S, R and W scale edges.
   constexpr int kSB = (C::kMB + C::kWaves - 1) / C::kWaves;
   constexpr int kWB = (C::kNB + C::kWaves - 1) / C::kWaves;
-  constexpr int kScA = BM / 64, kScW = (BN + 63) / 64, kNQ = 2 * kScA + kScW;
-  constexpr int kQB = (kNQ + C::kWaves - 1) / C::kWaves;
+  static_assert(C::kWaves >= 3, "scale copies need three waves");
 
   uint32_t offR[kSB], offC[kSB], offM[kSB];
 #pragma unroll
   for (int i = 0; i < kSB; ++i) {
-    const int64_t row = m0 + (int64_t)(wave + i * C::kWaves) * 16 + r16;
-    const bool ok = row < g.M;
-    offR[i] = ok ? (uint32_t)row * K2 + c4 * 16 : kOOB;
-    offC[i] = ok ? (uint32_t)row * K4 + c4 * 8 : kOOB;
-    offM[i] = ok ? (uint32_t)row * K8 + c4 * 4 : kOOB;
+    const int64_t rb = rb0 + wave + i * C::kWaves;
+    const bool ok = rb < RB;
+    offR[i] = ok ? (uint32_t)(rb * KT) * 1024u + lane * 16 : kOOB;
+    offC[i] = ok ? (uint32_t)(rb * KT) * 512u + lane * 16 : kOOB;   // lanes 0..31
+    offM[i] = ok ? (uint32_t)(rb * KT) * 256u + lane * 16 : kOOB;   // lanes 0..15
   }
   uint32_t offW[kWB];
 #pragma unroll
   for (int i = 0; i < kWB; ++i) {
-    const int64_t row = n0 + (int64_t)(wave + i * C::kWaves) * 16 + r16;
-    offW[i] = row < g.N ? (uint32_t)row * K2 + c4 * 16 : kOOB;
+    const int64_t nb = nb0 + wave + i * C::kWaves;
+    offW[i] = nb < NB ? (uint32_t)(nb * KT) * 1024u + lane * 16 : kOOB;
   }
-  uint32_t offQ[kQB];
-  int kindQ[kQB], ldsQ[kQB];
-#pragma unroll
-  for (int j = 0; j < kQB; ++j) {
-    const int q = wave + j * C::kWaves;
-    kindQ[j] = 3;
-    offQ[j] = kOOB;
-    ldsQ[j] = 0;
-    if (q < kScA) {
-      const int64_t row = m0 + q * 64 + lane;
-      kindQ[j] = 0; ldsQ[j] = C::kOffSS + q * 256;
-      offQ[j] = row < g.M ? (uint32_t)row * K32 : kOOB;
-    } else if (q < 2 * kScA) {
-      const int64_t row = m0 + (q - kScA) * 64 + lane;
-      kindQ[j] = 1; ldsQ[j] = C::kOffSR + (q - kScA) * 256;
-      offQ[j] = row < g.M ? (uint32_t)row * K32 : kOOB;
-    } else if (q < kNQ) {
-      const int qq = q - 2 * kScA;
-      const int64_t row = n0 + qq * 64 + lane;
-      kindQ[j] = 2; ldsQ[j] = C::kOffSW + qq * 256;
-      offQ[j] = (row < g.N && qq * 64 + lane < BN) ? (uint32_t)row * (uint32_t)g.w_scales_ld : kOOB;
-    }
-  }
+  // scale edge: 16 lanes per 64-byte block; lanes past the tile edge are masked
+  const int eb = lane >> 2;   // block of the edge this lane copies
+  const uint32_t offScA = rb0 + eb < RB ? (uint32_t)((rb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
+  const uint32_t offScW = nb0 + eb < NB ? (uint32_t)((nb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
+  const uint32_t strideScA = (uint32_t)RB * 64, strideScW = (uint32_t)g.w_scales_ld;
 
-  uint2 scode[kSB];
-  uint32_t smeta[kSB];
-
-  auto issue = [&](int ks, uint8_t* st) {
-    const uint32_t so2 = (uint32_t)ks * 64, so4 = (uint32_t)ks * 32, so8 = (uint32_t)ks * 16, so32 = (uint32_t)ks * 4;
+  // Copy K tile ks into the LDS stage at byte offset st.
+  auto issue = [&](int ks, uint32_t st) {
+    const uint32_t so1k = (uint32_t)ks * 1024, so512 = (uint32_t)ks * 512, so256 = (uint32_t)ks * 256;
 #pragma unroll
     for (int i = 0; i < kSB; ++i) {
       const int b = wave + i * C::kWaves;
       if (b < C::kMB) {
-        lds_copy16(rs_rc, st + C::kOffAR + b * 1024, offR[i], so2);
-        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rs_sc, offC[i], so4, 0);
-        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rs_sc, offC[i] + 4, so4, 0);
-        scode[i] = make_uint2(lo, hi);
-        smeta[i] = __builtin_amdgcn_raw_buffer_load_b32(rs_sm, offM[i], so8, 0);
+        lds_dma16(rs_rc, st + C::kOffAR + b * 1024, offR[i], so1k);
+        const uint32_t as = st + C::kOffAS + b * 1024;
+        if (lane < 32) lds_dma16(rs_sc, as, offC[i], so512);
+        if (lane < 16) lds_dma16(rs_sm, as + 512, offM[i], so256);
       }
     }
 #pragma unroll
     for (int i = 0; i < kWB; ++i) {
       const int b = wave + i * C::kWaves;
-      if (b < C::kNB) lds_copy16(rs_wc, st + C::kOffB + b * 1024, offW[i], so2);
+      if (b < C::kNB) lds_dma16(rs_wc, st + C::kOffB + b * 1024, offW[i], so1k);
     }
-#pragma unroll
-    for (int j = 0; j < kQB; ++j) {
-      if (kindQ[j] == 0) lds_copy4(rs_ss, st + ldsQ[j], offQ[j], so32);
-      else if (kindQ[j] == 1) lds_copy4(rs_rs, st + ldsQ[j], offQ[j], so32);
-      else if (kindQ[j] == 2) lds_copy4(rs_ws, st + ldsQ[j], offQ[j], so32);
-    }
+    if (wave == 0 && lane < C::kMB * 4) lds_dma16(rs_ss, st + C::kOffSS, offScA, ks * strideScA);
+    if (wave == 1 && lane < C::kMB * 4) lds_dma16(rs_rs, st + C::kOffSR, offScA, ks * strideScA);
+    if (wave == 2 && lane < C::kNB * 4) lds_dma16(rs_ws, st + C::kOffSW, offScW, ks * strideScW);
   };
+
+  // Expand this wave's backbone blocks of the stage at st in place: every lane
+  // reads its 12 compressed bytes, the wave waits for all of its reads, then
+  // every lane writes its 16 dense bytes (a block belongs to one wave).
   auto expand_store = [&](uint8_t* st) {
+    uint32_t lo[kSB], hi[kSB], mt[kSB];
 #pragma unroll
     for (int i = 0; i < kSB; ++i) {
       const int b = wave + i * C::kWaves;
       if (b < C::kMB) {
-        const uint4 d = expand_chunk(scode[i], smeta[i]);
-        *reinterpret_cast<uint4*>(st + C::kOffAS + b * 1024 + lane * 16) = d;
+        const uint8_t* blk = st + C::kOffAS + b * 1024;
+        lo[i] = *reinterpret_cast<const uint32_t*>(blk + lane * 4);
+        hi[i] = *reinterpret_cast<const uint32_t*>(blk + 256 + lane * 4);
+        mt[i] = *reinterpret_cast<const uint32_t*>(blk + 512 + lane * 4);
       }
+    }
+    wait_vm_lgkm<63, 0>();
+#pragma unroll
+    for (int i = 0; i < kSB; ++i) {
+      const int b = wave + i * C::kWaves;
+      if (b < C::kMB)
+        *reinterpret_cast<uint4*>(st + C::kOffAS + b * 1024 + lane * 16) = expand_chunk(lo[i], hi[i], mt[i]);
     }
   };
 
@@ -330,15 +325,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < C::kWNT; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  issue(0, smem);
-  expand_store(smem);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int ks = 0; ks < KT; ++ks) {
-    uint8_t* cur = smem + (ks & 1) * C::kStage;
-    uint8_t* nxt = smem + ((ks + 1) & 1) * C::kStage;
-    if (ks + 1 < KT) issue(ks + 1, nxt);
-
+  auto compute = [&](const uint8_t* cur) {
     v8i fs[C::kWMT], fr[C::kWMT], fb[C::kWNT];
     uint32_t ss[C::kWMT], sr[C::kWMT], sw[C::kWNT];
 #pragma unroll
@@ -346,14 +333,14 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
       const int blk = wm * C::kWMT + i;
       fs[i] = as_operand(*reinterpret_cast<const uint4*>(cur + C::kOffAS + blk * 1024 + lane * 16));
       fr[i] = as_operand(*reinterpret_cast<const uint4*>(cur + C::kOffAR + blk * 1024 + lane * 16));
-      ss[i] = cur[C::kOffSS + (blk * 16 + r16) * 4 + c4];
-      sr[i] = cur[C::kOffSR + (blk * 16 + r16) * 4 + c4];
+      ss[i] = cur[C::kOffSS + blk * 64 + lane];
+      sr[i] = cur[C::kOffSR + blk * 64 + lane];
     }
 #pragma unroll
     for (int j = 0; j < C::kWNT; ++j) {
       const int blk = wn * C::kWNT + j;
       fb[j] = as_operand(*reinterpret_cast<const uint4*>(cur + C::kOffB + blk * 1024 + lane * 16));
-      sw[j] = cur[C::kOffSW + (blk * 16 + r16) * 4 + c4];
+      sw[j] = cur[C::kOffSW + blk * 64 + lane];
     }
 #pragma unroll
     for (int i = 0; i < C::kWMT; ++i)
@@ -363,10 +350,44 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
       for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
+  };
 
-    if (ks + 1 < KT) expand_store(nxt);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // Pipeline: an LDS ring of NST stages; copies run D = NST-1 K steps ahead.
+  // Before expanding stage ks+1 a wave waits until only the copies of the
+  // stages after it are outstanding (vmcnt retires in issue order; every wave
+  // issues at least kLoadsMin copies per stage), then all waves meet at a
+  // barrier before the stage is read.
+  constexpr int D = NST - 1;
+  constexpr int kLoadsMin = C::kMB / C::kWaves * 3 + C::kNB / C::kWaves;
+  static_assert(kLoadsMin >= 1 && kLoadsMin * (D > 1 ? D - 1 : 1) < 64, "vmcnt range");
+  auto stage_off = [&](int ks) { return (uint32_t)((ks % NST) * C::kStage); };
+  // wait until at most `newer` stages' copies are still in flight
+  auto wait_stages = [&](int newer) {
+    static_assert(D <= 5, "wait table");
+    switch (newer) {
+      case 0: wait_vm_lgkm<0, 15>(); break;
+      case 1: wait_vm_lgkm<kLoadsMin, 15>(); break;
+      case 2: wait_vm_lgkm<(2 * kLoadsMin < 64 ? 2 * kLoadsMin : 63), 15>(); break;
+      case 3: wait_vm_lgkm<(3 * kLoadsMin < 64 ? 3 * kLoadsMin : 63), 15>(); break;
+      default: wait_vm_lgkm<(4 * kLoadsMin < 64 ? 4 * kLoadsMin : 63), 15>(); break;
+    }
+  };
+
+  const int pre = KT < D ? KT : D;     // stages copied before the loop
+  for (int s = 0; s < pre; ++s) issue(s, lds0 + stage_off(s));
+  wait_stages(pre - 1);
+  expand_store(smem + stage_off(0));
+  __syncthreads();
+
+  for (int ks = 0; ks < KT; ++ks) {
+    if (ks + D < KT) issue(ks + D, lds0 + stage_off(ks + D));
+    compute(smem + stage_off(ks));
+    if (ks + 1 < KT) {
+      const int last = ks + D < KT ? ks + D : KT - 1;   // newest stage copied so far
+      wait_stages(last - (ks + 1));
+      expand_store(smem + stage_off(ks + 1));
+      __syncthreads();
+    }
   }
 
   // single epilogue store of Y_S + Y_R
@@ -374,43 +395,38 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
     for (int j = 0; j < C::kWNT; ++j) {
-      const int64_t col = n0 + (wn * C::kWNT + j) * 16 + r16;
+      const int64_t col = (nb0 + wn * C::kWNT + j) * 16 + r16;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = m0 + (wm * C::kWMT + i) * 16 + 4 * c4 + q;
-        if (row < g.M && col < g.N) {
-          if (g.out_bf16) {
-            uint32_t u = __float_as_uint(acc[i][j][q]);
-            u += 0x7FFFu + ((u >> 16) & 1u);
-            reinterpret_cast<uint16_t*>(g.y)[row * g.ldy + col] = (uint16_t)(u >> 16);
-          } else {
-            reinterpret_cast<float*>(g.y)[row * g.ldy + col] = acc[i][j][q];
-          }
-        }
+        const int64_t row = (rb0 + wm * C::kWMT + i) * 16 + 4 * c4 + q;
+        if (row < g.M && col < g.N) store_out(g, row, col, acc[i][j][q]);
       }
     }
 }
 
-template <int BM, int BN, int NWM, int NWN>
+template <int BM, int BN, int NWM, int NWN, int NST>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
-  using C = TileCfg<BM, BN, NWM, NWN>;
-  auto kern = dual_gemm_tiled<BM, BN, NWM, NWN>;
+  using C = TileCfg<BM, BN, NWM, NWN, NST>;
+  auto kern = dual_gemm_tiled<BM, BN, NWM, NWN, NST>;
+  constexpr int lds = C::kStages * C::kStage;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * C::kStage);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::kThreads), 2 * C::kStage, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_linear(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   // the tiled kernel addresses every operand with 31-bit buffer offsets
-  const bool fits = (uint64_t)a.M * (a.K / 2) < 0x7FFFFFFFull && (uint64_t)a.N * (a.K / 2) < 0x7FFFFFFFull;
-  if (a.K % 128 == 0 && a.M > 64 && fits) return launch_tiled<256, 192, 4, 2>(a, stream);
+  const uint64_t kb = (a.K + 127) / 128;
+  const bool fits = (uint64_t)((a.M + 15) / 16) * kb * 1024 < 0x7FFFFFFFull &&
+                    (uint64_t)((a.N + 15) / 16) * kb * 1024 < 0x7FFFFFFFull;
+  if (a.M > 64 && fits) return launch_tiled<256, 192, 4, 2, 3>(a, stream);
   constexpr int WM = 2, WN = 4;
   dim3 grid((unsigned)((a.N + 2 * WN * 16 - 1) / (2 * WN * 16)), (unsigned)((a.M + 2 * WM * 16 - 1) / (2 * WM * 16)));
   hipLaunchKernelGGL((dual_gemm_direct<WM, WN>), grid, dim3(256), 0, stream, a);

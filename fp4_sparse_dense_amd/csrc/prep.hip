@@ -7,6 +7,10 @@
 // dense FP4 path.  The README page (sections "Evaluation", "Benchmarks") names
 // the fused normalisation RMSNorm.
 //
+// Outputs are written in the MFMA-tiled layout the GEMM copies with contiguous
+// loads (16 rows x 128 K per tile, lane order; see include/sharq.h), padding
+// rows and the K tail of the last tile as zeros.
+//
 // Mapping: one wavefront per activation row.  A row is covered in slots of
 // 512 elements; in a slot lane l owns elements [8l, 8l+8) (one 16-byte load),
 // so a wave load is 1 KiB contiguous, a 2:4 group never leaves a lane and a
@@ -138,9 +142,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
                                                    float eps, PrepOut o) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= M) return;  // uniform per wave
+  const int64_t RB = (M + 15) / 16;
+  if (row >= RB * 16) return;  // uniform per wave; rows M..RB*16 are zero padding
+  const bool row_ok = row < M;
+  const int KB = (K + 127) / 128, Kp = KB * 128;
   const int nslot = (K + kSlot - 1) / kSlot;
-  const uint16_t* xr = x + row * ldx;
+  const uint16_t* xr = x + (row_ok ? row : 0) * ldx;
   uint4 xb[kRegSlots];
   float inv = 1.0f;
 
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 #pragma unroll
       for (int s = 0; s < kRegSlots; ++s) {
         int k = (c0 + s) * kSlot + lane * 8;
-        xb[s] = load16_or_zero(xr + k, c0 + s < nslot && k < K);
+        xb[s] = load16_or_zero(xr + k, row_ok && c0 + s < nslot && k < K);
       }
 #pragma unroll
       for (int s = 0; s < kRegSlots; ++s) {
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int s = 0; s < kRegSlots; ++s) {
       int k = (c0 + s) * kSlot + lane * 8;
-      xb[s] = load16_or_zero(xr + k, c0 + s < nslot && k < K);
+      xb[s] = load16_or_zero(xr + k, row_ok && c0 + s < nslot && k < K);
     }
     if (NORM && nslot <= kRegSlots) {
       float mine = 0.0f;
@@ -188,7 +195,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
       const int slot = c0 + s;
       if (slot >= nslot) break;  // uniform
       const int k = slot * kSlot + lane * 8;
-      const bool active = k < K;
+      const bool active = k < K;          // real input
+      const bool store = k < Kp;          // real input or zero padding of the last K tile
       const uint4 w = xb[s];
       float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                     bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
@@ -199,15 +207,25 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = (v[i] * inv) * gv[i];
       }
+      if (!active || !row_ok) {   // padding is exact zeros whatever inv is (eps = 0, zero row)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+      }
       const Lane8 d = decompose8(v);
-      if (active) {
-        const int64_t K2 = K / 2, K4 = K / 4, K8 = K / 8, K32 = K / 32;
-        *reinterpret_cast<uint16_t*>(o.s_codes + row * K4 + k / 4) = (uint16_t)d.s_codes;
-        o.s_meta[row * K8 + k / 8] = (uint8_t)d.meta;
-        *reinterpret_cast<uint32_t*>(o.r_codes + row * K2 + k / 2) = d.r_codes;
-        if ((lane & 3) == 0) {
-          o.s_scales[row * K32 + k / 32] = (uint8_t)d.s_e8;
-          o.r_scales[row * K32 + k / 32] = (uint8_t)d.r_e8;
+      if (store) {
+        // tiled layout: tile (row/16, k/128), tile lane = 16*(32-chunk) + row%16,
+        // this lane's 8 elements are quarter q of that tile lane's 32
+        const int64_t tile = (row >> 4) * KB + (k >> 7);
+        const int tl = ((k >> 5) & 3) * 16 + (int)(row & 15);
+        const int q = (k >> 3) & 3;
+        *reinterpret_cast<uint32_t*>(o.r_codes + tile * 1024 + tl * 16 + q * 4) = d.r_codes;
+        *reinterpret_cast<uint16_t*>(o.s_codes + tile * 512 + (q >> 1) * 256 + tl * 4 + (q & 1) * 2) =
+            (uint16_t)d.s_codes;
+        o.s_meta[tile * 256 + tl * 4 + q] = (uint8_t)d.meta;
+        if (q == 0) {
+          const int64_t sc = ((int64_t)(k >> 7) * RB + (row >> 4)) * 64 + tl;
+          o.s_scales[sc] = (uint8_t)d.s_e8;
+          o.r_scales[sc] = (uint8_t)d.r_e8;
         }
       }
     }
@@ -220,12 +238,15 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
                                                           uint8_t* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= N) return;
-  const uint16_t* wr = w + row * ldw;
+  const int64_t NB = (N + 15) / 16;
+  if (row >= NB * 16) return;  // rows N..NB*16 are zero padding
+  const bool row_ok = row < N;
+  const int KB = (K + 127) / 128, Kp = KB * 128;
+  const uint16_t* wr = w + (row_ok ? row : 0) * ldw;
   const int nslot = (K + kSlot - 1) / kSlot;
   for (int slot = 0; slot < nslot; ++slot) {
     const int k = slot * kSlot + lane * 8;
-    const bool active = k < K;
+    const bool active = row_ok && k < K;
     const uint4 q = active ? *reinterpret_cast<const uint4*>(wr + k) : make_uint4(0, 0, 0, 0);
     float v[8] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y),
                   bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w)};
@@ -239,9 +260,12 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
     c = fp4_pack2<1>(c, v[2] * qs, v[3] * qs);
     c = fp4_pack2<2>(c, v[4] * qs, v[5] * qs);
     c = fp4_pack2<3>(c, v[6] * qs, v[7] * qs);
-    if (active) {
-      *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + k / 2) = c;
-      if ((lane & 3) == 0) scales[row * (K / 32) + k / 32] = (uint8_t)(e + 127);
+    if (k < Kp) {
+      const int64_t tile = (row >> 4) * KB + (k >> 7);
+      const int tl = ((k >> 5) & 3) * 16 + (int)(row & 15);
+      const int qq = (k >> 3) & 3;
+      *reinterpret_cast<uint32_t*>(codes + tile * 1024 + tl * 16 + qq * 4) = c;
+      if (qq == 0) scales[((int64_t)(k >> 7) * NB + (row >> 4)) * 64 + tl] = (uint8_t)(e + 127);
     }
   }
 }
@@ -249,7 +273,8 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
 hipError_t launch_prepare(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
                           float eps, PrepOut out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
+  const int64_t rows = (M + 15) / 16 * 16;   // includes the zero padding rows
+  dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
   if (gamma)
     hipLaunchKernelGGL(prep_kernel<true>, grid, block, 0, stream, x, M, K, ldx, gamma, eps, out);
   else
@@ -259,7 +284,8 @@ hipError_t launch_prepare(const uint16_t* x, int64_t M, int K, int64_t ldx, cons
 
 hipError_t launch_pack_weight(const uint16_t* w, int64_t N, int K, int64_t ldw, uint8_t* codes,
                               uint8_t* scales, hipStream_t stream) {
-  dim3 grid((unsigned)((N + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
+  const int64_t rows = (N + 15) / 16 * 16;
+  dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
   hipLaunchKernelGGL(pack_weight_kernel, grid, block, 0, stream, w, N, K, ldw, codes, scales);
   return hipGetLastError();
 }

@@ -23,9 +23,21 @@
  *    any error nothing is launched and outputs are untouched.  No C++ exception
  *    crosses this ABI.  sharq_last_error() gives a thread-local detail string.
  *  - Inputs must be finite (NaN/Inf give unspecified codes).
- *  - Layouts are row-major with the K (reduction) index fastest.  FP4 codes
- *    are E2M1 nibbles, two per byte, the lower k in the low nibble; the sign
- *    is nibble bit 3.  E8M0 scale bytes encode 2^(byte-127).
+ *  - FP4 codes are E2M1 nibbles, the lower k in the low nibble; the sign is
+ *    nibble bit 3.  E8M0 scale bytes encode 2^(byte-127).
+ *  - Tiled layout.  Every operand the GEMM reads is stored in blocks of 16
+ *    rows x 128 K ("tiles"), in the lane order of the gfx950 block-scaled FP4
+ *    MFMA: lane l of a tile is row 16*rb + l%16 and K range
+ *    [128*kb + 32*(l/16), +32).  Rows are padded to RB*16 (RB = ceil(rows/16))
+ *    and K to KB*128 (KB = ceil(K/128)); padding holds zero codes and zero
+ *    scale bytes.  Per tile (rb, kb), tiles ordered rb-major then kb:
+ *      dense codes    1024 B: lane l at 16*l (its 32 codes)
+ *      2:4 codes       512 B: two planes of 256 B; plane p, lane l at 256*p + 4*l
+ *                             holds the kept codes of groups 4p..4p+3 of the lane
+ *      2:4 metadata    256 B: lane l at 4*l, nibble g = group g of the lane
+ *    Scale bytes are K-step-major: [KB][RB][64], byte l of (kb, rb) is the
+ *    E8M0 of lane l's 32-block.  Canonical row-major arrays follow by
+ *    un-tiling (the tests do exactly that before comparing).
  */
 #ifndef SHARQ_H
 #define SHARQ_H
@@ -60,8 +72,8 @@ typedef enum { SHARQ_OUT_F32 = 0, SHARQ_OUT_BF16 = 1 } sharq_out_dtype;
 typedef enum { SHARQ_PATH_SPARSE = 0, SHARQ_PATH_DENSE = 1 } sharq_path;
 
 /* A scale view: how one GEMM path reads the weight's block scales.
- * base: device pointer to E8M0 bytes; ld: bytes between rows n; block: K
- * elements per scale byte.  On gfx950 both paths run the same block-scaled
+ * base: device pointer to E8M0 bytes (tiled, [KB][NB][64]); ld: bytes between
+ * K steps (NB*64); block: K elements per scale byte.  On gfx950 both paths run the same block-scaled
  * MFMA on dense 4-bit operands (the sparse operand is expanded on chip), so
  * sharq_pack_weight sets both views to the same array and layout. */
 typedef struct {
@@ -80,19 +92,18 @@ typedef struct {
   int64_t N, K;
   int32_t fmt;              /* sharq_format */
   int32_t reserved;
-  uint8_t* codes;           /* [N][K/2] E2M1, the single FP4 payload both paths read */
-  uint8_t* scales;          /* [N][K/32] E8M0 */
+  uint8_t* codes;           /* tiled dense codes, NB*KB tiles: the single FP4 payload both paths read */
+  uint8_t* scales;          /* tiled E8M0 scales [KB][NB][64] */
   sharq_scale_view view[2]; /* indexed by sharq_path */
 } sharq_weight;
 
-/* Prepared activation (output of sharq_prepare).  For 2:4 and MXFP4:
- *   s_codes  [M][K/4]   E2M1 of the kept S entries in k order
- *   s_meta   [M][K/8]   per group of 4 the kept offsets i0<i1 as nibble i0|i1<<2,
- *                       group j in byte j/2 (low nibble for even j)
- *   s_scales [M][K/32]  E8M0 of S per 32 logical positions
- *   r_codes  [M][K/2]   E2M1 of R
- *   r_scales [M][K/32]  E8M0 of R
- * Row strides are the packed widths above (rows are contiguous). */
+/* Prepared activation (output of sharq_prepare), 2:4 and MXFP4, tiled layout:
+ *   s_codes   2:4 codes of S: E2M1 of the kept entries in k order (RB*KB*512 B)
+ *   s_meta    2:4 metadata: per group of 4 the kept offsets i0<i1 as the
+ *             nibble i0 | i1<<2 (RB*KB*256 B)
+ *   s_scales  E8M0 of S per 32 logical positions ([KB][RB][64])
+ *   r_codes   dense E2M1 of R (RB*KB*1024 B)
+ *   r_scales  E8M0 of R ([KB][RB][64]) */
 typedef struct {
   uint32_t struct_size;     /* sizeof(sharq_act) */
   uint32_t layout_version;  /* SHARQ_ABI_VERSION */
@@ -116,13 +127,15 @@ const char* sharq_status_str(sharq_status s);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* sharq_last_error(void);
 
-/* Byte sizes of the packed weight buffers for W[N,K] in `fmt`.
+/* Byte sizes of the packed weight buffers for W[N,K] in `fmt` (tiled:
+ * codes NB*KB*1024, scales KB*NB*64).
  * Errors: INVALID_ARG for N<=0, K<=0, K%32, null outputs; UNSUPPORTED for NVFP4/HiF4. */
 sharq_status sharq_weight_bytes(int64_t N, int64_t K, int32_t fmt,
                                 size_t* codes_bytes, size_t* scales_bytes);
 
 /* Byte sizes of the five prepared-activation buffers, in the order
- * s_codes, s_meta, s_scales, r_codes, r_scales.  M == 0 gives zeros.
+ * s_codes, s_meta, s_scales, r_codes, r_scales (tiled: RB*KB*{512, 256, 64,
+ * 1024, 64}).  M == 0 gives zeros.
  * Errors: INVALID_ARG for M<0, K<=0, K%32, null output; UNSUPPORTED unless
  * (n,m) == (2,4) and fmt == MXFP4. */
 sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t fmt,
@@ -130,12 +143,14 @@ sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t
 
 /* Pack W[N,K] (bf16, row stride ldw elements) into the single FP4 weight
  * payload: per row n and 32-block b, E = floor(log2 amax)-2 (E8M0, clamped)
- * and E2M1 codes of w/2^E (round to nearest, ties to even, saturating at 6).
+ * and E2M1 codes of w/2^E (round to nearest, ties to even, saturating at 6),
+ * written in the tiled layout with zero padding.
  * SharQ abstract: both GEMM paths read this one payload.
  * `out` must have struct_size set and codes/scales pointing at buffers of the
  * sizes given by sharq_weight_bytes; N, K, fmt and both views are filled in.
  * Errors: INVALID_ARG (null, N<=0, K<=0, K%32, ldw<K, w not 16-B aligned or
- * ldw%8), UNSUPPORTED (fmt != MXFP4, device not gfx950), HIP. */
+ * ldw%8, a buffer not 16-B aligned), UNSUPPORTED (fmt != MXFP4, device not
+ * gfx950), HIP. */
 sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int64_t ldw,
                                int32_t fmt, sharq_weight* out, void* stream);
 
@@ -146,7 +161,8 @@ sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int
  *       v = (x*inv)*gamma;
  *   mask: in each group of 4 along K keep the 2 largest |v| (ties: lower index);
  *   S = v on kept entries, 0 elsewhere; Q(S) = MXFP4 over 32 logical positions;
- *   R = v - deq(Q(S)) (exact in binary32); Q(R) = MXFP4.
+ *   R = v - deq(Q(S)) (exact in binary32); Q(R) = MXFP4;
+ *   all five outputs in the tiled layout, padding rows and K written as zeros.
  * SharQ abstract: one fused operator absorbs mask generation, residual
  * construction and the normalisation; the residual is relative to the
  * quantised backbone.

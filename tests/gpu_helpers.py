@@ -6,6 +6,58 @@ from oracle import sharq_oracle as O
 FIELDS = ("s_codes", "s_meta", "s_scales", "r_codes", "r_scales")
 
 
+# ---------------------------------------------------------------------------
+# Un-tiling: the GPU stores operands in blocks of 16 rows x 128 K in MFMA lane
+# order (lane l = row l%16, 32-element chunk l/16); scales K-tile-major.  These
+# numpy conversions recover the canonical row-major arrays of the oracle and
+# check that all padding (rows past M, K past the end) holds what the method
+# gives for zero input: zero codes and scales, metadata 0x44 (offsets 0, 1).
+# ---------------------------------------------------------------------------
+def _dims(rows, K):
+    return -(-rows // 16), -(-K // 128)
+
+
+def _crop(full, rows, cols, label, pad=0):
+    assert np.all(full[rows:] == pad) and np.all(full[:, cols:] == pad), f"{label}: padding is not {pad:#x}"
+    return full[:rows, :cols]
+
+
+def untile_dense(buf, rows, K, label="codes"):
+    RB, KB = _dims(rows, K)
+    t = np.asarray(buf).reshape(RB, KB, 4, 16, 16).transpose(0, 3, 1, 2, 4)
+    return _crop(t.reshape(RB * 16, KB * 64), rows, K // 2, label)
+
+
+def untile_sparse_codes(buf, rows, K):
+    RB, KB = _dims(rows, K)
+    t = np.asarray(buf).reshape(RB, KB, 2, 4, 16, 4).transpose(0, 4, 1, 3, 2, 5)
+    return _crop(t.reshape(RB * 16, KB * 32), rows, K // 4, "s_codes")
+
+
+def untile_meta(buf, rows, K):
+    RB, KB = _dims(rows, K)
+    t = np.asarray(buf).reshape(RB, KB, 4, 16, 4).transpose(0, 3, 1, 2, 4)
+    return _crop(t.reshape(RB * 16, KB * 16), rows, K // 8, "s_meta", pad=0x44)
+
+
+def untile_scales(buf, rows, K, label="scales"):
+    RB, KB = _dims(rows, K)
+    t = np.asarray(buf).reshape(KB, RB, 4, 16).transpose(1, 3, 0, 2)
+    return _crop(t.reshape(RB * 16, KB * 4), rows, K // 32, label)
+
+
+def untile_act(raw: dict, M: int, K: int) -> dict:
+    return dict(s_codes=untile_sparse_codes(raw["s_codes"], M, K),
+                s_meta=untile_meta(raw["s_meta"], M, K),
+                s_scales=untile_scales(raw["s_scales"], M, K, "s_scales"),
+                r_codes=untile_dense(raw["r_codes"], M, K, "r_codes"),
+                r_scales=untile_scales(raw["r_scales"], M, K, "r_scales"))
+
+
+def untile_weight(codes, scales, N, K):
+    return untile_dense(codes, N, K, "w_codes"), untile_scales(scales, N, K, "w_scales")
+
+
 def dev_bf16(bits):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)

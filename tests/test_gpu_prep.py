@@ -7,7 +7,7 @@ import pytest
 import fp4_sparse_dense_amd as sq
 from fp4_sparse_dense_amd import synth
 from oracle import sharq_oracle as O
-from tests.gpu_helpers import assert_prep_equal, dev_bf16
+from tests.gpu_helpers import assert_prep_equal, dev_bf16, untile_act, untile_weight
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,7 @@ def run_prep(x_bits, gamma_bits, eps=1e-5, ldx=None):
     g = dev_bf16(gamma_bits) if gamma_bits is not None else None
     act = sq.sharq_prepare(xd, g, eps)
     torch.cuda.synchronize()
-    return act.host()
+    return untile_act(act.host(), M, K)
 
 
 CASES = [("tiny", 0), ("qkv", 0), ("qkv", 1), ("qkv", 2), ("down", 0),
@@ -109,7 +109,7 @@ def test_prep_empty():
     import torch
     x = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
     act = sq.sharq_prepare(x, None)
-    assert act.M == 0 and act.s_codes.shape == (0, 64)
+    assert act.M == 0 and act.s_codes.numel() == 0
 
 
 @pytest.mark.parametrize("name", ["tiny", "qkv", "down"])
@@ -120,8 +120,9 @@ def test_pack_weight(name):
     wc, ws = O.pack_weight(inp["w"])
     w = sq.sharq_pack_weight(dev_bf16(inp["w"]))
     torch.cuda.synchronize()
-    assert np.array_equal(w.codes.cpu().numpy(), wc)
-    assert np.array_equal(w.scales.cpu().numpy(), ws)
+    gc, gs = untile_weight(w.codes.cpu().numpy(), w.scales.cpu().numpy(), inp["N"], inp["K"])
+    assert np.array_equal(gc, wc)
+    assert np.array_equal(gs, ws)
     assert w.desc.view[0].base == w.desc.view[1].base == w.scales.data_ptr()
 
 
@@ -132,5 +133,6 @@ def test_pack_weight_edges():
     wc, ws = O.pack_weight(w)
     p = sq.sharq_pack_weight(dev_bf16(w))
     torch.cuda.synchronize()
-    assert np.array_equal(p.codes.cpu().numpy(), wc)
-    assert np.array_equal(p.scales.cpu().numpy(), ws)
+    gc, gs = untile_weight(p.codes.cpu().numpy(), p.scales.cpu().numpy(), w.shape[0], w.shape[1])
+    assert np.array_equal(gc, wc)
+    assert np.array_equal(gs, ws)
