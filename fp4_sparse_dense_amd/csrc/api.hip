@@ -8,7 +8,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/sharq.h"
+#include "sharq.h"
 #include "launch.h"
 
 namespace {

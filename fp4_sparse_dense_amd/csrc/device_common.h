@@ -89,4 +89,40 @@ __device__ __forceinline__ void fp4_unpack2(uint32_t packed, float& lo, float& h
   hi = v[1];
 }
 
+// ---------------------------------------------------------------- buffer copies
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for a raw byte buffer (stride 0, offsets checked against
+// num_records: reads past the end return zero).
+__device__ __forceinline__ u32x4 make_desc(const void* p, uint64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t n = bytes >= 0x7FFFFFFFull ? 0x7FFFFFFFu : (uint32_t)bytes;
+  return (u32x4){(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, n, 0x00020000u};
+}
+
+// Global -> LDS copies (buffer_load ... lds): lane l's bytes land at
+// lds_off + l*size.  They are issued from inline asm so that the compiler does
+// not make every later LDS access wait for them; the kernel waits for them
+// itself (vmcnt) before the barrier that publishes a stage.  They have no
+// register results.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_off, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t lds_off, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every buffer: reads as zero
+
+// s_waitcnt with vmcnt <= VM and lgkmcnt <= LG (expcnt not waited); gfx9 encoding
+template <int VM, int LG>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | ((LG & 15) << 8));
+}
+
 }  // namespace sharq

@@ -35,7 +35,8 @@ __device__ __forceinline__ v4f mfma_fp4(v8i a, v8i b, v4f c, uint32_t sa, uint32
 // ---------------------------------------------------------------------------
 // 2:4 expansion.  The compressed operand of 32 logical K positions (8 groups)
 // is 16 kept nibbles (group g in byte g, lower offset in the low nibble) plus
-// 8 metadata nibbles (group g: i0 | i1<<2 in nibble g).  The result is 32
+// 8 metadata nibbles (group g: i0 | i1<<2 in nibble g); codes_lo holds groups
+// 0-3, codes_hi groups 4-7.  The result is 32
 // dense nibbles with zero codes at dropped positions.  Two groups are handled
 // per dword, one in each 16-bit half, with byte permutes and packed shifts.
 // ---------------------------------------------------------------------------
@@ -107,8 +108,8 @@ __global__ __launch_bounds__(256) void dual_gemm_direct(GemmArgs g) {
       const bool ok = rb < RB;
       const int64_t tile = rb * KB + ks;
       uint4 rq = ok ? *reinterpret_cast<const uint4*>(g.r_codes + tile * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
-      uint32_t lo = ok ? *reinterpret_cast<const uint32_t*>(g.s_codes + tile * 512 + lane * 4) : 0u;
-      uint32_t hi = ok ? *reinterpret_cast<const uint32_t*>(g.s_codes + tile * 512 + 256 + lane * 4) : 0u;
+      const uint2 sq = ok ? *reinterpret_cast<const uint2*>(g.s_codes + tile * 512 + lane * 8) : make_uint2(0, 0);
+      const uint32_t lo = sq.x, hi = sq.y;
       uint32_t mq = ok ? *reinterpret_cast<const uint32_t*>(g.s_meta + tile * 256 + lane * 4) : 0x44444444u;
       ar[i] = as_operand(rq);
       as[i] = as_operand(expand_chunk(lo, hi, mq));
@@ -161,41 +162,6 @@ __global__ __launch_bounds__(256) void dual_gemm_direct(GemmArgs g) {
 // slot it will become, and the wave that copied it expands it in place.  Each
 // weight fragment feeds the sparse and the dense MFMA of the same output tile.
 // ---------------------------------------------------------------------------
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource for a raw byte buffer (stride 0, offsets checked against
-// num_records: reads past the end return zero).
-__device__ __forceinline__ u32x4 make_desc(const void* p, uint64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t n = bytes >= 0x7FFFFFFFull ? 0x7FFFFFFFu : (uint32_t)bytes;
-  return (u32x4){(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, n, 0x00020000u};
-}
-
-// Global -> LDS copies (buffer_load ... lds): lane l's bytes land at
-// lds_off + l*size.  They are issued from inline asm so that the compiler does
-// not make every later LDS access wait for them; the kernel waits for them
-// itself (vmcnt) before the barrier that publishes a stage.  They have no
-// register results.
-__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_off, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-__device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t lds_off, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every buffer: reads as zero
-
-// s_waitcnt with vmcnt <= VM and lgkmcnt <= LG (expcnt not waited); gfx9 encoding
-template <int VM, int LG>
-__device__ __forceinline__ void wait_vm_lgkm() {
-  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | ((LG & 15) << 8));
-}
-
 template <int BM, int BN, int NWM, int NWN, int NST>
 struct TileCfg {
   static constexpr int kWaves = NWM * NWN;
@@ -295,7 +261,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   };
 
   // Expand this wave's backbone blocks of the stage at st in place: every lane
-  // reads its 12 compressed bytes, the wave waits for all of its reads, then
+  // reads its 12 compressed bytes (8 code bytes at 8*lane, 4 metadata bytes at
+  // 512 + 4*lane), the wave waits for all of its reads, then
   // every lane writes its 16 dense bytes (a block belongs to one wave).
   auto expand_store = [&](uint8_t* st) {
     uint32_t lo[kSB], hi[kSB], mt[kSB];
@@ -304,8 +271,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
       const int b = wave + i * C::kWaves;
       if (b < C::kMB) {
         const uint8_t* blk = st + C::kOffAS + b * 1024;
-        lo[i] = *reinterpret_cast<const uint32_t*>(blk + lane * 4);
-        hi[i] = *reinterpret_cast<const uint32_t*>(blk + 256 + lane * 4);
+        const uint2 sq = *reinterpret_cast<const uint2*>(blk + lane * 8);
+        lo[i] = sq.x;
+        hi[i] = sq.y;
         mt[i] = *reinterpret_cast<const uint32_t*>(blk + 512 + lane * 4);
       }
     }

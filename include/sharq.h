@@ -32,8 +32,8 @@
  *    and K to KB*128 (KB = ceil(K/128)); padding holds zero codes and zero
  *    scale bytes.  Per tile (rb, kb), tiles ordered rb-major then kb:
  *      dense codes    1024 B: lane l at 16*l (its 32 codes)
- *      2:4 codes       512 B: two planes of 256 B; plane p, lane l at 256*p + 4*l
- *                             holds the kept codes of groups 4p..4p+3 of the lane
+ *      2:4 codes       512 B: lane l at 8*l, its 16 kept codes (groups 0-3 in
+ *                             the first 4 bytes, groups 4-7 in the next 4)
  *      2:4 metadata    256 B: lane l at 4*l, nibble g = group g of the lane
  *    Scale bytes are K-step-major: [KB][RB][64], byte l of (kb, rb) is the
  *    E8M0 of lane l's 32-block.  Canonical row-major arrays follow by

@@ -30,7 +30,7 @@ def untile_dense(buf, rows, K, label="codes"):
 
 def untile_sparse_codes(buf, rows, K):
     RB, KB = _dims(rows, K)
-    t = np.asarray(buf).reshape(RB, KB, 2, 4, 16, 4).transpose(0, 4, 1, 3, 2, 5)
+    t = np.asarray(buf).reshape(RB, KB, 4, 16, 8).transpose(0, 3, 1, 2, 4)
     return _crop(t.reshape(RB * 16, KB * 32), rows, K // 4, "s_codes")
 
 
