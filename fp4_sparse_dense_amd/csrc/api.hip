@@ -149,6 +149,7 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
   if (M < 0 || K <= 0 || K % 32) return fail(SHARQ_ERR_INVALID_ARG, "bad shape M=%lld K=%lld (K%%32 must be 0)", (long long)M, (long long)K);
   if (K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "K too large");
   if (gamma_bf16_dev && K > 32768) return fail(SHARQ_ERR_INVALID_ARG, "RMSNorm rows are limited to K <= 32768");
+  if (ldx > (int64_t(1) << 26)) return fail(SHARQ_ERR_INVALID_ARG, "ldx=%lld exceeds 2^26 elements", (long long)ldx);
   if (n != 2 || m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built (got %d:%d)", (int)n, (int)m);
   sharq_status s = check_fmt(fmt);
   if (s) return s;

@@ -11,19 +11,16 @@
 // loads (16 rows x 128 K per tile, lane order; see include/sharq.h), padding
 // rows and the K tail of the last tile as zeros.
 //
-// Mapping: one wavefront per activation row.  A row is covered in slots of
-// 512 elements; in a slot lane l owns elements [8l, 8l+8) (one 16-byte load),
-// so a wave load is 1 KiB contiguous, a 2:4 group never leaves a lane and a
-// 32-element MX block spans an aligned quad of lanes.  Up to eight slots are
-// loaded before any is processed (8 KiB in flight per wave).  All arithmetic is
-// binary32 with no contraction (built with -ffp-contract=off).
+// All arithmetic is binary32 with no contraction (built with -ffp-contract=off),
+// one rounding per operation, in the order the CPU reference states.
 #include "device_common.h"
 #include "launch.h"
 
 namespace sharq {
 
+// weight packing: one wave per row, slots of 512 elements, lane l owns
+// elements [8l, 8l+8) of a slot (a 32-element block spans an aligned quad)
 constexpr int kSlot = 512;
-constexpr int kRegSlots = 8;
 constexpr int kRowsPerBlock = 4;
 
 // ss -> 1/sqrt(ss/K + eps), each step correctly rounded to binary32.  The
@@ -49,19 +46,79 @@ struct Block32 {
 };
 
 // 2:4 mask of one group: element k is kept iff at most one other element
-// beats it (larger magnitude, or equal magnitude and lower index).  With
-// bij = |a_i| >= |a_j| for i < j, "at most one beater" is a majority of three
-// comparisons; ranks are a permutation, so exactly two are kept.
-struct Keep4 { bool k0, k1, k2, k3; };
-__device__ __forceinline__ Keep4 keep_2of4(float a0, float a1, float a2, float a3) {
-  const bool b01 = fabsf(a0) >= fabsf(a1), b02 = fabsf(a0) >= fabsf(a2), b03 = fabsf(a0) >= fabsf(a3);
-  const bool b12 = fabsf(a1) >= fabsf(a2), b13 = fabsf(a1) >= fabsf(a3), b23 = fabsf(a2) >= fabsf(a3);
-  Keep4 k;
-  k.k0 = (b01 && b02) || (b01 && b03) || (b02 && b03);
-  k.k1 = (!b01 && b12) || (!b01 && b13) || (b12 && b13);
-  k.k2 = (!b02 && !b12) || (!b02 && b23) || (!b12 && b23);
-  k.k3 = (!b03 && !b13) || (!b03 && !b23) || (!b13 && !b23);
+// beats it (larger magnitude, or equal magnitude and lower index).
+//  * Element 0 wins every tie, so it is kept iff at most one of |a1|,|a2|,|a3|
+//    exceeds |a0|, i.e. iff |a0| >= med3(|a1|,|a2|,|a3|).
+//  * Element 3 loses every tie, so it is kept iff at most one of
+//    |a0|,|a1|,|a2| reaches |a3|, i.e. iff med3(|a0|,|a1|,|a2|) < |a3|.
+//  * Exactly two are kept.  If both or neither of elements 0 and 3 are kept,
+//    elements 1 and 2 are both dropped or both kept; if exactly one is, the
+//    other kept element is whichever of 1 and 2 beats the other
+//    (|a1| >= |a2| for element 1).
+// group_keep evaluates this with lane masks in one asm block (so no mask
+// outlives its group), selects the kept values in index order (s0 = first
+// kept, s1 = second) and shifts the group's metadata nibble i0 | i1 << 2 into
+// `meta` most significant bit first (v_addc doubles and adds the carry-in
+// mask).  Its masks go to group_residual, which replaces a kept a_i by
+// a_i - dq_i, dq the dequantised kept value (dlo for the first kept, dhi for
+// the second); dropped elements keep a_i.
+struct Keep { uint64_t k0, k1, k2, k3; };
+
+__device__ __forceinline__ Keep group_keep(float a0, float a1, float a2, float a3, float& s0, float& s1,
+                                           uint32_t& meta) {
+  Keep k;
+  uint64_t b12, e, n, c;
+  float m;
+  asm volatile(
+      "v_med3_f32 %[m], |%[a1]|, |%[a2]|, |%[a3]|\n\t"
+      "v_cmp_ge_f32_e64 %[k0], |%[a0]|, %[m]\n\t"
+      "v_med3_f32 %[m], |%[a0]|, |%[a1]|, |%[a2]|\n\t"
+      "v_cmp_lt_f32_e64 %[k3], %[m], |%[a3]|\n\t"
+      "v_cmp_ge_f32_e64 %[b12], |%[a1]|, |%[a2]|\n\t"
+      // e = exactly one of k0, k3; n = neither
+      "s_xor_b64 %[e], %[k0], %[k3]\n\t"
+      "s_nor_b64 %[n], %[k0], %[k3]\n\t"
+      "s_and_b64 %[c], %[e], %[b12]\n\t"
+      "s_or_b64 %[k1], %[n], %[c]\n\t"
+      "s_andn2_b64 %[c], %[e], %[b12]\n\t"
+      "s_or_b64 %[k2], %[n], %[c]\n\t"
+      // s0 = k0 ? a0 : (k1 ? a1 : a2);  s1 = k3 ? a3 : (k2 ? a2 : a1)
+      "v_cndmask_b32_e64 %[s0], %[a2], %[a1], %[k1]\n\t"
+      "v_cndmask_b32_e64 %[s0], %[s0], %[a0], %[k0]\n\t"
+      "v_cndmask_b32_e64 %[s1], %[a1], %[a2], %[k2]\n\t"
+      "v_cndmask_b32_e64 %[s1], %[s1], %[a3], %[k3]\n\t"
+      // nibble bits, high to low: i1 = k3 ? 3 : (k2 ? 2 : 1), i0 = k0 ? 0 : (k1 ? 1 : 2)
+      "s_or_b64 %[c], %[k3], %[k2]\n\t"
+      "v_addc_co_u32_e64 %[meta], %[e], %[meta], %[meta], %[c]\n\t"
+      "s_orn2_b64 %[c], %[k3], %[k2]\n\t"
+      "v_addc_co_u32_e64 %[meta], %[e], %[meta], %[meta], %[c]\n\t"
+      "s_nor_b64 %[c], %[k0], %[k1]\n\t"
+      "v_addc_co_u32_e64 %[meta], %[e], %[meta], %[meta], %[c]\n\t"
+      "s_andn2_b64 %[c], %[k1], %[k0]\n\t"
+      "v_addc_co_u32_e64 %[meta], %[e], %[meta], %[meta], %[c]"
+      : [s0] "=&v"(s0), [s1] "=&v"(s1), [meta] "+v"(meta), [m] "=&v"(m), [k0] "=&s"(k.k0), [k1] "=&s"(k.k1),
+        [k2] "=&s"(k.k2), [k3] "=&s"(k.k3), [b12] "=&s"(b12), [e] "=&s"(e), [n] "=&s"(n), [c] "=&s"(c)
+      : [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
+      : "scc");
   return k;
+}
+
+__device__ __forceinline__ void group_residual(float& a0, float& a1, float& a2, float& a3, float dlo, float dhi,
+                                               const Keep& k) {
+  float t;
+  asm volatile(
+      "v_sub_f32_e32 %[t], %[a0], %[dlo]\n\t"
+      "v_cndmask_b32_e64 %[a0], %[a0], %[t], %[k0]\n\t"
+      "v_sub_f32_e32 %[t], %[a3], %[dhi]\n\t"
+      "v_cndmask_b32_e64 %[a3], %[a3], %[t], %[k3]\n\t"
+      "v_cndmask_b32_e64 %[t], %[dlo], %[dhi], %[k0]\n\t"
+      "v_sub_f32_e32 %[t], %[a1], %[t]\n\t"
+      "v_cndmask_b32_e64 %[a1], %[a1], %[t], %[k1]\n\t"
+      "v_cndmask_b32_e64 %[t], %[dhi], %[dlo], %[k3]\n\t"
+      "v_sub_f32_e32 %[t], %[a2], %[t]\n\t"
+      "v_cndmask_b32_e64 %[a2], %[a2], %[t], %[k2]"
+      : [a0] "+v"(a0), [a1] "+v"(a1), [a2] "+v"(a2), [a3] "+v"(a3), [t] "=&v"(t)
+      : [dlo] "v"(dlo), [dhi] "v"(dhi), [k0] "s"(k.k0), [k1] "s"(k.k1), [k2] "s"(k.k2), [k3] "s"(k.k3));
 }
 
 __device__ __forceinline__ float abs_max3(float m, float a, float b) {
@@ -84,128 +141,144 @@ __device__ __forceinline__ void fp4_dec(uint32_t packed, float scale, float& lo,
   hi = v[1];
 }
 
-// One group of four: mask, kept codes into byte SEL of *codes, metadata
-// nibble, and the residual of the four elements against the dequantised
-// backbone.  Returns the nibble.
-template <int SEL>
-__device__ __forceinline__ uint32_t group4(const float* a, float s_scale, uint32_t& codes, float* r) {
-  const Keep4 k = keep_2of4(a[0], a[1], a[2], a[3]);
-  const float s0 = k.k0 ? a[0] : (k.k1 ? a[1] : a[2]);   // kept values in k order
-  const float s1 = k.k3 ? a[3] : (k.k2 ? a[2] : a[1]);
-  codes = fp4_enc<SEL>(codes, s0, s1, s_scale);
-  float dlo, dhi;
-  fp4_dec<SEL>(codes, s_scale, dlo, dhi);
-  // a kept position is the group's first kept offset or its second;
-  // dropped positions keep v (v - (+0) == v for every v)
-  r[0] = a[0] - (k.k0 ? dlo : 0.0f);
-  r[1] = a[1] - (k.k1 ? (k.k0 ? dhi : dlo) : 0.0f);
-  r[2] = a[2] - (k.k2 ? ((k.k0 || k.k1) ? dhi : dlo) : 0.0f);
-  r[3] = a[3] - (k.k3 ? dhi : 0.0f);
-  const uint32_t i0 = k.k0 ? 0u : (k.k1 ? 1u : 2u), i1 = k.k3 ? 3u : (k.k2 ? 2u : 1u);
-  return i0 | (i1 << 2);
+// Group G of a block: mask, kept codes into byte G%4 of `codes`, metadata,
+// residual in place.
+template <int G>
+__device__ __forceinline__ void group4(float (&v)[32], float s_scale, uint32_t& codes, uint32_t& meta) {
+  float s0, s1, dlo, dhi;
+  const Keep k = group_keep(v[4 * G], v[4 * G + 1], v[4 * G + 2], v[4 * G + 3], s0, s1, meta);
+  codes = fp4_enc<G % 4>(codes, s0, s1, s_scale);
+  fp4_dec<G % 4>(codes, s_scale, dlo, dhi);
+  group_residual(v[4 * G], v[4 * G + 1], v[4 * G + 2], v[4 * G + 3], dlo, dhi, k);
 }
 
-__device__ __forceinline__ Block32 decompose32(const float (&v)[32]) {
+// The whole decomposition of one MX block; v is replaced by the residual.
+__device__ __forceinline__ Block32 decompose32(float (&v)[32]) {
   // S block scale: the block maximum of v is always kept, so amax(S) == amax(v)
   float am = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; i += 2) am = abs_max3(am, v[i], v[i + 1]);
-  const float ss = pow2(mx_shared_exp(__float_as_uint(am)));
+  const int es = mx_shared_exp(__float_as_uint(am));
+  const float ss = pow2(es);
 
+  // groups last to first: the metadata nibbles enter most significant first
   uint32_t lo = 0, hi = 0, meta = 0;
-  float r[32];
-  meta |= group4<0>(v + 0, ss, lo, r + 0);
-  meta |= group4<1>(v + 4, ss, lo, r + 4) << 4;
-  meta |= group4<2>(v + 8, ss, lo, r + 8) << 8;
-  meta |= group4<3>(v + 12, ss, lo, r + 12) << 12;
-  meta |= group4<0>(v + 16, ss, hi, r + 16) << 16;
-  meta |= group4<1>(v + 20, ss, hi, r + 20) << 20;
-  meta |= group4<2>(v + 24, ss, hi, r + 24) << 24;
-  meta |= group4<3>(v + 28, ss, hi, r + 28) << 28;
+  group4<7>(v, ss, hi, meta);
+  group4<6>(v, ss, hi, meta);
+  group4<5>(v, ss, hi, meta);
+  group4<4>(v, ss, hi, meta);
+  group4<3>(v, ss, lo, meta);
+  group4<2>(v, ss, lo, meta);
+  group4<1>(v, ss, lo, meta);
+  group4<0>(v, ss, lo, meta);
 
   float ar = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; i += 2) ar = abs_max3(ar, r[i], r[i + 1]);
+  for (int i = 0; i < 32; i += 2) ar = abs_max3(ar, v[i], v[i + 1]);
   const int er = mx_shared_exp(__float_as_uint(ar));
   const float rs = pow2(er);
   uint32_t rc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint32_t w = fp4_enc<0>(0u, r[8 * j], r[8 * j + 1], rs);
-    w = fp4_enc<1>(w, r[8 * j + 2], r[8 * j + 3], rs);
-    w = fp4_enc<2>(w, r[8 * j + 4], r[8 * j + 5], rs);
-    rc[j] = fp4_enc<3>(w, r[8 * j + 6], r[8 * j + 7], rs);
+    uint32_t w = fp4_enc<0>(0u, v[8 * j], v[8 * j + 1], rs);
+    w = fp4_enc<1>(w, v[8 * j + 2], v[8 * j + 3], rs);
+    w = fp4_enc<2>(w, v[8 * j + 4], v[8 * j + 5], rs);
+    rc[j] = fp4_enc<3>(w, v[8 * j + 6], v[8 * j + 7], rs);
   }
 
   Block32 o;
   o.r_codes = make_uint4(rc[0], rc[1], rc[2], rc[3]);
   o.s_codes = make_uint2(lo, hi);
   o.meta = meta;
-  o.s_e8 = (uint32_t)(mx_shared_exp(__float_as_uint(am)) + 127);
+  o.s_e8 = (uint32_t)(es + 127);
   o.r_e8 = (uint32_t)(er + 127);
   return o;
 }
 
 // ---------------------------------------------------------------------------
-// Prep kernel.  A workgroup owns 8 rows (one half of a 16-row tile) and all of
-// K, in chunks of up to 4096 elements staged in LDS.  Rows arrive by 1 KiB
-// contiguous global -> LDS copies; inside each 256-byte window the 16-byte
-// units of row r are XOR-permuted by sw(r) so that the block reads below hit
-// 16 distinct bank groups per 16-lane phase (64 banks x 4 bytes).
+// Prep kernel.  A workgroup owns 8 rows (one half of a 16-row tile block) and
+// all of K.  K is cut into units of 256 elements (two K tiles); wave w of the
+// 16 owns units w, w+16, w+32, ... and streams them through a private ring of LDS
+// slots (8 rows x 512 bytes = 4 KiB each) filled by its own global -> LDS
+// copies, so no other wave ever waits for them.  The one workgroup-wide step
+// is the RMSNorm sum of squares.
 //
-// A wave's 64 lanes cover 8 rows x 2 K tiles: lane l takes row l%8, 32-chunk
-// (l/8)%4 and tile l/32, i.e. one MX block, and writes it in tile-lane order
-// (chunk*16 + half*8 + row), so every output store is a contiguous run.
+// Slot layout: copy c (0..3) of a unit fills bytes [1024c, 1024c+1024); its
+// lane l brings 16 bytes of row l/8 from unit bytes 128c + 16*((l%8) ^ sw(l/8)).
+// A reader lane takes row r8 = l%8, chunk c4 = (l/8)%4 and tile t2 = l/32 (one
+// MX block): copy 2*t2 + c4/2, 16-byte pieces (c4%2)*4 + i.  The XOR by
+// sw(r) = (r/2)%4 makes each 16-lane phase of those reads touch 16 distinct
+// 16-byte bank groups (64 banks x 4 bytes).  Output lane order inside a tile
+// is chunk*16 + row, so the 8 lanes of one chunk store one contiguous run.
 //
-// RMSNorm: the sum of squares of a block is a pairwise tree of its 32 squares
-// (the leaf pairs as fma(x0,x0,x1*x1), exact since bf16 squares are exact in
-// binary32), the blocks of a 256-element unit combine by lane exchanges in K
-// order, units by a 16-leaf tree in LDS, chunks by an 8-leaf tree: all of it
-// is the balanced tree of the zero-padded row.
+// A wave waits for a unit with a vmcnt equal to the copies it issued after
+// that unit (loads complete in order).  A unit's stores are issued one
+// iteration late -- after the next unit's copy, before a block of arithmetic --
+// so a wait seldom has to cover stores that were just issued.
+//
+// RMSNorm: the sum of squares of a row is the balanced pairwise tree of its
+// zero-padded squares: per block a 32-leaf tree (each square rounded on its
+// own, as a square below 2^-126 is not exact), per unit the 8
+// blocks by lane exchanges in K order, then the units by an in-place tree in
+// LDS over the next power of two.
 // ---------------------------------------------------------------------------
 constexpr int kPrepRows = 8;
-constexpr int kPrepThreads = 512;
-constexpr int kPrepChunk = 4096;                 // K elements per LDS stage
-constexpr int kPrepUnits = kPrepChunk / 256;     // 256-element units per chunk (16)
-constexpr int kPrepMaxChunks = 8;                // K <= 32768 with RMSNorm
+constexpr int kPrepWaves = 16;
+constexpr int kPrepThreads = kPrepWaves * 64;
+constexpr int kUnitK = 256;
+constexpr int kSlotBytes = kPrepRows * kUnitK * 2;
+constexpr uint32_t kPrepLdsMax = 160 * 1024;
+constexpr int kMaxSlots = 4;
 
-__device__ __forceinline__ uint32_t prep_swz(int r) { return (uint32_t)((r & 3) | ((r & 4) << 1)); }
-
-struct PrepLds {
-  uint32_t row_bytes;   // LDS bytes per staged row (multiple of 1 KiB)
-  uint32_t off_g;       // gamma, binary32
-  uint32_t off_us;      // unit sums [16][8]
-  uint32_t off_cs;      // chunk sums [8][8]
-  uint32_t total;
+struct PrepPlan {
+  int nunits;      // units of 256 along K
+  int units_p2;    // next power of two (RMSNorm tree width)
+  int slots;       // LDS slots per wave
+  int single;      // RMSNorm rows staged once (every unit of the wave resident)
+  int gamma_f32;   // gamma held as binary32 (else bf16 words)
+  uint32_t off_gamma, off_sums, total;
 };
-__host__ __device__ inline PrepLds prep_lds_layout(int K) {
-  PrepLds L;
-  const int kc = K < kPrepChunk ? ((K + 511) / 512) * 512 : kPrepChunk;
-  L.row_bytes = (uint32_t)kc * 2;
-  L.off_g = L.row_bytes * kPrepRows;
-  L.off_us = L.off_g + (uint32_t)kc * 4;
-  L.off_cs = L.off_us + kPrepUnits * kPrepRows * 4;
-  L.total = L.off_cs + kPrepMaxChunks * kPrepRows * 4;
-  return L;
+
+static PrepPlan prep_plan(int K, bool norm) {
+  PrepPlan p{};
+  p.nunits = (K + kUnitK - 1) / kUnitK;
+  p.units_p2 = 1;
+  while (p.units_p2 < p.nunits) p.units_p2 *= 2;
+  const int per_wave = (p.nunits + kPrepWaves - 1) / kPrepWaves;
+  const uint32_t kp = (uint32_t)p.nunits * kUnitK;
+  const uint32_t sums = norm ? (uint32_t)p.units_p2 * kPrepRows * 4 : 0;
+  for (int f32 = norm ? 1 : 0; f32 >= 0; --f32) {
+    const uint32_t gbytes = norm ? kp * (f32 ? 4u : 2u) : 0;
+    const uint32_t avail = kPrepLdsMax - gbytes - sums;
+    int s = (int)(avail / (kPrepWaves * kSlotBytes));
+    s = s < kMaxSlots ? s : kMaxSlots;
+    p.gamma_f32 = f32;
+    p.single = norm && per_wave <= s;
+    // a single staging needs one slot per unit; a stream keeps one unit in
+    // flight per slot and gains nothing past the wave's units
+    const int want = per_wave > 0 ? per_wave : 1;
+    p.slots = p.single ? (per_wave > 0 ? per_wave : 1) : (want < s ? want : s);
+    p.off_gamma = (uint32_t)p.slots * kPrepWaves * kSlotBytes;
+    p.off_sums = p.off_gamma + gbytes;
+    p.total = p.off_sums + sums;
+    if (!norm || p.single || f32 == 0) break;
+  }
+  return p;
 }
 
-__device__ __forceinline__ float tree16(const float* p, int stride) {
-  float t[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) t[i] = p[i * stride];
-#pragma unroll
-  for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-    for (int i = 0; i < w; ++i) t[i] = t[2 * i] + t[2 * i + 1];
-  return t[0];
+// s_waitcnt vmcnt(4n): at most n units (4 copies each) still in flight
+__device__ __forceinline__ void wait_units(int n) {
+  if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (n == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
 }
 
-template <bool NORM>
+template <bool NORM, bool GF32>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
                                                             int64_t ldx, const uint16_t* __restrict__ gamma,
-                                                            float eps, PrepOut o) {
+                                                            float eps, PrepPlan P, PrepOut o) {
   extern __shared__ __align__(1024) uint8_t smem[];
-  const PrepLds L = prep_lds_layout(K);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -219,137 +292,167 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
   const int64_t row0 = rb * 16 + half * 8;
 
   const int KB = (K + 127) / 128;
-  const int nchunk = (K + kPrepChunk - 1) / kPrepChunk;
   const int r8 = lane & 7, c4 = (lane >> 3) & 3, t2 = lane >> 5;
-  const int64_t my_row = row0 + r8;
-  const bool row_ok = my_row < M;
-  const uint32_t lds0 = lds_addr(smem);
-  const uint32_t sw_me = prep_swz(r8);
-  float* gs = reinterpret_cast<float*>(smem + L.off_g);
-  float* us = reinterpret_cast<float*>(smem + L.off_us);
-  float* cs = reinterpret_cast<float*>(smem + L.off_cs);
-  const int segs = (int)(L.row_bytes / 1024);
+  const bool row_ok = row0 + r8 < M;
+  const bool pad_rows = row0 + kPrepRows > M;
 
-  // stage chunk ch: rows by 1 KiB copies (wave-strided), gamma widened by every thread
-  auto stage = [&](int ch) {
-    const uint32_t kbyte0 = (uint32_t)ch * kPrepChunk * 2;
-    for (int j = wave; j < kPrepRows * segs; j += 8) {
-      const int r = j / segs, sg = j % segs;
-      const int64_t row = row0 + r;
-      const u32x4 d = make_desc(x + (row < M ? row : 0) * ldx, row < M ? (uint64_t)K * 2 : 0);
-      const uint32_t unit = (uint32_t)sg * 64 + ((uint32_t)lane ^ prep_swz(r));
-      lds_dma16(d, lds0 + (uint32_t)r * L.row_bytes + (uint32_t)sg * 1024, kbyte0 + unit * 16, 0);
+  // copy lanes: row lane/8, source piece (lane%8) ^ sw(row)
+  const int crow = lane >> 3;
+  const int cpiece = (lane & 7) ^ ((crow >> 1) & 3);
+  const bool crow_ok = row0 + crow < M;
+  const uint32_t clane_off = (uint32_t)crow * (uint32_t)ldx * 2u + (uint32_t)cpiece * 16u;
+  const int clane_k = cpiece * 8;
+  const int64_t rows_here = M - row0 < kPrepRows ? (M - row0 > 0 ? M - row0 : 0) : kPrepRows;
+  const u32x4 desc = make_desc(x + (rows_here > 0 ? row0 : 0) * ldx, (uint64_t)rows_here * (uint64_t)ldx * 2u);
+
+  const uint32_t ring_off = (uint32_t)wave * P.slots * kSlotBytes;
+  const uint32_t ring = lds_addr(smem) + ring_off;
+  const int nu_w = P.nunits > wave ? (P.nunits - wave + kPrepWaves - 1) / kPrepWaves : 0;
+  // streaming look-ahead: one unit per slot.  A slot is refilled as soon as
+  // its block reads have returned (the copies need no registers), so all
+  // slots can be in flight while a block is being decomposed.
+  const int D = P.slots;
+
+  auto issue = [&](int j) {
+    const int u = wave + kPrepWaves * j;
+    const uint32_t slot = ring + (uint32_t)(j % P.slots) * kSlotBytes;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = u * kUnitK + c * 64 + clane_k;
+      const uint32_t off = (crow_ok && k < K) ? clane_off + (uint32_t)u * 512u + (uint32_t)c * 128u : kOOB;
+      lds_dma16(desc, slot + (uint32_t)c * 1024u, off, 0);
     }
-    if (NORM) {
-      const int kc = (int)(L.row_bytes / 2);
-      for (int e = tid * 8; e < kc; e += kPrepThreads * 8) {
-        const int k = ch * kPrepChunk + e;
-        uint4 q = k < K ? *reinterpret_cast<const uint4*>(gamma + k) : make_uint4(0, 0, 0, 0);
-        float4 lo = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
-        float4 hi = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
-        *reinterpret_cast<float4*>(gs + e) = lo;
-        *reinterpret_cast<float4*>(gs + e + 4) = hi;
-      }
-    }
-    wait_vm_lgkm<0, 0>();
-    __syncthreads();
   };
 
-  // the lane's 32 bf16 of unit u (chunk-local), read back through the swizzle
-  auto load_block = [&](int u, uint32_t (&xw)[16]) {
-    const uint32_t g0 = (uint32_t)(2 * u + t2) * 16 + c4 * 4;   // first 16-byte unit
-    const uint8_t* rowp = smem + (uint32_t)r8 * L.row_bytes;
+  const uint32_t rsw = (uint32_t)((r8 >> 1) & 3);
+  auto read_block = [&](int j, uint32_t (&xw)[16]) {
+    const uint8_t* base = smem + ring_off + (uint32_t)(j % P.slots) * kSlotBytes +
+                          (uint32_t)(2 * t2 + (c4 >> 1)) * 1024u + (uint32_t)r8 * 128u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t g = g0 + i;
-      const uint4 q = *reinterpret_cast<const uint4*>(rowp + (((g & ~15u) | ((g & 15u) ^ sw_me)) * 16));
+      const uint32_t p = (uint32_t)((c4 & 1) * 4 + i) ^ rsw;
+      const uint4 q = *reinterpret_cast<const uint4*>(base + p * 16u);
       xw[4 * i] = q.x; xw[4 * i + 1] = q.y; xw[4 * i + 2] = q.z; xw[4 * i + 3] = q.w;
     }
   };
 
-  // balanced tree of the 32 squares of a block
-  auto block_ss = [&](const uint32_t (&xw)[16]) {
-    float p[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float a = bf16_lo(xw[j]), b = bf16_hi(xw[j]);
-      p[j] = __builtin_fmaf(a, a, b * b);
-    }
-#pragma unroll
-    for (int w2 = 8; w2 >= 1; w2 >>= 1)
-#pragma unroll
-      for (int j = 0; j < w2; ++j) p[j] = p[2 * j] + p[2 * j + 1];
-    return p[0];
-  };
-
-  const int nunit_tot = (KB + 1) / 2;
-
-  // ---- RMSNorm denominators
+  // ---- RMSNorm denominator of row r8
   float inv = 1.0f;
   if (NORM) {
-    for (int ch = 0; ch < nchunk; ++ch) {
-      if (nchunk > 1 || ch == 0) stage(ch);
-      const int nu = min(kPrepUnits, nunit_tot - ch * kPrepUnits);
-      for (int u = wave; u < kPrepUnits; u += 8) {
-        float t = 0.0f;
-        if (u < nu) {
-          uint32_t xw[16];
-          load_block(u, xw);
-          t = block_ss(xw);
-          t = t + __shfl_xor(t, 8, 64);    // blocks of a tile, in K order
-          t = t + __shfl_xor(t, 16, 64);
-          t = t + __shfl_xor(t, 32, 64);   // the two tiles of the unit
-        }
-        if (lane < 8) us[u * kPrepRows + lane] = t;
+    float* sums = reinterpret_cast<float*>(smem + P.off_sums);
+    // gamma into LDS (binary32, or bf16 words for long rows), zero past K
+    const int kp = P.nunits * kUnitK;
+    for (int e = tid * 8; e < kp; e += kPrepThreads * 8) {
+      const uint4 q = e < K ? *reinterpret_cast<const uint4*>(gamma + e) : make_uint4(0, 0, 0, 0);
+      if (GF32) {
+        float* gs = reinterpret_cast<float*>(smem + P.off_gamma);
+        *reinterpret_cast<float4*>(gs + e) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+        *reinterpret_cast<float4*>(gs + e + 4) = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
+      } else {
+        *reinterpret_cast<uint4*>(smem + P.off_gamma + e * 2) = q;
       }
-      __syncthreads();
-      if (tid < kPrepRows) cs[ch * kPrepRows + tid] = tree16(us + tid, kPrepRows);
-      __syncthreads();
     }
-    float c8[kPrepMaxChunks];
+    for (int i = P.nunits * kPrepRows + tid; i < P.units_p2 * kPrepRows; i += kPrepThreads) sums[i] = 0.0f;
+
+    auto unit_ss = [&](const uint32_t (&xw)[16], int j) {
+      float p[16];
 #pragma unroll
-    for (int i = 0; i < kPrepMaxChunks; ++i) c8[i] = i < nchunk ? cs[i * kPrepRows + r8] : 0.0f;
+      for (int i = 0; i < 16; ++i) {
+        const float a = bf16_lo(xw[i]), b = bf16_hi(xw[i]);
+        p[i] = a * a + b * b;
+      }
 #pragma unroll
-    for (int w2 = 4; w2 >= 1; w2 >>= 1)
+      for (int w2 = 8; w2 >= 1; w2 >>= 1)
 #pragma unroll
-      for (int i = 0; i < w2; ++i) c8[i] = c8[2 * i] + c8[2 * i + 1];
-    inv = rms_inverse(c8[0], K, eps);
+        for (int i = 0; i < w2; ++i) p[i] = p[2 * i] + p[2 * i + 1];
+      float t = p[0];
+      t = t + __shfl_xor(t, 8, 64);    // blocks of a tile, in K order
+      t = t + __shfl_xor(t, 16, 64);
+      t = t + __shfl_xor(t, 32, 64);   // the two tiles of the unit
+      if (lane < 8) sums[(wave + kPrepWaves * j) * kPrepRows + lane] = t;
+    };
+
+    if (P.single) {
+      for (int j = 0; j < nu_w; ++j) issue(j);
+      for (int j = 0; j < nu_w; ++j) {
+        wait_units(nu_w - 1 - j);
+        uint32_t xw[16];
+        read_block(j, xw);
+        unit_ss(xw, j);
+      }
+    } else {
+      for (int j = 0; j < D && j < nu_w; ++j) issue(j);
+      for (int j = 0; j < nu_w; ++j) {
+        wait_units(min(D - 1, nu_w - 1 - j));
+        uint32_t xw[16];
+        read_block(j, xw);
+        if (j + D < nu_w) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot j % D read back
+          issue(j + D);
+        }
+        unit_ss(xw, j);
+      }
+    }
+    for (int s = 1; s < P.units_p2; s *= 2) {
+      __syncthreads();
+      const int pairs = P.units_p2 / (2 * s);
+      for (int i = tid; i < pairs * kPrepRows; i += kPrepThreads) {
+        const int a = (i / kPrepRows) * 2 * s, r = i % kPrepRows;
+        sums[a * kPrepRows + r] = sums[a * kPrepRows + r] + sums[(a + s) * kPrepRows + r];
+      }
+    }
+    __syncthreads();
+    inv = rms_inverse(sums[r8], K, eps);
   }
 
-  // ---- decomposition, chunk by chunk
-  for (int ch = 0; ch < nchunk; ++ch) {
-    if (!NORM || nchunk > 1) {
-      if (ch > 0 || NORM) __syncthreads();   // previous chunk fully read
-      stage(ch);
-    }
-    const int nu = min(kPrepUnits, nunit_tot - ch * kPrepUnits);
-    for (int u = wave; u < nu; u += 8) {
-      const int kt = ch * (kPrepChunk / 128) + 2 * u + t2;     // global K tile of this lane
-      if (kt >= KB) continue;
-      const int kloc = (2 * u + t2) * 128 + c4 * 32;           // chunk-local first element
-      const bool live = row_ok && ch * kPrepChunk + kloc < K;  // real input (else zero padding)
-      uint32_t xw[16];
-      load_block(u, xw);
-      float v[32];
+  // ---- decomposition
+  auto compute = [&](const uint32_t (&xw)[16], int j) {
+    float v[32];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) { v[2 * j] = bf16_lo(xw[j]); v[2 * j + 1] = bf16_hi(xw[j]); }
-      if (NORM) {
+    for (int i = 0; i < 16; ++i) { v[2 * i] = bf16_lo(xw[i]); v[2 * i + 1] = bf16_hi(xw[i]); }
+    const int u = wave + kPrepWaves * j;
+    const int kb = (2 * u + t2) * 128 + c4 * 32;   // first element of the block
+    if (NORM) {
+      if (GF32) {
+        const float* gs = reinterpret_cast<const float*>(smem + P.off_gamma) + kb;
 #pragma unroll
         for (int i = 0; i < 32; i += 4) {
-          const float4 gv = *reinterpret_cast<const float4*>(gs + kloc + i);
-          v[i] = (v[i] * inv) * gv.x;
-          v[i + 1] = (v[i + 1] * inv) * gv.y;
-          v[i + 2] = (v[i + 2] * inv) * gv.z;
-          v[i + 3] = (v[i + 3] * inv) * gv.w;
+          const float4 g = *reinterpret_cast<const float4*>(gs + i);
+          v[i] = (v[i] * inv) * g.x;
+          v[i + 1] = (v[i + 1] * inv) * g.y;
+          v[i + 2] = (v[i + 2] * inv) * g.z;
+          v[i + 3] = (v[i + 3] * inv) * g.w;
+        }
+      } else {
+        const uint8_t* gb = smem + P.off_gamma + kb * 2;
+#pragma unroll
+        for (int i = 0; i < 32; i += 8) {
+          const uint4 g = *reinterpret_cast<const uint4*>(gb + i * 2);
+          const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            v[i + 2 * h] = (v[i + 2 * h] * inv) * bf16_lo(gw[h]);
+            v[i + 2 * h + 1] = (v[i + 2 * h + 1] * inv) * bf16_hi(gw[h]);
+          }
         }
       }
-      if (!live) {
+      // positions past K or rows past M are zero input (x reads as zero, but
+      // x * inv may not be zero when inv is not finite)
+      if (pad_rows || (u + 1) * kUnitK > K) {
+        if (!(row_ok && kb < K)) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+          for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+        }
       }
-      const Block32 b = decompose32(v);
+    }
+    return decompose32(v);
+  };
+
+  const int tl = c4 * 16 + (int)half * 8 + r8;
+  auto store = [&](const Block32& b, int j) {
+    const int kt = 2 * (wave + kPrepWaves * j) + t2;
+    if (kt < KB) {
       const int64_t tile = rb * KB + kt;
-      const int tl = c4 * 16 + (int)half * 8 + r8;
       *reinterpret_cast<uint4*>(o.r_codes + tile * 1024 + tl * 16) = b.r_codes;
       *reinterpret_cast<uint2*>(o.s_codes + tile * 512 + tl * 8) = b.s_codes;
       *reinterpret_cast<uint32_t*>(o.s_meta + tile * 256 + tl * 4) = b.meta;
@@ -357,7 +460,31 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
       o.s_scales[sc] = (uint8_t)b.s_e8;
       o.r_scales[sc] = (uint8_t)b.r_e8;
     }
+  };
+
+  Block32 prev;
+  if (NORM && P.single) {
+    for (int j = 0; j < nu_w; ++j) {
+      uint32_t xw[16];
+      read_block(j, xw);
+      if (j > 0) store(prev, j - 1);
+      prev = compute(xw, j);
+    }
+  } else {
+    for (int j = 0; j < D && j < nu_w; ++j) issue(j);
+    for (int j = 0; j < nu_w; ++j) {
+      wait_units(min(D - 1, nu_w - 1 - j));
+      uint32_t xw[16];
+      read_block(j, xw);
+      if (j + D < nu_w) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot j % D read back
+        issue(j + D);
+      }
+      if (j > 0) store(prev, j - 1);
+      prev = compute(xw, j);
+    }
   }
+  if (nu_w > 0) store(prev, nu_w - 1);
 }
 
 // Weight payload: MXFP4 over each 32-block of a row of W, no mask, no norm.
@@ -401,17 +528,18 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
 hipError_t launch_prepare(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
                           float eps, PrepOut out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const PrepLds L = prep_lds_layout(K);
-  const int64_t nwg = (M + 15) / 16 * 2;
-  auto kn = gamma ? prep_kernel<true> : prep_kernel<false>;
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[gamma ? 1 : 0]) {
-    hipError_t e = hipFuncSetAttribute((const void*)kn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       prep_lds_layout(kPrepChunk).total);
+  const PrepPlan P = prep_plan(K, gamma != nullptr);
+  if (P.slots < 1 || P.total > kPrepLdsMax) return hipErrorInvalidValue;
+  auto kn = !gamma ? prep_kernel<false, false> : (P.gamma_f32 ? prep_kernel<true, true> : prep_kernel<true, false>);
+  const int which = !gamma ? 0 : (P.gamma_f32 ? 1 : 2);
+  static bool attr_set[3] = {false, false, false};
+  if (!attr_set[which]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kn, hipFuncAttributeMaxDynamicSharedMemorySize, kPrepLdsMax);
     if (e != hipSuccess) return e;
-    attr_set[gamma ? 1 : 0] = true;
+    attr_set[which] = true;
   }
-  hipLaunchKernelGGL(kn, dim3((unsigned)nwg), dim3(kPrepThreads), L.total, stream, x, M, K, ldx, gamma, eps, out);
+  const int64_t nwg = (M + 15) / 16 * 2;
+  hipLaunchKernelGGL(kn, dim3((unsigned)nwg), dim3(kPrepThreads), P.total, stream, x, M, K, ldx, gamma, eps, P, out);
   return hipGetLastError();
 }
 

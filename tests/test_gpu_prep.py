@@ -57,6 +57,7 @@ def _edge_rows(K, rng):
     rows.append(np.tile(np.array([2, -2, 2, -2], np.float32), K // 4))  # ties with signs
     rows.append(rng.standard_normal(K).astype(np.float32) * np.float32(1e-39))   # subnormal bf16
     t = rng.standard_normal(K).astype(np.float32) * np.float32(2.0 ** -120); rows.append(t)   # tiny normals
+    u = rng.standard_normal(K).astype(np.float32) * np.float32(2.0 ** -68); rows.append(u)    # squares below 2^-126
     big = rng.standard_normal(K).astype(np.float32) * np.float32(1e37); rows.append(big)      # huge
     o = rng.standard_normal(K).astype(np.float32); o[::32] = 3e4; rows.append(o)               # outliers
     s = rng.standard_normal(K).astype(np.float32); s[5] = 7.0 * 2 ** 10; rows.append(s)
