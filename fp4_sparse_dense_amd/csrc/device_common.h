@@ -104,14 +104,25 @@ __device__ __forceinline__ u32x4 make_desc(const void* p, uint64_t bytes) {
 // lds_off + l*size.  They are issued from inline asm so that the compiler does
 // not make every later LDS access wait for them; the kernel waits for them
 // itself (vmcnt) before the barrier that publishes a stage.  They have no
-// register results.
+// register results.  M0 (the LDS base) needs one wait state between its SALU
+// write and the copy that reads it, hence the s_nop.
 __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_off, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 __device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t lds_off, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :: "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+// The same 16-byte copy for the lanes set in `lanes` only.  EXEC is switched
+// inside the asm and restored before it ends, so no branch is generated and
+// the copy stays in the caller's basic block.
+__device__ __forceinline__ void lds_dma16_lanes(u32x4 rsrc, uint32_t lds_off, uint32_t voff, uint32_t soff,
+                                                uint64_t lanes) {
+  uint64_t saved;
+  asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %1\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+               "buffer_load_dwordx4 %3, %4, %5 offen lds\n\ts_mov_b64 exec, %0"
+               : "=&s"(saved) : "s"(lanes), "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -119,10 +130,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every buffer: reads as zero
 
-// s_waitcnt with vmcnt <= VM and lgkmcnt <= LG (expcnt not waited); gfx9 encoding
-template <int VM, int LG>
-__device__ __forceinline__ void wait_vm_lgkm() {
-  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | ((LG & 15) << 8));
+// s_waitcnt vmcnt(VM): at most VM vector memory operations of this wave still
+// in flight.  Inline asm with a memory clobber, so the compiler keeps every
+// memory access on its side of the wait.
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VM) : "memory");
 }
 
 }  // namespace sharq

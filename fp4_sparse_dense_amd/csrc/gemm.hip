@@ -162,6 +162,10 @@ __global__ __launch_bounds__(256) void dual_gemm_direct(GemmArgs g) {
 // slot it will become, and the wave that copied it expands it in place.  Each
 // weight fragment feeds the sparse and the dense MFMA of the same output tile.
 // ---------------------------------------------------------------------------
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+// lane mask of lanes 0 .. n-1 (n <= 64)
+constexpr uint64_t low_lanes(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1); }
+
 template <int BM, int BN, int NWM, int NWN, int NST>
 struct TileCfg {
   static constexpr int kWaves = NWM * NWN;
@@ -185,7 +189,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
   extern __shared__ __align__(1024) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets go to M0
+  static_assert((C::kWaves & (C::kWaves - 1)) == 0, "wave count is a power of two");
+  // uniform (LDS targets go to M0); the mask tells the compiler wave < kWaves
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (C::kWaves - 1);
   const int KT = (g.K + 127) / 128;                       // K tiles (zero padded)
   const int64_t RB = (g.M + 15) / 16, NB = (g.N + 15) / 16; // padded 16-row blocks
 
@@ -209,11 +215,17 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   const uint32_t lds0 = lds_addr(smem);
   const int r16 = lane & 15, c4 = lane >> 4;
 
-  // ---- per-lane buffer offsets at K tile 0 (blocks past the padding -> kOOB),
-  // hoisted out of the K loop.  A-side blocks and W blocks are dealt to waves
-  // round-robin; waves 0, 1, 2 copy the S, R and W scale edges.
-  constexpr int kSB = (C::kMB + C::kWaves - 1) / C::kWaves;
+  // ---- copies.  A-side blocks and weight blocks are dealt to waves round
+  // robin; a wave whose share of weight blocks runs past the tile copies one
+  // of the first blocks again, and the three scale edges go to waves w % 3, so
+  // that every wave issues the same kItems copies per K step with no branch
+  // (identical data written twice to one place is harmless).  Per-lane buffer
+  // offsets are taken at K tile 0 (blocks past the padding -> kOOB) and
+  // hoisted out of the K loop.
+  static_assert(C::kMB % C::kWaves == 0, "A-side blocks split evenly over the waves");
+  constexpr int kSB = C::kMB / C::kWaves;
   constexpr int kWB = (C::kNB + C::kWaves - 1) / C::kWaves;
+  constexpr int kItems = 3 * kSB + kWB + 1;
   static_assert(C::kWaves >= 3, "scale copies need three waves");
 
   uint32_t offR[kSB], offC[kSB], offM[kSB];
@@ -225,66 +237,76 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     offC[i] = ok ? (uint32_t)(rb * KT) * 512u + lane * 16 : kOOB;   // lanes 0..31
     offM[i] = ok ? (uint32_t)(rb * KT) * 256u + lane * 16 : kOOB;   // lanes 0..15
   }
+  int wblk[kWB];
   uint32_t offW[kWB];
 #pragma unroll
   for (int i = 0; i < kWB; ++i) {
-    const int64_t nb = nb0 + wave + i * C::kWaves;
+    const int b = wave + i * C::kWaves;
+    wblk[i] = b < C::kNB ? b : b - C::kNB;
+    const int64_t nb = nb0 + wblk[i];
     offW[i] = nb < NB ? (uint32_t)(nb * KT) * 1024u + lane * 16 : kOOB;
   }
-  // scale edge: 16 lanes per 64-byte block; lanes past the tile edge are masked
+  // scale edge of this wave: 0 = backbone, 1 = residual, 2 = weight;
+  // 16 lanes per 64-byte block
+  const int edge = wave % 3;
   const int eb = lane >> 2;   // block of the edge this lane copies
   const uint32_t offScA = rb0 + eb < RB ? (uint32_t)((rb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
   const uint32_t offScW = nb0 + eb < NB ? (uint32_t)((nb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
-  const uint32_t strideScA = (uint32_t)RB * 64, strideScW = (uint32_t)g.w_scales_ld;
+  const u32x4 rs_edge = edge == 0 ? rs_ss : (edge == 1 ? rs_rs : rs_ws);
+  const uint32_t off_edge = edge == 2 ? offScW : offScA;
+  const uint32_t stride_edge = edge == 2 ? (uint32_t)g.w_scales_ld : (uint32_t)RB * 64;
+  const uint32_t lds_edge = edge == 0 ? C::kOffSS : (edge == 1 ? C::kOffSR : C::kOffSW);
+  const uint64_t lanes_edge = edge == 2 ? low_lanes(C::kNB * 4) : low_lanes(C::kMB * 4);
 
-  // Copy K tile ks into the LDS stage at byte offset st.
+  // copy item `it` of K step ks into the LDS stage at st: 3 per A-side block
+  // (dense codes, compressed codes, metadata), one per weight block, then the
+  // scale edge
+  auto issue_item = [&](int it, int ks, uint32_t st) {
+    if (it < 3 * kSB) {
+      const int i = it / 3, kind = it % 3;
+      const int b = wave + i * C::kWaves;
+      const uint32_t as = st + C::kOffAS + b * 1024;
+      if (kind == 0) lds_dma16(rs_rc, st + C::kOffAR + b * 1024, offR[i], (uint32_t)ks * 1024);
+      else if (kind == 1) lds_dma16_lanes(rs_sc, as, offC[i], (uint32_t)ks * 512, 0xFFFFFFFFull);
+      else lds_dma16_lanes(rs_sm, as + 512, offM[i], (uint32_t)ks * 256, 0xFFFFull);
+    } else if (it < 3 * kSB + kWB) {
+      const int i = it - 3 * kSB;
+      lds_dma16(rs_wc, st + C::kOffB + wblk[i] * 1024, offW[i], (uint32_t)ks * 1024);
+    } else {
+      lds_dma16_lanes(rs_edge, st + lds_edge, off_edge, (uint32_t)ks * stride_edge, lanes_edge);
+    }
+  };
   auto issue = [&](int ks, uint32_t st) {
-    const uint32_t so1k = (uint32_t)ks * 1024, so512 = (uint32_t)ks * 512, so256 = (uint32_t)ks * 256;
 #pragma unroll
-    for (int i = 0; i < kSB; ++i) {
-      const int b = wave + i * C::kWaves;
-      if (b < C::kMB) {
-        lds_dma16(rs_rc, st + C::kOffAR + b * 1024, offR[i], so1k);
-        const uint32_t as = st + C::kOffAS + b * 1024;
-        if (lane < 32) lds_dma16(rs_sc, as, offC[i], so512);
-        if (lane < 16) lds_dma16(rs_sm, as + 512, offM[i], so256);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kWB; ++i) {
-      const int b = wave + i * C::kWaves;
-      if (b < C::kNB) lds_dma16(rs_wc, st + C::kOffB + b * 1024, offW[i], so1k);
-    }
-    if (wave == 0 && lane < C::kMB * 4) lds_dma16(rs_ss, st + C::kOffSS, offScA, ks * strideScA);
-    if (wave == 1 && lane < C::kMB * 4) lds_dma16(rs_rs, st + C::kOffSR, offScA, ks * strideScA);
-    if (wave == 2 && lane < C::kNB * 4) lds_dma16(rs_ws, st + C::kOffSW, offScW, ks * strideScW);
+    for (int it = 0; it < kItems; ++it) issue_item(it, ks, st);
   };
 
   // Expand this wave's backbone blocks of the stage at st in place: every lane
   // reads its 12 compressed bytes (8 code bytes at 8*lane, 4 metadata bytes at
-  // 512 + 4*lane), the wave waits for all of its reads, then
-  // every lane writes its 16 dense bytes (a block belongs to one wave).
-  auto expand_store = [&](uint8_t* st) {
-    uint32_t lo[kSB], hi[kSB], mt[kSB];
+  // 512 + 4*lane), then writes its 16 dense bytes (a block belongs to one
+  // wave).  The writes overlap other lanes' reads, which is safe because the
+  // LDS executes one wave's accesses in issue order.  The reads are issued
+  // early and the arithmetic is left to interleave with MFMAs.
+  struct Packed { uint32_t lo[kSB], hi[kSB], mt[kSB]; };
+  auto expand_read = [&](const uint8_t* st) {
+    Packed p;
 #pragma unroll
     for (int i = 0; i < kSB; ++i) {
-      const int b = wave + i * C::kWaves;
-      if (b < C::kMB) {
-        const uint8_t* blk = st + C::kOffAS + b * 1024;
-        const uint2 sq = *reinterpret_cast<const uint2*>(blk + lane * 8);
-        lo[i] = sq.x;
-        hi[i] = sq.y;
-        mt[i] = *reinterpret_cast<const uint32_t*>(blk + 512 + lane * 4);
-      }
+      const uint8_t* blk = st + C::kOffAS + (wave + i * C::kWaves) * 1024;
+      const uint2 sq = *reinterpret_cast<const uint2*>(blk + lane * 8);
+      p.lo[i] = sq.x;
+      p.hi[i] = sq.y;
+      p.mt[i] = *reinterpret_cast<const uint32_t*>(blk + 512 + lane * 4);
     }
-    wait_vm_lgkm<63, 0>();
-#pragma unroll
-    for (int i = 0; i < kSB; ++i) {
-      const int b = wave + i * C::kWaves;
-      if (b < C::kMB)
-        *reinterpret_cast<uint4*>(st + C::kOffAS + b * 1024 + lane * 16) = expand_chunk(lo[i], hi[i], mt[i]);
-    }
+    return p;
   };
+  auto expand_write = [&](uint8_t* st, const Packed& p) {
+#pragma unroll
+    for (int i = 0; i < kSB; ++i)
+      *reinterpret_cast<uint4*>(st + C::kOffAS + (wave + i * C::kWaves) * 1024 + lane * 16) =
+          expand_chunk(p.lo[i], p.hi[i], p.mt[i]);
+  };
+  auto expand_store = [&](uint8_t* st) { expand_write(st, expand_read(st)); };
 
   const int wm = wave / NWN, wn = wave % NWN;
   v4f acc[C::kWMT][C::kWNT];
@@ -293,70 +315,122 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < C::kWNT; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint8_t* cur) {
-    v8i fs[C::kWMT], fr[C::kWMT], fb[C::kWNT];
-    uint32_t ss[C::kWMT], sr[C::kWMT], sw[C::kWNT];
+  // operand fragments of one K step (lane order: one 16-byte load per block)
+  auto frag = [&](const uint8_t* st, int off, int blk) {
+    return as_operand(*reinterpret_cast<const uint4*>(st + off + blk * 1024 + lane * 16));
+  };
+  v8i fs[C::kWMT], fr[C::kWMT], fb[C::kWNT];
+  uint32_t ss[C::kWMT], sr[C::kWMT], sw[C::kWNT];
+  auto read_all = [&](const uint8_t* st) {
 #pragma unroll
     for (int i = 0; i < C::kWMT; ++i) {
       const int blk = wm * C::kWMT + i;
-      fs[i] = as_operand(*reinterpret_cast<const uint4*>(cur + C::kOffAS + blk * 1024 + lane * 16));
-      fr[i] = as_operand(*reinterpret_cast<const uint4*>(cur + C::kOffAR + blk * 1024 + lane * 16));
-      ss[i] = cur[C::kOffSS + blk * 64 + lane];
-      sr[i] = cur[C::kOffSR + blk * 64 + lane];
+      fs[i] = frag(st, C::kOffAS, blk);
+      fr[i] = frag(st, C::kOffAR, blk);
+      ss[i] = st[C::kOffSS + blk * 64 + lane];
+      sr[i] = st[C::kOffSR + blk * 64 + lane];
     }
 #pragma unroll
     for (int j = 0; j < C::kWNT; ++j) {
       const int blk = wn * C::kWNT + j;
-      fb[j] = as_operand(*reinterpret_cast<const uint4*>(cur + C::kOffB + blk * 1024 + lane * 16));
-      sw[j] = cur[C::kOffSW + blk * 64 + lane];
+      fb[j] = frag(st, C::kOffB, blk);
+      sw[j] = st[C::kOffSW + blk * 64 + lane];
     }
-#pragma unroll
-    for (int i = 0; i < C::kWMT; ++i)
-#pragma unroll
-      for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
-#pragma unroll
-    for (int i = 0; i < C::kWMT; ++i)
-#pragma unroll
-      for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
   };
 
-  // Pipeline: an LDS ring of NST stages; copies run D = NST-1 K steps ahead.
-  // Before expanding stage ks+1 a wave waits until only the copies of the
-  // stages after it are outstanding (vmcnt retires in issue order; every wave
-  // issues at least kLoadsMin copies per stage), then all waves meet at a
-  // barrier before the stage is read.
-  constexpr int D = NST - 1;
-  constexpr int kLoadsMin = C::kMB / C::kWaves * 3 + C::kNB / C::kWaves;
-  static_assert(kLoadsMin >= 1 && kLoadsMin * (D > 1 ? D - 1 : 1) < 64, "vmcnt range");
+  // Pipeline: an LDS ring of NST stages, one K step each.  The prologue copies
+  // steps 0..NST-1; step ks runs the backbone MFMAs of ks (fragments already
+  // in registers) while this wave expands its blocks of step ks+1, meets the
+  // other waves at one barrier, then runs the residual MFMAs of ks while it
+  // issues the copy of step ks+NST (into the slot of step ks, whose data is
+  // all in registers by now) and reads the fragments of step ks+1.  Before
+  // expanding step ks+1 a wave waits until only the copies of later steps are
+  // outstanding (loads retire in issue order; each step is kItems copies).
+  static_assert(kItems * (NST > 2 ? NST - 2 : 1) < 64, "vmcnt range");
   auto stage_off = [&](int ks) { return (uint32_t)((ks % NST) * C::kStage); };
-  // wait until at most `newer` stages' copies are still in flight
   auto wait_stages = [&](int newer) {
-    static_assert(D <= 5, "wait table");
+    static_assert(NST <= 6, "wait table");
     switch (newer) {
-      case 0: wait_vm_lgkm<0, 15>(); break;
-      case 1: wait_vm_lgkm<kLoadsMin, 15>(); break;
-      case 2: wait_vm_lgkm<(2 * kLoadsMin < 64 ? 2 * kLoadsMin : 63), 15>(); break;
-      case 3: wait_vm_lgkm<(3 * kLoadsMin < 64 ? 3 * kLoadsMin : 63), 15>(); break;
-      default: wait_vm_lgkm<(4 * kLoadsMin < 64 ? 4 * kLoadsMin : 63), 15>(); break;
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<kItems>(); break;
+      case 2: wait_vm<(2 * kItems < 64 ? 2 * kItems : 63)>(); break;
+      case 3: wait_vm<(3 * kItems < 64 ? 3 * kItems : 63)>(); break;
+      default: wait_vm<(4 * kItems < 64 ? 4 * kItems : 63)>(); break;
     }
   };
 
-  const int pre = KT < D ? KT : D;     // stages copied before the loop
+  const int pre = KT < NST ? KT : NST;   // steps copied before the loop
   for (int s = 0; s < pre; ++s) issue(s, lds0 + stage_off(s));
   wait_stages(pre - 1);
   expand_store(smem + stage_off(0));
   __syncthreads();
+  read_all(smem + stage_off(0));
 
-  for (int ks = 0; ks < KT; ++ks) {
-    if (ks + D < KT) issue(ks + D, lds0 + stage_off(ks + D));
-    compute(smem + stage_off(ks));
-    if (ks + 1 < KT) {
-      const int last = ks + D < KT ? ks + D : KT - 1;   // newest stage copied so far
-      wait_stages(last - (ks + 1));
-      expand_store(smem + stage_off(ks + 1));
-      __syncthreads();
+  // one K step (not the last); COPY: issue the copy of step ks+NST
+  auto step = [&](int ks, int newer, auto copy_tag) {
+    constexpr bool kCopy = decltype(copy_tag)::value;
+    wait_stages(newer);
+    const Packed pk = expand_read(smem + stage_off(ks + 1));
+#pragma unroll
+    for (int i = 0; i < C::kWMT; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
+    expand_write(smem + stage_off(ks + 1), pk);
+    // schedule: each backbone MFMA followed by a few expansion instructions,
+    // so the matrix pipe never waits for the expansion
+#pragma unroll
+    for (int k = 0; k < C::kWMT * C::kWNT; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // up to four VALU
     }
-  }
+    __syncthreads();
+    const uint32_t cst = lds0 + stage_off(ks);   // slot of step ks, free after the barrier
+    const uint8_t* nx = smem + stage_off(ks + 1);
+    // the backbone fragments are free: refill them first
+#pragma unroll
+    for (int i = 0; i < C::kWMT; ++i) {
+      const int blk = wm * C::kWMT + i;
+      fs[i] = frag(nx, C::kOffAS, blk);
+      ss[i] = nx[C::kOffSS + blk * 64 + lane];
+    }
+    // residual MFMAs column by column; a weight fragment is refilled right
+    // after its last use, the residual fragments after the last column; the
+    // copies are spread over the columns
+#pragma unroll
+    for (int j = 0; j < C::kWNT; ++j) {
+#pragma unroll
+      for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
+      __builtin_amdgcn_sched_barrier(0);   // keep the refill after the column's last use
+      const int blk = wn * C::kWNT + j;
+      fb[j] = frag(nx, C::kOffB, blk);
+      sw[j] = nx[C::kOffSW + blk * 64 + lane];
+      if constexpr (kCopy) {
+#pragma unroll
+        for (int it = j * kItems / C::kWNT; it < (j + 1) * kItems / C::kWNT; ++it) issue_item(it, ks + NST, cst);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < C::kWMT; ++i) {
+      const int blk = wm * C::kWMT + i;
+      fr[i] = frag(nx, C::kOffAR, blk);
+      sr[i] = nx[C::kOffSR + blk * 64 + lane];
+    }
+  };
+  int ks = 0;
+  // steady state: copies issued so far end at step ks+NST-1, so NST-2 steps
+  // are newer than ks+1
+  for (; ks + NST < KT; ++ks) step(ks, NST - 2, BoolTag<true>{});
+  for (; ks + 1 < KT; ++ks) step(ks, KT - 2 - ks, BoolTag<false>{});
+  // last step
+#pragma unroll
+  for (int i = 0; i < C::kWMT; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
+#pragma unroll
+  for (int j = 0; j < C::kWNT; ++j)
+#pragma unroll
+    for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
 
   // single epilogue store of Y_S + Y_R
 #pragma unroll
