@@ -211,6 +211,8 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   if (!vs.base || !vd.base || vs.block != 32 || vd.block != 32 || vs.ld != nb64 || vd.ld != nb64 ||
       !aligned(vs.base, 16) || !aligned(vd.base, 16))
     return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be tiled MX views (block 32, K-tile stride NB*64)");
+  if (vs.base != vd.base)
+    return fail(SHARQ_ERR_UNSUPPORTED, "the two paths must view the same packed scale array (distinct per-path scale arrays are not built)");
   s = check_device();
   if (s) return s;
   sharq::GemmArgs g;

@@ -80,73 +80,88 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, int64_t row, int64_
 }
 
 // ---------------------------------------------------------------------------
-// Direct kernel (small M): each wave owns WM x WN MFMA tiles (16 x 16) and
-// reads its fragments straight from global memory.  In the tiled layout a
-// fragment is 64 contiguous lanes, so these reads are contiguous too.
+// Small-M kernel (decode, M <= 64): the weight is streamed once and the work
+// is HBM-bound on it.  One workgroup per 16-column block of W (and per group
+// of RBG 16-row blocks); its NW waves split K (wave w takes K tiles w, w+NW,
+// ...) and read their fragments straight from global memory -- in the tiled
+// layout a fragment is 64 lanes x 16 contiguous bytes, so each read is one
+// contiguous KiB.  The backbone is expanded in registers.  The NW partial
+// sums meet in LDS and are added in wave order.  Both paths read the weight
+// scales through one load: the API admits only views of one scale array.
 // ---------------------------------------------------------------------------
-template <int WM, int WN>
-__global__ __launch_bounds__(256) void dual_gemm_direct(GemmArgs g) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t RB = (g.M + 15) / 16, NB = (g.N + 15) / 16;
-  const int KB = (g.K + 127) / 128;
-  const int64_t rb_base = (int64_t)blockIdx.y * (2 * WM) + (wave >> 1) * WM;
-  const int64_t nb_base = (int64_t)blockIdx.x * (2 * WN) + (wave & 1) * WN;
-  const int r16 = lane & 15, chunk = lane >> 4;
+template <int RBG, int NW>
+__global__ __launch_bounds__(64 * NW) void dual_gemm_splitk(GemmArgs g) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1);
+  const int64_t RB = (g.M + 15) / 16;
+  const int KT = (g.K + 127) / 128;
+  const int64_t nb = blockIdx.x;                      // 16-column block
+  const int64_t rb0 = (int64_t)blockIdx.y * RBG;      // first 16-row block
+  const int r16 = lane & 15, c4 = lane >> 4;
 
-  v4f acc[WM][WN];
+  // one accumulator per path (shorter dependent MFMA chains); Y_S + Y_R is
+  // formed once, before the cross-wave sum
+  v4f acs[RBG], acr[RBG];
 #pragma unroll
-  for (int i = 0; i < WM; ++i)
-#pragma unroll
-    for (int j = 0; j < WN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < RBG; ++r) acs[r] = acr[r] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = 0; ks < KB; ++ks) {
-    v8i as[WM], ar[WM], b[WN];
-    uint32_t ss[WM], sr[WM], sw_s[WN], sw_d[WN];
+  // K tiles in chunks of CH per wave, all loads of a chunk issued before its
+  // MFMAs.  Indices are clamped into range: a tile past K gets a zero weight
+  // fragment (it adds exactly zero) and a row block past the padding only feeds
+  // output rows that are never stored.
+  constexpr int CH = (RBG == 1 ? 8 : (RBG == 2 ? 4 : 2)) * 4 / NW;
+  for (int base = 0; base < KT; base += NW * CH) {
+    v8i b[CH], as[CH][RBG], ar[CH][RBG];
+    uint32_t sw[CH], ss[CH][RBG], sr[CH][RBG];
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const int64_t rb = rb_base + i;
-      const bool ok = rb < RB;
-      const int64_t tile = rb * KB + ks;
-      uint4 rq = ok ? *reinterpret_cast<const uint4*>(g.r_codes + tile * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
-      const uint2 sq = ok ? *reinterpret_cast<const uint2*>(g.s_codes + tile * 512 + lane * 8) : make_uint2(0, 0);
-      const uint32_t lo = sq.x, hi = sq.y;
-      uint32_t mq = ok ? *reinterpret_cast<const uint32_t*>(g.s_meta + tile * 256 + lane * 4) : 0x44444444u;
-      ar[i] = as_operand(rq);
-      as[i] = as_operand(expand_chunk(lo, hi, mq));
-      ss[i] = ok ? g.s_scales[((int64_t)ks * RB + rb) * 64 + lane] : 0u;
-      sr[i] = ok ? g.r_scales[((int64_t)ks * RB + rb) * 64 + lane] : 0u;
-    }
+    for (int c = 0; c < CH; ++c) {
+      const int kt = base + wave + NW * c;
+      const int ktc = kt < KT ? kt : KT - 1;
+      uint4 wq = *reinterpret_cast<const uint4*>(g.w_codes + (nb * KT + ktc) * 1024 + lane * 16);
+      if (kt >= KT) wq = make_uint4(0, 0, 0, 0);
+      b[c] = as_operand(wq);
+      sw[c] = g.w_scales_dense[(int64_t)ktc * g.w_scales_ld + nb * 64 + lane];   // both views (one array)
 #pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int64_t nb = nb_base + j;
-      const bool ok = nb < NB;
-      uint4 wq = ok ? *reinterpret_cast<const uint4*>(g.w_codes + (nb * KB + ks) * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
-      b[j] = as_operand(wq);
-      sw_s[j] = ok ? g.w_scales_sparse[(int64_t)ks * g.w_scales_ld + nb * 64 + lane] : 0u;
-      sw_d[j] = ok ? g.w_scales_dense[(int64_t)ks * g.w_scales_ld + nb * 64 + lane] : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-      for (int j = 0; j < WN; ++j) acc[i][j] = mfma_fp4(as[i], b[j], acc[i][j], ss[i], sw_s[j]);
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-      for (int j = 0; j < WN; ++j) acc[i][j] = mfma_fp4(ar[i], b[j], acc[i][j], sr[i], sw_d[j]);
-  }
-
-  // single epilogue store of Y_S + Y_R
-#pragma unroll
-  for (int i = 0; i < WM; ++i)
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int64_t col = (nb_base + j) * 16 + r16;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t row = (rb_base + i) * 16 + 4 * chunk + t;
-        if (row < g.M && col < g.N) store_out(g, row, col, acc[i][j][t]);
+      for (int r = 0; r < RBG; ++r) {
+        const int64_t rb = rb0 + r < RB ? rb0 + r : RB - 1;
+        const int64_t tile = rb * KT + ktc;
+        const uint4 rq = *reinterpret_cast<const uint4*>(g.r_codes + tile * 1024 + lane * 16);
+        const uint2 sq = *reinterpret_cast<const uint2*>(g.s_codes + tile * 512 + lane * 8);
+        const uint32_t mq = *reinterpret_cast<const uint32_t*>(g.s_meta + tile * 256 + lane * 4);
+        ss[c][r] = g.s_scales[((int64_t)ktc * RB + rb) * 64 + lane];
+        sr[c][r] = g.r_scales[((int64_t)ktc * RB + rb) * 64 + lane];
+        ar[c][r] = as_operand(rq);
+        as[c][r] = as_operand(expand_chunk(sq.x, sq.y, mq));
       }
     }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int r = 0; r < RBG; ++r) {
+        acs[r] = mfma_fp4(as[c][r], b[c], acs[r], ss[c][r], sw[c]);
+        acr[r] = mfma_fp4(ar[c][r], b[c], acr[r], sr[c][r], sw[c]);
+      }
+  }
+
+  // partial sums of the waves, added in wave order; one store of Y_S + Y_R
+  __shared__ v4f part[NW][RBG][64];
+#pragma unroll
+  for (int r = 0; r < RBG; ++r) part[wave][r][lane] = acs[r] + acr[r];
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t col = nb * 16 + r16;
+#pragma unroll
+    for (int r = 0; r < RBG; ++r) {
+      v4f v = part[0][r][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v = v + part[w][r][lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = (rb0 + r) * 16 + 4 * c4 + q;
+        if (row < g.M && col < g.N) store_out(g, row, col, v[q]);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -469,9 +484,19 @@ hipError_t launch_linear(const GemmArgs& a, hipStream_t stream) {
   const bool fits = (uint64_t)((a.M + 15) / 16) * kb * 1024 < 0x7FFFFFFFull &&
                     (uint64_t)((a.N + 15) / 16) * kb * 1024 < 0x7FFFFFFFull;
   if (a.M > 64 && fits) return launch_tiled<256, 192, 4, 2, 3>(a, stream);
-  constexpr int WM = 2, WN = 4;
-  dim3 grid((unsigned)((a.N + 2 * WN * 16 - 1) / (2 * WN * 16)), (unsigned)((a.M + 2 * WM * 16 - 1) / (2 * WM * 16)));
-  hipLaunchKernelGGL((dual_gemm_direct<WM, WN>), grid, dim3(256), 0, stream, a);
+  // M <= 64 (or operands past 31-bit buffer offsets): split-K weight streaming;
+  // eight waves per column block for one or two row blocks, four for more
+  const int64_t RB = (a.M + 15) / 16, NB = (a.N + 15) / 16;
+  if (NB > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (RB == 1) {
+    hipLaunchKernelGGL((dual_gemm_splitk<1, 8>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
+  } else if (RB == 2) {
+    hipLaunchKernelGGL((dual_gemm_splitk<2, 8>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
+  } else {
+    const int64_t groups = (RB + 3) / 4;
+    if (groups > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dual_gemm_splitk<4, 4>), dim3((unsigned)NB, (unsigned)groups), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -130,5 +130,9 @@ def test_pack_and_linear_reject_before_launch(lib):
     assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 5, None) == _lib.ERR_INVALID_ARG
     # scale views must describe the MX payload
     assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 0, None) == _lib.ERR_INVALID_ARG
+    # well-formed views over two different scale arrays: refused as unsupported
+    for p, base in ((0, 0x200000), (1, 0x210000)):
+        w.view[p].base, w.view[p].ld, w.view[p].block = base, 2 * 64, 32
+    assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 0, None) == _lib.ERR_UNSUPPORTED
     a.M = 0
     assert lib.sharq_linear(C.byref(a), C.byref(w), None, 32, 0, None) == _lib.OK

@@ -33,7 +33,8 @@ def test_linear_tiny_full():
 
 
 @pytest.mark.parametrize("M,K,N,norm", [(37, 96, 53, True), (1, 4096, 4096, False), (130, 768, 200, False),
-                                        (64, 4096, 4096, False), (17, 2048, 1536, False), (256, 256, 272, True)])
+                                        (64, 4096, 4096, False), (17, 2048, 1536, False), (256, 256, 272, True),
+                                        (5, 1376, 100, False), (3, 14336, 64, False), (49, 640, 48, True)])
 def test_linear_ragged_full(M, K, N, norm):
     print(f"linear M={M} K={K} N={N}", flush=True)
     rng = np.random.default_rng(M + K + N)
@@ -45,6 +46,18 @@ def test_linear_ragged_full(M, K, N, norm):
     wc, ws = O.pack_weight(w)
     yr, b = O.linear(ref, wc, ws)
     assert_linear_close(y.cpu().numpy(), yr, b, f"M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("name", ["decode8", "decode32"])
+def test_linear_decode_full(name):
+    """Decode shapes (M in {8, 32}, K = N = 4096): every output against the oracle."""
+    print(f"linear {name}", flush=True)
+    inp = synth.layer_inputs(name, seed=0)
+    act, wt, y = gpu_layer(inp["x"], inp["gamma"], inp["w"])
+    ref = O.prepare(inp["x"], inp["gamma"], inp["eps"])
+    wc, ws = O.pack_weight(inp["w"])
+    yr, b = O.linear(ref, wc, ws)
+    assert_linear_close(y.cpu().numpy(), yr, b, name)
 
 
 def _sample_rows(M, rng, n=24):
