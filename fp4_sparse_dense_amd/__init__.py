@@ -132,3 +132,43 @@ def sharq_linear(act: SharqAct, weight: SharqWeight, out=None, out_dtype: int = 
     _lib.check(lib.sharq_linear(C.byref(act.desc), C.byref(weight.desc), _ptr(out), out.stride(0), out_dtype,
                                 _stream_ptr(stream)), "sharq_linear")
     return out
+
+
+def grouped_workspace_bytes(rows: int, experts: int, K: int) -> int:
+    lib = _lib.load()
+    n = C.c_size_t()
+    _lib.check(lib.sharq_grouped_workspace_bytes(rows, experts, K, C.byref(n)), "sharq_grouped_workspace_bytes")
+    return n.value
+
+
+def sharq_linear_grouped(act: SharqAct, weight: SharqWeight, seg_offsets, experts: int, row_index=None,
+                         rows: int | None = None, out=None, out_dtype: int = OUT_F32, workspace=None, stream=None):
+    """Grouped expert layer: expert e computes the SharQ linear layer of routed rows
+    [seg[e], seg[e+1]) with its N_e = weight.N / experts rows of the stacked weight.
+
+    seg_offsets: device int64 [E+1]; row_index: device int32 [rows] (routed row i
+    reads activation row row_index[i]) or None (rows are the activation rows).
+    Returns Y [rows, N_e]."""
+    torch = _torch()
+    dev = act.s_codes.device
+    if rows is None:
+        rows = int(row_index.numel()) if row_index is not None else act.M
+    if seg_offsets.dtype != torch.int64 or not seg_offsets.is_contiguous() or seg_offsets.numel() != experts + 1:
+        raise ValueError("seg_offsets must be a contiguous int64 tensor of E+1 entries")
+    if row_index is not None and (row_index.dtype != torch.int32 or not row_index.is_contiguous()):
+        raise ValueError("row_index must be a contiguous int32 tensor")
+    ne = weight.N // experts
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty(rows, ne, dtype=dt, device=dev)
+    if out.dtype != dt or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be 2-D with unit inner stride and the requested dtype")
+    need = grouped_workspace_bytes(rows, experts, act.K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    _lib.check(lib.sharq_linear_grouped(C.byref(act.desc), _ptr(row_index), rows, _ptr(seg_offsets), experts,
+                                        C.byref(weight.desc), _ptr(out), out.stride(0), out_dtype,
+                                        _ptr(workspace), workspace.numel(), _stream_ptr(stream)),
+               "sharq_linear_grouped")
+    return out

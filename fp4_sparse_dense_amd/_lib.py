@@ -58,6 +58,10 @@ PROTOTYPES = {
                                 C.c_int32, C.c_int32, C.c_int32, C.POINTER(ActDesc), C.c_void_p]),
     "sharq_linear": (C.c_int, [C.POINTER(ActDesc), C.POINTER(WeightDesc), C.c_void_p, C.c_int64,
                                C.c_int32, C.c_void_p]),
+    "sharq_grouped_workspace_bytes": (C.c_int, [C.c_int64, C.c_int32, C.c_int64, C.POINTER(C.c_size_t)]),
+    "sharq_linear_grouped": (C.c_int, [C.POINTER(ActDesc), C.c_void_p, C.c_int64, C.c_void_p, C.c_int32,
+                                       C.POINTER(WeightDesc), C.c_void_p, C.c_int64, C.c_int32,
+                                       C.c_void_p, C.c_size_t, C.c_void_p]),
 }
 
 _LIB = None

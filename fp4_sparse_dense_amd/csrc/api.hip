@@ -231,8 +231,104 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   g.N = w->N;
   g.K = (int)a->K;
   g.out_bf16 = out_dtype == SHARQ_OUT_BF16;
+  g.a_blocks = (a->M + 15) / 16;
+  g.seg = nullptr;
+  g.pseg = nullptr;
+  g.tprefix = nullptr;
+  g.E = 0;
   hipError_t e = sharq::launch_linear(g, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "linear launch");
+  return SHARQ_OK;
+}
+
+sharq_status sharq_grouped_workspace_bytes(int64_t rows, int32_t E, int64_t K, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(SHARQ_ERR_INVALID_ARG, "null output");
+  if (rows < 0 || E < 1 || E > 1024) return fail(SHARQ_ERR_INVALID_ARG, "bad rows=%lld or E=%d (1..1024)", (long long)rows, (int)E);
+  if (K <= 0 || K % 32 || K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "bad K=%lld", (long long)K);
+  *bytes = sharq::grouped_workspace_bytes(rows, E, (int)K);
+  return SHARQ_OK;
+}
+
+sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
+                                  const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
+                                  void* y_dev, int64_t ldy, int32_t out_dtype,
+                                  void* ws_dev, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!a || !w) return fail(SHARQ_ERR_INVALID_ARG, "null descriptor");
+  if (a->struct_size != sizeof(sharq_act) || w->struct_size != sizeof(sharq_weight))
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor struct_size mismatch");
+  if (a->layout_version != SHARQ_ABI_VERSION || w->layout_version != SHARQ_ABI_VERSION)
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor layout_version mismatch (not produced by this library?)");
+  if (a->K != w->K) return fail(SHARQ_ERR_INVALID_ARG, "K mismatch: activation %lld, weight %lld", (long long)a->K, (long long)w->K);
+  if (a->M < 0 || w->N <= 0 || a->K <= 0 || a->K % 32 || a->K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "bad shapes");
+  if (out_dtype != SHARQ_OUT_F32 && out_dtype != SHARQ_OUT_BF16) return fail(SHARQ_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
+  if (a->n != 2 || a->m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built");
+  if (a->fmt != w->fmt) return fail(SHARQ_ERR_INVALID_ARG, "activation and weight formats differ");
+  sharq_status s = check_fmt(a->fmt);
+  if (s) return s;
+  if (E < 1 || E > 1024) return fail(SHARQ_ERR_INVALID_ARG, "E=%d outside 1..1024", (int)E);
+  if (w->N % E || (w->N / E) % 16)
+    return fail(SHARQ_ERR_INVALID_ARG, "stacked weight N=%lld is not E=%d experts of a multiple of 16 rows", (long long)w->N, (int)E);
+  const int64_t Ne = w->N / E;
+  if (rows < 0) return fail(SHARQ_ERR_INVALID_ARG, "rows=%lld", (long long)rows);
+  if (!row_index_dev && rows != a->M) return fail(SHARQ_ERR_INVALID_ARG, "without a row index the routed rows are the activation rows (rows=%lld, M=%lld)", (long long)rows, (long long)a->M);
+  if (rows == 0) return SHARQ_OK;
+  if (!seg_offsets_dev || !aligned(seg_offsets_dev, 8)) return fail(SHARQ_ERR_INVALID_ARG, "segment offsets null or misaligned");
+  if (row_index_dev && !aligned(row_index_dev, 4)) return fail(SHARQ_ERR_INVALID_ARG, "row index misaligned");
+  if (!y_dev) return fail(SHARQ_ERR_INVALID_ARG, "null output pointer");
+  if (ldy < Ne) return fail(SHARQ_ERR_INVALID_ARG, "ldy=%lld < N_e=%lld", (long long)ldy, (long long)Ne);
+  if (!aligned(y_dev, out_dtype == SHARQ_OUT_F32 ? 4 : 2)) return fail(SHARQ_ERR_INVALID_ARG, "output misaligned");
+  if (a->M > 0) {
+    if (!a->s_codes || !a->s_meta || !a->s_scales || !a->r_codes || !a->r_scales)
+      return fail(SHARQ_ERR_INVALID_ARG, "activation buffers not set");
+    if (!aligned(a->s_codes, 16) || !aligned(a->s_meta, 16) || !aligned(a->r_codes, 16) ||
+        !aligned(a->s_scales, 16) || !aligned(a->r_scales, 16))
+      return fail(SHARQ_ERR_INVALID_ARG, "activation buffers must be 16-byte aligned");
+  }
+  if (!w->codes || !aligned(w->codes, 16)) return fail(SHARQ_ERR_INVALID_ARG, "weight codes null or misaligned");
+  const sharq_scale_view& vs = w->view[SHARQ_PATH_SPARSE];
+  const sharq_scale_view& vd = w->view[SHARQ_PATH_DENSE];
+  const int64_t nb64 = (w->N + 15) / 16 * 64;
+  if (!vs.base || !vd.base || vs.block != 32 || vd.block != 32 || vs.ld != nb64 || vd.ld != nb64 ||
+      !aligned(vs.base, 16) || !aligned(vd.base, 16))
+    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be tiled MX views (block 32, K-tile stride NB*64)");
+  if (vs.base != vd.base)
+    return fail(SHARQ_ERR_UNSUPPORTED, "the two paths must view the same packed scale array (distinct per-path scale arrays are not built)");
+  const size_t need = sharq::grouped_workspace_bytes(rows, E, (int)a->K);
+  if (!ws_dev || ws_bytes < need || !aligned(ws_dev, 256))
+    return fail(SHARQ_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", need, ws_bytes);
+  s = check_device();
+  if (s) return s;
+  sharq::GroupedArgs ga;
+  sharq::GemmArgs& g = ga.gemm;
+  g.s_codes = a->s_codes;
+  g.s_meta = a->s_meta;
+  g.s_scales = a->s_scales;
+  g.r_codes = a->r_codes;
+  g.r_scales = a->r_scales;
+  g.w_codes = w->codes;
+  g.w_scales_sparse = vs.base;
+  g.w_scales_dense = vd.base;
+  g.w_scales_ld = vs.ld;
+  g.y = y_dev;
+  g.ldy = ldy;
+  g.M = a->M;
+  g.N = w->N;
+  g.K = (int)a->K;
+  g.out_bf16 = out_dtype == SHARQ_OUT_BF16;
+  g.a_blocks = (a->M + 15) / 16;
+  g.seg = nullptr;
+  g.pseg = nullptr;
+  g.tprefix = nullptr;
+  g.E = E;
+  ga.row_index = row_index_dev;
+  ga.seg_in = seg_offsets_dev;
+  ga.rows = rows;
+  ga.src_blocks = (a->M + 15) / 16;
+  ga.ws = static_cast<uint8_t*>(ws_dev);
+  hipError_t e = sharq::launch_linear_grouped(ga, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "grouped linear launch");
   return SHARQ_OK;
 }
 

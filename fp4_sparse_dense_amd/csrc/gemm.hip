@@ -199,7 +199,7 @@ struct TileCfg {
   static_assert(kMB % NWM == 0 && kNB % NWN == 0, "wave split");
 };
 
-template <int BM, int BN, int NWM, int NWN, int NST>
+template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED>
 __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
   extern __shared__ __align__(1024) uint8_t smem[];
@@ -208,17 +208,50 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   // uniform (LDS targets go to M0); the mask tells the compiler wave < kWaves
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (C::kWaves - 1);
   const int KT = (g.K + 127) / 128;                       // K tiles (zero padded)
-  const int64_t RB = (g.M + 15) / 16, NB = (g.N + 15) / 16; // padded 16-row blocks
+  const int64_t RB = g.a_blocks, NB = (g.N + 15) / 16;   // padded 16-row blocks
 
-  // tile selection: blocks on one XCD (block id mod 8) take a contiguous
-  // range of tiles, walked M-fastest, so they share weight and activation rows in L2
-  const int tiles_m = (int)((g.M + BM - 1) / BM);
-  const int tiles_n = (int)((g.N + BN - 1) / BN);
-  const int T = tiles_m * tiles_n;
-  int t = blockIdx.x;
-  if (T % 8 == 0) t = (t % 8) * (T / 8) + t / 8;
-  const int64_t rb0 = (int64_t)(t % tiles_m) * C::kMB;      // first 16-row block of the tile
-  const int64_t nb0 = (int64_t)(t / tiles_m) * C::kNB;
+  // Tile of this workgroup: activation row blocks [rb0, rb0 + kMB) (valid below
+  // rb_end), weight column blocks [nb0, nb0 + kNB) (valid below nb_end); output
+  // row of activation block rb, row r: y_row0 + (rb - rb_first) * 16 + r, valid
+  // below y_rows; output column of weight block nb, column c:
+  // (nb - nb_first) * 16 + c, valid below y_cols.
+  int64_t rb0, nb0, rb_end, nb_end, rb_first, nb_first, y_row0, y_rows, y_cols;
+  if constexpr (!GROUPED) {
+    // blocks on one XCD (block id mod 8) take a contiguous range of tiles,
+    // walked M-fastest, so they share weight and activation rows in L2
+    const int tiles_m = (int)((g.M + BM - 1) / BM);
+    const int tiles_n = (int)((g.N + BN - 1) / BN);
+    const int T = tiles_m * tiles_n;
+    int t = blockIdx.x;
+    if (T % 8 == 0) t = (t % 8) * (T / 8) + t / 8;
+    rb0 = (int64_t)(t % tiles_m) * C::kMB;
+    nb0 = (int64_t)(t / tiles_m) * C::kNB;
+    rb_end = RB; nb_end = NB; rb_first = 0; nb_first = 0;
+    y_row0 = 0; y_rows = g.M; y_cols = g.N;
+  } else {
+    // (expert, M tile, N tile): M tiles of all experts are numbered through
+    // tprefix; the weight holds the experts' column blocks one after another
+    const int64_t NBe = NB / g.E;
+    const int tiles_n = (int)((NBe + C::kNB - 1) / C::kNB);
+    const int nt = (int)(blockIdx.x % tiles_n);
+    const int mtg = (int)(blockIdx.x / tiles_n);
+    if (mtg >= g.tprefix[g.E]) return;              // the whole workgroup: past the last tile
+    int lo = 0, hi = g.E;                            // expert e: tprefix[e] <= mtg < tprefix[e+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (g.tprefix[mid] <= mtg) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    rb_first = g.pseg[e];
+    rb0 = rb_first + (int64_t)(mtg - g.tprefix[e]) * C::kMB;
+    rb_end = g.pseg[e + 1];
+    nb_first = (int64_t)e * NBe;
+    nb0 = nb_first + (int64_t)nt * C::kNB;
+    nb_end = nb_first + NBe;
+    y_row0 = g.seg[e];
+    y_rows = g.seg[e + 1] - g.seg[e];
+    y_cols = g.N / g.E;
+  }
 
   const u32x4 rs_sc = make_desc(g.s_codes, (uint64_t)RB * KT * 512);
   const u32x4 rs_sm = make_desc(g.s_meta, (uint64_t)RB * KT * 256);
@@ -247,7 +280,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < kSB; ++i) {
     const int64_t rb = rb0 + wave + i * C::kWaves;
-    const bool ok = rb < RB;
+    const bool ok = rb < rb_end;
     offR[i] = ok ? (uint32_t)(rb * KT) * 1024u + lane * 16 : kOOB;
     offC[i] = ok ? (uint32_t)(rb * KT) * 512u + lane * 16 : kOOB;   // lanes 0..31
     offM[i] = ok ? (uint32_t)(rb * KT) * 256u + lane * 16 : kOOB;   // lanes 0..15
@@ -259,14 +292,14 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     const int b = wave + i * C::kWaves;
     wblk[i] = b < C::kNB ? b : b - C::kNB;
     const int64_t nb = nb0 + wblk[i];
-    offW[i] = nb < NB ? (uint32_t)(nb * KT) * 1024u + lane * 16 : kOOB;
+    offW[i] = nb < nb_end ? (uint32_t)(nb * KT) * 1024u + lane * 16 : kOOB;
   }
   // scale edge of this wave: 0 = backbone, 1 = residual, 2 = weight;
   // 16 lanes per 64-byte block
   const int edge = wave % 3;
   const int eb = lane >> 2;   // block of the edge this lane copies
-  const uint32_t offScA = rb0 + eb < RB ? (uint32_t)((rb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
-  const uint32_t offScW = nb0 + eb < NB ? (uint32_t)((nb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
+  const uint32_t offScA = rb0 + eb < rb_end ? (uint32_t)((rb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
+  const uint32_t offScW = nb0 + eb < nb_end ? (uint32_t)((nb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
   const u32x4 rs_edge = edge == 0 ? rs_ss : (edge == 1 ? rs_rs : rs_ws);
   const uint32_t off_edge = edge == 2 ? offScW : offScA;
   const uint32_t stride_edge = edge == 2 ? (uint32_t)g.w_scales_ld : (uint32_t)RB * 64;
@@ -452,19 +485,19 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
     for (int j = 0; j < C::kWNT; ++j) {
-      const int64_t col = (nb0 + wn * C::kWNT + j) * 16 + r16;
+      const int64_t col = (nb0 - nb_first + wn * C::kWNT + j) * 16 + r16;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = (rb0 + wm * C::kWMT + i) * 16 + 4 * c4 + q;
-        if (row < g.M && col < g.N) store_out(g, row, col, acc[i][j][q]);
+        const int64_t row = (rb0 - rb_first + wm * C::kWMT + i) * 16 + 4 * c4 + q;
+        if (row < y_rows && col < y_cols) store_out(g, y_row0 + row, col, acc[i][j][q]);
       }
     }
 }
 
-template <int BM, int BN, int NWM, int NWN, int NST>
-static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
+template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED>
+static hipError_t launch_tiled(const GemmArgs& a, int64_t tiles, hipStream_t stream) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
-  auto kern = dual_gemm_tiled<BM, BN, NWM, NWN, NST>;
+  auto kern = dual_gemm_tiled<BM, BN, NWM, NWN, NST, GROUPED>;
   constexpr int lds = C::kStages * C::kStage;
   static bool attr_set = false;
   if (!attr_set) {
@@ -472,9 +505,20 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::kThreads), lds, stream, a);
   return hipGetLastError();
+}
+
+// tile shape of the tiled kernel (M tile also used to count grouped tiles)
+constexpr int kTileM = 256, kTileN = 192;
+int grouped_tile_m() { return kTileM; }
+
+hipError_t launch_linear_grouped_gemm(const GemmArgs& a, int64_t max_mtiles, hipStream_t stream) {
+  const int64_t NBe = (a.N / a.E + 15) / 16;
+  const int64_t tiles_n = (NBe + kTileN / 16 - 1) / (kTileN / 16);
+  return launch_tiled<kTileM, kTileN, 4, 2, 3, true>(a, max_mtiles * tiles_n, stream);
 }
 
 hipError_t launch_linear(const GemmArgs& a, hipStream_t stream) {
@@ -483,7 +527,9 @@ hipError_t launch_linear(const GemmArgs& a, hipStream_t stream) {
   const uint64_t kb = (a.K + 127) / 128;
   const bool fits = (uint64_t)((a.M + 15) / 16) * kb * 1024 < 0x7FFFFFFFull &&
                     (uint64_t)((a.N + 15) / 16) * kb * 1024 < 0x7FFFFFFFull;
-  if (a.M > 64 && fits) return launch_tiled<256, 192, 4, 2, 3>(a, stream);
+  if (a.M > 64 && fits)
+    return launch_tiled<kTileM, kTileN, 4, 2, 3, false>(
+        a, ((a.M + kTileM - 1) / kTileM) * ((a.N + kTileN - 1) / kTileN), stream);
   // M <= 64 (or operands past 31-bit buffer offsets): split-K weight streaming;
   // eight waves per column block for one or two row blocks, four for more
   const int64_t RB = (a.M + 15) / 16, NB = (a.N + 15) / 16;

@@ -1,0 +1,176 @@
+// Grouped expert layer (mixture-of-experts) on top of the tiled dual GEMM.
+//
+// SharQ paper page (mlsanity), Abstract: the method is evaluated on mixture-of-
+// experts models as well as dense ones; each expert is an ordinary SharQ
+// linear layer over the tokens routed to it.  Prep is row-local, so each token
+// is prepared once and its prepared row is reused by every expert it is routed
+// to (the result is identical to preparing it per expert).
+//
+// Three launches on the caller's stream:
+//   1. setup   (one workgroup): clamps the caller's segment offsets into a
+//      nondecreasing sequence in [0, rows], and tabulates, per expert, its
+//      first 16-row block in the gathered activation (segments padded to whole
+//      blocks) and the number of 256-row M tiles before it;
+//   2. gather  (one wave per gathered 16-row block and K tile): copies each
+//      routed row's codes, metadata and scales from the source activation (row
+//      row_index[i], or i) into expert order, writing zero-input blocks (codes
+//      0, metadata 0x44, scales 0) for the padding rows;
+//   3. the tiled dual GEMM with one workgroup per (expert, M tile, N tile).
+#include "device_common.h"
+#include "launch.h"
+
+namespace sharq {
+
+namespace {
+
+constexpr int kMaxExperts = 1024;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+  int64_t blocks;        // 16-row blocks of the gathered activation (upper bound)
+  size_t r_codes, s_codes, s_meta, s_scales, r_scales, seg, pseg, tprefix, total;
+};
+
+WsLayout ws_layout(int64_t rows, int E, int K) {
+  WsLayout L;
+  const int64_t KT = (K + 127) / 128;
+  L.blocks = (rows + 15 * (int64_t)E + 15) / 16;
+  size_t o = 0;
+  L.r_codes = o;  o = align_up(o + (size_t)L.blocks * KT * 1024);
+  L.s_codes = o;  o = align_up(o + (size_t)L.blocks * KT * 512);
+  L.s_meta = o;   o = align_up(o + (size_t)L.blocks * KT * 256);
+  L.s_scales = o; o = align_up(o + (size_t)L.blocks * KT * 64);
+  L.r_scales = o; o = align_up(o + (size_t)L.blocks * KT * 64);
+  L.seg = o;      o = align_up(o + (size_t)(E + 1) * 8);
+  L.pseg = o;     o = align_up(o + (size_t)(E + 1) * 8);
+  L.tprefix = o;  o = align_up(o + (size_t)(E + 1) * 4);
+  L.total = o;
+  return L;
+}
+
+__global__ __launch_bounds__(256) void grouped_setup_kernel(const int64_t* __restrict__ seg_in, int E, int64_t rows,
+                                                           int tile_m, int64_t* __restrict__ seg,
+                                                           int64_t* __restrict__ pseg,
+                                                           int32_t* __restrict__ tprefix) {
+  __shared__ int64_t s[kMaxExperts + 1];
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+    int64_t v = seg_in[e];
+    s[e] = v < 0 ? 0 : (v > rows ? rows : v);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t prev = 0, pb = 0;
+    int64_t tp = 0;
+    s[0] = 0;
+    for (int e = 0; e <= E; ++e) {
+      const int64_t v = e == E ? rows : (s[e] < prev ? prev : s[e]);   // nondecreasing, ends at rows
+      if (e > 0) {
+        const int64_t n = v - prev;
+        pb += (n + 15) / 16;
+        tp += (n + tile_m - 1) / tile_m;
+      }
+      seg[e] = v;
+      pseg[e] = pb;
+      tprefix[e] = (int32_t)tp;
+      prev = v;
+    }
+  }
+}
+
+struct GatherArgs {
+  const uint8_t *s_codes, *s_meta, *s_scales, *r_codes, *r_scales;   // source activation
+  uint8_t *g_s_codes, *g_s_meta, *g_s_scales, *g_r_codes, *g_r_scales;
+  const int32_t* row_index;
+  const int64_t *seg, *pseg;
+  int64_t src_rows, src_blocks, dst_blocks;
+  int KT, E;
+};
+
+__global__ __launch_bounds__(256) void grouped_gather_kernel(GatherArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rbp = w / a.KT;
+  const int kt = (int)(w % a.KT);
+  if (rbp >= a.pseg[a.E]) return;                     // wave-uniform
+  int lo = 0, hi = a.E;                               // expert: pseg[e] <= rbp < pseg[e+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.pseg[mid] <= rbp) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int r = lane & 15, c4 = lane >> 4;
+  const int64_t lr = (rbp - a.pseg[e]) * 16 + r;      // row within the expert
+  const int64_t n = a.seg[e + 1] - a.seg[e];
+  uint4 rc = make_uint4(0, 0, 0, 0);
+  uint2 sc = make_uint2(0, 0);
+  uint32_t mt = 0x44444444u, ssc = 0, rsc = 0;
+  if (lr < n) {
+    const int64_t i = a.seg[e] + lr;
+    const int64_t src = a.row_index ? (int64_t)a.row_index[i] : i;
+    if (src >= 0 && src < a.src_rows) {               // a row index out of range reads as zero input
+      const int64_t sb = src / 16, st = sb * a.KT + kt;
+      const int sl = c4 * 16 + (int)(src % 16);
+      rc = *reinterpret_cast<const uint4*>(a.r_codes + st * 1024 + sl * 16);
+      sc = *reinterpret_cast<const uint2*>(a.s_codes + st * 512 + sl * 8);
+      mt = *reinterpret_cast<const uint32_t*>(a.s_meta + st * 256 + sl * 4);
+      ssc = a.s_scales[((int64_t)kt * a.src_blocks + sb) * 64 + sl];
+      rsc = a.r_scales[((int64_t)kt * a.src_blocks + sb) * 64 + sl];
+    }
+  }
+  const int64_t dt = rbp * a.KT + kt;
+  *reinterpret_cast<uint4*>(a.g_r_codes + dt * 1024 + lane * 16) = rc;
+  *reinterpret_cast<uint2*>(a.g_s_codes + dt * 512 + lane * 8) = sc;
+  *reinterpret_cast<uint32_t*>(a.g_s_meta + dt * 256 + lane * 4) = mt;
+  a.g_s_scales[((int64_t)kt * a.dst_blocks + rbp) * 64 + lane] = (uint8_t)ssc;
+  a.g_r_scales[((int64_t)kt * a.dst_blocks + rbp) * 64 + lane] = (uint8_t)rsc;
+}
+
+}  // namespace
+
+size_t grouped_workspace_bytes(int64_t rows, int E, int K) { return ws_layout(rows, E, K).total; }
+
+hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
+  const int E = a.gemm.E;
+  if (E < 1 || E > kMaxExperts) return hipErrorInvalidValue;
+  const WsLayout L = ws_layout(a.rows, E, a.gemm.K);
+  const int KT = (a.gemm.K + 127) / 128;
+  int64_t* seg = reinterpret_cast<int64_t*>(a.ws + L.seg);
+  int64_t* pseg = reinterpret_cast<int64_t*>(a.ws + L.pseg);
+  int32_t* tprefix = reinterpret_cast<int32_t*>(a.ws + L.tprefix);
+
+  hipLaunchKernelGGL(grouped_setup_kernel, dim3(1), dim3(256), 0, stream, a.seg_in, E, a.rows,
+                     grouped_tile_m(), seg, pseg, tprefix);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  GatherArgs g;
+  g.s_codes = a.gemm.s_codes; g.s_meta = a.gemm.s_meta; g.s_scales = a.gemm.s_scales;
+  g.r_codes = a.gemm.r_codes; g.r_scales = a.gemm.r_scales;
+  g.g_r_codes = a.ws + L.r_codes; g.g_s_codes = a.ws + L.s_codes; g.g_s_meta = a.ws + L.s_meta;
+  g.g_s_scales = a.ws + L.s_scales; g.g_r_scales = a.ws + L.r_scales;
+  g.row_index = a.row_index;
+  g.seg = seg; g.pseg = pseg;
+  g.src_rows = a.gemm.M; g.src_blocks = a.src_blocks; g.dst_blocks = L.blocks;
+  g.KT = KT; g.E = E;
+  const int64_t waves = L.blocks * KT;
+  if (waves > 0) {
+    const int64_t wgs = (waves + 3) / 4;
+    if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(grouped_gather_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, g);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+
+  GemmArgs m = a.gemm;
+  m.s_codes = g.g_s_codes; m.s_meta = g.g_s_meta; m.s_scales = g.g_s_scales;
+  m.r_codes = g.g_r_codes; m.r_scales = g.g_r_scales;
+  m.a_blocks = L.blocks;
+  m.M = a.rows;
+  m.seg = seg; m.pseg = pseg; m.tprefix = tprefix;
+  const int64_t max_mtiles = (a.rows + grouped_tile_m() - 1) / grouped_tile_m() + E;
+  return launch_linear_grouped_gemm(m, max_mtiles, stream);
+}
+
+}  // namespace sharq

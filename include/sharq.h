@@ -188,6 +188,38 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
 sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w,
                           void* y_dev, int64_t ldy, int32_t out_dtype, void* stream);
 
+/* Workspace bytes sharq_linear_grouped needs for `rows` routed rows, E
+ * experts and reduction length K (the routed activation rows gathered into
+ * expert order, each expert padded to whole 16-row blocks, plus small tables).
+ * Errors: INVALID_ARG (null, rows<0, E<1 or E>1024, K<=0 or K%32). */
+sharq_status sharq_grouped_workspace_bytes(int64_t rows, int32_t E, int64_t K, size_t* bytes);
+
+/* Grouped expert layer (mixture of experts).  SharQ abstract: the method is
+ * evaluated on mixture-of-experts models too; each expert is a SharQ linear
+ * layer over the rows routed to it.
+ *   a:          prepared activation of the source rows (e.g. the tokens, each
+ *               prepared once: prep is row-local, so this equals preparing
+ *               each routed copy);
+ *   row_index:  device int32[rows]: routed row i reads source row
+ *               row_index[i]; NULL means row i of `a` (then rows == a->M);
+ *               an index outside [0, a->M) reads as an all-zero row;
+ *   seg_offsets: device int64[E+1], nondecreasing, seg[0] = 0, seg[E] = rows:
+ *               expert e owns routed rows [seg[e], seg[e+1]) (values outside
+ *               that contract are clamped into it on the device);
+ *   w:          the E experts' weights stacked along N and packed as one
+ *               weight of N = E * N_e rows (sharq_pack_weight of the [E*N_e, K]
+ *               stack); N_e must be a multiple of 16;
+ *   y:          device [rows][ldy] (ldy >= N_e), row i = expert e's output for
+ *               routed row i, in fp32 or bf16 per out_dtype;
+ *   ws:         device workspace of ws_bytes >= sharq_grouped_workspace_bytes,
+ *               owned by the caller; calls that share it must not overlap.
+ * Errors: INVALID_ARG (null, shapes, K mismatch, ldy < N_e, workspace too
+ * small, misaligned buffers), UNSUPPORTED (fmt, pattern, not gfx950), HIP. */
+sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
+                                  const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
+                                  void* y_dev, int64_t ldy, int32_t out_dtype,
+                                  void* ws_dev, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

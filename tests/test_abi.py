@@ -136,3 +136,32 @@ def test_pack_and_linear_reject_before_launch(lib):
     assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 0, None) == _lib.ERR_UNSUPPORTED
     a.M = 0
     assert lib.sharq_linear(C.byref(a), C.byref(w), None, 32, 0, None) == _lib.OK
+
+
+def test_grouped_rejects_before_launch(lib):
+    n = C.c_size_t()
+    assert lib.sharq_grouped_workspace_bytes(100, 0, 256, C.byref(n)) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_grouped_workspace_bytes(100, 1025, 256, C.byref(n)) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_grouped_workspace_bytes(100, 8, 250, C.byref(n)) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_grouped_workspace_bytes(100, 8, 256, C.byref(n)) == _lib.OK
+    # gathered rows of 8 experts padded to 16-row blocks: (100 + 8*15 + 15) // 16 blocks x 2 K tiles x 1920 B
+    assert n.value >= (100 + 8 * 15 + 15) // 16 * 2 * 1920
+    a = _act()
+    a.layout_version = _lib.SHARQ_ABI_VERSION
+    a.M, a.K, a.n, a.m = 64, 256, 2, 4
+    w = _lib.WeightDesc()
+    w.struct_size = C.sizeof(_lib.WeightDesc)
+    w.layout_version = _lib.SHARQ_ABI_VERSION
+    w.N, w.K, w.codes, w.scales = 8 * 16, 256, 0x100000, 0x200000   # 8 experts of 16 rows
+    for p in (0, 1):
+        w.view[p].base, w.view[p].ld, w.view[p].block = 0x200000, 8 * 64, 32
+    seg, y, ws = C.c_void_p(0x500000), C.c_void_p(0x600000), C.c_void_p(0x700000)
+    call = lambda rows, E, ri=None, ldy=32, wsb=1 << 30: lib.sharq_linear_grouped(
+        C.byref(a), ri, rows, seg, E, C.byref(w), y, ldy, 0, ws, wsb, None)
+    assert call(64, 0) == _lib.ERR_INVALID_ARG                   # E < 1
+    assert call(64, 3) == _lib.ERR_INVALID_ARG                   # N is not 3 equal experts
+    assert call(64, 16) == _lib.ERR_INVALID_ARG                  # N_e = 8, not a multiple of 16
+    assert call(63, 8) == _lib.ERR_INVALID_ARG                   # rows != M without a row index
+    assert call(64, 8, ldy=8) == _lib.ERR_INVALID_ARG            # ldy < N_e
+    assert call(64, 8, wsb=100) == _lib.ERR_WORKSPACE            # workspace too small
+    assert call(0, 8, ri=C.c_void_p(0x800000)) == _lib.OK        # nothing routed: no launch
