@@ -1,19 +1,28 @@
 """Benchmark of the SharQ linear hot path on one MI355X.
 
 One step = fused prep (RMSNorm, 2:4 mask, MXFP4 of S, residual, MXFP4 of R)
-followed by the dual FP4 GEMM with its single epilogue, on one batch of the
-Llama-3.1-8B fused-QKV workload (M=2048 tokens, K=4096, N=6144).  The weight
-payload is packed once, outside the timed region (it is an offline step).
+followed by the dual FP4 GEMM with its single epilogue, on one batch of a
+workload.  The default workload -- the headline line -- is the Llama-3.1-8B
+fused QKV projection (M=2048 tokens, K=4096, N=6144, RMSNorm).  Other
+workloads (``--workload``): gateup (N=28672, RMSNorm), down (K=14336, N=4096,
+SiLU-product inputs, no norm), decode (``--m`` in 1, 8, 32, 64; K=N=4096, no
+norm) and moe (Qwen3-30B-A3B-shaped expert layer: 4096 tokens routed top-8 of
+128 experts with Zipf(1.1) loads; step = prep of the tokens + grouped gate/up
+(K=2048, N_e=1536) + prep of the 32768 expert-sorted down rows + grouped down
+(K=768, N_e=2048)).  Weight payloads are packed once, outside the timed region
+(an offline step).
 
-Inputs are seeded synthetic tensors (fp4_sparse_dense_amd.synth) and are
-resident in HBM before timing starts.  Eight input/weight/output sets
-(> 512 MB together) rotate from step to step so the 256 MB MALL cannot serve
-a step's operands from the previous one.
+Inputs are seeded synthetic tensors (fp4_sparse_dense_amd.synth for
+activations and the router; weights N(0, 0.02) drawn on the device from a
+seeded generator and rounded to bf16) and are resident in HBM before timing
+starts.  Input/weight/output sets rotate from step to step, enough of them
+(> 512 MB together) that the 256 MB MALL cannot serve a step's operands from
+an earlier one.
 
 Prints one JSON line.  value = layer TFLOP/s = 4*M*N*K (2*M*N*K per path) /
-(wall time per step); prep GB/s and the GEMM's MFMA fraction are reported
-beside it; ``roofline`` describes the dominant kernel (the dual GEMM), timed
-with HIP events on the stream it is launched on.
+(wall time per step); prep GB/s and the GEMM's fractions are reported beside
+it; ``roofline`` describes the dominant kernel (the dual GEMM), timed with HIP
+events on the stream it is launched on.
 """
 from __future__ import annotations
 
@@ -30,7 +39,18 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
-WORKLOAD = dict(name="qkv", M=2048, K=4096, N=6144)
+WORKLOADS = {
+    "qkv": dict(M=2048, K=4096, N=6144, norm=True, law="outlier",
+                desc="Llama-3.1-8B fused QKV projection: M=2048 tokens, K=4096, N=6144; RMSNorm"),
+    "gateup": dict(M=2048, K=4096, N=28672, norm=True, law="outlier",
+                   desc="Llama-3.1-8B MLP gate/up: M=2048, K=4096, N=28672; RMSNorm"),
+    "down": dict(M=2048, K=14336, N=4096, norm=False, law="silu",
+                 desc="Llama-3.1-8B MLP down: M=2048, K=14336, N=4096; SiLU(g)*u inputs, no norm"),
+    "decode": dict(M=None, K=4096, N=4096, norm=False, law="outlier",
+                   desc="decode: M rows, K=N=4096, no norm"),
+}
+MOE = dict(tokens=4096, experts=128, top_k=8, d_model=2048, d_ff=768)
+ROTATE_BYTES = 600 << 20       # rotating sets exceed the 256 MB MALL
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dual_gemm_qkv.txt")
 GEMM_SRC = os.path.join(ROOT, "fp4_sparse_dense_amd", "csrc", "gemm.hip")
 
@@ -42,6 +62,12 @@ def prep_bytes(M, K, norm=True):
 
 def gemm_flops(M, N, K):
     return 4 * M * N * K
+
+
+def gemm_bytes(M, N, K, out_bytes=4):
+    """Algorithmic HBM bytes of one dual GEMM: prepared A (0.9375 B/elem), the
+    packed weight read once for both paths (0.53125 B/elem), Y."""
+    return M * K * 15 // 16 + N * K * 17 // 32 + out_bytes * M * N
 
 
 def source_digest(path):
@@ -90,12 +116,79 @@ def cpu_baseline(rows: int = 2048):
                       f"{inp['N']} outputs ({dt:.1f} s)"}
 
 
+def device_weight(gen, N, K):
+    """W ~ N(0, 0.02) rounded to bf16, drawn on the device from a seeded generator."""
+    import torch
+    return (torch.randn(N, K, generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+
+
+def timed(step, steps, warmup, graph=False):
+    """Wall time per step over `steps` steps after `warmup`, bracketed by
+    synchronisations, then per-kernel HIP-event times over the same steps.
+
+    graph=True (workloads whose kernels are shorter than a host launch): the
+    steps are captured once in a HIP graph and replayed, so the timed region
+    holds device work only; per-kernel times then come from graphs holding only
+    that kernel's launches, timed with events around the replay."""
+    import numpy as np
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    if not graph:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        evs = []
+        for i in range(steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+            step(i, ev, stream)
+            evs.append(ev)
+        torch.cuda.synchronize()
+        return wall * 1e3 / steps, [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(step.parts)]
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        return g
+
+    def replay_ms(g, reps=5):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / steps
+
+    g_all = capture(lambda i: step(i))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_all.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    parts = []
+    for j in range(step.parts):
+        gj = capture(lambda i, j=j: step(i, part=j))
+        parts.append([replay_ms(gj)])
+    return wall * 1e3 / steps, parts
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sets", type=int, default=8, help="rotating input/weight/output sets")
+    ap.add_argument("--workload", default="qkv", choices=sorted(list(WORKLOADS) + ["moe"]))
+    ap.add_argument("--m", type=int, default=1, help="rows of the decode workload")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input/weight/output sets (0: enough for > 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration under rocprofv3)")
@@ -104,104 +197,196 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    import torch
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.workload == "moe":
+        rec = run_moe(args)
+    else:
+        rec = run_dense(args)
+    print(json.dumps(rec), flush=True)
+
+
+def run_dense(args):
     import numpy as np
     import torch
 
     import fp4_sparse_dense_amd as sq
     from fp4_sparse_dense_amd import synth
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    M, K, N = WORKLOAD["M"], WORKLOAD["K"], WORKLOAD["N"]
+    wl = dict(WORKLOADS[args.workload])
+    M = args.m if args.workload == "decode" else wl["M"]
+    K, N, norm = wl["K"], wl["N"], wl["norm"]
 
     def up(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
+    per_set = M * K * 2 + N * K * 17 // 32 + M * K * 15 // 16 + 4 * M * N
+    nsets = args.sets or max(2, min(64, -(-ROTATE_BYTES // per_set)))
+    nx = min(nsets, 4)                       # distinct activation draws (CPU-generated)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    xs, gammas = [], []
+    for s in range(nx):
+        if args.workload == "qkv":
+            inp = synth.layer_inputs("qkv", seed=100 + s, with_weight=False)
+        else:
+            rng = np.random.default_rng(200 + s)
+            x = synth.outlier_activations(rng, M, K) if wl["law"] == "outlier" else synth.silu_product_activations(rng, M, K)
+            inp = dict(x=x, gamma=synth.norm_weight(rng, K) if norm else None)
+        xs.append(up(inp["x"]))
+        gammas.append(up(inp["gamma"]) if norm else None)
     sets = []
-    for s in range(args.sets):
-        inp = synth.layer_inputs("qkv", seed=100 + s)
-        x, g = up(inp["x"]), up(inp["gamma"])
-        w = sq.sharq_pack_weight(up(inp["w"]))
-        act = sq.SharqAct(M, K, dev)
-        y = torch.empty(M, N, dtype=torch.float32, device=dev)
-        sets.append((x, g, w, act, y))
+    for s in range(nsets):
+        w = sq.sharq_pack_weight(device_weight(gen, N, K))
+        sets.append((w, sq.SharqAct(M, K, torch.device("cuda")), torch.empty(M, N, dtype=torch.float32, device="cuda")))
     torch.cuda.synchronize()
 
-    if args.copy_calibration:
-        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        x, g, w, act, y = sets[i % len(sets)]
+    def step(i, ev=None, stream=None, part=None):
+        w, act, y = sets[i % nsets]
+        x, g = xs[i % nx], gammas[i % nx]
         if ev is not None:
             ev[0].record(stream)
-        sq.sharq_prepare(x, g, 1e-5, out=act)
+        if part in (None, 0):
+            sq.sharq_prepare(x, g, 1e-5, out=act)
         if ev is not None:
             ev[1].record(stream)
-        sq.sharq_linear(act, w, out=y)
+        if part in (None, 1):
+            sq.sharq_linear(act, w, out=y)
         if ev is not None:
             ev[2].record(stream)
+    step.parts = 2
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: wall clock over exactly `steps` steps
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # per-kernel durations: HIP events on the launch stream, same steps again
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-
-    ms_per_step = wall * 1e3 / args.steps
+    graph = args.workload == "decode"
+    ms, parts = timed(step, args.steps, args.warmup, graph=graph)
+    prep_ms, gemm_ms = float(np.mean(parts[0])), float(np.mean(parts[1]))
     flops = gemm_flops(M, N, K)
-    value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    pbytes = prep_bytes(M, K)
+    gbytes = gemm_bytes(M, N, K)
+    gemm_gbs = gbytes / (gemm_ms * 1e-3) / 1e9
+    pbytes = prep_bytes(M, K, norm)
     prep_gbs = pbytes / (prep_ms * 1e-3) / 1e9
-
-    cpu = None if args.no_cpu_baseline else cpu_baseline()
-
-    rec = {
+    hbm_bound = gbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_FP4_TFLOPS * 1e12)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
+                "traffic": read_traffic() if args.workload == "qkv" else None}
+    cpu = None if (args.no_cpu_baseline or args.workload != "qkv") else cpu_baseline()
+    wname = args.workload if args.workload != "decode" else f"decode{M}"
+    return {
         "metric": "SharQ linear TFLOPS + prep GB/s (fraction of peak), Llama-8B shapes M=2048",
-        "value": round(value, 2),
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "mxfp4",
         "data": "synthetic",
-        "config": {"workload": "Llama-3.1-8B fused QKV projection: M=2048 tokens, K=4096, N=6144; RMSNorm; "
-                               "2:4 mask; MXFP4 activations and weight; fp32 output",
-                   "M": M, "K": K, "N": N, "pattern": "2:4", "format": "MXFP4", "rotating_sets": args.sets},
+        "config": {"workload": f"{wname}: " + wl["desc"].split(": ", 1)[1].replace("M rows", f"M={M}") +
+                               "; 2:4 mask; MXFP4 activations and weight; fp32 output",
+                   "M": M, "K": K, "N": N, "pattern": "2:4", "format": "MXFP4", "rotating_sets": nsets},
         "prep": {"us": round(prep_ms * 1e3, 3), "GB/s": round(prep_gbs, 1),
                  "frac_hbm": round(prep_gbs / PEAK_HBM_GBS, 4), "bytes": pbytes},
         "gemm": {"us": round(gemm_ms * 1e3, 3), "TFLOP/s": round(gemm_tflops, 1),
-                 "frac_mfma": round(gemm_tflops / PEAK_FP4_TFLOPS, 4)},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP4_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
-                     "traffic": read_traffic()},
+                 "frac_mfma": round(gemm_tflops / PEAK_FP4_TFLOPS, 4), "GB/s": round(gemm_gbs, 1),
+                 "frac_hbm": round(gemm_gbs / PEAK_HBM_GBS, 4), "bytes": gbytes},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec), flush=True)
+
+
+def run_moe(args):
+    import numpy as np
+    import torch
+
+    import fp4_sparse_dense_amd as sq
+    from fp4_sparse_dense_amd import synth
+
+    T, E, k, dm, dff = MOE["tokens"], MOE["experts"], MOE["top_k"], MOE["d_model"], MOE["d_ff"]
+    rows = T * k
+    rng = np.random.default_rng(300)
+    expert, token, seg = synth.zipf_router(rng, T, E, k)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    x_tok = up(synth.outlier_activations(rng, T, dm))
+    x_down = up(synth.outlier_activations(rng, rows, dff))
+    seg_d = torch.from_numpy(seg).cuda()
+    ri = torch.from_numpy(token.astype(np.int32)).cuda()
+    n_gu, n_d = 2 * dff, dm
+    per_set = (E * n_gu * dm + E * n_d * dff) * 17 // 32 + 4 * rows * (n_gu + n_d)
+    nsets = args.sets or max(2, -(-ROTATE_BYTES // per_set))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+    sets = []
+    for s in range(nsets):
+        wgu = sq.sharq_pack_weight(device_weight(gen, E * n_gu, dm))
+        wd = sq.sharq_pack_weight(device_weight(gen, E * n_d, dff))
+        sets.append((wgu, wd, torch.empty(rows, n_gu, device="cuda"), torch.empty(rows, n_d, device="cuda")))
+    a_tok = sq.SharqAct(T, dm, torch.device("cuda"))
+    a_down = sq.SharqAct(rows, dff, torch.device("cuda"))
+    ws = torch.empty(max(sq.grouped_workspace_bytes(rows, E, dm), sq.grouped_workspace_bytes(rows, E, dff)),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(i, ev=None, stream=None, part=None):
+        wgu, wd, ygu, yd = sets[i % nsets]
+        rec = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        rec(0)
+        sq.sharq_prepare(x_tok, None, out=a_tok)
+        rec(1)
+        sq.sharq_linear_grouped(a_tok, wgu, seg_d, E, row_index=ri, rows=rows, out=ygu, workspace=ws)
+        rec(2)
+        sq.sharq_prepare(x_down, None, out=a_down)
+        rec(3)
+        sq.sharq_linear_grouped(a_down, wd, seg_d, E, rows=rows, out=yd, workspace=ws)
+        rec(4)
+    step.parts = 4
+
+    ms, parts = timed(step, args.steps, args.warmup)
+    t = [float(np.mean(p)) for p in parts[:4]]
+    f_gu, f_d = gemm_flops(rows, n_gu, dm), gemm_flops(rows, n_d, dff)
+    # algorithmic bytes: prepared rows read once (distinct tokens for gate/up), all
+    # experts' weights once, Y once
+    b_gu = T * dm * 15 // 16 + E * n_gu * dm * 17 // 32 + 4 * rows * n_gu
+    b_d = rows * dff * 15 // 16 + E * n_d * dff * 17 // 32 + 4 * rows * n_d
+    gbs_gu = b_gu / (t[1] * 1e-3) / 1e9
+    loads = np.diff(seg)
+    return {
+        "metric": "SharQ linear TFLOPS + prep GB/s (fraction of peak), Llama-8B shapes M=2048",
+        "value": round((f_gu + f_d) / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": f"moe: Qwen3-30B-A3B-shaped expert layer, {T} tokens top-{k} of {E} experts "
+                               f"(Zipf(1.1) loads, max {int(loads.max())} min {int(loads.min())} rows), "
+                               f"gate/up K={dm} N_e={n_gu}, down K={dff} N_e={n_d}; no norm; 2:4 mask; MXFP4; fp32 output",
+                   "rows": rows, "experts": E, "rotating_sets": nsets},
+        "prep": {"tokens_us": round(t[0] * 1e3, 3), "down_rows_us": round(t[2] * 1e3, 3),
+                 "GB/s": round((prep_bytes(T, dm, False) + prep_bytes(rows, dff, False)) / ((t[0] + t[2]) * 1e-3) / 1e9, 1)},
+        "gemm": {"gate_up_us": round(t[1] * 1e3, 3), "down_us": round(t[3] * 1e3, 3),
+                 "gate_up_TFLOP/s": round(f_gu / (t[1] * 1e-3) / 1e12, 1),
+                 "down_TFLOP/s": round(f_d / (t[3] * 1e-3) / 1e12, 1),
+                 "gate_up_GB/s": round(gbs_gu, 1), "down_GB/s": round(b_d / (t[3] * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs_gu, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs_gu / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
 
 
 if __name__ == "__main__":
