@@ -232,6 +232,7 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   g.K = (int)a->K;
   g.out_bf16 = out_dtype == SHARQ_OUT_BF16;
   g.a_blocks = (a->M + 15) / 16;
+  g.xcd_bm = 0;
   g.seg = nullptr;
   g.pseg = nullptr;
   g.tprefix = nullptr;
@@ -318,6 +319,7 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
   g.K = (int)a->K;
   g.out_bf16 = out_dtype == SHARQ_OUT_BF16;
   g.a_blocks = (a->M + 15) / 16;
+  g.xcd_bm = 0;
   g.seg = nullptr;
   g.pseg = nullptr;
   g.tprefix = nullptr;

@@ -217,15 +217,27 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   // (nb - nb_first) * 16 + c, valid below y_cols.
   int64_t rb0, nb0, rb_end, nb_end, rb_first, nb_first, y_row0, y_rows, y_cols;
   if constexpr (!GROUPED) {
-    // blocks on one XCD (block id mod 8) take a contiguous range of tiles,
-    // walked M-fastest, so they share weight and activation rows in L2
+    // Workgroups on one XCD (block id mod 8) take one region of xcd_bm M tiles
+    // x bn N tiles, so the activation and weight tiles they share stay in that
+    // XCD's L2 (the host picks the region shape with the fewest bytes per XCD);
+    // without a region shape the tiles are dealt in plain order.
     const int tiles_m = (int)((g.M + BM - 1) / BM);
     const int tiles_n = (int)((g.N + BN - 1) / BN);
     const int T = tiles_m * tiles_n;
-    int t = blockIdx.x;
-    if (T % 8 == 0) t = (t % 8) * (T / 8) + t / 8;
-    rb0 = (int64_t)(t % tiles_m) * C::kMB;
-    nb0 = (int64_t)(t / tiles_m) * C::kNB;
+    const int t = blockIdx.x;
+    int tm, tn;
+    if (g.xcd_bm > 0) {
+      const int bm = g.xcd_bm, bn = T / 8 / bm;
+      const int x = t % 8, i = t / 8;                  // XCD, index on it
+      const int regions_m = tiles_m / bm;
+      tm = (x % regions_m) * bm + i % bm;
+      tn = (x / regions_m) * bn + i / bm;
+    } else {
+      tm = t % tiles_m;
+      tn = t / tiles_m;
+    }
+    rb0 = (int64_t)tm * C::kMB;
+    nb0 = (int64_t)tn * C::kNB;
     rb_end = RB; nb_end = NB; rb_first = 0; nb_first = 0;
     y_row0 = 0; y_rows = g.M; y_cols = g.N;
   } else {
@@ -515,6 +527,27 @@ static hipError_t launch_tiled(const GemmArgs& a, int64_t tiles, hipStream_t str
 constexpr int kTileM = 256, kTileN = 192;
 int grouped_tile_m() { return kTileM; }
 
+// M tiles per XCD region for a tm x tn tile grid split into 8 equal regions of
+// bm x bn tiles: the shape that minimises the operand bytes one XCD reads
+// (bm activation tiles at 0.9375 B/elem, bn weight tiles at 0.53125 B/elem);
+// 0 when no such split exists.
+static int xcd_region_m(int64_t tm, int64_t tn, int K) {
+  const int64_t T = tm * tn;
+  if (T % 8 != 0) return 0;
+  const int64_t per = T / 8;
+  int best = 0;
+  double best_cost = 0.0;
+  for (int64_t bm = 1; bm <= tm && bm <= per; ++bm) {
+    if (tm % bm || per % bm) continue;
+    const int64_t bn = per / bm;
+    if (tn % bn) continue;
+    const double cost = (double)bm * kTileM * 0.9375 + (double)bn * kTileN * 0.53125;
+    if (best == 0 || cost < best_cost) { best = (int)bm; best_cost = cost; }
+  }
+  (void)K;
+  return best;
+}
+
 hipError_t launch_linear_grouped_gemm(const GemmArgs& a, int64_t max_mtiles, hipStream_t stream) {
   const int64_t NBe = (a.N / a.E + 15) / 16;
   const int64_t tiles_n = (NBe + kTileN / 16 - 1) / (kTileN / 16);
@@ -527,9 +560,12 @@ hipError_t launch_linear(const GemmArgs& a, hipStream_t stream) {
   const uint64_t kb = (a.K + 127) / 128;
   const bool fits = (uint64_t)((a.M + 15) / 16) * kb * 1024 < 0x7FFFFFFFull &&
                     (uint64_t)((a.N + 15) / 16) * kb * 1024 < 0x7FFFFFFFull;
-  if (a.M > 64 && fits)
-    return launch_tiled<kTileM, kTileN, 4, 2, 3, false>(
-        a, ((a.M + kTileM - 1) / kTileM) * ((a.N + kTileN - 1) / kTileN), stream);
+  if (a.M > 64 && fits) {
+    const int64_t tm = (a.M + kTileM - 1) / kTileM, tn = (a.N + kTileN - 1) / kTileN;
+    GemmArgs b = a;
+    b.xcd_bm = xcd_region_m(tm, tn, a.K);
+    return launch_tiled<kTileM, kTileN, 4, 2, 3, false>(b, tm * tn, stream);
+  }
   // M <= 64 (or operands past 31-bit buffer offsets): split-K weight streaming;
   // eight waves per column block for one or two row blocks, four for more
   const int64_t RB = (a.M + 15) / 16, NB = (a.N + 15) / 16;

@@ -36,6 +36,7 @@ struct GemmArgs {
   int K;
   int out_bf16;
   int64_t a_blocks;                // 16-row blocks of the activation buffers (scale stride)
+  int xcd_bm;                      // tiled kernel: M tiles per XCD region (0: plain XCD order)
   // grouped expert layer; seg == nullptr for a single problem
   const int64_t* seg;              // [E+1] first output row of each expert (sanitised)
   const int64_t* pseg;             // [E+1] first activation 16-row block of each expert
