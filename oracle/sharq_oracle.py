@@ -314,6 +314,170 @@ def linear(act: dict, w_codes, w_scales, rows=None):
     return y, b
 
 
+# --------------------------------------------------------------------------
+# NVFP4-style format: a reading.  The SharQ abstract reports the method under
+# NVFP4 (and HiF4, MXFP4) but prints no definition; this follows the public
+# two-level NVFP4 description: E2M1 elements in 16-element blocks, an OCP E4M3
+# block scale, and one binary32 scale per tensor.
+#   g_T = A_T / 2688 (A_T = max |u| over the whole tensor T; 2688 = 6 * 448,
+#         the largest E2M1 times the largest E4M3), g_T = 1 when A_T = 0;
+#   s_b = E4M3(amax_b / (6 g_T)), round to nearest even, saturating at 448;
+#   code = E2M1(u / (s_b g_T)), or the signed zero code when s_b = 0;
+#   value = val(code) * s_b * g_T.
+# Every operation above is one binary32 operation, rounded once.  T is S, R
+# and W separately, so the residual's tensor scale depends on Q(S).
+# --------------------------------------------------------------------------
+NV_BLOCK = 16
+E4M3_MAX = 448.0
+NV_TENSOR_DIV = F32(2688.0)
+
+
+def e4m3_value(byte) -> np.ndarray:
+    """Value of an OCP E4M3 byte with the sign bit clear (float64): exponent
+    field E (bias 7) and mantissa m (3 bits); E = 0 is subnormal m * 2^-9;
+    0x7F is NaN (excluded, never produced here)."""
+    b = np.asarray(byte, dtype=np.int64) & 0x7F
+    e = b >> 3
+    m = (b & 7).astype(np.float64)
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+
+
+def e4m3_round(x):
+    """E4M3 of binary32 x >= 0: nearest representable value, ties to the even
+    mantissa, values above 448 saturate to 448 (no infinity/NaN produced).
+
+    Normal range (x >= 2^-6): the spacing is 2^(floor(log2 x) - 3); below it the
+    spacing is the subnormal step 2^-9.  x / spacing is exact in float64 and
+    np.rint rounds half to even.  Returns (value float64, byte uint8).
+    Pinned by: brute force over all 127 non-negative E4M3 values on every
+    midpoint and its binary32 neighbours, round trip of every byte.
+    """
+    x = np.asarray(x, dtype=F32).astype(np.float64)
+    if np.any(x < 0) or not np.all(np.isfinite(x)):
+        raise ValueError("e4m3_round takes finite x >= 0")
+    step = np.full(x.shape, 2.0 ** -9)
+    nrm = x >= 2.0 ** -6
+    step[nrm] = np.exp2((floor_log2(x[nrm]) - 3).astype(np.float64))
+    val = np.minimum(np.rint(x / step) * step, E4M3_MAX)
+    byte = np.zeros(x.shape, dtype=np.uint8)
+    nv = val >= 2.0 ** -6
+    e = floor_log2(val[nv]) if np.any(nv) else np.zeros(0, np.int32)
+    mant = (val[nv] / np.exp2(e.astype(np.float64)) - 1.0) * 8.0
+    byte[nv] = ((e + 7) << 3).astype(np.uint8) | mant.astype(np.uint8)
+    byte[~nv] = (val[~nv] / 2.0 ** -9).astype(np.uint8)
+    return val, byte
+
+
+def nv_tensor_scale(amax) -> np.float32:
+    """g = A / 2688 in binary32; 1 for an all-zero tensor."""
+    a = F32(amax)
+    return F32(1.0) if a == 0 else F32(a / NV_TENSOR_DIV)
+
+
+def quantize_nv(u: np.ndarray, g):
+    """NVFP4-style quantisation along the last axis (length a multiple of 16)
+    with tensor scale g.  Returns (E4M3 bytes [..., K/16], nibbles [..., K]).
+
+    Per block: s = E4M3(amax / (6 * g)); t = s * g; code = E2M1(u / t)
+    (binary32 quotient, then e2m1_nearest); s == 0 gives the signed zero code.
+    Pinned by: closed-form block, the block-maximum-code invariant, exact
+    rational brute force of each element's code.
+    """
+    u = np.asarray(u, dtype=F32)
+    g = F32(g)
+    K = u.shape[-1]
+    if K % NV_BLOCK:
+        raise ValueError("K must be a multiple of 16")
+    blocks = u.reshape(u.shape[:-1] + (K // NV_BLOCK, NV_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    sval, sbyte = e4m3_round(amax / (F32(6.0) * g))
+    t = (sval.astype(F32) * g)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = blocks / t
+    nib = e2m1_nearest(q)
+    zero = np.broadcast_to((sbyte == 0)[..., None], blocks.shape)
+    nib = np.where(zero, np.signbit(blocks).astype(np.uint8) << 3, nib)
+    return sbyte, nib.reshape(u.shape)
+
+
+def dequant_nv(scales: np.ndarray, nib: np.ndarray, g) -> np.ndarray:
+    """val(code) * s * g in float64 (exact: at most 6 + 24 significant bits)."""
+    K = nib.shape[-1]
+    s = e4m3_value(scales)
+    val = e2m1_value(nib).reshape(nib.shape[:-1] + (K // NV_BLOCK, NV_BLOCK))
+    return (val * s[..., None] * np.float64(F32(g))).reshape(nib.shape)
+
+
+def dequant_nv_f32(scales: np.ndarray, nib: np.ndarray, g) -> np.ndarray:
+    """The binary32 dequantisation the residual uses: (val(code) * s) * g with
+    val * s exact and one rounding for the product with g."""
+    K = nib.shape[-1]
+    s = e4m3_value(scales)
+    vs = (e2m1_value(nib).reshape(nib.shape[:-1] + (K // NV_BLOCK, NV_BLOCK)) * s[..., None]).astype(F32)
+    return (vs * F32(g)).reshape(nib.shape)
+
+
+def prepare_nv(x_bits, gamma_bits=None, eps: float = 1e-5, n: int = 2, m: int = 4):
+    """Sparse-dense decomposition in the NVFP4-style format (2:4 outputs).
+
+    Same steps as prepare() with the quantiser replaced: S over 16 logical
+    positions per block with tensor scale g_s = scale of max|S|; residual
+    r = v - d in binary32 with d = (val * s) * g_s; R quantised with g_r =
+    scale of max|r|.  Returns the byte outputs of prepare() (scales are E4M3
+    per 16 positions, [M, K/16]) plus g_s, g_r and the intermediates.
+    Pinned by: v == d + r exactly; max|S| == max|v|; the per-element code
+    brute force of quantize_nv on both tensors; zero tensors.
+    """
+    if (n, m) != (2, 4):
+        raise ValueError("byte outputs are defined for 2:4")
+    v = rmsnorm(x_bits, gamma_bits, eps)
+    kept = nm_mask(v, n, m)
+    s = np.where(kept, v, F32(0.0))
+    g_s = nv_tensor_scale(np.abs(s).max() if s.size else 0.0)
+    s_scales, s_nib = quantize_nv(s, g_s)
+    d = np.where(kept, dequant_nv_f32(s_scales, s_nib, g_s), F32(0.0)).astype(F32)
+    r = v - d
+    g_r = nv_tensor_scale(np.abs(r).max() if r.size else 0.0)
+    r_scales, r_nib = quantize_nv(r, g_r)
+    M, K = v.shape
+    return dict(
+        fmt="nvfp4",
+        s_codes=pack_nibbles(s_nib[kept].reshape(M, K // 2)),
+        s_meta=pack_meta_24(kept),
+        s_scales=s_scales,
+        r_codes=pack_nibbles(r_nib),
+        r_scales=r_scales,
+        g_s=g_s, g_r=g_r,
+        v=v, kept=kept, s_nib=s_nib, d=d, r=r,
+    )
+
+
+def pack_weight_nv(w_bits):
+    """NVFP4-style weight payload: g_w from max|W| over the whole tensor, then
+    quantize_nv per row.  Returns (codes [N, K/2], E4M3 scales [N, K/16], g_w)."""
+    u = widen_bf16(w_bits)
+    g_w = nv_tensor_scale(np.abs(u).max())
+    scales, nib = quantize_nv(u, g_w)
+    return pack_nibbles(nib), scales, g_w
+
+
+def linear_nv(act: dict, w_codes, w_scales, g_w, rows=None):
+    """NVFP4-style dual GEMM: y = D^S D^W^T + D^R D^W^T with D = val * s * g
+    (float64, exact), plus the bound B = sum|terms|.  Returns (y, B)."""
+    K = 2 * np.asarray(w_codes).shape[1]
+    sl = slice(None) if rows is None else rows
+    kept = unpack_meta_24(act["s_meta"][sl], K)
+    M = kept.shape[0]
+    nib = np.zeros((M, K), dtype=np.uint8)
+    nib[kept] = unpack_nibbles(act["s_codes"][sl]).reshape(-1)
+    ds = np.where(kept, dequant_nv(act["s_scales"][sl], nib, act["g_s"]), 0.0)
+    dr = dequant_nv(act["r_scales"][sl], unpack_nibbles(act["r_codes"][sl]), act["g_r"])
+    dw = dequant_nv(w_scales, unpack_nibbles(w_codes), g_w)
+    y = ds @ dw.T + dr @ dw.T
+    b = np.abs(ds) @ np.abs(dw).T + np.abs(dr) @ np.abs(dw).T
+    return y, b
+
+
 def within_tolerance(y_gpu, y_ref, bound, rel: float = 1e-5, abs_: float = 1e-6):
     """Elementwise |y_gpu - y_ref| <= rel * sum|terms| + abs."""
     err = np.abs(np.asarray(y_gpu, dtype=np.float64) - y_ref)
