@@ -6,7 +6,8 @@ workload.  The default workload -- the headline line -- is the Llama-3.1-8B
 fused QKV projection (M=2048 tokens, K=4096, N=6144, RMSNorm).  Other
 workloads (``--workload``): gateup (N=28672, RMSNorm), down (K=14336, N=4096,
 SiLU-product inputs, no norm), decode (``--m`` in 1, 8, 32, 64; K=N=4096, no
-norm) and moe (Qwen3-30B-A3B-shaped expert layer: 4096 tokens routed top-8 of
+norm; ``--fmt nvfp4`` runs it in the NVFP4-style format: E4M3 scale per 16,
+binary32 tensor scales, bf16 MFMA on exactly expanded codes) and moe (Qwen3-30B-A3B-shaped expert layer: 4096 tokens routed top-8 of
 128 experts with Zipf(1.1) loads; step = prep of the tokens + grouped gate/up
 (K=2048, N_e=1536) + prep of the 32768 expert-sorted down rows + grouped down
 (K=768, N_e=2048)).  Weight payloads are packed once, outside the timed region
@@ -39,6 +40,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (the NVFP4-style GEMM's instruction)
 WORKLOADS = {
     "qkv": dict(M=2048, K=4096, N=6144, norm=True, law="outlier",
                 desc="Llama-3.1-8B fused QKV projection: M=2048 tokens, K=4096, N=6144; RMSNorm"),
@@ -55,18 +57,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dual_gemm_qkv.txt")
 GEMM_SRC = os.path.join(ROOT, "fp4_sparse_dense_amd", "csrc", "gemm.hip")
 
 
-def prep_bytes(M, K, norm=True):
-    """Algorithmic HBM bytes of one prep launch: bf16 X in, 0.9375 B/elem out, gamma once."""
-    return M * K * 2 + M * K * 15 // 16 + (2 * K if norm else 0)
+def prep_bytes(M, K, norm=True, nv=False):
+    """Algorithmic HBM bytes of one prep: bf16 X in once, 0.9375 B/elem out
+    (NVFP4-style: 1 B/elem), gamma once."""
+    return M * K * 2 + (M * K if nv else M * K * 15 // 16) + (2 * K if norm else 0)
 
 
 def gemm_flops(M, N, K):
     return 4 * M * N * K
 
 
-def gemm_bytes(M, N, K, out_bytes=4):
-    """Algorithmic HBM bytes of one dual GEMM: prepared A (0.9375 B/elem), the
-    packed weight read once for both paths (0.53125 B/elem), Y."""
+def gemm_bytes(M, N, K, out_bytes=4, nv=False):
+    """Algorithmic HBM bytes of one dual GEMM: prepared A (MXFP4 0.9375 B/elem;
+    NVFP4-style 1 B/elem: scales per 16), the packed weight read once for both
+    paths (MXFP4 0.53125 B/elem; NVFP4-style 0.5625), Y."""
+    if nv:
+        return M * K + N * K * 9 // 16 + out_bytes * M * N
     return M * K * 15 // 16 + N * K * 17 // 32 + out_bytes * M * N
 
 
@@ -188,6 +194,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qkv", choices=sorted(list(WORKLOADS) + ["moe"]))
     ap.add_argument("--m", type=int, default=1, help="rows of the decode workload")
+    ap.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "nvfp4"],
+                    help="FP4 format (nvfp4: the decode workload only)")
     ap.add_argument("--sets", type=int, default=0, help="rotating input/weight/output sets (0: enough for > 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -206,6 +214,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.fmt == "nvfp4" and args.workload != "decode":
+        print("the NVFP4-style path is built for the decode workload (--workload decode)", file=sys.stderr)
+        sys.exit(2)
     if args.workload == "moe":
         rec = run_moe(args)
     else:
@@ -223,11 +234,13 @@ def run_dense(args):
     wl = dict(WORKLOADS[args.workload])
     M = args.m if args.workload == "decode" else wl["M"]
     K, N, norm = wl["K"], wl["N"], wl["norm"]
+    nv = args.fmt == "nvfp4"
+    fmt = sq.FMT_NVFP4 if nv else sq.FMT_MXFP4
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
-    per_set = M * K * 2 + N * K * 17 // 32 + M * K * 15 // 16 + 4 * M * N
+    per_set = M * K * 2 + gemm_bytes(M, N, K, nv=nv)
     nsets = args.sets or max(2, min(64, -(-ROTATE_BYTES // per_set)))
     nx = min(nsets, 4)                       # distinct activation draws (CPU-generated)
     gen = torch.Generator(device="cuda")
@@ -244,8 +257,9 @@ def run_dense(args):
         gammas.append(up(inp["gamma"]) if norm else None)
     sets = []
     for s in range(nsets):
-        w = sq.sharq_pack_weight(device_weight(gen, N, K))
-        sets.append((w, sq.SharqAct(M, K, torch.device("cuda")), torch.empty(M, N, dtype=torch.float32, device="cuda")))
+        w = sq.sharq_pack_weight(device_weight(gen, N, K), fmt=fmt)
+        sets.append((w, sq.SharqAct(M, K, torch.device("cuda"), fmt=fmt),
+                     torch.empty(M, N, dtype=torch.float32, device="cuda")))
     torch.cuda.synchronize()
 
     def step(i, ev=None, stream=None, part=None):
@@ -254,7 +268,7 @@ def run_dense(args):
         if ev is not None:
             ev[0].record(stream)
         if part in (None, 0):
-            sq.sharq_prepare(x, g, 1e-5, out=act)
+            sq.sharq_prepare(x, g, 1e-5, fmt=fmt, out=act)
         if ev is not None:
             ev[1].record(stream)
         if part in (None, 1):
@@ -268,17 +282,18 @@ def run_dense(args):
     prep_ms, gemm_ms = float(np.mean(parts[0])), float(np.mean(parts[1]))
     flops = gemm_flops(M, N, K)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    gbytes = gemm_bytes(M, N, K)
+    gbytes = gemm_bytes(M, N, K, nv=nv)
     gemm_gbs = gbytes / (gemm_ms * 1e-3) / 1e9
-    pbytes = prep_bytes(M, K, norm)
+    pbytes = prep_bytes(M, K, norm, nv=nv)
     prep_gbs = pbytes / (prep_ms * 1e-3) / 1e9
-    hbm_bound = gbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_FP4_TFLOPS * 1e12)
+    peak_mfma = PEAK_BF16_TFLOPS if nv else PEAK_FP4_TFLOPS
+    hbm_bound = gbytes / (PEAK_HBM_GBS * 1e9) > flops / (peak_mfma * 1e12)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": None}
     else:
-        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak_mfma, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / peak_mfma, 4),
                 "traffic": read_traffic() if args.workload == "qkv" else None}
     cpu = None if (args.no_cpu_baseline or args.workload != "qkv") else cpu_baseline()
     wname = args.workload if args.workload != "decode" else f"decode{M}"
@@ -293,15 +308,19 @@ def run_dense(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4",
+        "dtype": "nvfp4" if nv else "mxfp4",
         "data": "synthetic",
-        "config": {"workload": f"{wname}: " + wl["desc"].split(": ", 1)[1].replace("M rows", f"M={M}") +
-                               "; 2:4 mask; MXFP4 activations and weight; fp32 output",
-                   "M": M, "K": K, "N": N, "pattern": "2:4", "format": "MXFP4", "rotating_sets": nsets},
+        "config": {"workload": f"{wname}{'-nvfp4' if nv else ''}: " +
+                               wl["desc"].split(": ", 1)[1].replace("M rows", f"M={M}") +
+                               ("; 2:4 mask; NVFP4-style activations and weight (E4M3 scale per 16, binary32 tensor "
+                                "scales, bf16 MFMA on exactly expanded codes); fp32 output" if nv else
+                                "; 2:4 mask; MXFP4 activations and weight; fp32 output"),
+                   "M": M, "K": K, "N": N, "pattern": "2:4", "format": "NVFP4-style" if nv else "MXFP4",
+                   "rotating_sets": nsets},
         "prep": {"us": round(prep_ms * 1e3, 3), "GB/s": round(prep_gbs, 1),
                  "frac_hbm": round(prep_gbs / PEAK_HBM_GBS, 4), "bytes": pbytes},
         "gemm": {"us": round(gemm_ms * 1e3, 3), "TFLOP/s": round(gemm_tflops, 1),
-                 "frac_mfma": round(gemm_tflops / PEAK_FP4_TFLOPS, 4), "GB/s": round(gemm_gbs, 1),
+                 "frac_mfma": round(gemm_tflops / peak_mfma, 4), "GB/s": round(gemm_gbs, 1),
                  "frac_hbm": round(gemm_gbs / PEAK_HBM_GBS, 4), "bytes": gbytes},
         "roofline": roof,
         "cpu_baseline": cpu,

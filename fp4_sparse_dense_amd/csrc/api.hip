@@ -50,9 +50,10 @@ sharq_status check_device() {
   return SHARQ_OK;
 }
 
-sharq_status check_fmt(int32_t fmt) {
+sharq_status check_fmt(int32_t fmt, bool nv_ok = true) {
   if (fmt == SHARQ_FMT_MXFP4) return SHARQ_OK;
-  if (fmt == SHARQ_FMT_NVFP4) return fail(SHARQ_ERR_UNSUPPORTED, "NVFP4 is not built in this library");
+  if (fmt == SHARQ_FMT_NVFP4)
+    return nv_ok ? SHARQ_OK : fail(SHARQ_ERR_UNSUPPORTED, "the grouped expert layer is built for MXFP4 only");
   if (fmt == SHARQ_FMT_HIF4) return fail(SHARQ_ERR_UNSUPPORTED, "HiF4 is not defined on the SharQ pages");
   return fail(SHARQ_ERR_INVALID_ARG, "unknown format %d", (int)fmt);
 }
@@ -86,7 +87,7 @@ sharq_status sharq_weight_bytes(int64_t N, int64_t K, int32_t fmt, size_t* codes
   if (s) return s;
   const size_t nb = (size_t)((N + 15) / 16), kb = (size_t)((K + 127) / 128);
   *codes_bytes = nb * kb * 1024;
-  *scales_bytes = nb * kb * 64;
+  *scales_bytes = fmt == SHARQ_FMT_NVFP4 ? sharq::nv_weight_layout(N, K).bytes : nb * kb * 64;
   return SHARQ_OK;
 }
 
@@ -104,6 +105,11 @@ sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t
   sizes[2] = tiles * 64;
   sizes[3] = tiles * 1024;
   sizes[4] = tiles * 64;
+  if (fmt == SHARQ_FMT_NVFP4) {
+    const sharq::NvActLayout L = sharq::nv_act_layout(M, K);
+    sizes[2] = M > 0 ? L.s_bytes : 0;
+    sizes[4] = M > 0 ? L.r_bytes : 0;
+  }
   return SHARQ_OK;
 }
 
@@ -124,8 +130,11 @@ sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int
   if (s) return s;
   s = check_device();
   if (s) return s;
-  hipError_t e = sharq::launch_pack_weight(static_cast<const uint16_t*>(w_bf16_dev), N, (int)K, ldw, out->codes,
-                                           out->scales, static_cast<hipStream_t>(stream));
+  const bool nv = fmt == SHARQ_FMT_NVFP4;
+  hipError_t e = nv ? sharq::launch_pack_weight_nv(static_cast<const uint16_t*>(w_bf16_dev), N, (int)K, ldw,
+                                                   out->codes, out->scales, static_cast<hipStream_t>(stream))
+                    : sharq::launch_pack_weight(static_cast<const uint16_t*>(w_bf16_dev), N, (int)K, ldw,
+                                                out->codes, out->scales, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pack_weight launch");
   out->layout_version = SHARQ_ABI_VERSION;
   out->N = N;
@@ -133,8 +142,8 @@ sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int
   out->fmt = fmt;
   for (int p = 0; p < 2; ++p) {
     out->view[p].base = out->scales;
-    out->view[p].ld = (N + 15) / 16 * 64;   // bytes between K tiles of the [KB][NB][64] scale array
-    out->view[p].block = 32;
+    out->view[p].ld = (N + 15) / 16 * (nv ? 128 : 64);   // bytes between K tiles of the tiled scale array
+    out->view[p].block = nv ? 16 : 32;
     out->view[p].reserved = 0;
   }
   return SHARQ_OK;
@@ -166,9 +175,13 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
     s = check_device();
     if (s) return s;
     sharq::PrepOut po{out->s_codes, out->s_meta, out->s_scales, out->r_codes, out->r_scales};
-    hipError_t e = sharq::launch_prepare(static_cast<const uint16_t*>(x_bf16_dev), M, (int)K, ldx,
-                                         static_cast<const uint16_t*>(gamma_bf16_dev), eps, po,
-                                         static_cast<hipStream_t>(stream));
+    hipError_t e = fmt == SHARQ_FMT_NVFP4
+                       ? sharq::launch_prepare_nv(static_cast<const uint16_t*>(x_bf16_dev), M, (int)K, ldx,
+                                                  static_cast<const uint16_t*>(gamma_bf16_dev), eps, po,
+                                                  static_cast<hipStream_t>(stream))
+                       : sharq::launch_prepare(static_cast<const uint16_t*>(x_bf16_dev), M, (int)K, ldx,
+                                               static_cast<const uint16_t*>(gamma_bf16_dev), eps, po,
+                                               static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prepare launch");
   }
   out->layout_version = SHARQ_ABI_VERSION;
@@ -205,12 +218,15 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   if (!aligned(a->s_codes, 16) || !aligned(a->s_meta, 16) || !aligned(a->r_codes, 16) || !aligned(w->codes, 16) ||
       !aligned(a->s_scales, 16) || !aligned(a->r_scales, 16))
     return fail(SHARQ_ERR_INVALID_ARG, "operand buffers must be 16-byte aligned");
+  const bool nv = a->fmt == SHARQ_FMT_NVFP4;
   const sharq_scale_view& vs = w->view[SHARQ_PATH_SPARSE];
   const sharq_scale_view& vd = w->view[SHARQ_PATH_DENSE];
-  const int64_t nb64 = (w->N + 15) / 16 * 64;
-  if (!vs.base || !vd.base || vs.block != 32 || vd.block != 32 || vs.ld != nb64 || vd.ld != nb64 ||
+  const int blk = nv ? 16 : 32;
+  const int64_t nbld = (w->N + 15) / 16 * (nv ? 128 : 64);
+  if (!vs.base || !vd.base || vs.block != blk || vd.block != blk || vs.ld != nbld || vd.ld != nbld ||
       !aligned(vs.base, 16) || !aligned(vd.base, 16))
-    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be tiled MX views (block 32, K-tile stride NB*64)");
+    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be the tiled views of the weight's format (block %d, K-tile stride %lld)",
+                blk, (long long)nbld);
   if (vs.base != vd.base)
     return fail(SHARQ_ERR_UNSUPPORTED, "the two paths must view the same packed scale array (distinct per-path scale arrays are not built)");
   s = check_device();
@@ -237,7 +253,16 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   g.pseg = nullptr;
   g.tprefix = nullptr;
   g.E = 0;
-  hipError_t e = sharq::launch_linear(g, static_cast<hipStream_t>(stream));
+  g.g_s = g.g_r = g.g_w = nullptr;
+  if (nv) {
+    const sharq::NvActLayout la = sharq::nv_act_layout(a->M, a->K);
+    const sharq::NvWeightLayout lw = sharq::nv_weight_layout(w->N, w->K);
+    g.g_s = reinterpret_cast<const float*>(a->s_scales + la.g);
+    g.g_r = reinterpret_cast<const float*>(a->r_scales + la.g);
+    g.g_w = reinterpret_cast<const float*>(vs.base + lw.g);
+  }
+  hipError_t e = nv ? sharq::launch_linear_nv(g, static_cast<hipStream_t>(stream))
+                    : sharq::launch_linear(g, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "linear launch");
   return SHARQ_OK;
 }
@@ -266,7 +291,7 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
   if (out_dtype != SHARQ_OUT_F32 && out_dtype != SHARQ_OUT_BF16) return fail(SHARQ_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
   if (a->n != 2 || a->m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built");
   if (a->fmt != w->fmt) return fail(SHARQ_ERR_INVALID_ARG, "activation and weight formats differ");
-  sharq_status s = check_fmt(a->fmt);
+  sharq_status s = check_fmt(a->fmt, false);
   if (s) return s;
   if (E < 1 || E > 1024) return fail(SHARQ_ERR_INVALID_ARG, "E=%d outside 1..1024", (int)E);
   if (w->N % E || (w->N / E) % 16)
@@ -324,6 +349,7 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
   g.pseg = nullptr;
   g.tprefix = nullptr;
   g.E = E;
+  g.g_s = g.g_r = g.g_w = nullptr;
   ga.row_index = row_index_dev;
   ga.seg_in = seg_offsets_dev;
   ga.rows = rows;

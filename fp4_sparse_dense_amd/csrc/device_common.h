@@ -72,6 +72,18 @@ __device__ __forceinline__ float pow2(int e) {
   return e >= -126 ? __uint_as_float((uint32_t)(127 + e) << 23) : __uint_as_float(0x00400000u);
 }
 
+// ---------------------------------------------------------------- RMSNorm
+// ss -> 1/sqrt(ss/K + eps), each step correctly rounded to binary32.  The
+// quotient and the square root are taken in binary64 and rounded once more to
+// binary32; with 53 >= 2*24+2 bits that second rounding equals direct
+// correct rounding.
+__device__ __forceinline__ float rms_inverse(float ss, int K, float eps) {
+  float mean = (float)((double)ss / (double)K);
+  float a = mean + eps;
+  float root = (float)__dsqrt_rn((double)a);
+  return (float)(1.0 / (double)root);
+}
+
 // ---------------------------------------------------------------- E2M1
 // Two binary32 values -> two E2M1 nibbles placed in byte SEL of `old`.
 // v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to nearest, ties to even,

@@ -42,6 +42,10 @@ struct GemmArgs {
   const int64_t* pseg;             // [E+1] first activation 16-row block of each expert
   const int32_t* tprefix;          // [E+1] M tiles of the experts before each expert
   int E;
+  // NVFP4-style operands: binary32 tensor scales of S, R and W (device)
+  const float* g_s;
+  const float* g_r;
+  const float* g_w;
 };
 
 hipError_t launch_linear(const GemmArgs& a, hipStream_t stream);
@@ -61,5 +65,57 @@ size_t grouped_workspace_bytes(int64_t rows, int E, int K);
 int grouped_tile_m();
 hipError_t launch_linear_grouped_gemm(const GemmArgs& a, int64_t max_mtiles, hipStream_t stream);
 hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// NVFP4-style format (E2M1 codes, E4M3 scale per 16 elements, binary32 scale
+// per tensor).  Codes use the MX tiled layout; block scales are tiled
+// [KB][RB][128]: lane l of tile (rb, kb) owns bytes 2l (its first 16
+// elements) and 2l+1 (the next 16).  Each scale buffer continues, at the
+// first 256-byte boundary after the block scales, with a 256-byte record
+// whose first word is the tensor scale; the residual's and the weight's
+// buffers then hold the scratch of the kernels that compute those scales.
+// ---------------------------------------------------------------------------
+constexpr size_t nv_round256(size_t b) { return (b + 255) / 256 * 256; }
+struct NvActLayout {
+  size_t g;                        // tensor-scale offset (both scale buffers)
+  size_t s_bytes;                  // s_scales buffer size
+  size_t rowamax, inv, rparts;     // r_scales: per-row max |v|, per-row 1/rms, per-workgroup max |r|
+  size_t r_bytes;                  // r_scales buffer size
+  int wx;                          // workgroups along K (4 K tiles each)
+};
+inline NvActLayout nv_act_layout(int64_t M, int64_t K) {
+  const size_t RB = (size_t)((M + 15) / 16), KB = (size_t)((K + 127) / 128);
+  NvActLayout l;
+  l.wx = (int)((KB + 3) / 4);
+  l.g = nv_round256(RB * KB * 128);
+  l.s_bytes = l.g + 256;
+  l.rowamax = l.g + 256;
+  l.inv = l.rowamax + nv_round256(RB * 16 * 4);
+  l.rparts = l.inv + nv_round256(RB * 16 * 4);
+  l.r_bytes = l.rparts + nv_round256(RB * (size_t)l.wx * 4);
+  return l;
+}
+struct NvWeightLayout {
+  size_t g;                        // tensor-scale offset
+  size_t parts;                    // per-workgroup max |w|
+  size_t bytes;
+  int wx;
+};
+inline NvWeightLayout nv_weight_layout(int64_t N, int64_t K) {
+  const size_t NB = (size_t)((N + 15) / 16), KB = (size_t)((K + 127) / 128);
+  NvWeightLayout l;
+  l.wx = (int)((KB + 3) / 4);
+  l.g = nv_round256(NB * KB * 128);
+  l.parts = l.g + 256;
+  l.bytes = l.parts + nv_round256(NB * (size_t)l.wx * 4);
+  return l;
+}
+
+hipError_t launch_prepare_nv(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
+                             float eps, PrepOut out, hipStream_t stream);
+hipError_t launch_pack_weight_nv(const uint16_t* w, int64_t N, int K, int64_t ldw, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream);
+// GemmArgs with the NVFP4-style tiled scales and g_s / g_r / g_w set
+hipError_t launch_linear_nv(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace sharq

@@ -1,0 +1,633 @@
+// SharQ layer in the NVFP4-style format for gfx950: preparation, weight
+// packing and the dual GEMM.
+//
+// SharQ paper page (mlsanity), Abstract: the method is reported under NVFP4 as
+// well as MXFP4 and HiF4.  The pages do not define NVFP4; this file follows
+// the public two-level NVFP4 description: E2M1 elements in 16-element blocks,
+// an OCP E4M3 block scale, and one binary32 scale per tensor
+//   g = amax(tensor) / 2688   (2688 = 6 * 448; g = 1 for an all-zero tensor)
+//   s = E4M3(amax(block) / (6 g)), round to nearest even, saturating at 448
+//   code = E2M1(u / (s g))  (the signed zero code when s = 0)
+// with every step one binary32 operation, rounded once (built with
+// -ffp-contract=off and IEEE division).  Backbone S, residual R and weight W
+// each have their own tensor scale; R's depends on Q(S), so the preparation
+// runs as three launches: per-row statistics, the backbone (and max |R|), the
+// residual.
+//
+// gfx950's block-scaled MFMA takes E8M0 scales per 32 elements, which cannot
+// carry an E4M3 scale per 16.  The GEMM therefore expands each code to
+// val(code) * s -- at most 6 significant bits, so exact in bf16 -- and runs the
+// bf16 MFMA with one fp32 accumulator per path; the tensor scales enter once,
+// in the epilogue: y = g_S g_W acc_S + g_R g_W acc_R.
+#include "device_common.h"
+#include "launch.h"
+
+namespace sharq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+constexpr float kNvTensorDiv = 2688.0f;
+constexpr int kNvWaves = 4;          // one K tile per wave, 4 per workgroup
+
+__device__ __forceinline__ float tensor_scale(float amax) { return amax > 0.0f ? amax / kNvTensorDiv : 1.0f; }
+
+// E4M3 (OCP: bias 7, 3 mantissa bits, subnormal step 2^-9, largest 448) of a
+// binary32 x >= 0, round to nearest even, saturating; returns the value and
+// sets the byte.  Normal range: round the binary32 significand to 3 bits (add
+// half an ulp of the target minus one plus the kept LSB, then truncate).
+// Below 2^-6: the subnormal grid, rint(x * 2^9) * 2^-9 (v_rndne: half to even).
+__device__ __forceinline__ float e4m3_round(float x, uint32_t& byte) {
+  if (x >= 448.0f) {
+    byte = 0x7Eu;
+    return 448.0f;
+  }
+  if (x >= 0x1p-6f) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFFu + ((u >> 20) & 1u);
+    u &= 0xFFF00000u;
+    byte = ((((u >> 23) & 0xFFu) - 120u) << 3) | ((u >> 20) & 7u);
+    return __uint_as_float(u);
+  }
+  const float n = __builtin_rintf(x * 512.0f);
+  byte = (uint32_t)n;                  // 0..8; 8 is 2^-6, byte 0x08
+  return n * 0x1p-9f;
+}
+
+// E4M3 byte (sign clear) -> binary32
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// max over the workgroup of non-negative v (all threads must call)
+template <int NWAVES>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < NWAVES; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+// 32 bf16 of one row -> binary32
+__device__ __forceinline__ void load32(const uint16_t* p, float (&v)[32]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 d = *reinterpret_cast<const uint4*>(p + 8 * q);
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[8 * q + 2 * h] = bf16_lo(w[h]);
+      v[8 * q + 2 * h + 1] = bf16_hi(w[h]);
+    }
+  }
+}
+
+// v = (x * inv) * gamma, elementwise, two roundings
+__device__ __forceinline__ void apply_norm(float (&v)[32], const uint16_t* gamma, float inv) {
+  float g[32];
+  load32(gamma, g);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = (v[i] * inv) * g[i];
+}
+
+// Pairwise tree of squares over 32 consecutive elements: leaves x0^2 + x1^2
+// (squares of bf16 values are exact), then halving in index order.
+__device__ __forceinline__ float chunk_sumsq(const float (&v)[32]) {
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = v[2 * i] * v[2 * i] + v[2 * i + 1] * v[2 * i + 1];
+#pragma unroll
+  for (int n = 8; n >= 1; n >>= 1)
+#pragma unroll
+    for (int i = 0; i < n; ++i) p[i] = p[2 * i] + p[2 * i + 1];
+  return p[0];
+}
+
+// E2M1 nibble of binary32 q (round to nearest even, saturating at 6, sign of
+// zero kept): the convert instruction with unit scale.
+__device__ __forceinline__ uint32_t e2m1_pair(float lo, float hi) { return fp4_pack2<0>(0u, lo, hi) & 0xFFu; }
+
+struct NvPrepArgs {
+  const uint16_t* x;
+  int64_t M, ldx;
+  int K;
+  const uint16_t* gamma;
+  float eps;
+  int64_t RB;
+  int KB, WX;
+  PrepOut o;
+  float* g_s;       // tensor scale of S (s_scales record)
+  float* g_r;       // tensor scale of R (r_scales record)
+  float* rowamax;   // [RB*16] max |v| of each row
+  float* inv;       // [RB*16] 1/rms of each row
+  float* rparts;    // [RB*WX] max |r| of each workgroup
+};
+
+// ---------------------------------------------------------------------------
+// Phase 1: one workgroup per row.  With RMSNorm, the sum of squares follows
+// the pairwise tree over the row zero-padded to a power of two: aligned
+// 32-element chunks are subtrees, and the chunk sums are combined pairwise in
+// LDS.  Writes 1/rms (when normalising) and max |v| of the row.
+// ---------------------------------------------------------------------------
+template <bool NORM>
+__global__ __launch_bounds__(256) void nv_rowstats_kernel(NvPrepArgs a) {
+  __shared__ float cs[1024];
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = a.x + row * a.ldx;
+  const int KC = a.K / 32;
+  float inv = 1.0f;
+  if (NORM) {
+    int P = 1;
+    while (P < KC) P *= 2;
+    for (int c = t; c < P; c += 256) {
+      float s = 0.0f;
+      if (c < KC) {
+        float v[32];
+        load32(xr + 32 * c, v);
+        s = chunk_sumsq(v);
+      }
+      cs[c] = s;
+    }
+    __syncthreads();
+    for (int n = P; n > 1; n >>= 1) {
+      const int h = n >> 1;
+      const float s0 = t < h ? cs[2 * t] + cs[2 * t + 1] : 0.0f;
+      const float s1 = t + 256 < h ? cs[2 * (t + 256)] + cs[2 * (t + 256) + 1] : 0.0f;
+      __syncthreads();
+      if (t < h) cs[t] = s0;
+      if (t + 256 < h) cs[t + 256] = s1;
+      __syncthreads();
+    }
+    inv = rms_inverse(cs[0], a.K, a.eps);
+  }
+  float am = 0.0f;
+  for (int c = t; c < KC; c += 256) {
+    float v[32];
+    load32(xr + 32 * c, v);
+    if (NORM) apply_norm(v, a.gamma + 32 * c, inv);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+  }
+  am = block_max<4>(am, red);
+  if (t == 0) {
+    a.rowamax[row] = am;
+    if (NORM) a.inv[row] = inv;
+  }
+}
+
+// 2:4 mask of one group: element i is kept iff at most one other element beats
+// it (larger magnitude, or equal magnitude and lower index).  Returns the
+// metadata nibble i0 | i1 << 2 and the kept offsets.
+__device__ __forceinline__ uint32_t keep24(const float* a, int& i0, int& i1) {
+  const float m0 = fabsf(a[0]), m1 = fabsf(a[1]), m2 = fabsf(a[2]), m3 = fabsf(a[3]);
+  const int b01 = m0 >= m1, b02 = m0 >= m2, b03 = m0 >= m3, b12 = m1 >= m2, b13 = m1 >= m3, b23 = m2 >= m3;
+  const bool k0 = (3 - b01 - b02 - b03) <= 1;
+  const bool k1 = (b01 + 2 - b12 - b13) <= 1;
+  const bool k2 = (b02 + b12 + 1 - b23) <= 1;
+  const bool k3 = (b03 + b13 + b23) <= 1;
+  i0 = k0 ? 0 : (k1 ? 1 : 2);
+  i1 = k3 ? 3 : (k2 ? 2 : 1);
+  return (uint32_t)i0 | ((uint32_t)i1 << 2);
+}
+
+// ---------------------------------------------------------------------------
+// Phases 2 and 3: one wave per 16-row x 128-K tile, 4 tiles of one row block
+// per workgroup; lane l owns row 16 rb + l%16 and K [128 kb + 32 (l/16), +32),
+// the lane order of the tiled layout.  Both phases rebuild v, the mask, Q(S)
+// and the residual; phase 2 stores the backbone and each workgroup's max |r|,
+// phase 3 quantises R with the tensor scale those maxima give.
+// ---------------------------------------------------------------------------
+template <bool NORM, bool RESID>
+__global__ __launch_bounds__(256) void nv_decompose_kernel(NvPrepArgs a) {
+  __shared__ float red[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t rb = blockIdx.y;
+  const int kb = blockIdx.x * kNvWaves + wave;
+
+  // tensor scales from the previous phases' maxima (max |S| = max |v|: the
+  // mask keeps each group's largest magnitude)
+  float am = 0.0f;
+  for (int64_t i = t; i < a.M; i += 256) am = fmaxf(am, a.rowamax[i]);
+  const float g_s = tensor_scale(block_max<4>(am, red));
+  float g_r = 1.0f;
+  if (RESID) {
+    float ar = 0.0f;
+    for (int64_t i = t; i < a.RB * a.WX; i += 256) ar = fmaxf(ar, a.rparts[i]);
+    g_r = tensor_scale(block_max<4>(ar, red));
+  }
+
+  const int64_t row = rb * 16 + (lane & 15);
+  const int k0 = kb * 128 + 32 * (lane >> 4);
+  const bool valid = kb < a.KB && row < a.M && k0 < a.K;
+  float v[32];
+  if (valid) {
+    load32(a.x + row * a.ldx + k0, v);
+    if (NORM) apply_norm(v, a.gamma + k0, a.inv[row]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+
+  // backbone: mask, per-16 block scale, kept codes; residual in place
+  const float six_g = 6.0f * g_s;
+  uint32_t scodes[2] = {0u, 0u}, meta = 0u, sbytes = 0u;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float bm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[16 * b + i]));
+    uint32_t byte;
+    const float s = e4m3_round(bm / six_g, byte);
+    sbytes |= byte << (8 * b);
+    const float tq = s * g_s;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int G = 4 * b + gq;
+      int i0, i1;
+      meta |= keep24(&v[4 * G], i0, i1) << (4 * G);
+      const float x0 = v[4 * G + i0], x1 = v[4 * G + i1];
+      const float q0 = s > 0.0f ? x0 / tq : x0 * 0.0f;
+      const float q1 = s > 0.0f ? x1 / tq : x1 * 0.0f;
+      const uint32_t c = e2m1_pair(q0, q1);
+      scodes[b] |= c << (8 * gq);
+      float d0, d1;
+      fp4_unpack2<0>(c, d0, d1);
+      d0 = (d0 * s) * g_s;
+      d1 = (d1 * s) * g_s;
+      v[4 * G + i0] = x0 - d0;
+      v[4 * G + i1] = x1 - d1;
+    }
+  }
+  const int64_t tile = rb * a.KB + kb;
+  const int64_t sc = ((int64_t)kb * a.RB + rb) * 128 + 2 * lane;
+
+  if (!RESID) {
+    if (kb < a.KB) {
+      *reinterpret_cast<uint2*>(a.o.s_codes + tile * 512 + lane * 8) = make_uint2(scodes[0], scodes[1]);
+      *reinterpret_cast<uint32_t*>(a.o.s_meta + tile * 256 + lane * 4) = meta;
+      *reinterpret_cast<uint16_t*>(a.o.s_scales + sc) = (uint16_t)sbytes;
+    }
+    float ar = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ar = fmaxf(ar, fabsf(v[i]));
+    ar = block_max<4>(ar, red);
+    if (t == 0) a.rparts[rb * a.WX + blockIdx.x] = ar;
+    if (t == 0 && blockIdx.x == 0 && blockIdx.y == 0) *a.g_s = g_s;
+  } else {
+    const float six_r = 6.0f * g_r;
+    uint32_t rc[4] = {0u, 0u, 0u, 0u}, rbytes = 0u;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float bm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[16 * b + i]));
+      uint32_t byte;
+      const float s = e4m3_round(bm / six_r, byte);
+      rbytes |= byte << (8 * b);
+      const float tq = s * g_r;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float x0 = v[16 * b + i], x1 = v[16 * b + i + 1];
+        const float q0 = s > 0.0f ? x0 / tq : x0 * 0.0f;
+        const float q1 = s > 0.0f ? x1 / tq : x1 * 0.0f;
+        const int e = 16 * b + i;                 // element index; 8 per dword
+        rc[e / 8] |= e2m1_pair(q0, q1) << (4 * (e % 8));
+      }
+    }
+    if (kb < a.KB) {
+      *reinterpret_cast<uint4*>(a.o.r_codes + tile * 1024 + lane * 16) = make_uint4(rc[0], rc[1], rc[2], rc[3]);
+      *reinterpret_cast<uint16_t*>(a.o.r_scales + sc) = (uint16_t)rbytes;
+    }
+    if (t == 0 && blockIdx.x == 0 && blockIdx.y == 0) *a.g_r = g_r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing: max |w| per workgroup, the tensor scale, then the codes.
+// Same tile / lane mapping as the preparation (16 weight rows per tile).
+// ---------------------------------------------------------------------------
+struct NvWeightArgs {
+  const uint16_t* w;
+  int64_t N, ldw;
+  int K;
+  int64_t NB;
+  int KB, WX;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* g;
+  float* parts;
+};
+
+__global__ __launch_bounds__(256) void nv_weight_amax_kernel(NvWeightArgs a) {
+  __shared__ float red[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t nb = blockIdx.y;
+  const int kb = blockIdx.x * kNvWaves + wave;
+  const int64_t row = nb * 16 + (lane & 15);
+  const int k0 = kb * 128 + 32 * (lane >> 4);
+  float am = 0.0f;
+  if (kb < a.KB && row < a.N && k0 < a.K) {
+    float v[32];
+    load32(a.w + row * a.ldw + k0, v);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+  }
+  am = block_max<4>(am, red);
+  if (t == 0) a.parts[nb * a.WX + blockIdx.x] = am;
+}
+
+__global__ __launch_bounds__(256) void nv_weight_scale_kernel(NvWeightArgs a) {
+  __shared__ float red[4];
+  float am = 0.0f;
+  for (int64_t i = threadIdx.x; i < a.NB * a.WX; i += 256) am = fmaxf(am, a.parts[i]);
+  am = block_max<4>(am, red);
+  if (threadIdx.x == 0) *a.g = tensor_scale(am);
+}
+
+__global__ __launch_bounds__(256) void nv_pack_weight_kernel(NvWeightArgs a) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t nb = blockIdx.y;
+  const int kb = blockIdx.x * kNvWaves + wave;
+  if (kb >= a.KB) return;
+  const int64_t row = nb * 16 + (lane & 15);
+  const int k0 = kb * 128 + 32 * (lane >> 4);
+  float v[32];
+  if (row < a.N && k0 < a.K) {
+    load32(a.w + row * a.ldw + k0, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+  const float g = *a.g, six_g = 6.0f * g;
+  uint32_t c[4] = {0u, 0u, 0u, 0u}, bytes = 0u;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float bm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[16 * b + i]));
+    uint32_t byte;
+    const float s = e4m3_round(bm / six_g, byte);
+    bytes |= byte << (8 * b);
+    const float tq = s * g;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float x0 = v[16 * b + i], x1 = v[16 * b + i + 1];
+      const float q0 = s > 0.0f ? x0 / tq : x0 * 0.0f;
+      const float q1 = s > 0.0f ? x1 / tq : x1 * 0.0f;
+      const int e = 16 * b + i;
+      c[e / 8] |= e2m1_pair(q0, q1) << (4 * (e % 8));
+    }
+  }
+  const int64_t tile = nb * a.KB + kb;
+  *reinterpret_cast<uint4*>(a.codes + tile * 1024 + lane * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+  *reinterpret_cast<uint16_t*>(a.scales + ((int64_t)kb * a.NB + nb) * 128 + 2 * lane) = (uint16_t)bytes;
+}
+
+// ---------------------------------------------------------------------------
+// Dual GEMM (small M: decode).  As the MXFP4 small-M kernel: one workgroup per
+// 16 weight rows (and per group of RBG 16-row activation blocks), NW waves
+// split K, operands read straight from the tiled layout.  Each lane's 32 codes
+// of a K tile are expanded to val * s in bf16 (exact) and feed four
+// 16x16x32 bf16 MFMAs; MFMA j takes elements [8j, 8j+8) of every lane for
+// both operands, so A and B see the same K order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  // upper halves: exact, the low 16 bits of val * s are zero
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+template <int SEL>
+__device__ __forceinline__ uint32_t deq_pair(uint32_t codes, float s) {
+  float lo, hi;
+  fp4_unpack2<SEL>(codes, lo, hi);
+  return bf16_pair(lo * s, hi * s);
+}
+
+__device__ __forceinline__ bf16x8 deq8(uint32_t codes, float s) {
+  u32x4v r;
+  r[0] = deq_pair<0>(codes, s);
+  r[1] = deq_pair<1>(codes, s);
+  r[2] = deq_pair<2>(codes, s);
+  r[3] = deq_pair<3>(codes, s);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 32 codes (uint4) + two E4M3 bytes -> four MFMA operands
+__device__ __forceinline__ void deq32(uint4 q, uint32_t sb, bf16x8 (&o)[4]) {
+  const float s0 = e4m3_value(sb & 0xFFu), s1 = e4m3_value((sb >> 8) & 0xFFu);
+  o[0] = deq8(q.x, s0);
+  o[1] = deq8(q.y, s0);
+  o[2] = deq8(q.z, s1);
+  o[3] = deq8(q.w, s1);
+}
+
+// 2:4 expansion of one lane's compressed operand (16 kept codes + 8 offset
+// nibbles) into 32 dense codes.
+__device__ __forceinline__ uint32_t expand_dword_nv(uint32_t codes2, uint32_t meta2) {
+  // codes2: bytes g0, g1 of two groups (low nibble = lower kept offset); meta2: their nibbles
+  uint32_t out = 0u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t c = (codes2 >> (8 * h)) & 0xFFu;
+    const uint32_t m = (meta2 >> (4 * h)) & 0xFu;
+    const uint32_t i0 = m & 3u, i1 = m >> 2;
+    out |= ((c & 0xFu) << (4 * i0 + 16 * h)) | ((c >> 4) << (4 * i1 + 16 * h));
+  }
+  return out;
+}
+
+__device__ __forceinline__ uint4 expand24(uint2 codes, uint32_t meta) {
+  uint4 d;
+  d.x = expand_dword_nv(codes.x & 0xFFFFu, meta & 0xFFu);
+  d.y = expand_dword_nv(codes.x >> 16, (meta >> 8) & 0xFFu);
+  d.z = expand_dword_nv(codes.y & 0xFFFFu, (meta >> 16) & 0xFFu);
+  d.w = expand_dword_nv(codes.y >> 16, meta >> 24);
+  return d;
+}
+
+__device__ __forceinline__ v4f mfma_bf16(bf16x8 a, bf16x8 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void store_y(const GemmArgs& g, int64_t row, int64_t col, float v) {
+  if (g.out_bf16) {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    reinterpret_cast<uint16_t*>(g.y)[row * g.ldy + col] = (uint16_t)(u >> 16);
+  } else {
+    reinterpret_cast<float*>(g.y)[row * g.ldy + col] = v;
+  }
+}
+
+template <int RBG, int NW>
+__global__ __launch_bounds__(64 * NW) void nv_dual_gemm_kernel(GemmArgs g) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1);
+  const int64_t RB = g.a_blocks, NB = (g.N + 15) / 16;
+  const int KT = (g.K + 127) / 128;
+  const int64_t nb = blockIdx.x;
+  const int64_t rb0 = (int64_t)blockIdx.y * RBG;
+
+  v4f acs[RBG], acr[RBG];
+#pragma unroll
+  for (int r = 0; r < RBG; ++r) acs[r] = acr[r] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  constexpr int CH = (RBG == 1 ? 8 : (RBG == 2 ? 4 : 2)) * 4 / NW;
+  for (int base = 0; base < KT; base += NW * CH) {
+    uint4 wq[CH], rq[CH][RBG];
+    uint2 sq[CH][RBG];
+    uint32_t wsb[CH], mq[CH][RBG], ssb[CH][RBG], rsb[CH][RBG];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // clamped tile index; a tile past K gets a zero weight fragment
+      const int kt = base + wave + NW * c;
+      const int ktc = kt < KT ? kt : KT - 1;
+      wq[c] = *reinterpret_cast<const uint4*>(g.w_codes + (nb * KT + ktc) * 1024 + lane * 16);
+      wsb[c] = *reinterpret_cast<const uint16_t*>(g.w_scales_dense + ((int64_t)ktc * NB + nb) * 128 + 2 * lane);
+      if (kt >= KT) { wq[c] = make_uint4(0, 0, 0, 0); wsb[c] = 0u; }
+#pragma unroll
+      for (int r = 0; r < RBG; ++r) {
+        const int64_t rb = rb0 + r < RB ? rb0 + r : RB - 1;
+        const int64_t tile = rb * KT + ktc;
+        const int64_t sc = ((int64_t)ktc * RB + rb) * 128 + 2 * lane;
+        rq[c][r] = *reinterpret_cast<const uint4*>(g.r_codes + tile * 1024 + lane * 16);
+        sq[c][r] = *reinterpret_cast<const uint2*>(g.s_codes + tile * 512 + lane * 8);
+        mq[c][r] = *reinterpret_cast<const uint32_t*>(g.s_meta + tile * 256 + lane * 4);
+        ssb[c][r] = *reinterpret_cast<const uint16_t*>(g.s_scales + sc);
+        rsb[c][r] = *reinterpret_cast<const uint16_t*>(g.r_scales + sc);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      bf16x8 b[4];
+      deq32(wq[c], wsb[c], b);
+#pragma unroll
+      for (int r = 0; r < RBG; ++r) {
+        bf16x8 x[4];
+        deq32(expand24(sq[c][r], mq[c][r]), ssb[c][r], x);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acs[r] = mfma_bf16(x[j], b[j], acs[r]);
+        deq32(rq[c][r], rsb[c][r], x);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acr[r] = mfma_bf16(x[j], b[j], acr[r]);
+      }
+    }
+  }
+
+  // tensor scales once per path, then the waves' partial sums in wave order
+  const float gw = *g.g_w;
+  const float fs = *g.g_s * gw, fr = *g.g_r * gw;
+  __shared__ v4f part[NW][RBG][64];
+#pragma unroll
+  for (int r = 0; r < RBG; ++r) {
+    v4f p;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = fs * acs[r][q] + fr * acr[r][q];
+    part[wave][r][lane] = p;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t col = nb * 16 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < RBG; ++r) {
+      v4f v = part[0][r][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v = v + part[w][r][lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = (rb0 + r) * 16 + 4 * (lane >> 4) + q;
+        if (row < g.M && col < g.N) store_y(g, row, col, v[q]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prepare_nv(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma, float eps,
+                             PrepOut out, hipStream_t stream) {
+  const NvActLayout L = nv_act_layout(M, K);
+  NvPrepArgs a;
+  a.x = x;
+  a.M = M;
+  a.ldx = ldx;
+  a.K = K;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.RB = (M + 15) / 16;
+  a.KB = (K + 127) / 128;
+  a.WX = L.wx;
+  a.o = out;
+  a.g_s = reinterpret_cast<float*>(out.s_scales + L.g);
+  a.g_r = reinterpret_cast<float*>(out.r_scales + L.g);
+  a.rowamax = reinterpret_cast<float*>(out.r_scales + L.rowamax);
+  a.inv = reinterpret_cast<float*>(out.r_scales + L.inv);
+  a.rparts = reinterpret_cast<float*>(out.r_scales + L.rparts);
+  if (M > 0x7FFFFFFF || a.RB > 65535) return hipErrorInvalidValue;
+  const dim3 rows((unsigned)M), tiles((unsigned)a.WX, (unsigned)a.RB), blk(256);
+  if (gamma) {
+    hipLaunchKernelGGL((nv_rowstats_kernel<true>), rows, blk, 0, stream, a);
+    hipLaunchKernelGGL((nv_decompose_kernel<true, false>), tiles, blk, 0, stream, a);
+    hipLaunchKernelGGL((nv_decompose_kernel<true, true>), tiles, blk, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((nv_rowstats_kernel<false>), rows, blk, 0, stream, a);
+    hipLaunchKernelGGL((nv_decompose_kernel<false, false>), tiles, blk, 0, stream, a);
+    hipLaunchKernelGGL((nv_decompose_kernel<false, true>), tiles, blk, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weight_nv(const uint16_t* w, int64_t N, int K, int64_t ldw, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream) {
+  const NvWeightLayout L = nv_weight_layout(N, K);
+  NvWeightArgs a;
+  a.w = w;
+  a.N = N;
+  a.ldw = ldw;
+  a.K = K;
+  a.NB = (N + 15) / 16;
+  a.KB = (K + 127) / 128;
+  a.WX = L.wx;
+  a.codes = codes;
+  a.scales = scales;
+  a.g = reinterpret_cast<float*>(scales + L.g);
+  a.parts = reinterpret_cast<float*>(scales + L.parts);
+  if (a.NB > 65535) return hipErrorInvalidValue;
+  const dim3 tiles((unsigned)a.WX, (unsigned)a.NB), blk(256);
+  hipLaunchKernelGGL(nv_weight_amax_kernel, tiles, blk, 0, stream, a);
+  hipLaunchKernelGGL(nv_weight_scale_kernel, dim3(1), blk, 0, stream, a);
+  hipLaunchKernelGGL(nv_pack_weight_kernel, tiles, blk, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_nv(const GemmArgs& a, hipStream_t stream) {
+  const int64_t NB = (a.N + 15) / 16, RB = a.a_blocks;
+  if (NB > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (RB == 1) {
+    hipLaunchKernelGGL((nv_dual_gemm_kernel<1, 8>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
+  } else if (RB == 2) {
+    hipLaunchKernelGGL((nv_dual_gemm_kernel<2, 8>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
+  } else {
+    const int64_t groups = (RB + 3) / 4;
+    if (groups > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((nv_dual_gemm_kernel<4, 4>), dim3((unsigned)NB, (unsigned)groups), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sharq

@@ -23,16 +23,6 @@ namespace sharq {
 constexpr int kSlot = 512;
 constexpr int kRowsPerBlock = 4;
 
-// ss -> 1/sqrt(ss/K + eps), each step correctly rounded to binary32.  The
-// quotient and the square root are taken in binary64 and rounded once more to
-// binary32; with 53 >= 2*24+2 bits that second rounding equals direct
-// correct rounding.
-__device__ __forceinline__ float rms_inverse(float ss, int K, float eps) {
-  float mean = (float)((double)ss / (double)K);
-  float a = mean + eps;
-  float root = (float)__dsqrt_rn((double)a);
-  return (float)(1.0 / (double)root);
-}
 
 
 // ---------------------------------------------------------------------------

@@ -60,9 +60,27 @@ typedef enum {
 } sharq_status;
 
 /* FP4 formats named by the SharQ abstract (it reports results in NVFP4, HiF4
- * and MXFP4).  MXFP4 = OCP Microscaling v1.0: 32-element blocks, E8M0 scale.
- * NVFP4 and HiF4 are declared for the format slot; this build returns
- * SHARQ_ERR_UNSUPPORTED for them (HiF4 is not defined on the pages). */
+ * and MXFP4).
+ *  MXFP4 = OCP Microscaling v1.0: 32-element blocks, E8M0 scale.
+ *  NVFP4 (the pages name it without a definition; this follows the public
+ *  two-level NVFP4 description): E2M1 codes in 16-element blocks with an OCP
+ *  E4M3 block scale (bias 7, subnormals, largest 448) and one binary32 scale
+ *  per tensor.  For a tensor T (S, R or W, each separately) with largest
+ *  magnitude A: g = A / 2688 (2688 = 6 * 448; g = 1 when A == 0); per block
+ *  s = E4M3(amax_b / (6 g)) rounded to nearest even and saturated at 448;
+ *  code = E2M1(u / (s g)), or the signed zero code when s == 0; value =
+ *  val(code) * s * g.  Every step is one binary32 operation.  Tensors whose
+ *  largest magnitude is nonzero but below 2^-126 are outside the supported
+ *  range (their codes are unspecified).
+ *  NVFP4 buffers: codes in the MX tiled layout; block scales tiled
+ *  [KB][RB][128], lane l of a tile owning byte 2l (its first 16 elements) and
+ *  2l+1 (the next 16); each scale buffer continues at the first 256-byte
+ *  boundary after the block scales (offset round_up(KB*RB*128, 256)) with the
+ *  binary32 tensor scale.  The residual's and the weight's scale buffers then
+ *  hold scratch of the kernels that compute the scale (sizes from the
+ *  *_bytes queries).
+ *  HiF4 is not defined on the pages: every entry point returns
+ *  SHARQ_ERR_UNSUPPORTED for it. */
 typedef enum { SHARQ_FMT_MXFP4 = 0, SHARQ_FMT_NVFP4 = 1, SHARQ_FMT_HIF4 = 2 } sharq_format;
 
 typedef enum { SHARQ_OUT_F32 = 0, SHARQ_OUT_BF16 = 1 } sharq_out_dtype;
@@ -72,8 +90,9 @@ typedef enum { SHARQ_OUT_F32 = 0, SHARQ_OUT_BF16 = 1 } sharq_out_dtype;
 typedef enum { SHARQ_PATH_SPARSE = 0, SHARQ_PATH_DENSE = 1 } sharq_path;
 
 /* A scale view: how one GEMM path reads the weight's block scales.
- * base: device pointer to E8M0 bytes (tiled, [KB][NB][64]); ld: bytes between
- * K steps (NB*64); block: K elements per scale byte.  On gfx950 both paths run the same block-scaled
+ * base: device pointer to the tiled scale bytes (MXFP4: E8M0 [KB][NB][64];
+ * NVFP4: E4M3 [KB][NB][128] followed by the tensor scale); ld: bytes between
+ * K steps (NB*64 or NB*128); block: K elements per scale byte (32 or 16).  On gfx950 both paths run the same block-scaled
  * MFMA on dense 4-bit operands (the sparse operand is expanded on chip), so
  * sharq_pack_weight sets both views to the same array and layout. */
 typedef struct {
@@ -128,29 +147,33 @@ const char* sharq_status_str(sharq_status s);
 const char* sharq_last_error(void);
 
 /* Byte sizes of the packed weight buffers for W[N,K] in `fmt` (tiled:
- * codes NB*KB*1024, scales KB*NB*64).
- * Errors: INVALID_ARG for N<=0, K<=0, K%32, null outputs; UNSUPPORTED for NVFP4/HiF4. */
+ * codes NB*KB*1024; scales KB*NB*64 for MXFP4, for NVFP4 the E4M3 scales,
+ * the tensor scale and scratch).
+ * Errors: INVALID_ARG for N<=0, K<=0, K%32, null outputs; UNSUPPORTED for HiF4. */
 sharq_status sharq_weight_bytes(int64_t N, int64_t K, int32_t fmt,
                                 size_t* codes_bytes, size_t* scales_bytes);
 
 /* Byte sizes of the five prepared-activation buffers, in the order
- * s_codes, s_meta, s_scales, r_codes, r_scales (tiled: RB*KB*{512, 256, 64,
- * 1024, 64}).  M == 0 gives zeros.
+ * s_codes, s_meta, s_scales, r_codes, r_scales (MXFP4 tiled: RB*KB*{512, 256,
+ * 64, 1024, 64}; NVFP4: the scale buffers hold E4M3 scales, the tensor scale
+ * and, for r_scales, the preparation's scratch).  M == 0 gives zeros.
  * Errors: INVALID_ARG for M<0, K<=0, K%32, null output; UNSUPPORTED unless
- * (n,m) == (2,4) and fmt == MXFP4. */
+ * (n,m) == (2,4) and fmt is MXFP4 or NVFP4. */
 sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t fmt,
                              size_t sizes[5]);
 
 /* Pack W[N,K] (bf16, row stride ldw elements) into the single FP4 weight
- * payload: per row n and 32-block b, E = floor(log2 amax)-2 (E8M0, clamped)
- * and E2M1 codes of w/2^E (round to nearest, ties to even, saturating at 6),
- * written in the tiled layout with zero padding.
+ * payload: MXFP4: per row n and 32-block b, E = floor(log2 amax)-2 (E8M0,
+ * clamped) and E2M1 codes of w/2^E (round to nearest, ties to even,
+ * saturating at 6); NVFP4: the tensor scale of all of W, then per row and
+ * 16-block the E4M3 scale and codes (format rules above); written in the
+ * tiled layout with zero padding.
  * SharQ abstract: both GEMM paths read this one payload.
  * `out` must have struct_size set and codes/scales pointing at buffers of the
  * sizes given by sharq_weight_bytes; N, K, fmt and both views are filled in.
  * Errors: INVALID_ARG (null, N<=0, K<=0, K%32, ldw<K, w not 16-B aligned or
- * ldw%8, a buffer not 16-B aligned), UNSUPPORTED (fmt != MXFP4, device not
- * gfx950), HIP. */
+ * ldw%8, a buffer not 16-B aligned), UNSUPPORTED (HiF4, device not gfx950),
+ * HIP. */
 sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int64_t ldw,
                                int32_t fmt, sharq_weight* out, void* stream);
 
@@ -163,6 +186,10 @@ sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int
  *   S = v on kept entries, 0 elsewhere; Q(S) = MXFP4 over 32 logical positions;
  *   R = v - deq(Q(S)) (exact in binary32); Q(R) = MXFP4;
  *   all five outputs in the tiled layout, padding rows and K written as zeros.
+ * With fmt == NVFP4 the quantiser is the NVFP4 one (blocks of 16 logical
+ * positions; S's tensor scale from max|S|, R's from max|R|, so R's depends
+ * on Q(S)); deq(Q(S)) = (val * s) * g in binary32.  This runs as three
+ * dependent launches on `stream` (row statistics, backbone, residual).
  * SharQ abstract: one fused operator absorbs mask generation, residual
  * construction and the normalisation; the residual is relative to the
  * quantised backbone.
@@ -170,7 +197,7 @@ sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int
  * sharq_act_bytes; M, K, n, m, fmt are filled in.  M == 0 launches nothing.
  * Errors: INVALID_ARG (null, K<=0, K%32, K>32768 with gamma, ldx<K, x not
  * 16-B aligned or ldx%8, gamma misaligned), UNSUPPORTED ((n,m) != (2,4),
- * fmt != MXFP4, not gfx950), HIP. */
+ * HiF4, not gfx950), HIP. */
 sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx,
                            const void* gamma_bf16_dev, float eps,
                            int32_t n, int32_t m, int32_t fmt,
@@ -182,9 +209,15 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
  * On gfx950 the compressed 2:4 operand is expanded to dense 4-bit codes on
  * chip and both paths run block-scaled MXFP4 MFMA into one fp32 accumulator,
  * reading each weight tile once for both paths.
+ * NVFP4: the E4M3 scales cannot ride the MX MFMA, so each code is expanded
+ * on chip to val * s (exact in bf16), the bf16 MFMA accumulates each path in
+ * fp32, and the epilogue applies the tensor scales:
+ * y = g_S g_W acc_S + g_R g_W acc_R.  It is built for small M (decode); a
+ * larger M reads the weight once per 64 rows.
  * y: device, fp32 or bf16 per out_dtype, row stride ldy elements (>= N).
- * Errors: INVALID_ARG (null, K mismatch, ldy<N, misaligned y),
- * UNSUPPORTED (fmt, pattern, not gfx950), HIP. */
+ * Errors: INVALID_ARG (null, K mismatch, formats differ, scale views not those
+ * of the format, ldy<N, misaligned y), UNSUPPORTED (HiF4, pattern, not
+ * gfx950), HIP. */
 sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w,
                           void* y_dev, int64_t ldy, int32_t out_dtype, void* stream);
 
@@ -214,7 +247,8 @@ sharq_status sharq_grouped_workspace_bytes(int64_t rows, int32_t E, int64_t K, s
  *   ws:         device workspace of ws_bytes >= sharq_grouped_workspace_bytes,
  *               owned by the caller; calls that share it must not overlap.
  * Errors: INVALID_ARG (null, shapes, K mismatch, ldy < N_e, workspace too
- * small, misaligned buffers), UNSUPPORTED (fmt, pattern, not gfx950), HIP. */
+ * small, misaligned buffers), UNSUPPORTED (any format but MXFP4, pattern, not
+ * gfx950), HIP. */
 sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
                                   const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
                                   void* y_dev, int64_t ldy, int32_t out_dtype,

@@ -83,3 +83,29 @@ def assert_linear_close(y_gpu, y_ref, bound, label: str, extra=None):
         i, j = np.argwhere(~ok)[0]
         raise AssertionError(f"{label}: {int((~ok).sum())} outputs out of tolerance; first [{i},{j}] gpu={y_gpu[i, j]!r} "
                              f"ref={y_ref[i, j]!r} bound={bound[i, j]!r}")
+
+
+# NVFP4-style buffers: two E4M3 bytes per lane ([KB][RB][64][2]), then at the
+# next 256-byte boundary the binary32 tensor scale.
+def untile_scales_nv(buf, rows, K, label="scales"):
+    RB, KB = _dims(rows, K)
+    raw = np.asarray(buf)
+    t = raw[:KB * RB * 128].reshape(KB, RB, 4, 16, 2).transpose(1, 3, 0, 2, 4)
+    scales = _crop(t.reshape(RB * 16, KB * 8), rows, K // 16, label)
+    off = -(-KB * RB * 128 // 256) * 256
+    g = raw[off:off + 4].copy().view(np.float32)[0]
+    return scales, g
+
+
+def untile_act_nv(raw: dict, M: int, K: int) -> dict:
+    s_scales, g_s = untile_scales_nv(raw["s_scales"], M, K, "s_scales")
+    r_scales, g_r = untile_scales_nv(raw["r_scales"], M, K, "r_scales")
+    return dict(s_codes=untile_sparse_codes(raw["s_codes"], M, K),
+                s_meta=untile_meta(raw["s_meta"], M, K),
+                s_scales=s_scales, r_codes=untile_dense(raw["r_codes"], M, K, "r_codes"),
+                r_scales=r_scales, g_s=g_s, g_r=g_r)
+
+
+def untile_weight_nv(codes, scales, N, K):
+    s, g = untile_scales_nv(scales, N, K, "w_scales")
+    return untile_dense(codes, N, K, "w_codes"), s, g

@@ -63,12 +63,31 @@ def test_size_queries(lib):
     assert lib.sharq_act_bytes(0, 4096, 2, 4, 0, sizes) == 0 and sum(sizes) == 0
 
 
+def test_size_queries_nvfp4(lib):
+    """NVFP4-style: codes as MXFP4; block scales of two bytes per lane ([KB][RB][128])
+    followed, at the next 256-byte boundary, by a 256-byte record holding the
+    tensor scale; the residual's and the weight's records are followed by the
+    kernels' scratch (per-row maxima and 1/rms, per-workgroup maxima)."""
+    cb, sb = C.c_size_t(), C.c_size_t()
+    assert lib.sharq_weight_bytes(4096, 4096, 1, C.byref(cb), C.byref(sb)) == 0
+    NB, KB = 256, 32
+    assert cb.value == 4096 * 2048
+    assert sb.value == NB * KB * 128 + 256 + NB * (KB // 4) * 4
+    sizes = (C.c_size_t * 5)()
+    assert lib.sharq_act_bytes(8, 4096, 2, 4, 1, sizes) == 0
+    RB = 1
+    assert list(sizes)[0::2][:2] == [RB * KB * 512, RB * KB * 128 + 256]
+    assert sizes[1] == RB * KB * 256 and sizes[3] == RB * KB * 1024
+    assert sizes[4] == RB * KB * 128 + 256 + 256 + 256 + 256
+    assert lib.sharq_act_bytes(0, 4096, 2, 4, 1, sizes) == 0 and sum(sizes) == 0
+
+
 @pytest.mark.parametrize("args,status", [
     ((2048, 4008, 2, 4, 0), _lib.ERR_INVALID_ARG),   # K % 32
     ((2048, 0, 2, 4, 0), _lib.ERR_INVALID_ARG),
     ((-1, 4096, 2, 4, 0), _lib.ERR_INVALID_ARG),
     ((16, 4096, 1, 4, 0), _lib.ERR_UNSUPPORTED),     # only 2:4
-    ((16, 4096, 2, 4, 1), _lib.ERR_UNSUPPORTED),     # NVFP4 not built
+    ((16, 4088, 2, 4, 1), _lib.ERR_INVALID_ARG),     # NVFP4 also needs K % 32
     ((16, 4096, 2, 4, 2), _lib.ERR_UNSUPPORTED),     # HiF4 undefined
     ((16, 4096, 2, 4, 7), _lib.ERR_INVALID_ARG),
 ])
@@ -118,7 +137,7 @@ def test_pack_and_linear_reject_before_launch(lib):
     assert lib.sharq_pack_weight(src, 16, 250, 256, 0, C.byref(w), None) == _lib.ERR_INVALID_ARG
     assert lib.sharq_pack_weight(src, 0, 256, 256, 0, C.byref(w), None) == _lib.ERR_INVALID_ARG
     assert lib.sharq_pack_weight(src, 16, 256, 100, 0, C.byref(w), None) == _lib.ERR_INVALID_ARG
-    assert lib.sharq_pack_weight(src, 16, 256, 256, 1, C.byref(w), None) == _lib.ERR_UNSUPPORTED
+    assert lib.sharq_pack_weight(src, 16, 256, 256, 2, C.byref(w), None) == _lib.ERR_UNSUPPORTED   # HiF4
     # linear: descriptors that were never filled by the library are refused
     a = _act()
     assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 16, 0, None) == _lib.ERR_INVALID_ARG
@@ -134,6 +153,16 @@ def test_pack_and_linear_reject_before_launch(lib):
     for p, base in ((0, 0x200000), (1, 0x210000)):
         w.view[p].base, w.view[p].ld, w.view[p].block = base, 2 * 64, 32
     assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 0, None) == _lib.ERR_UNSUPPORTED
+    # formats must agree; NVFP4-style descriptors need NVFP4-style views (block 16, stride NB*128)
+    a.fmt, w.fmt = 1, 0
+    assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 0, None) == _lib.ERR_INVALID_ARG
+    w.fmt = 1
+    for p in (0, 1):
+        w.view[p].base, w.view[p].ld, w.view[p].block = 0x200000, 2 * 64, 32
+    assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 0, None) == _lib.ERR_INVALID_ARG
+    a.fmt = w.fmt = 2
+    assert lib.sharq_linear(C.byref(a), C.byref(w), C.c_void_p(0x400000), 32, 0, None) == _lib.ERR_UNSUPPORTED
+    a.fmt = w.fmt = 0
     a.M = 0
     assert lib.sharq_linear(C.byref(a), C.byref(w), None, 32, 0, None) == _lib.OK
 
@@ -165,3 +194,5 @@ def test_grouped_rejects_before_launch(lib):
     assert call(64, 8, ldy=8) == _lib.ERR_INVALID_ARG            # ldy < N_e
     assert call(64, 8, wsb=100) == _lib.ERR_WORKSPACE            # workspace too small
     assert call(0, 8, ri=C.c_void_p(0x800000)) == _lib.OK        # nothing routed: no launch
+    a.fmt = w.fmt = 1
+    assert call(64, 8) == _lib.ERR_UNSUPPORTED                   # grouped layer is MXFP4 only
