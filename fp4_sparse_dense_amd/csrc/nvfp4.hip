@@ -120,6 +120,14 @@ __device__ __forceinline__ float chunk_sumsq(const float (&v)[32]) {
 // zero kept): the convert instruction with unit scale.
 __device__ __forceinline__ uint32_t e2m1_pair(float lo, float hi) { return fp4_pack2<0>(0u, lo, hi) & 0xFFu; }
 
+// Element quotient u / (s g) (IEEE division), or a signed zero when the block
+// scale is zero.  Both sides are computed and selected, so the lanes of a wave
+// never diverge around the division.
+__device__ __forceinline__ float nv_quot(float u, float tq, float s) {
+  const float q = u / tq;
+  return s > 0.0f ? q : u * 0.0f;
+}
+
 struct NvPrepArgs {
   const uint16_t* x;
   int64_t M, ldx;
@@ -190,19 +198,32 @@ __global__ __launch_bounds__(256) void nv_rowstats_kernel(NvPrepArgs a) {
   }
 }
 
-// 2:4 mask of one group: element i is kept iff at most one other element beats
-// it (larger magnitude, or equal magnitude and lower index).  Returns the
-// metadata nibble i0 | i1 << 2 and the kept offsets.
-__device__ __forceinline__ uint32_t keep24(const float* a, int& i0, int& i1) {
-  const float m0 = fabsf(a[0]), m1 = fabsf(a[1]), m2 = fabsf(a[2]), m3 = fabsf(a[3]);
+// 2:4 mask of one group a0..a3: element i is kept iff at most one other
+// element beats it (larger magnitude, or equal magnitude and lower index).
+// The first kept element is i0 (never 3), the second i1 (never 0); the
+// metadata nibble is i0 | i1 << 2.  Only fixed register indices are used.
+struct Keep24 {
+  bool f1, f2;       // element 1 / 2 is the first kept one (element 0 is iff k0)
+  bool s1, s2;       // element 1 / 2 is the second kept one (element 3 is iff k3)
+  bool k0, k3;
+  uint32_t nib;
+};
+__device__ __forceinline__ Keep24 keep24(float a0, float a1, float a2, float a3) {
+  const float m0 = fabsf(a0), m1 = fabsf(a1), m2 = fabsf(a2), m3 = fabsf(a3);
   const int b01 = m0 >= m1, b02 = m0 >= m2, b03 = m0 >= m3, b12 = m1 >= m2, b13 = m1 >= m3, b23 = m2 >= m3;
-  const bool k0 = (3 - b01 - b02 - b03) <= 1;
+  Keep24 k;
+  k.k0 = (3 - b01 - b02 - b03) <= 1;
   const bool k1 = (b01 + 2 - b12 - b13) <= 1;
   const bool k2 = (b02 + b12 + 1 - b23) <= 1;
-  const bool k3 = (b03 + b13 + b23) <= 1;
-  i0 = k0 ? 0 : (k1 ? 1 : 2);
-  i1 = k3 ? 3 : (k2 ? 2 : 1);
-  return (uint32_t)i0 | ((uint32_t)i1 << 2);
+  k.k3 = (b03 + b13 + b23) <= 1;
+  k.f1 = !k.k0 && k1;
+  k.f2 = !k.k0 && !k1;
+  k.s1 = !k.k3 && !k2;
+  k.s2 = !k.k3 && k2;
+  const uint32_t i0 = k.k0 ? 0u : (k1 ? 1u : 2u);
+  const uint32_t i1 = k.k3 ? 3u : (k2 ? 2u : 1u);
+  k.nib = i0 | (i1 << 2);
+  return k;
 }
 
 // ---------------------------------------------------------------------------
@@ -258,19 +279,26 @@ __global__ __launch_bounds__(256) void nv_decompose_kernel(NvPrepArgs a) {
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const int G = 4 * b + gq;
-      int i0, i1;
-      meta |= keep24(&v[4 * G], i0, i1) << (4 * G);
-      const float x0 = v[4 * G + i0], x1 = v[4 * G + i1];
-      const float q0 = s > 0.0f ? x0 / tq : x0 * 0.0f;
-      const float q1 = s > 0.0f ? x1 / tq : x1 * 0.0f;
+      float& a0 = v[4 * G];
+      float& a1 = v[4 * G + 1];
+      float& a2 = v[4 * G + 2];
+      float& a3 = v[4 * G + 3];
+      const Keep24 k = keep24(a0, a1, a2, a3);
+      meta |= k.nib << (4 * G);
+      const float x0 = k.k0 ? a0 : (k.f1 ? a1 : a2);
+      const float x1 = k.k3 ? a3 : (k.s2 ? a2 : a1);
+      const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
       const uint32_t c = e2m1_pair(q0, q1);
       scodes[b] |= c << (8 * gq);
       float d0, d1;
       fp4_unpack2<0>(c, d0, d1);
       d0 = (d0 * s) * g_s;
       d1 = (d1 * s) * g_s;
-      v[4 * G + i0] = x0 - d0;
-      v[4 * G + i1] = x1 - d1;
+      const float r0 = x0 - d0, r1 = x1 - d1;
+      a0 = k.k0 ? r0 : a0;
+      a1 = k.f1 ? r0 : (k.s1 ? r1 : a1);
+      a2 = k.f2 ? r0 : (k.s2 ? r1 : a2);
+      a3 = k.k3 ? r1 : a3;
     }
   }
   const int64_t tile = rb * a.KB + kb;
@@ -303,8 +331,7 @@ __global__ __launch_bounds__(256) void nv_decompose_kernel(NvPrepArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const float x0 = v[16 * b + i], x1 = v[16 * b + i + 1];
-        const float q0 = s > 0.0f ? x0 / tq : x0 * 0.0f;
-        const float q1 = s > 0.0f ? x1 / tq : x1 * 0.0f;
+        const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
         const int e = 16 * b + i;                 // element index; 8 per dword
         rc[e / 8] |= e2m1_pair(q0, q1) << (4 * (e % 8));
       }
@@ -387,8 +414,7 @@ __global__ __launch_bounds__(256) void nv_pack_weight_kernel(NvWeightArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const float x0 = v[16 * b + i], x1 = v[16 * b + i + 1];
-      const float q0 = s > 0.0f ? x0 / tq : x0 * 0.0f;
-      const float q1 = s > 0.0f ? x1 / tq : x1 * 0.0f;
+      const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
       const int e = 16 * b + i;
       c[e / 8] |= e2m1_pair(q0, q1) << (4 * (e % 8));
     }
