@@ -315,6 +315,28 @@ def linear(act: dict, w_codes, w_scales, rows=None):
 
 
 # --------------------------------------------------------------------------
+# Plain FP4 linear: the comparator the SharQ README benchmarks against (its
+# dense FP4 baseline mode): no backbone, the whole normalised row quantised
+# once, one GEMM.  In the descriptors this is the N:M pattern 0:4.
+# --------------------------------------------------------------------------
+def prepare_dense(x_bits, gamma_bits=None, eps: float = 1e-5):
+    """v = RMSNorm(x) (or x), then MXFP4 of v.  Returns r_codes [M, K/2] and
+    r_scales [M, K/32] (the dense operand; the backbone arrays are empty) and v.
+    Pinned by: per-element exact-rational codes and closed-form scales."""
+    v = rmsnorm(x_bits, gamma_bits, eps)
+    scales, nib = quantize_mx(v)
+    return dict(r_codes=pack_nibbles(nib), r_scales=scales, v=v)
+
+
+def linear_dense(act: dict, w_codes, w_scales, rows=None):
+    """y = deq(Q(v)) deq(W)^T in float64 and the bound sum|terms|."""
+    sl = slice(None) if rows is None else rows
+    d = deq_dense(act["r_codes"][sl], act["r_scales"][sl])
+    dw = deq_dense(w_codes, w_scales)
+    return d @ dw.T, np.abs(d) @ np.abs(dw).T
+
+
+# --------------------------------------------------------------------------
 # NVFP4-style format: a reading.  The SharQ abstract reports the method under
 # NVFP4 (and HiF4, MXFP4) but prints no definition; this follows the public
 # two-level NVFP4 description: E2M1 elements in 16-element blocks, an OCP E4M3
