@@ -10,8 +10,10 @@ norm; ``--fmt nvfp4`` runs it in the NVFP4-style format: E4M3 scale per 16,
 binary32 tensor scales, bf16 MFMA on exactly expanded codes) and moe (Qwen3-30B-A3B-shaped expert layer: 4096 tokens routed top-8 of
 128 experts with Zipf(1.1) loads; step = prep of the tokens + grouped gate/up
 (K=2048, N_e=1536) + prep of the 32768 expert-sorted down rows + grouped down
-(K=768, N_e=2048)).  Weight payloads are packed once, outside the timed region
-(an offline step).
+(K=768, N_e=2048)).  ``--mode dense`` times the plain MXFP4 linear instead
+(pattern 0:4: no backbone, MXFP4 of the normalised row, one GEMM) -- the dense
+FP4 baseline SharQ is compared against; its flops are 2*M*N*K.  Weight payloads
+are packed once, outside the timed region (an offline step).
 
 Inputs are seeded synthetic tensors (fp4_sparse_dense_amd.synth for
 activations and the router; weights N(0, 0.02) drawn on the device from a
@@ -57,22 +59,25 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dual_gemm_qkv.txt")
 GEMM_SRC = os.path.join(ROOT, "fp4_sparse_dense_amd", "csrc", "gemm.hip")
 
 
-def prep_bytes(M, K, norm=True, nv=False):
+def prep_bytes(M, K, norm=True, nv=False, dense=False):
     """Algorithmic HBM bytes of one prep: bf16 X in once, 0.9375 B/elem out
-    (NVFP4-style: 1 B/elem), gamma once."""
-    return M * K * 2 + (M * K if nv else M * K * 15 // 16) + (2 * K if norm else 0)
+    (NVFP4-style: 1 B/elem; plain FP4: 0.53125), gamma once."""
+    out = M * K if nv else (M * K * 17 // 32 if dense else M * K * 15 // 16)
+    return M * K * 2 + out + (2 * K if norm else 0)
 
 
 def gemm_flops(M, N, K):
     return 4 * M * N * K
 
 
-def gemm_bytes(M, N, K, out_bytes=4, nv=False):
+def gemm_bytes(M, N, K, out_bytes=4, nv=False, dense=False):
     """Algorithmic HBM bytes of one dual GEMM: prepared A (MXFP4 0.9375 B/elem;
     NVFP4-style 1 B/elem: scales per 16), the packed weight read once for both
     paths (MXFP4 0.53125 B/elem; NVFP4-style 0.5625), Y."""
     if nv:
         return M * K + N * K * 9 // 16 + out_bytes * M * N
+    if dense:
+        return M * K * 17 // 32 + N * K * 17 // 32 + out_bytes * M * N
     return M * K * 15 // 16 + N * K * 17 // 32 + out_bytes * M * N
 
 
@@ -196,6 +201,8 @@ def main():
     ap.add_argument("--m", type=int, default=1, help="rows of the decode workload")
     ap.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "nvfp4"],
                     help="FP4 format (nvfp4: the decode workload only)")
+    ap.add_argument("--mode", default="sharq", choices=["sharq", "dense"],
+                    help="dense: the plain MXFP4 linear (no backbone), the baseline SharQ is compared against")
     ap.add_argument("--sets", type=int, default=0, help="rotating input/weight/output sets (0: enough for > 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -217,6 +224,9 @@ def main():
     if args.fmt == "nvfp4" and args.workload != "decode":
         print("the NVFP4-style path is built for the decode workload (--workload decode)", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "dense" and (args.fmt != "mxfp4" or args.workload == "moe"):
+        print("the plain FP4 linear is built for MXFP4 dense layers", file=sys.stderr)
+        sys.exit(2)
     if args.workload == "moe":
         rec = run_moe(args)
     else:
@@ -236,11 +246,13 @@ def run_dense(args):
     K, N, norm = wl["K"], wl["N"], wl["norm"]
     nv = args.fmt == "nvfp4"
     fmt = sq.FMT_NVFP4 if nv else sq.FMT_MXFP4
+    dense = args.mode == "dense"
+    pat_n = 0 if dense else 2
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
-    per_set = M * K * 2 + gemm_bytes(M, N, K, nv=nv)
+    per_set = M * K * 2 + gemm_bytes(M, N, K, nv=nv, dense=dense)
     nsets = args.sets or max(2, min(64, -(-ROTATE_BYTES // per_set)))
     nx = min(nsets, 4)                       # distinct activation draws (CPU-generated)
     gen = torch.Generator(device="cuda")
@@ -258,7 +270,7 @@ def run_dense(args):
     sets = []
     for s in range(nsets):
         w = sq.sharq_pack_weight(device_weight(gen, N, K), fmt=fmt)
-        sets.append((w, sq.SharqAct(M, K, torch.device("cuda"), fmt=fmt),
+        sets.append((w, sq.SharqAct(M, K, torch.device("cuda"), n=pat_n, fmt=fmt),
                      torch.empty(M, N, dtype=torch.float32, device="cuda")))
     torch.cuda.synchronize()
 
@@ -268,7 +280,7 @@ def run_dense(args):
         if ev is not None:
             ev[0].record(stream)
         if part in (None, 0):
-            sq.sharq_prepare(x, g, 1e-5, fmt=fmt, out=act)
+            sq.sharq_prepare(x, g, 1e-5, n=pat_n, fmt=fmt, out=act)
         if ev is not None:
             ev[1].record(stream)
         if part in (None, 1):
@@ -280,11 +292,11 @@ def run_dense(args):
     graph = args.workload == "decode"
     ms, parts = timed(step, args.steps, args.warmup, graph=graph)
     prep_ms, gemm_ms = float(np.mean(parts[0])), float(np.mean(parts[1]))
-    flops = gemm_flops(M, N, K)
+    flops = gemm_flops(M, N, K) // (2 if dense else 1)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    gbytes = gemm_bytes(M, N, K, nv=nv)
+    gbytes = gemm_bytes(M, N, K, nv=nv, dense=dense)
     gemm_gbs = gbytes / (gemm_ms * 1e-3) / 1e9
-    pbytes = prep_bytes(M, K, norm, nv=nv)
+    pbytes = prep_bytes(M, K, norm, nv=nv, dense=dense)
     prep_gbs = pbytes / (prep_ms * 1e-3) / 1e9
     peak_mfma = PEAK_BF16_TFLOPS if nv else PEAK_FP4_TFLOPS
     hbm_bound = gbytes / (PEAK_HBM_GBS * 1e9) > flops / (peak_mfma * 1e12)
@@ -294,11 +306,14 @@ def run_dense(args):
     else:
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak_mfma, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / peak_mfma, 4),
-                "traffic": read_traffic() if args.workload == "qkv" else None}
-    cpu = None if (args.no_cpu_baseline or args.workload != "qkv") else cpu_baseline()
+                "traffic": read_traffic() if (args.workload == "qkv" and not dense) else None}
+    cpu = None if (args.no_cpu_baseline or args.workload != "qkv" or dense) else cpu_baseline()
     wname = args.workload if args.workload != "decode" else f"decode{M}"
+    if dense:
+        wname += "-plainfp4"
     return {
-        "metric": "SharQ linear TFLOPS + prep GB/s (fraction of peak), Llama-8B shapes M=2048",
+        "metric": ("plain MXFP4 linear TFLOPS (dense FP4 baseline, 2*M*N*K), Llama-8B shapes" if dense else
+                   "SharQ linear TFLOPS + prep GB/s (fraction of peak), Llama-8B shapes M=2048"),
         "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -314,8 +329,10 @@ def run_dense(args):
                                wl["desc"].split(": ", 1)[1].replace("M rows", f"M={M}") +
                                ("; 2:4 mask; NVFP4-style activations and weight (E4M3 scale per 16, binary32 tensor "
                                 "scales, bf16 MFMA on exactly expanded codes); fp32 output" if nv else
+                                "; no backbone (plain MXFP4 of the row), MXFP4 weight; fp32 output" if dense else
                                 "; 2:4 mask; MXFP4 activations and weight; fp32 output"),
-                   "M": M, "K": K, "N": N, "pattern": "2:4", "format": "NVFP4-style" if nv else "MXFP4",
+                   "M": M, "K": K, "N": N, "pattern": "0:4" if dense else "2:4",
+                   "format": "NVFP4-style" if nv else "MXFP4",
                    "rotating_sets": nsets},
         "prep": {"us": round(prep_ms * 1e3, 3), "GB/s": round(prep_gbs, 1),
                  "frac_hbm": round(prep_gbs / PEAK_HBM_GBS, 4), "bytes": pbytes},

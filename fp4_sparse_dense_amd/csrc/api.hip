@@ -58,6 +58,21 @@ sharq_status check_fmt(int32_t fmt, bool nv_ok = true) {
   return fail(SHARQ_ERR_INVALID_ARG, "unknown format %d", (int)fmt);
 }
 
+// Patterns built: 2:4, and 0:4 -- no backbone, the plain FP4 linear (MXFP4 only).
+sharq_status check_pattern(int32_t n, int32_t m, int32_t fmt) {
+  if (m == 4 && n == 2) return SHARQ_OK;
+  if (m == 4 && n == 0)
+    return fmt == SHARQ_FMT_MXFP4 ? SHARQ_OK
+                                  : fail(SHARQ_ERR_UNSUPPORTED, "the plain FP4 linear (pattern 0:4) is built for MXFP4 only");
+  return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern (and 0:4, no backbone) is built (got %d:%d)", (int)n, (int)m);
+}
+
+// the backbone buffers are needed (set and 16-byte aligned) unless the pattern is 0:4
+bool backbone_ok(const sharq_act* a, int32_t n) {
+  return n == 0 || (a->s_codes && a->s_meta && a->s_scales && aligned(a->s_codes, 16) &&
+                    aligned(a->s_meta, 16) && aligned(a->s_scales, 16));
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,8 +111,9 @@ sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t
   if (!sizes) return fail(SHARQ_ERR_INVALID_ARG, "null output pointer");
   if (M < 0 || K <= 0) return fail(SHARQ_ERR_INVALID_ARG, "bad shape M=%lld K=%lld", (long long)M, (long long)K);
   if (K % 32) return fail(SHARQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 32", (long long)K);
-  if (n != 2 || m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built (got %d:%d)", (int)n, (int)m);
   sharq_status s = check_fmt(fmt);
+  if (s) return s;
+  s = check_pattern(n, m, fmt);
   if (s) return s;
   const size_t tiles = (size_t)((M + 15) / 16) * (size_t)((K + 127) / 128);
   sizes[0] = tiles * 512;
@@ -110,6 +126,7 @@ sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t
     sizes[2] = M > 0 ? L.s_bytes : 0;
     sizes[4] = M > 0 ? L.r_bytes : 0;
   }
+  if (n == 0) sizes[0] = sizes[1] = sizes[2] = 0;   // no backbone
   return SHARQ_OK;
 }
 
@@ -159,23 +176,26 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
   if (K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "K too large");
   if (gamma_bf16_dev && K > 32768) return fail(SHARQ_ERR_INVALID_ARG, "RMSNorm rows are limited to K <= 32768");
   if (ldx > (int64_t(1) << 26)) return fail(SHARQ_ERR_INVALID_ARG, "ldx=%lld exceeds 2^26 elements", (long long)ldx);
-  if (n != 2 || m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built (got %d:%d)", (int)n, (int)m);
   sharq_status s = check_fmt(fmt);
+  if (s) return s;
+  s = check_pattern(n, m, fmt);
   if (s) return s;
   if (M > 0) {
     if (!x_bf16_dev) return fail(SHARQ_ERR_INVALID_ARG, "null activation pointer");
-    if (!out->s_codes || !out->s_meta || !out->s_scales || !out->r_codes || !out->r_scales)
-      return fail(SHARQ_ERR_INVALID_ARG, "activation output buffers not set");
+    if (!out->r_codes || !out->r_scales || !backbone_ok(out, n))
+      return fail(SHARQ_ERR_INVALID_ARG, "activation output buffers not set or not 16-byte aligned");
     if (ldx < K || ldx % 8) return fail(SHARQ_ERR_INVALID_ARG, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
     if (!aligned(x_bf16_dev, 16)) return fail(SHARQ_ERR_INVALID_ARG, "activation not 16-byte aligned");
     if (gamma_bf16_dev && !aligned(gamma_bf16_dev, 16)) return fail(SHARQ_ERR_INVALID_ARG, "gamma not 16-byte aligned");
-    if (!aligned(out->s_codes, 16) || !aligned(out->s_meta, 16) || !aligned(out->r_codes, 16) ||
-        !aligned(out->s_scales, 16) || !aligned(out->r_scales, 16))
+    if (!aligned(out->r_codes, 16) || !aligned(out->r_scales, 16))
       return fail(SHARQ_ERR_INVALID_ARG, "activation output buffers must be 16-byte aligned");
     s = check_device();
     if (s) return s;
     sharq::PrepOut po{out->s_codes, out->s_meta, out->s_scales, out->r_codes, out->r_scales};
-    hipError_t e = fmt == SHARQ_FMT_NVFP4
+    hipError_t e = n == 0 ? sharq::launch_prepare_dense(static_cast<const uint16_t*>(x_bf16_dev), M, (int)K, ldx,
+                                                        static_cast<const uint16_t*>(gamma_bf16_dev), eps, po,
+                                                        static_cast<hipStream_t>(stream))
+                   : fmt == SHARQ_FMT_NVFP4
                        ? sharq::launch_prepare_nv(static_cast<const uint16_t*>(x_bf16_dev), M, (int)K, ldx,
                                                   static_cast<const uint16_t*>(gamma_bf16_dev), eps, po,
                                                   static_cast<hipStream_t>(stream))
@@ -205,18 +225,18 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   if (a->M < 0 || w->N <= 0 || a->K <= 0 || a->K % 32) return fail(SHARQ_ERR_INVALID_ARG, "bad shapes");
   if (a->K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "K too large");
   if (out_dtype != SHARQ_OUT_F32 && out_dtype != SHARQ_OUT_BF16) return fail(SHARQ_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
-  if (a->n != 2 || a->m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built");
   if (a->fmt != w->fmt) return fail(SHARQ_ERR_INVALID_ARG, "activation and weight formats differ");
   sharq_status s = check_fmt(a->fmt);
+  if (s) return s;
+  s = check_pattern(a->n, a->m, a->fmt);
   if (s) return s;
   if (a->M == 0) return SHARQ_OK;
   if (!y_dev) return fail(SHARQ_ERR_INVALID_ARG, "null output pointer");
   if (ldy < w->N) return fail(SHARQ_ERR_INVALID_ARG, "ldy=%lld < N=%lld", (long long)ldy, (long long)w->N);
   if (!aligned(y_dev, out_dtype == SHARQ_OUT_F32 ? 4 : 2)) return fail(SHARQ_ERR_INVALID_ARG, "output misaligned");
-  if (!a->s_codes || !a->s_meta || !a->s_scales || !a->r_codes || !a->r_scales || !w->codes)
-    return fail(SHARQ_ERR_INVALID_ARG, "descriptor buffers not set");
-  if (!aligned(a->s_codes, 16) || !aligned(a->s_meta, 16) || !aligned(a->r_codes, 16) || !aligned(w->codes, 16) ||
-      !aligned(a->s_scales, 16) || !aligned(a->r_scales, 16))
+  if (!a->r_codes || !a->r_scales || !w->codes || !backbone_ok(a, a->n))
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor buffers not set or not 16-byte aligned");
+  if (!aligned(a->r_codes, 16) || !aligned(w->codes, 16) || !aligned(a->r_scales, 16))
     return fail(SHARQ_ERR_INVALID_ARG, "operand buffers must be 16-byte aligned");
   const bool nv = a->fmt == SHARQ_FMT_NVFP4;
   const sharq_scale_view& vs = w->view[SHARQ_PATH_SPARSE];
@@ -262,7 +282,8 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
     g.g_w = reinterpret_cast<const float*>(vs.base + lw.g);
   }
   hipError_t e = nv ? sharq::launch_linear_nv(g, static_cast<hipStream_t>(stream))
-                    : sharq::launch_linear(g, static_cast<hipStream_t>(stream));
+                 : a->n == 0 ? sharq::launch_linear_dense(g, static_cast<hipStream_t>(stream))
+                             : sharq::launch_linear(g, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "linear launch");
   return SHARQ_OK;
 }
@@ -289,7 +310,7 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
   if (a->K != w->K) return fail(SHARQ_ERR_INVALID_ARG, "K mismatch: activation %lld, weight %lld", (long long)a->K, (long long)w->K);
   if (a->M < 0 || w->N <= 0 || a->K <= 0 || a->K % 32 || a->K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "bad shapes");
   if (out_dtype != SHARQ_OUT_F32 && out_dtype != SHARQ_OUT_BF16) return fail(SHARQ_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
-  if (a->n != 2 || a->m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "only the 2:4 pattern is built");
+  if (a->n != 2 || a->m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "the grouped layer is built for the 2:4 pattern only");
   if (a->fmt != w->fmt) return fail(SHARQ_ERR_INVALID_ARG, "activation and weight formats differ");
   sharq_status s = check_fmt(a->fmt, false);
   if (s) return s;

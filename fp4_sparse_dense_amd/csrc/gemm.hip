@@ -16,6 +16,8 @@
 // l%16 and K range [32*(l/16), 32*(l/16)+32) as 16 bytes, lower k in the low
 // nibble; its scale byte is that row's E8M0 for the same 32-block; the
 // accumulator of lane l holds D[4*(l/16)+i][l%16], i = 0..3.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -89,7 +91,7 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, int64_t row, int64_
 // sums meet in LDS and are added in wave order.  Both paths read the weight
 // scales through one load: the API admits only views of one scale array.
 // ---------------------------------------------------------------------------
-template <int RBG, int NW>
+template <int RBG, int NW, bool DENSE>
 __global__ __launch_bounds__(64 * NW) void dual_gemm_splitk(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1);
@@ -126,19 +128,21 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_splitk(GemmArgs g) {
         const int64_t rb = rb0 + r < RB ? rb0 + r : RB - 1;
         const int64_t tile = rb * KT + ktc;
         const uint4 rq = *reinterpret_cast<const uint4*>(g.r_codes + tile * 1024 + lane * 16);
-        const uint2 sq = *reinterpret_cast<const uint2*>(g.s_codes + tile * 512 + lane * 8);
-        const uint32_t mq = *reinterpret_cast<const uint32_t*>(g.s_meta + tile * 256 + lane * 4);
-        ss[c][r] = g.s_scales[((int64_t)ktc * RB + rb) * 64 + lane];
         sr[c][r] = g.r_scales[((int64_t)ktc * RB + rb) * 64 + lane];
         ar[c][r] = as_operand(rq);
-        as[c][r] = as_operand(expand_chunk(sq.x, sq.y, mq));
+        if constexpr (!DENSE) {
+          const uint2 sq = *reinterpret_cast<const uint2*>(g.s_codes + tile * 512 + lane * 8);
+          const uint32_t mq = *reinterpret_cast<const uint32_t*>(g.s_meta + tile * 256 + lane * 4);
+          ss[c][r] = g.s_scales[((int64_t)ktc * RB + rb) * 64 + lane];
+          as[c][r] = as_operand(expand_chunk(sq.x, sq.y, mq));
+        }
       }
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c)
 #pragma unroll
       for (int r = 0; r < RBG; ++r) {
-        acs[r] = mfma_fp4(as[c][r], b[c], acs[r], ss[c][r], sw[c]);
+        if constexpr (!DENSE) acs[r] = mfma_fp4(as[c][r], b[c], acs[r], ss[c][r], sw[c]);
         acr[r] = mfma_fp4(ar[c][r], b[c], acr[r], sr[c][r], sw[c]);
       }
   }
@@ -199,7 +203,7 @@ struct TileCfg {
   static_assert(kMB % NWM == 0 && kNB % NWN == 0, "wave split");
 };
 
-template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED>
+template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE>
 __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
   extern __shared__ __align__(1024) uint8_t smem[];
@@ -283,10 +287,13 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   // offsets are taken at K tile 0 (blocks past the padding -> kOOB) and
   // hoisted out of the K loop.
   static_assert(C::kMB % C::kWaves == 0, "A-side blocks split evenly over the waves");
+  static_assert(!(DENSE && GROUPED), "the grouped layer runs both paths");
   constexpr int kSB = C::kMB / C::kWaves;
   constexpr int kWB = (C::kNB + C::kWaves - 1) / C::kWaves;
-  constexpr int kItems = 3 * kSB + kWB + 1;
-  static_assert(C::kWaves >= 3, "scale copies need three waves");
+  constexpr int kPerA = DENSE ? 1 : 3;                 // copies per A-side block
+  constexpr int kEdges = DENSE ? 2 : 3;                // scale edges
+  constexpr int kItems = kPerA * kSB + kWB + 1;
+  static_assert(C::kWaves >= kEdges, "one wave per scale edge");
 
   uint32_t offR[kSB], offC[kSB], offM[kSB];
 #pragma unroll
@@ -306,9 +313,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     const int64_t nb = nb0 + wblk[i];
     offW[i] = nb < nb_end ? (uint32_t)(nb * KT) * 1024u + lane * 16 : kOOB;
   }
-  // scale edge of this wave: 0 = backbone, 1 = residual, 2 = weight;
-  // 16 lanes per 64-byte block
-  const int edge = wave % 3;
+  // scale edge of this wave: 0 = backbone, 1 = residual, 2 = weight (without
+  // a backbone: 1 or 2); 16 lanes per 64-byte block
+  const int edge = DENSE ? 1 + wave % 2 : wave % 3;
   const int eb = lane >> 2;   // block of the edge this lane copies
   const uint32_t offScA = rb0 + eb < rb_end ? (uint32_t)((rb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
   const uint32_t offScW = nb0 + eb < nb_end ? (uint32_t)((nb0 + eb) * 64 + (lane & 3) * 16) : kOOB;
@@ -322,15 +329,15 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   // (dense codes, compressed codes, metadata), one per weight block, then the
   // scale edge
   auto issue_item = [&](int it, int ks, uint32_t st) {
-    if (it < 3 * kSB) {
-      const int i = it / 3, kind = it % 3;
+    if (it < kPerA * kSB) {
+      const int i = it / kPerA, kind = it % kPerA;
       const int b = wave + i * C::kWaves;
       const uint32_t as = st + C::kOffAS + b * 1024;
       if (kind == 0) lds_dma16(rs_rc, st + C::kOffAR + b * 1024, offR[i], (uint32_t)ks * 1024);
       else if (kind == 1) lds_dma16_lanes(rs_sc, as, offC[i], (uint32_t)ks * 512, 0xFFFFFFFFull);
       else lds_dma16_lanes(rs_sm, as + 512, offM[i], (uint32_t)ks * 256, 0xFFFFull);
-    } else if (it < 3 * kSB + kWB) {
-      const int i = it - 3 * kSB;
+    } else if (it < kPerA * kSB + kWB) {
+      const int i = it - kPerA * kSB;
       lds_dma16(rs_wc, st + C::kOffB + wblk[i] * 1024, offW[i], (uint32_t)ks * 1024);
     } else {
       lds_dma16_lanes(rs_edge, st + lds_edge, off_edge, (uint32_t)ks * stride_edge, lanes_edge);
@@ -385,9 +392,11 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < C::kWMT; ++i) {
       const int blk = wm * C::kWMT + i;
-      fs[i] = frag(st, C::kOffAS, blk);
+      if constexpr (!DENSE) {
+        fs[i] = frag(st, C::kOffAS, blk);
+        ss[i] = st[C::kOffSS + blk * 64 + lane];
+      }
       fr[i] = frag(st, C::kOffAR, blk);
-      ss[i] = st[C::kOffSS + blk * 64 + lane];
       sr[i] = st[C::kOffSR + blk * 64 + lane];
     }
 #pragma unroll
@@ -422,7 +431,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   const int pre = KT < NST ? KT : NST;   // steps copied before the loop
   for (int s = 0; s < pre; ++s) issue(s, lds0 + stage_off(s));
   wait_stages(pre - 1);
-  expand_store(smem + stage_off(0));
+  if constexpr (!DENSE) expand_store(smem + stage_off(0));
   __syncthreads();
   read_all(smem + stage_off(0));
 
@@ -477,16 +486,63 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
       sr[i] = nx[C::kOffSR + blk * 64 + lane];
     }
   };
+  // one K step without a backbone: the first half of the columns runs on the
+  // fragments already in registers before the barrier, the rest after it;
+  // every weight fragment is refilled after its column, the residual
+  // fragments after the last column, the copies spread over the columns
+  auto step_dense = [&](int ks, int newer, auto copy_tag) {
+    constexpr bool kCopy = decltype(copy_tag)::value;
+    constexpr int JH = C::kWNT / 2;
+    wait_stages(newer);
+#pragma unroll
+    for (int j = 0; j < JH; ++j)
+#pragma unroll
+      for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    const uint32_t cst = lds0 + stage_off(ks);
+    const uint8_t* nx = smem + stage_off(ks + 1);
+#pragma unroll
+    for (int j = 0; j < C::kWNT; ++j) {
+      if (j >= JH) {
+#pragma unroll
+        for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int blk = wn * C::kWNT + j;
+      fb[j] = frag(nx, C::kOffB, blk);
+      sw[j] = nx[C::kOffSW + blk * 64 + lane];
+      if constexpr (kCopy) {
+#pragma unroll
+        for (int it = j * kItems / C::kWNT; it < (j + 1) * kItems / C::kWNT; ++it) issue_item(it, ks + NST, cst);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < C::kWMT; ++i) {
+      const int blk = wm * C::kWMT + i;
+      fr[i] = frag(nx, C::kOffAR, blk);
+      sr[i] = nx[C::kOffSR + blk * 64 + lane];
+    }
+  };
+
   int ks = 0;
   // steady state: copies issued so far end at step ks+NST-1, so NST-2 steps
   // are newer than ks+1
-  for (; ks + NST < KT; ++ks) step(ks, NST - 2, BoolTag<true>{});
-  for (; ks + 1 < KT; ++ks) step(ks, KT - 2 - ks, BoolTag<false>{});
+  if constexpr (DENSE) {
+    for (; ks + NST < KT; ++ks) step_dense(ks, NST - 2, BoolTag<true>{});
+    for (; ks + 1 < KT; ++ks) step_dense(ks, KT - 2 - ks, BoolTag<false>{});
+  } else {
+    for (; ks + NST < KT; ++ks) step(ks, NST - 2, BoolTag<true>{});
+    for (; ks + 1 < KT; ++ks) step(ks, KT - 2 - ks, BoolTag<false>{});
+  }
   // last step
+  if constexpr (!DENSE) {
 #pragma unroll
-  for (int i = 0; i < C::kWMT; ++i)
+    for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
-    for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
+      for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
+  }
 #pragma unroll
   for (int j = 0; j < C::kWNT; ++j)
 #pragma unroll
@@ -506,16 +562,21 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     }
 }
 
-template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED>
+template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE>
 static hipError_t launch_tiled(const GemmArgs& a, int64_t tiles, hipStream_t stream) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
-  auto kern = dual_gemm_tiled<BM, BN, NWM, NWN, NST, GROUPED>;
+  auto kern = dual_gemm_tiled<BM, BN, NWM, NWN, NST, GROUPED, DENSE>;
   constexpr int lds = C::kStages * C::kStage;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  // the LDS limit is a per-function attribute: set it once per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  static std::atomic<bool> attr_set[64];
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -551,10 +612,11 @@ static int xcd_region_m(int64_t tm, int64_t tn, int K) {
 hipError_t launch_linear_grouped_gemm(const GemmArgs& a, int64_t max_mtiles, hipStream_t stream) {
   const int64_t NBe = (a.N / a.E + 15) / 16;
   const int64_t tiles_n = (NBe + kTileN / 16 - 1) / (kTileN / 16);
-  return launch_tiled<kTileM, kTileN, 4, 2, 3, true>(a, max_mtiles * tiles_n, stream);
+  return launch_tiled<kTileM, kTileN, 4, 2, 3, true, false>(a, max_mtiles * tiles_n, stream);
 }
 
-hipError_t launch_linear(const GemmArgs& a, hipStream_t stream) {
+template <bool DENSE>
+static hipError_t launch_linear_t(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   // the tiled kernel addresses every operand with 31-bit buffer offsets
   const uint64_t kb = (a.K + 127) / 128;
@@ -564,22 +626,26 @@ hipError_t launch_linear(const GemmArgs& a, hipStream_t stream) {
     const int64_t tm = (a.M + kTileM - 1) / kTileM, tn = (a.N + kTileN - 1) / kTileN;
     GemmArgs b = a;
     b.xcd_bm = xcd_region_m(tm, tn, a.K);
-    return launch_tiled<kTileM, kTileN, 4, 2, 3, false>(b, tm * tn, stream);
+    return launch_tiled<kTileM, kTileN, 4, 2, 3, false, DENSE>(b, tm * tn, stream);
   }
   // M <= 64 (or operands past 31-bit buffer offsets): split-K weight streaming;
   // eight waves per column block for one or two row blocks, four for more
   const int64_t RB = (a.M + 15) / 16, NB = (a.N + 15) / 16;
   if (NB > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (RB == 1) {
-    hipLaunchKernelGGL((dual_gemm_splitk<1, 8>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((dual_gemm_splitk<1, 8, DENSE>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
   } else if (RB == 2) {
-    hipLaunchKernelGGL((dual_gemm_splitk<2, 8>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((dual_gemm_splitk<2, 8, DENSE>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
   } else {
     const int64_t groups = (RB + 3) / 4;
     if (groups > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dual_gemm_splitk<4, 4>), dim3((unsigned)NB, (unsigned)groups), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((dual_gemm_splitk<4, 4, DENSE>), dim3((unsigned)NB, (unsigned)groups), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
+
+hipError_t launch_linear(const GemmArgs& a, hipStream_t stream) { return launch_linear_t<false>(a, stream); }
+
+hipError_t launch_linear_dense(const GemmArgs& a, hipStream_t stream) { return launch_linear_t<true>(a, stream); }
 
 }  // namespace sharq

@@ -50,6 +50,12 @@ struct GemmArgs {
 
 hipError_t launch_linear(const GemmArgs& a, hipStream_t stream);
 
+// Plain FP4 linear (no backbone): prep writes only the MXFP4 codes and scales
+// of v into r_codes / r_scales; the GEMM runs the dense path alone.
+hipError_t launch_prepare_dense(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
+                                float eps, PrepOut out, hipStream_t stream);
+hipError_t launch_linear_dense(const GemmArgs& a, hipStream_t stream);
+
 // Grouped expert layer: rows of a prepared activation gathered (or taken in
 // order) into expert segments padded to whole 16-row blocks, then one tiled
 // dual GEMM over every (expert, tile).  See sharq_linear_grouped.

@@ -13,6 +13,8 @@
 //
 // All arithmetic is binary32 with no contraction (built with -ffp-contract=off),
 // one rounding per operation, in the order the CPU reference states.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -143,24 +145,30 @@ __device__ __forceinline__ void group4(float (&v)[32], float s_scale, uint32_t& 
 }
 
 // The whole decomposition of one MX block; v is replaced by the residual.
+// DENSE (the plain FP4 linear, no backbone): the residual is v itself and
+// only its MXFP4 codes are produced.
+template <bool DENSE>
 __device__ __forceinline__ Block32 decompose32(float (&v)[32]) {
-  // S block scale: the block maximum of v is always kept, so amax(S) == amax(v)
-  float am = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; i += 2) am = abs_max3(am, v[i], v[i + 1]);
-  const int es = mx_shared_exp(__float_as_uint(am));
-  const float ss = pow2(es);
-
-  // groups last to first: the metadata nibbles enter most significant first
   uint32_t lo = 0, hi = 0, meta = 0;
-  group4<7>(v, ss, hi, meta);
-  group4<6>(v, ss, hi, meta);
-  group4<5>(v, ss, hi, meta);
-  group4<4>(v, ss, hi, meta);
-  group4<3>(v, ss, lo, meta);
-  group4<2>(v, ss, lo, meta);
-  group4<1>(v, ss, lo, meta);
-  group4<0>(v, ss, lo, meta);
+  int es = -127;
+  if constexpr (!DENSE) {
+    // S block scale: the block maximum of v is always kept, so amax(S) == amax(v)
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) am = abs_max3(am, v[i], v[i + 1]);
+    es = mx_shared_exp(__float_as_uint(am));
+    const float ss = pow2(es);
+
+    // groups last to first: the metadata nibbles enter most significant first
+    group4<7>(v, ss, hi, meta);
+    group4<6>(v, ss, hi, meta);
+    group4<5>(v, ss, hi, meta);
+    group4<4>(v, ss, hi, meta);
+    group4<3>(v, ss, lo, meta);
+    group4<2>(v, ss, lo, meta);
+    group4<1>(v, ss, lo, meta);
+    group4<0>(v, ss, lo, meta);
+  }
 
   float ar = 0.0f;
 #pragma unroll
@@ -264,7 +272,7 @@ __device__ __forceinline__ void wait_units(int n) {
   else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
 }
 
-template <bool NORM, bool GF32>
+template <bool NORM, bool GF32, bool DENSE>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
                                                             int64_t ldx, const uint16_t* __restrict__ gamma,
                                                             float eps, PrepPlan P, PrepOut o) {
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
         }
       }
     }
-    return decompose32(v);
+    return decompose32<DENSE>(v);
   };
 
   const int tl = c4 * 16 + (int)half * 8 + r8;
@@ -444,11 +452,13 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
     if (kt < KB) {
       const int64_t tile = rb * KB + kt;
       *reinterpret_cast<uint4*>(o.r_codes + tile * 1024 + tl * 16) = b.r_codes;
-      *reinterpret_cast<uint2*>(o.s_codes + tile * 512 + tl * 8) = b.s_codes;
-      *reinterpret_cast<uint32_t*>(o.s_meta + tile * 256 + tl * 4) = b.meta;
       const int64_t sc = ((int64_t)kt * RB + rb) * 64 + tl;
-      o.s_scales[sc] = (uint8_t)b.s_e8;
       o.r_scales[sc] = (uint8_t)b.r_e8;
+      if constexpr (!DENSE) {
+        *reinterpret_cast<uint2*>(o.s_codes + tile * 512 + tl * 8) = b.s_codes;
+        *reinterpret_cast<uint32_t*>(o.s_meta + tile * 256 + tl * 4) = b.meta;
+        o.s_scales[sc] = (uint8_t)b.s_e8;
+      }
     }
   };
 
@@ -515,22 +525,39 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
   }
 }
 
-hipError_t launch_prepare(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
-                          float eps, PrepOut out, hipStream_t stream) {
+template <bool DENSE>
+static hipError_t launch_prepare_t(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
+                                   float eps, PrepOut out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const PrepPlan P = prep_plan(K, gamma != nullptr);
   if (P.slots < 1 || P.total > kPrepLdsMax) return hipErrorInvalidValue;
-  auto kn = !gamma ? prep_kernel<false, false> : (P.gamma_f32 ? prep_kernel<true, true> : prep_kernel<true, false>);
+  auto kn = !gamma ? prep_kernel<false, false, DENSE>
+                   : (P.gamma_f32 ? prep_kernel<true, true, DENSE> : prep_kernel<true, false, DENSE>);
+  // the LDS limit is a per-function attribute: set it once per device
   const int which = !gamma ? 0 : (P.gamma_f32 ? 1 : 2);
-  static bool attr_set[3] = {false, false, false};
-  if (!attr_set[which]) {
-    hipError_t e = hipFuncSetAttribute((const void*)kn, hipFuncAttributeMaxDynamicSharedMemorySize, kPrepLdsMax);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  static std::atomic<bool> attr_set[64][3];
+  if (!attr_set[dev][which].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute((const void*)kn, hipFuncAttributeMaxDynamicSharedMemorySize, kPrepLdsMax);
     if (e != hipSuccess) return e;
-    attr_set[which] = true;
+    attr_set[dev][which].store(true, std::memory_order_release);
   }
   const int64_t nwg = (M + 15) / 16 * 2;
   hipLaunchKernelGGL(kn, dim3((unsigned)nwg), dim3(kPrepThreads), P.total, stream, x, M, K, ldx, gamma, eps, P, out);
   return hipGetLastError();
+}
+
+hipError_t launch_prepare(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
+                          float eps, PrepOut out, hipStream_t stream) {
+  return launch_prepare_t<false>(x, M, K, ldx, gamma, eps, out, stream);
+}
+
+hipError_t launch_prepare_dense(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
+                                float eps, PrepOut out, hipStream_t stream) {
+  return launch_prepare_t<true>(x, M, K, ldx, gamma, eps, out, stream);
 }
 
 hipError_t launch_pack_weight(const uint16_t* w, int64_t N, int K, int64_t ldw, uint8_t* codes,

@@ -82,6 +82,15 @@ def test_size_queries_nvfp4(lib):
     assert lib.sharq_act_bytes(0, 4096, 2, 4, 1, sizes) == 0 and sum(sizes) == 0
 
 
+def test_size_queries_plain_fp4(lib):
+    """Pattern 0:4 (no backbone, the plain FP4 linear): only the dense operand."""
+    sizes = (C.c_size_t * 5)()
+    assert lib.sharq_act_bytes(2048, 4096, 0, 4, 0, sizes) == 0
+    assert list(sizes) == [0, 0, 0, 2048 * 2048, 2048 * 128]
+    assert lib.sharq_act_bytes(16, 4096, 0, 4, 1, sizes) == _lib.ERR_UNSUPPORTED   # MXFP4 only
+    assert lib.sharq_act_bytes(16, 4096, 1, 4, 0, sizes) == _lib.ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("args,status", [
     ((2048, 4008, 2, 4, 0), _lib.ERR_INVALID_ARG),   # K % 32
     ((2048, 0, 2, 4, 0), _lib.ERR_INVALID_ARG),
@@ -196,3 +205,6 @@ def test_grouped_rejects_before_launch(lib):
     assert call(0, 8, ri=C.c_void_p(0x800000)) == _lib.OK        # nothing routed: no launch
     a.fmt = w.fmt = 1
     assert call(64, 8) == _lib.ERR_UNSUPPORTED                   # grouped layer is MXFP4 only
+    a.fmt = w.fmt = 0
+    a.n = 0
+    assert call(64, 8) == _lib.ERR_UNSUPPORTED                   # and 2:4 only
