@@ -157,8 +157,10 @@ sharq_status sharq_weight_bytes(int64_t N, int64_t K, int32_t fmt,
  * s_codes, s_meta, s_scales, r_codes, r_scales (MXFP4 tiled: RB*KB*{512, 256,
  * 64, 1024, 64}; NVFP4: the scale buffers hold E4M3 scales, the tensor scale
  * and, for r_scales, the preparation's scratch).  M == 0 gives zeros.
+ * Pattern (n,m) == (0,4) means no backbone: the plain FP4 linear (the dense
+ * FP4 baseline SharQ is measured against); the three backbone sizes are 0.
  * Errors: INVALID_ARG for M<0, K<=0, K%32, null output; UNSUPPORTED unless
- * (n,m) == (2,4) and fmt is MXFP4 or NVFP4. */
+ * (n,m) == (2,4) with MXFP4 or NVFP4, or (n,m) == (0,4) with MXFP4. */
 sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t fmt,
                              size_t sizes[5]);
 
@@ -186,6 +188,8 @@ sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int
  *   S = v on kept entries, 0 elsewhere; Q(S) = MXFP4 over 32 logical positions;
  *   R = v - deq(Q(S)) (exact in binary32); Q(R) = MXFP4;
  *   all five outputs in the tiled layout, padding rows and K written as zeros.
+ * With (n,m) == (0,4) there is no backbone: r_codes / r_scales receive the
+ * MXFP4 of v itself and the s_* buffers are not used (they may be NULL).
  * With fmt == NVFP4 the quantiser is the NVFP4 one (blocks of 16 logical
  * positions; S's tensor scale from max|S|, R's from max|R|, so R's depends
  * on Q(S)); deq(Q(S)) = (val * s) * g in binary32.  This runs as three
@@ -209,6 +213,8 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
  * On gfx950 the compressed 2:4 operand is expanded to dense 4-bit codes on
  * chip and both paths run block-scaled MXFP4 MFMA into one fp32 accumulator,
  * reading each weight tile once for both paths.
+ * An activation prepared with pattern 0:4 runs the dense GEMM alone:
+ * Y = deq(Q(v)) deq(W)^T (the plain FP4 linear).
  * NVFP4: the E4M3 scales cannot ride the MX MFMA, so each code is expanded
  * on chip to val * s (exact in bf16), the bf16 MFMA accumulates each path in
  * fp32, and the epilogue applies the tensor scales:
@@ -247,8 +253,8 @@ sharq_status sharq_grouped_workspace_bytes(int64_t rows, int32_t E, int64_t K, s
  *   ws:         device workspace of ws_bytes >= sharq_grouped_workspace_bytes,
  *               owned by the caller; calls that share it must not overlap.
  * Errors: INVALID_ARG (null, shapes, K mismatch, ldy < N_e, workspace too
- * small, misaligned buffers), UNSUPPORTED (any format but MXFP4, pattern, not
- * gfx950), HIP. */
+ * small, misaligned buffers), UNSUPPORTED (any format but MXFP4, any pattern
+ * but 2:4, not gfx950), HIP. */
 sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
                                   const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
                                   void* y_dev, int64_t ldy, int32_t out_dtype,
