@@ -60,9 +60,11 @@ GEMM_SRC = os.path.join(ROOT, "fp4_sparse_dense_amd", "csrc", "gemm.hip")
 
 
 def prep_bytes(M, K, norm=True, nv=False, dense=False):
-    """Algorithmic HBM bytes of one prep: bf16 X in once, 0.9375 B/elem out
-    (NVFP4-style: 1 B/elem; plain FP4: 0.53125), gamma once."""
-    out = M * K if nv else (M * K * 17 // 32 if dense else M * K * 15 // 16)
+    """Algorithmic HBM bytes of one prep: bf16 X in once; out 1.1875 B/elem
+    (backbone and residual codes 0.5 each -- the backbone is a masked dense
+    operand -- metadata 0.125, scales 1/32 each; NVFP4-style: scales 1/16 each,
+    1.25 B/elem; plain FP4: 0.53125), gamma once."""
+    out = M * K * 5 // 4 if nv else (M * K * 17 // 32 if dense else M * K * 19 // 16)
     return M * K * 2 + out + (2 * K if norm else 0)
 
 
@@ -71,14 +73,15 @@ def gemm_flops(M, N, K):
 
 
 def gemm_bytes(M, N, K, out_bytes=4, nv=False, dense=False):
-    """Algorithmic HBM bytes of one dual GEMM: prepared A (MXFP4 0.9375 B/elem;
-    NVFP4-style 1 B/elem: scales per 16), the packed weight read once for both
-    paths (MXFP4 0.53125 B/elem; NVFP4-style 0.5625), Y."""
+    """Algorithmic HBM bytes of one dual GEMM: the prepared A it reads (backbone
+    and residual codes and scales, MXFP4 1.0625 B/elem; NVFP4-style 1.125 B/elem,
+    scales per 16; the metadata is not read), the packed weight read once for
+    both paths (MXFP4 0.53125 B/elem; NVFP4-style 0.5625), Y."""
     if nv:
-        return M * K + N * K * 9 // 16 + out_bytes * M * N
+        return M * K * 9 // 8 + N * K * 9 // 16 + out_bytes * M * N
     if dense:
         return M * K * 17 // 32 + N * K * 17 // 32 + out_bytes * M * N
-    return M * K * 15 // 16 + N * K * 17 // 32 + out_bytes * M * N
+    return M * K * 17 // 16 + N * K * 17 // 32 + out_bytes * M * N
 
 
 def source_digest(path):
@@ -398,8 +401,8 @@ def run_moe(args):
     f_gu, f_d = gemm_flops(rows, n_gu, dm), gemm_flops(rows, n_d, dff)
     # algorithmic bytes: prepared rows read once (distinct tokens for gate/up), all
     # experts' weights once, Y once
-    b_gu = T * dm * 15 // 16 + E * n_gu * dm * 17 // 32 + 4 * rows * n_gu
-    b_d = rows * dff * 15 // 16 + E * n_d * dff * 17 // 32 + 4 * rows * n_d
+    b_gu = T * dm * 17 // 16 + E * n_gu * dm * 17 // 32 + 4 * rows * n_gu
+    b_d = rows * dff * 17 // 16 + E * n_d * dff * 17 // 32 + 4 * rows * n_d
     gbs_gu = b_gu / (t[1] * 1e-3) / 1e9
     loads = np.diff(seg)
     return {

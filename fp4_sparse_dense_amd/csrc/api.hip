@@ -116,7 +116,7 @@ sharq_status sharq_act_bytes(int64_t M, int64_t K, int32_t n, int32_t m, int32_t
   s = check_pattern(n, m, fmt);
   if (s) return s;
   const size_t tiles = (size_t)((M + 15) / 16) * (size_t)((K + 127) / 128);
-  sizes[0] = tiles * 512;
+  sizes[0] = tiles * 1024;
   sizes[1] = tiles * 256;
   sizes[2] = tiles * 64;
   sizes[3] = tiles * 1024;

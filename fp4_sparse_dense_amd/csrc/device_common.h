@@ -101,6 +101,42 @@ __device__ __forceinline__ void fp4_unpack2(uint32_t packed, float& lo, float& h
   hi = v[1];
 }
 
+// ---------------------------------------------------------------- 2:4 expansion
+// The kept codes of 32 logical K positions (8 groups) are 16 nibbles (group g
+// in byte g, lower offset in the low nibble) plus 8 metadata nibbles (group g:
+// i0 | i1<<2 in nibble g); codes_lo holds groups 0-3, codes_hi groups 4-7.
+// The result is the 32 dense nibbles, zero codes at dropped positions.  Two
+// groups are handled per dword, one in each 16-bit half, with byte permutes
+// and packed 16-bit shifts.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+template <int H>
+__device__ __forceinline__ uint32_t expand_dword(uint32_t cw, uint32_t mb4, int j) {
+  // code bytes 2H and 2H+1 of cw -> low byte of half 0 and half 1
+  constexpr uint32_t sel = H == 0 ? 0x0C010C00u : 0x0C030C02u;
+  const uint32_t d = __builtin_amdgcn_perm(0u, cw, sel);
+  const uint32_t lo = d & 0x000F000Fu, hi = d & 0x00F000F0u;
+  // metadata byte j -> both halves; the second half keeps the upper nibble
+  const uint32_t msel = 0x0C000C00u | (uint32_t)j | ((uint32_t)j << 16);
+  u16x2 tv = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(0u, mb4, msel));
+  tv = tv >> (u16x2){0, 4};
+  const uint32_t t = __builtin_bit_cast(uint32_t, tv);
+  const uint32_t sl = (t << 2) & 0x000C000Cu;            // 4*i0 per half
+  const uint32_t sh = (t & 0x000C000Cu) - 0x00040004u;   // 4*i1 - 4 per half (i1 >= 1)
+  const u16x2 los = __builtin_bit_cast(u16x2, lo) << __builtin_bit_cast(u16x2, sl);
+  const u16x2 his = __builtin_bit_cast(u16x2, hi) << __builtin_bit_cast(u16x2, sh);
+  return __builtin_bit_cast(uint32_t, los) | __builtin_bit_cast(uint32_t, his);
+}
+
+__device__ __forceinline__ uint4 expand_chunk(uint32_t codes_lo, uint32_t codes_hi, uint32_t meta) {
+  uint4 d;
+  d.x = expand_dword<0>(codes_lo, meta, 0);
+  d.y = expand_dword<1>(codes_lo, meta, 1);
+  d.z = expand_dword<0>(codes_hi, meta, 2);
+  d.w = expand_dword<1>(codes_hi, meta, 3);
+  return d;
+}
+
 // ---------------------------------------------------------------- buffer copies
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

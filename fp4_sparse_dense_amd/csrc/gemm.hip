@@ -6,9 +6,9 @@
 // "Benchmarks": an epilogue fusion sums the two paths.
 //
 // gfx950 has block-scaled FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) but no
-// sparse FP4 MFMA, so the sparse path is a packed-K scheme: Q(S) stays
-// compressed in memory (K/2 codes + 2-bit offsets) and is expanded to dense
-// 4-bit codes on chip right before the MFMA.  Both paths then issue the same
+// sparse FP4 MFMA, so the backbone Q(S) is a masked dense operand: its kept
+// codes in place and zero codes at the dropped positions (the preparation
+// writes it so, beside the 2:4 metadata).  Both paths then issue the same
 // instruction against the same weight fragment into one fp32 accumulator, and
 // one store writes the sum.
 //
@@ -34,43 +34,6 @@ __device__ __forceinline__ v4f mfma_fp4(v8i a, v8i b, v4f c, uint32_t sa, uint32
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
-// ---------------------------------------------------------------------------
-// 2:4 expansion.  The compressed operand of 32 logical K positions (8 groups)
-// is 16 kept nibbles (group g in byte g, lower offset in the low nibble) plus
-// 8 metadata nibbles (group g: i0 | i1<<2 in nibble g); codes_lo holds groups
-// 0-3, codes_hi groups 4-7.  The result is 32
-// dense nibbles with zero codes at dropped positions.  Two groups are handled
-// per dword, one in each 16-bit half, with byte permutes and packed shifts.
-// ---------------------------------------------------------------------------
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-
-template <int H>
-__device__ __forceinline__ uint32_t expand_dword(uint32_t cw, uint32_t mb4, int j) {
-  // code bytes 2H and 2H+1 of cw -> low byte of half 0 and half 1
-  constexpr uint32_t sel = H == 0 ? 0x0C010C00u : 0x0C030C02u;
-  const uint32_t d = __builtin_amdgcn_perm(0u, cw, sel);
-  const uint32_t lo = d & 0x000F000Fu, hi = d & 0x00F000F0u;
-  // metadata byte j -> both halves; the second half keeps the upper nibble
-  const uint32_t msel = 0x0C000C00u | (uint32_t)j | ((uint32_t)j << 16);
-  u16x2 tv = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(0u, mb4, msel));
-  tv = tv >> (u16x2){0, 4};
-  const uint32_t t = __builtin_bit_cast(uint32_t, tv);
-  const uint32_t sl = (t << 2) & 0x000C000Cu;            // 4*i0 per half
-  const uint32_t sh = (t & 0x000C000Cu) - 0x00040004u;   // 4*i1 - 4 per half (i1 >= 1)
-  const u16x2 los = __builtin_bit_cast(u16x2, lo) << __builtin_bit_cast(u16x2, sl);
-  const u16x2 his = __builtin_bit_cast(u16x2, hi) << __builtin_bit_cast(u16x2, sh);
-  return __builtin_bit_cast(uint32_t, los) | __builtin_bit_cast(uint32_t, his);
-}
-
-__device__ __forceinline__ uint4 expand_chunk(uint32_t codes_lo, uint32_t codes_hi, uint32_t meta) {
-  uint4 d;
-  d.x = expand_dword<0>(codes_lo, meta, 0);
-  d.y = expand_dword<1>(codes_lo, meta, 1);
-  d.z = expand_dword<0>(codes_hi, meta, 2);
-  d.w = expand_dword<1>(codes_hi, meta, 3);
-  return d;
-}
-
 __device__ __forceinline__ void store_out(const GemmArgs& g, int64_t row, int64_t col, float v) {
   if (g.out_bf16) {
     uint32_t u = __float_as_uint(v);
@@ -87,7 +50,7 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, int64_t row, int64_
 // of RBG 16-row blocks); its NW waves split K (wave w takes K tiles w, w+NW,
 // ...) and read their fragments straight from global memory -- in the tiled
 // layout a fragment is 64 lanes x 16 contiguous bytes, so each read is one
-// contiguous KiB.  The backbone is expanded in registers.  The NW partial
+// contiguous KiB.  The NW partial
 // sums meet in LDS and are added in wave order.  Both paths read the weight
 // scales through one load: the API admits only views of one scale array.
 // ---------------------------------------------------------------------------
@@ -131,10 +94,9 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_splitk(GemmArgs g) {
         sr[c][r] = g.r_scales[((int64_t)ktc * RB + rb) * 64 + lane];
         ar[c][r] = as_operand(rq);
         if constexpr (!DENSE) {
-          const uint2 sq = *reinterpret_cast<const uint2*>(g.s_codes + tile * 512 + lane * 8);
-          const uint32_t mq = *reinterpret_cast<const uint32_t*>(g.s_meta + tile * 256 + lane * 4);
+          const uint4 sq = *reinterpret_cast<const uint4*>(g.s_codes + tile * 1024 + lane * 16);
           ss[c][r] = g.s_scales[((int64_t)ktc * RB + rb) * 64 + lane];
-          as[c][r] = as_operand(expand_chunk(sq.x, sq.y, mq));
+          as[c][r] = as_operand(sq);
         }
       }
     }
@@ -172,14 +134,12 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_splitk(GemmArgs g) {
 // Tiled kernel (M > 64).
 //
 // Operands arrive in the MFMA-tiled layout (16 rows x 128 K per tile, lane
-// order), so every global -> LDS copy is a contiguous run: one 1 KiB dense
-// tile per instruction, the 512-byte compressed tile and its 256-byte
-// metadata, and the scale bytes of a whole tile edge in one go.  Copies are
-// buffer loads with an LDS destination (no register staging).  Tiles past the
-// padded row count get an out-of-range buffer offset, which reads as zero.
-// The compressed backbone of a tile lands in the first 768 bytes of the 1 KiB
-// slot it will become, and the wave that copied it expands it in place.  Each
-// weight fragment feeds the sparse and the dense MFMA of the same output tile.
+// order), so every global -> LDS copy is a contiguous run: one 1 KiB tile
+// (backbone, residual or weight) per instruction and the scale bytes of a
+// whole tile edge in one go.  Copies are buffer loads with an LDS destination
+// (no register staging).  Tiles past the padded row count get an out-of-range
+// buffer offset, which reads as zero.  Each weight fragment feeds the sparse
+// and the dense MFMA of the same output tile.
 // ---------------------------------------------------------------------------
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 // lane mask of lanes 0 .. n-1 (n <= 64)
@@ -269,8 +229,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     y_cols = g.N / g.E;
   }
 
-  const u32x4 rs_sc = make_desc(g.s_codes, (uint64_t)RB * KT * 512);
-  const u32x4 rs_sm = make_desc(g.s_meta, (uint64_t)RB * KT * 256);
+  const u32x4 rs_sc = make_desc(g.s_codes, (uint64_t)RB * KT * 1024);
   const u32x4 rs_ss = make_desc(g.s_scales, (uint64_t)RB * KT * 64);
   const u32x4 rs_rc = make_desc(g.r_codes, (uint64_t)RB * KT * 1024);
   const u32x4 rs_rs = make_desc(g.r_scales, (uint64_t)RB * KT * 64);
@@ -290,19 +249,16 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   static_assert(!(DENSE && GROUPED), "the grouped layer runs both paths");
   constexpr int kSB = C::kMB / C::kWaves;
   constexpr int kWB = (C::kNB + C::kWaves - 1) / C::kWaves;
-  constexpr int kPerA = DENSE ? 1 : 3;                 // copies per A-side block
+  constexpr int kPerA = DENSE ? 1 : 2;                 // copies per A-side block
   constexpr int kEdges = DENSE ? 2 : 3;                // scale edges
   constexpr int kItems = kPerA * kSB + kWB + 1;
   static_assert(C::kWaves >= kEdges, "one wave per scale edge");
 
-  uint32_t offR[kSB], offC[kSB], offM[kSB];
+  uint32_t offA[kSB];   // both A-side operands: 1 KiB tiles, rb-major then K
 #pragma unroll
   for (int i = 0; i < kSB; ++i) {
     const int64_t rb = rb0 + wave + i * C::kWaves;
-    const bool ok = rb < rb_end;
-    offR[i] = ok ? (uint32_t)(rb * KT) * 1024u + lane * 16 : kOOB;
-    offC[i] = ok ? (uint32_t)(rb * KT) * 512u + lane * 16 : kOOB;   // lanes 0..31
-    offM[i] = ok ? (uint32_t)(rb * KT) * 256u + lane * 16 : kOOB;   // lanes 0..15
+    offA[i] = rb < rb_end ? (uint32_t)(rb * KT) * 1024u + lane * 16 : kOOB;
   }
   int wblk[kWB];
   uint32_t offW[kWB];
@@ -325,17 +281,15 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   const uint32_t lds_edge = edge == 0 ? C::kOffSS : (edge == 1 ? C::kOffSR : C::kOffSW);
   const uint64_t lanes_edge = edge == 2 ? low_lanes(C::kNB * 4) : low_lanes(C::kMB * 4);
 
-  // copy item `it` of K step ks into the LDS stage at st: 3 per A-side block
-  // (dense codes, compressed codes, metadata), one per weight block, then the
-  // scale edge
+  // copy item `it` of K step ks into the LDS stage at st: per A-side block the
+  // residual tile and (with a backbone) the backbone tile, one per weight
+  // block, then the scale edge
   auto issue_item = [&](int it, int ks, uint32_t st) {
     if (it < kPerA * kSB) {
       const int i = it / kPerA, kind = it % kPerA;
       const int b = wave + i * C::kWaves;
-      const uint32_t as = st + C::kOffAS + b * 1024;
-      if (kind == 0) lds_dma16(rs_rc, st + C::kOffAR + b * 1024, offR[i], (uint32_t)ks * 1024);
-      else if (kind == 1) lds_dma16_lanes(rs_sc, as, offC[i], (uint32_t)ks * 512, 0xFFFFFFFFull);
-      else lds_dma16_lanes(rs_sm, as + 512, offM[i], (uint32_t)ks * 256, 0xFFFFull);
+      if (kind == 0) lds_dma16(rs_rc, st + C::kOffAR + b * 1024, offA[i], (uint32_t)ks * 1024);
+      else lds_dma16(rs_sc, st + C::kOffAS + b * 1024, offA[i], (uint32_t)ks * 1024);
     } else if (it < kPerA * kSB + kWB) {
       const int i = it - kPerA * kSB;
       lds_dma16(rs_wc, st + C::kOffB + wblk[i] * 1024, offW[i], (uint32_t)ks * 1024);
@@ -347,33 +301,6 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int it = 0; it < kItems; ++it) issue_item(it, ks, st);
   };
-
-  // Expand this wave's backbone blocks of the stage at st in place: every lane
-  // reads its 12 compressed bytes (8 code bytes at 8*lane, 4 metadata bytes at
-  // 512 + 4*lane), then writes its 16 dense bytes (a block belongs to one
-  // wave).  The writes overlap other lanes' reads, which is safe because the
-  // LDS executes one wave's accesses in issue order.  The reads are issued
-  // early and the arithmetic is left to interleave with MFMAs.
-  struct Packed { uint32_t lo[kSB], hi[kSB], mt[kSB]; };
-  auto expand_read = [&](const uint8_t* st) {
-    Packed p;
-#pragma unroll
-    for (int i = 0; i < kSB; ++i) {
-      const uint8_t* blk = st + C::kOffAS + (wave + i * C::kWaves) * 1024;
-      const uint2 sq = *reinterpret_cast<const uint2*>(blk + lane * 8);
-      p.lo[i] = sq.x;
-      p.hi[i] = sq.y;
-      p.mt[i] = *reinterpret_cast<const uint32_t*>(blk + 512 + lane * 4);
-    }
-    return p;
-  };
-  auto expand_write = [&](uint8_t* st, const Packed& p) {
-#pragma unroll
-    for (int i = 0; i < kSB; ++i)
-      *reinterpret_cast<uint4*>(st + C::kOffAS + (wave + i * C::kWaves) * 1024 + lane * 16) =
-          expand_chunk(p.lo[i], p.hi[i], p.mt[i]);
-  };
-  auto expand_store = [&](uint8_t* st) { expand_write(st, expand_read(st)); };
 
   const int wm = wave / NWN, wn = wave % NWN;
   v4f acc[C::kWMT][C::kWNT];
@@ -408,13 +335,13 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   };
 
   // Pipeline: an LDS ring of NST stages, one K step each.  The prologue copies
-  // steps 0..NST-1; step ks runs the backbone MFMAs of ks (fragments already
-  // in registers) while this wave expands its blocks of step ks+1, meets the
-  // other waves at one barrier, then runs the residual MFMAs of ks while it
-  // issues the copy of step ks+NST (into the slot of step ks, whose data is
-  // all in registers by now) and reads the fragments of step ks+1.  Before
-  // expanding step ks+1 a wave waits until only the copies of later steps are
-  // outstanding (loads retire in issue order; each step is kItems copies).
+  // steps 0..NST-1; step ks waits until only this wave's copies of later steps
+  // than ks+1 are outstanding (loads retire in issue order; each step is
+  // kItems copies), runs the backbone MFMAs of ks (fragments already in
+  // registers), meets the other waves at one barrier -- after it step ks+1 is
+  // in LDS and nobody reads step ks's slot any more -- then runs the residual
+  // MFMAs of ks while it issues the copy of step ks+NST into that slot and
+  // reads the fragments of step ks+1.
   static_assert(kItems * (NST > 2 ? NST - 2 : 1) < 64, "vmcnt range");
   auto stage_off = [&](int ks) { return (uint32_t)((ks % NST) * C::kStage); };
   auto wait_stages = [&](int newer) {
@@ -431,7 +358,6 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   const int pre = KT < NST ? KT : NST;   // steps copied before the loop
   for (int s = 0; s < pre; ++s) issue(s, lds0 + stage_off(s));
   wait_stages(pre - 1);
-  if constexpr (!DENSE) expand_store(smem + stage_off(0));
   __syncthreads();
   read_all(smem + stage_off(0));
 
@@ -439,19 +365,11 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   auto step = [&](int ks, int newer, auto copy_tag) {
     constexpr bool kCopy = decltype(copy_tag)::value;
     wait_stages(newer);
-    const Packed pk = expand_read(smem + stage_off(ks + 1));
 #pragma unroll
     for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
       for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
-    expand_write(smem + stage_off(ks + 1), pk);
-    // schedule: each backbone MFMA followed by a few expansion instructions,
-    // so the matrix pipe never waits for the expansion
-#pragma unroll
-    for (int k = 0; k < C::kWMT * C::kWNT; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // up to four VALU
-    }
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     const uint32_t cst = lds0 + stage_off(ks);   // slot of step ks, free after the barrier
     const uint8_t* nx = smem + stage_off(ks + 1);

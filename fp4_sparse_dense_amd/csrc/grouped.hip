@@ -12,9 +12,9 @@
 //      first 16-row block in the gathered activation (segments padded to whole
 //      blocks) and the number of 256-row M tiles before it;
 //   2. gather  (one wave per gathered 16-row block and K tile): copies each
-//      routed row's codes, metadata and scales from the source activation (row
-//      row_index[i], or i) into expert order, writing zero-input blocks (codes
-//      0, metadata 0x44, scales 0) for the padding rows;
+//      routed row's backbone and residual codes and scales (the GEMM does not
+//      read the metadata) from the source activation (row row_index[i], or i)
+//      into expert order, writing zero codes and scales for the padding rows;
 //   3. the tiled dual GEMM with one workgroup per (expert, M tile, N tile).
 #include "device_common.h"
 #include "launch.h"
@@ -30,7 +30,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
   int64_t blocks;        // 16-row blocks of the gathered activation (upper bound)
-  size_t r_codes, s_codes, s_meta, s_scales, r_scales, seg, pseg, tprefix, total;
+  size_t r_codes, s_codes, s_scales, r_scales, seg, pseg, tprefix, total;
 };
 
 WsLayout ws_layout(int64_t rows, int E, int K) {
@@ -39,8 +39,7 @@ WsLayout ws_layout(int64_t rows, int E, int K) {
   L.blocks = (rows + 15 * (int64_t)E + 15) / 16;
   size_t o = 0;
   L.r_codes = o;  o = align_up(o + (size_t)L.blocks * KT * 1024);
-  L.s_codes = o;  o = align_up(o + (size_t)L.blocks * KT * 512);
-  L.s_meta = o;   o = align_up(o + (size_t)L.blocks * KT * 256);
+  L.s_codes = o;  o = align_up(o + (size_t)L.blocks * KT * 1024);
   L.s_scales = o; o = align_up(o + (size_t)L.blocks * KT * 64);
   L.r_scales = o; o = align_up(o + (size_t)L.blocks * KT * 64);
   L.seg = o;      o = align_up(o + (size_t)(E + 1) * 8);
@@ -80,8 +79,8 @@ __global__ __launch_bounds__(256) void grouped_setup_kernel(const int64_t* __res
 }
 
 struct GatherArgs {
-  const uint8_t *s_codes, *s_meta, *s_scales, *r_codes, *r_scales;   // source activation
-  uint8_t *g_s_codes, *g_s_meta, *g_s_scales, *g_r_codes, *g_r_scales;
+  const uint8_t *s_codes, *s_scales, *r_codes, *r_scales;   // source activation
+  uint8_t *g_s_codes, *g_s_scales, *g_r_codes, *g_r_scales;
   const int32_t* row_index;
   const int64_t *seg, *pseg;
   int64_t src_rows, src_blocks, dst_blocks;
@@ -103,9 +102,8 @@ __global__ __launch_bounds__(256) void grouped_gather_kernel(GatherArgs a) {
   const int r = lane & 15, c4 = lane >> 4;
   const int64_t lr = (rbp - a.pseg[e]) * 16 + r;      // row within the expert
   const int64_t n = a.seg[e + 1] - a.seg[e];
-  uint4 rc = make_uint4(0, 0, 0, 0);
-  uint2 sc = make_uint2(0, 0);
-  uint32_t mt = 0x44444444u, ssc = 0, rsc = 0;
+  uint4 rc = make_uint4(0, 0, 0, 0), sc = make_uint4(0, 0, 0, 0);
+  uint32_t ssc = 0, rsc = 0;
   if (lr < n) {
     const int64_t i = a.seg[e] + lr;
     const int64_t src = a.row_index ? (int64_t)a.row_index[i] : i;
@@ -113,16 +111,14 @@ __global__ __launch_bounds__(256) void grouped_gather_kernel(GatherArgs a) {
       const int64_t sb = src / 16, st = sb * a.KT + kt;
       const int sl = c4 * 16 + (int)(src % 16);
       rc = *reinterpret_cast<const uint4*>(a.r_codes + st * 1024 + sl * 16);
-      sc = *reinterpret_cast<const uint2*>(a.s_codes + st * 512 + sl * 8);
-      mt = *reinterpret_cast<const uint32_t*>(a.s_meta + st * 256 + sl * 4);
+      sc = *reinterpret_cast<const uint4*>(a.s_codes + st * 1024 + sl * 16);
       ssc = a.s_scales[((int64_t)kt * a.src_blocks + sb) * 64 + sl];
       rsc = a.r_scales[((int64_t)kt * a.src_blocks + sb) * 64 + sl];
     }
   }
   const int64_t dt = rbp * a.KT + kt;
   *reinterpret_cast<uint4*>(a.g_r_codes + dt * 1024 + lane * 16) = rc;
-  *reinterpret_cast<uint2*>(a.g_s_codes + dt * 512 + lane * 8) = sc;
-  *reinterpret_cast<uint32_t*>(a.g_s_meta + dt * 256 + lane * 4) = mt;
+  *reinterpret_cast<uint4*>(a.g_s_codes + dt * 1024 + lane * 16) = sc;
   a.g_s_scales[((int64_t)kt * a.dst_blocks + rbp) * 64 + lane] = (uint8_t)ssc;
   a.g_r_scales[((int64_t)kt * a.dst_blocks + rbp) * 64 + lane] = (uint8_t)rsc;
 }
@@ -146,9 +142,9 @@ hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
 
   GatherArgs g;
-  g.s_codes = a.gemm.s_codes; g.s_meta = a.gemm.s_meta; g.s_scales = a.gemm.s_scales;
+  g.s_codes = a.gemm.s_codes; g.s_scales = a.gemm.s_scales;
   g.r_codes = a.gemm.r_codes; g.r_scales = a.gemm.r_scales;
-  g.g_r_codes = a.ws + L.r_codes; g.g_s_codes = a.ws + L.s_codes; g.g_s_meta = a.ws + L.s_meta;
+  g.g_r_codes = a.ws + L.r_codes; g.g_s_codes = a.ws + L.s_codes;
   g.g_s_scales = a.ws + L.s_scales; g.g_r_scales = a.ws + L.r_scales;
   g.row_index = a.row_index;
   g.seg = seg; g.pseg = pseg;
@@ -164,7 +160,7 @@ hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   }
 
   GemmArgs m = a.gemm;
-  m.s_codes = g.g_s_codes; m.s_meta = g.g_s_meta; m.s_scales = g.g_s_scales;
+  m.s_codes = g.g_s_codes; m.s_meta = nullptr; m.s_scales = g.g_s_scales;
   m.r_codes = g.g_r_codes; m.r_scales = g.g_r_scales;
   m.a_blocks = L.blocks;
   m.M = a.rows;

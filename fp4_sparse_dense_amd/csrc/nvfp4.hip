@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256) void nv_decompose_kernel(NvPrepArgs a) {
 
   if (!RESID) {
     if (kb < a.KB) {
-      *reinterpret_cast<uint2*>(a.o.s_codes + tile * 512 + lane * 8) = make_uint2(scodes[0], scodes[1]);
+      *reinterpret_cast<uint4*>(a.o.s_codes + tile * 1024 + lane * 16) = expand_chunk(scodes[0], scodes[1], meta);
       *reinterpret_cast<uint32_t*>(a.o.s_meta + tile * 256 + lane * 4) = meta;
       *reinterpret_cast<uint16_t*>(a.o.s_scales + sc) = (uint16_t)sbytes;
     }
@@ -462,30 +462,6 @@ __device__ __forceinline__ void deq32(uint4 q, uint32_t sb, bf16x8 (&o)[4]) {
   o[3] = deq8(q.w, s1);
 }
 
-// 2:4 expansion of one lane's compressed operand (16 kept codes + 8 offset
-// nibbles) into 32 dense codes.
-__device__ __forceinline__ uint32_t expand_dword_nv(uint32_t codes2, uint32_t meta2) {
-  // codes2: bytes g0, g1 of two groups (low nibble = lower kept offset); meta2: their nibbles
-  uint32_t out = 0u;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t c = (codes2 >> (8 * h)) & 0xFFu;
-    const uint32_t m = (meta2 >> (4 * h)) & 0xFu;
-    const uint32_t i0 = m & 3u, i1 = m >> 2;
-    out |= ((c & 0xFu) << (4 * i0 + 16 * h)) | ((c >> 4) << (4 * i1 + 16 * h));
-  }
-  return out;
-}
-
-__device__ __forceinline__ uint4 expand24(uint2 codes, uint32_t meta) {
-  uint4 d;
-  d.x = expand_dword_nv(codes.x & 0xFFFFu, meta & 0xFFu);
-  d.y = expand_dword_nv(codes.x >> 16, (meta >> 8) & 0xFFu);
-  d.z = expand_dword_nv(codes.y & 0xFFFFu, (meta >> 16) & 0xFFu);
-  d.w = expand_dword_nv(codes.y >> 16, meta >> 24);
-  return d;
-}
-
 __device__ __forceinline__ v4f mfma_bf16(bf16x8 a, bf16x8 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -515,9 +491,8 @@ __global__ __launch_bounds__(64 * NW) void nv_dual_gemm_kernel(GemmArgs g) {
 
   constexpr int CH = (RBG == 1 ? 8 : (RBG == 2 ? 4 : 2)) * 4 / NW;
   for (int base = 0; base < KT; base += NW * CH) {
-    uint4 wq[CH], rq[CH][RBG];
-    uint2 sq[CH][RBG];
-    uint32_t wsb[CH], mq[CH][RBG], ssb[CH][RBG], rsb[CH][RBG];
+    uint4 wq[CH], rq[CH][RBG], sq[CH][RBG];
+    uint32_t wsb[CH], ssb[CH][RBG], rsb[CH][RBG];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       // clamped tile index; a tile past K gets a zero weight fragment
@@ -532,8 +507,7 @@ __global__ __launch_bounds__(64 * NW) void nv_dual_gemm_kernel(GemmArgs g) {
         const int64_t tile = rb * KT + ktc;
         const int64_t sc = ((int64_t)ktc * RB + rb) * 128 + 2 * lane;
         rq[c][r] = *reinterpret_cast<const uint4*>(g.r_codes + tile * 1024 + lane * 16);
-        sq[c][r] = *reinterpret_cast<const uint2*>(g.s_codes + tile * 512 + lane * 8);
-        mq[c][r] = *reinterpret_cast<const uint32_t*>(g.s_meta + tile * 256 + lane * 4);
+        sq[c][r] = *reinterpret_cast<const uint4*>(g.s_codes + tile * 1024 + lane * 16);
         ssb[c][r] = *reinterpret_cast<const uint16_t*>(g.s_scales + sc);
         rsb[c][r] = *reinterpret_cast<const uint16_t*>(g.r_scales + sc);
       }
@@ -545,7 +519,7 @@ __global__ __launch_bounds__(64 * NW) void nv_dual_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < RBG; ++r) {
         bf16x8 x[4];
-        deq32(expand24(sq[c][r], mq[c][r]), ssb[c][r], x);
+        deq32(sq[c][r], ssb[c][r], x);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acs[r] = mfma_bf16(x[j], b[j], acs[r]);
         deq32(rq[c][r], rsb[c][r], x);

@@ -32,7 +32,7 @@ constexpr int kRowsPerBlock = 4;
 // ---------------------------------------------------------------------------
 struct Block32 {
   uint4 r_codes;     // 32 R nibbles
-  uint2 s_codes;     // 16 kept S nibbles: groups 0-3, groups 4-7
+  uint4 s_codes;     // 32 S nibbles: the kept codes in place, zero codes at dropped positions
   uint32_t meta;     // 8 metadata nibbles
   uint32_t s_e8, r_e8;
 };
@@ -186,7 +186,7 @@ __device__ __forceinline__ Block32 decompose32(float (&v)[32]) {
 
   Block32 o;
   o.r_codes = make_uint4(rc[0], rc[1], rc[2], rc[3]);
-  o.s_codes = make_uint2(lo, hi);
+  o.s_codes = DENSE ? make_uint4(0, 0, 0, 0) : expand_chunk(lo, hi, meta);
   o.meta = meta;
   o.s_e8 = (uint32_t)(es + 127);
   o.r_e8 = (uint32_t)(er + 127);
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
       const int64_t sc = ((int64_t)kt * RB + rb) * 64 + tl;
       o.r_scales[sc] = (uint8_t)b.r_e8;
       if constexpr (!DENSE) {
-        *reinterpret_cast<uint2*>(o.s_codes + tile * 512 + tl * 8) = b.s_codes;
+        *reinterpret_cast<uint4*>(o.s_codes + tile * 1024 + tl * 16) = b.s_codes;
         *reinterpret_cast<uint32_t*>(o.s_meta + tile * 256 + tl * 4) = b.meta;
         o.s_scales[sc] = (uint8_t)b.s_e8;
       }

@@ -31,10 +31,14 @@
  *    [128*kb + 32*(l/16), +32).  Rows are padded to RB*16 (RB = ceil(rows/16))
  *    and K to KB*128 (KB = ceil(K/128)); padding holds zero codes and zero
  *    scale bytes.  Per tile (rb, kb), tiles ordered rb-major then kb:
- *      dense codes    1024 B: lane l at 16*l (its 32 codes)
- *      2:4 codes       512 B: lane l at 8*l, its 16 kept codes (groups 0-3 in
- *                             the first 4 bytes, groups 4-7 in the next 4)
+ *      codes          1024 B: lane l at 16*l (its 32 codes).  The backbone is
+ *                             stored this way too, as a masked dense operand:
+ *                             its kept codes in place, zero codes at the
+ *                             dropped positions (gfx950 has no sparse FP4
+ *                             MFMA; expanding a compressed form on chip cost
+ *                             the GEMM more than the bytes it saves)
  *      2:4 metadata    256 B: lane l at 4*l, nibble g = group g of the lane
+ *                             (the mask; the GEMM does not read it)
  *    Scale bytes are K-step-major: [KB][RB][64], byte l of (kb, rb) is the
  *    E8M0 of lane l's 32-block.  Canonical row-major arrays follow by
  *    un-tiling (the tests do exactly that before comparing).
@@ -92,9 +96,10 @@ typedef enum { SHARQ_PATH_SPARSE = 0, SHARQ_PATH_DENSE = 1 } sharq_path;
 /* A scale view: how one GEMM path reads the weight's block scales.
  * base: device pointer to the tiled scale bytes (MXFP4: E8M0 [KB][NB][64];
  * NVFP4: E4M3 [KB][NB][128] followed by the tensor scale); ld: bytes between
- * K steps (NB*64 or NB*128); block: K elements per scale byte (32 or 16).  On gfx950 both paths run the same block-scaled
- * MFMA on dense 4-bit operands (the sparse operand is expanded on chip), so
- * sharq_pack_weight sets both views to the same array and layout. */
+ * K steps (NB*64 or NB*128); block: K elements per scale byte (32 or 16).
+ * On gfx950 both paths run the same MFMA on dense 4-bit operands (the
+ * backbone is a masked dense operand), so sharq_pack_weight sets both views
+ * to the same array and layout. */
 typedef struct {
   const uint8_t* base;
   int64_t ld;
@@ -117,7 +122,8 @@ typedef struct {
 } sharq_weight;
 
 /* Prepared activation (output of sharq_prepare), 2:4 and MXFP4, tiled layout:
- *   s_codes   2:4 codes of S: E2M1 of the kept entries in k order (RB*KB*512 B)
+ *   s_codes   codes of S: E2M1 of the kept entries in place, the zero code at
+ *             dropped positions (RB*KB*1024 B)
  *   s_meta    2:4 metadata: per group of 4 the kept offsets i0<i1 as the
  *             nibble i0 | i1<<2 (RB*KB*256 B)
  *   s_scales  E8M0 of S per 32 logical positions ([KB][RB][64])
@@ -154,7 +160,7 @@ sharq_status sharq_weight_bytes(int64_t N, int64_t K, int32_t fmt,
                                 size_t* codes_bytes, size_t* scales_bytes);
 
 /* Byte sizes of the five prepared-activation buffers, in the order
- * s_codes, s_meta, s_scales, r_codes, r_scales (MXFP4 tiled: RB*KB*{512, 256,
+ * s_codes, s_meta, s_scales, r_codes, r_scales (MXFP4 tiled: RB*KB*{1024, 256,
  * 64, 1024, 64}; NVFP4: the scale buffers hold E4M3 scales, the tensor scale
  * and, for r_scales, the preparation's scratch).  M == 0 gives zeros.
  * Pattern (n,m) == (0,4) means no backbone: the plain FP4 linear (the dense
@@ -210,9 +216,9 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
 /* Y[M,N] = deq(Q(S)) deq(W)^T + deq(Q(R)) deq(W)^T with one epilogue store.
  * SharQ abstract: a sparse FP4 GEMM on the backbone and a dense FP4 GEMM on
  * the residual; README "Benchmarks": the epilogue fusion sums them.
- * On gfx950 the compressed 2:4 operand is expanded to dense 4-bit codes on
- * chip and both paths run block-scaled MXFP4 MFMA into one fp32 accumulator,
- * reading each weight tile once for both paths.
+ * On gfx950 the backbone is a masked dense operand and both paths run
+ * block-scaled MXFP4 MFMA into one fp32 accumulator, reading each weight tile
+ * once for both paths.
  * An activation prepared with pattern 0:4 runs the dense GEMM alone:
  * Y = deq(Q(v)) deq(W)^T (the plain FP4 linear).
  * NVFP4: the E4M3 scales cannot ride the MX MFMA, so each code is expanded

@@ -28,12 +28,6 @@ def untile_dense(buf, rows, K, label="codes"):
     return _crop(t.reshape(RB * 16, KB * 64), rows, K // 2, label)
 
 
-def untile_sparse_codes(buf, rows, K):
-    RB, KB = _dims(rows, K)
-    t = np.asarray(buf).reshape(RB, KB, 4, 16, 8).transpose(0, 3, 1, 2, 4)
-    return _crop(t.reshape(RB * 16, KB * 32), rows, K // 4, "s_codes")
-
-
 def untile_meta(buf, rows, K):
     RB, KB = _dims(rows, K)
     t = np.asarray(buf).reshape(RB, KB, 4, 16, 4).transpose(0, 3, 1, 2, 4)
@@ -47,7 +41,7 @@ def untile_scales(buf, rows, K, label="scales"):
 
 
 def untile_act(raw: dict, M: int, K: int) -> dict:
-    return dict(s_codes=untile_sparse_codes(raw["s_codes"], M, K),
+    return dict(s_codes=untile_dense(raw["s_codes"], M, K, "s_codes"),
                 s_meta=untile_meta(raw["s_meta"], M, K),
                 s_scales=untile_scales(raw["s_scales"], M, K, "s_scales"),
                 r_codes=untile_dense(raw["r_codes"], M, K, "r_codes"),
@@ -65,7 +59,11 @@ def dev_bf16(bits):
 
 
 def assert_prep_equal(gpu: dict, ref: dict, label: str):
-    """Byte-exact comparison of the five prepared arrays, with a readable first mismatch."""
+    """Byte-exact comparison of the five prepared arrays, with a readable first
+    mismatch.  The GPU stores the backbone as a masked dense operand (kept codes
+    in place, zero codes at dropped positions): that is the oracle's dense S
+    nibbles, packed two per byte."""
+    ref = dict(ref, s_codes=O.pack_nibbles(ref["s_nib"]))
     for f in FIELDS:
         g, r = gpu[f], ref[f]
         assert g.shape == r.shape, (label, f, g.shape, r.shape)
@@ -100,7 +98,7 @@ def untile_scales_nv(buf, rows, K, label="scales"):
 def untile_act_nv(raw: dict, M: int, K: int) -> dict:
     s_scales, g_s = untile_scales_nv(raw["s_scales"], M, K, "s_scales")
     r_scales, g_r = untile_scales_nv(raw["r_scales"], M, K, "r_scales")
-    return dict(s_codes=untile_sparse_codes(raw["s_codes"], M, K),
+    return dict(s_codes=untile_dense(raw["s_codes"], M, K, "s_codes"),
                 s_meta=untile_meta(raw["s_meta"], M, K),
                 s_scales=s_scales, r_codes=untile_dense(raw["r_codes"], M, K, "r_codes"),
                 r_scales=r_scales, g_s=g_s, g_r=g_r)

@@ -57,9 +57,10 @@ def test_size_queries(lib):
     assert (cb.value, sb.value) == (6144 * 2048, 6144 * 128)
     sizes = (C.c_size_t * 5)()
     assert lib.sharq_act_bytes(2048, 4096, 2, 4, 0, sizes) == 0
-    assert list(sizes) == [2048 * 1024, 2048 * 512, 2048 * 128, 2048 * 2048, 2048 * 128]
-    # prep writes 0.9375 B per element
-    assert sum(sizes) == int(2048 * 4096 * 0.9375)
+    assert list(sizes) == [2048 * 2048, 2048 * 512, 2048 * 128, 2048 * 2048, 2048 * 128]
+    # prep writes 1.1875 B per element: backbone and residual codes 0.5 each,
+    # metadata 0.125, two scale bytes per 32
+    assert sum(sizes) == int(2048 * 4096 * 1.1875)
     assert lib.sharq_act_bytes(0, 4096, 2, 4, 0, sizes) == 0 and sum(sizes) == 0
 
 
@@ -76,7 +77,7 @@ def test_size_queries_nvfp4(lib):
     sizes = (C.c_size_t * 5)()
     assert lib.sharq_act_bytes(8, 4096, 2, 4, 1, sizes) == 0
     RB = 1
-    assert list(sizes)[0::2][:2] == [RB * KB * 512, RB * KB * 128 + 256]
+    assert list(sizes)[0::2][:2] == [RB * KB * 1024, RB * KB * 128 + 256]
     assert sizes[1] == RB * KB * 256 and sizes[3] == RB * KB * 1024
     assert sizes[4] == RB * KB * 128 + 256 + 256 + 256 + 256
     assert lib.sharq_act_bytes(0, 4096, 2, 4, 1, sizes) == 0 and sum(sizes) == 0
@@ -182,8 +183,8 @@ def test_grouped_rejects_before_launch(lib):
     assert lib.sharq_grouped_workspace_bytes(100, 1025, 256, C.byref(n)) == _lib.ERR_INVALID_ARG
     assert lib.sharq_grouped_workspace_bytes(100, 8, 250, C.byref(n)) == _lib.ERR_INVALID_ARG
     assert lib.sharq_grouped_workspace_bytes(100, 8, 256, C.byref(n)) == _lib.OK
-    # gathered rows of 8 experts padded to 16-row blocks: (100 + 8*15 + 15) // 16 blocks x 2 K tiles x 1920 B
-    assert n.value >= (100 + 8 * 15 + 15) // 16 * 2 * 1920
+    # gathered rows of 8 experts padded to 16-row blocks: (100 + 8*15 + 15) // 16 blocks x 2 K tiles x 2176 B
+    assert n.value >= (100 + 8 * 15 + 15) // 16 * 2 * 2176
     a = _act()
     a.layout_version = _lib.SHARQ_ABI_VERSION
     a.M, a.K, a.n, a.m = 64, 256, 2, 4
