@@ -508,7 +508,7 @@ int grouped_tile_m() { return kTileM; }
 
 // M tiles per XCD region for a tm x tn tile grid split into 8 equal regions of
 // bm x bn tiles: the shape that minimises the operand bytes one XCD reads
-// (bm activation tiles at 0.9375 B/elem, bn weight tiles at 0.53125 B/elem);
+// (bm activation tiles at 1.0625 B/elem, bn weight tiles at 0.53125 B/elem);
 // 0 when no such split exists.
 static int xcd_region_m(int64_t tm, int64_t tn, int K) {
   const int64_t T = tm * tn;
@@ -520,7 +520,7 @@ static int xcd_region_m(int64_t tm, int64_t tn, int K) {
     if (tm % bm || per % bm) continue;
     const int64_t bn = per / bm;
     if (tn % bn) continue;
-    const double cost = (double)bm * kTileM * 0.9375 + (double)bn * kTileN * 0.53125;
+    const double cost = (double)bm * kTileM * 1.0625 + (double)bn * kTileN * 0.53125;
     if (best == 0 || cost < best_cost) { best = (int)bm; best_cost = cost; }
   }
   (void)K;
