@@ -49,32 +49,73 @@ WsLayout ws_layout(int64_t rows, int E, int K) {
   return L;
 }
 
-__global__ __launch_bounds__(256) void grouped_setup_kernel(const int64_t* __restrict__ seg_in, int E, int64_t rows,
-                                                           int tile_m, int64_t* __restrict__ seg,
-                                                           int64_t* __restrict__ pseg,
-                                                           int32_t* __restrict__ tprefix) {
-  __shared__ int64_t s[kMaxExperts + 1];
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
-    int64_t v = seg_in[e];
-    s[e] = v < 0 ? 0 : (v > rows ? rows : v);
+// Setup, one workgroup of kSetupThreads: thread t owns offsets t, t +
+// kSetupThreads, ...  The sanitised offsets are the running maximum of the
+// clamped inputs with seg[0] = 0 and seg[E] = rows; each expert's 16-row blocks
+// and M tiles are then summed exclusively.  Scans are Hillis-Steele in LDS.
+constexpr int kSetupThreads = 1024;
+constexpr int kSetupPer = (kMaxExperts + 1 + kSetupThreads - 1) / kSetupThreads;   // entries per thread
+
+__global__ __launch_bounds__(kSetupThreads) void grouped_setup_kernel(const int64_t* __restrict__ seg_in, int E,
+                                                                      int64_t rows, int tile_m,
+                                                                      int64_t* __restrict__ seg,
+                                                                      int64_t* __restrict__ pseg,
+                                                                      int32_t* __restrict__ tprefix) {
+  __shared__ int64_t a[kMaxExperts + 1], b[kMaxExperts + 1];
+  const int t = threadIdx.x;
+  const int n = E + 1;
+  for (int e = t; e < n; e += kSetupThreads) {
+    const int64_t v = seg_in[e];
+    a[e] = e == 0 ? 0 : (e == E ? rows : (v < 0 ? 0 : (v > rows ? rows : v)));
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t prev = 0, pb = 0;
-    int64_t tp = 0;
-    s[0] = 0;
-    for (int e = 0; e <= E; ++e) {
-      const int64_t v = e == E ? rows : (s[e] < prev ? prev : s[e]);   // nondecreasing, ends at rows
-      if (e > 0) {
-        const int64_t n = v - prev;
-        pb += (n + 15) / 16;
-        tp += (n + tile_m - 1) / tile_m;
-      }
-      seg[e] = v;
-      pseg[e] = pb;
-      tprefix[e] = (int32_t)tp;
-      prev = v;
+  // inclusive running maximum: nondecreasing, ends at rows (every value <= rows)
+  for (int d = 1; d < n; d *= 2) {
+    int64_t tmp[kSetupPer];
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) {
+      const int e = t + k * kSetupThreads;
+      tmp[k] = e < n ? (e >= d && a[e - d] > a[e] ? a[e - d] : a[e]) : 0;
     }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) {
+      const int e = t + k * kSetupThreads;
+      if (e < n) a[e] = tmp[k];
+    }
+    __syncthreads();
+  }
+  // per expert e (entry e + 1): blocks in the low 32 bits, tiles in the high 32
+  for (int e = t; e < n; e += kSetupThreads) {
+    seg[e] = a[e];
+    int64_t c = 0;
+    if (e > 0) {
+      const int64_t len = a[e] - a[e - 1];
+      c = ((len + 15) / 16) | (((len + tile_m - 1) / tile_m) << 32);
+    }
+    b[e] = c;
+  }
+  __syncthreads();
+  // inclusive sums of the packed pairs (no carry across halves: each half stays
+  // below 2^32 -- blocks <= (rows + 15 E) / 16 and tiles <= blocks)
+  for (int d = 1; d < n; d *= 2) {
+    int64_t tmp[kSetupPer];
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) {
+      const int e = t + k * kSetupThreads;
+      tmp[k] = e < n ? (e >= d ? b[e - d] + b[e] : b[e]) : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) {
+      const int e = t + k * kSetupThreads;
+      if (e < n) b[e] = tmp[k];
+    }
+    __syncthreads();
+  }
+  for (int e = t; e < n; e += kSetupThreads) {
+    pseg[e] = b[e] & 0xFFFFFFFFll;
+    tprefix[e] = (int32_t)(b[e] >> 32);
   }
 }
 
@@ -136,7 +177,7 @@ hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   int64_t* pseg = reinterpret_cast<int64_t*>(a.ws + L.pseg);
   int32_t* tprefix = reinterpret_cast<int32_t*>(a.ws + L.tprefix);
 
-  hipLaunchKernelGGL(grouped_setup_kernel, dim3(1), dim3(256), 0, stream, a.seg_in, E, a.rows,
+  hipLaunchKernelGGL(grouped_setup_kernel, dim3(1), dim3(kSetupThreads), 0, stream, a.seg_in, E, a.rows,
                      grouped_tile_m(), seg, pseg, tprefix);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
