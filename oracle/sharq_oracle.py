@@ -315,6 +315,36 @@ def linear(act: dict, w_codes, w_scales, rows=None):
 
 
 # --------------------------------------------------------------------------
+# Fusion ablations (SharQ README, Benchmarks: the RMSNorm fusion and the
+# epilogue fusion can be switched off).  Unfused RMSNorm writes the normalised
+# row in bf16 and the preparation then runs without gamma; the unfused epilogue
+# computes the two paths separately and adds them.
+# --------------------------------------------------------------------------
+def round_bf16(a) -> np.ndarray:
+    """binary32 -> bf16 bit patterns, round to nearest, ties to even (finite
+    inputs): keep the upper 16 bits after adding 0x7FFF plus the kept LSB.
+    Pinned by: exact rationals on neighbourhoods of midpoints, round trip."""
+    u = np.asarray(a, dtype=F32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def rmsnorm_bf16(x_bits, gamma_bits, eps: float) -> np.ndarray:
+    """The unfused RMSNorm's output: bf16 bits of rmsnorm(x) (binary32)."""
+    return round_bf16(rmsnorm(x_bits, gamma_bits, eps))
+
+
+def linear_paths(act: dict, w_codes, w_scales, rows=None):
+    """The two paths of the dual GEMM on their own (float64): (y_s, y_r, bound)."""
+    K = 2 * np.asarray(w_codes).shape[1]
+    sl = slice(None) if rows is None else rows
+    ds = deq_sparse(act["s_codes"][sl], act["s_meta"][sl], act["s_scales"][sl], K)
+    dr = deq_dense(act["r_codes"][sl], act["r_scales"][sl])
+    dw = deq_dense(w_codes, w_scales)
+    return ds @ dw.T, dr @ dw.T, np.abs(ds) @ np.abs(dw).T + np.abs(dr) @ np.abs(dw).T
+
+
+# --------------------------------------------------------------------------
 # Plain FP4 linear: the comparator the SharQ README benchmarks against (its
 # dense FP4 baseline mode): no backbone, the whole normalised row quantised
 # once, one GEMM.  In the descriptors this is the N:M pattern 0:4.

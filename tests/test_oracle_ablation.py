@@ -1,0 +1,70 @@
+"""Pins for the oracle's fusion-ablation pieces: bf16 rounding (exact rationals,
+ties to even), the unfused RMSNorm, and the two GEMM paths on their own."""
+from fractions import Fraction
+
+import numpy as np
+
+from fp4_sparse_dense_amd import synth
+from oracle import sharq_oracle as O
+
+
+def _bf16_value(bits) -> Fraction:
+    return Fraction(float(np.array([int(bits) << 16], dtype=np.uint32).view(np.float32)[0]))
+
+
+def test_round_bf16_against_exact_rationals():
+    rng = np.random.default_rng(4)
+    base = rng.integers(0, 0x7F7F, 300).astype(np.uint32) << 16      # finite positive bf16
+    vals = []
+    for b in base:
+        for d in (0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x10000 - 0x8000):
+            vals.append(int(b) + d)
+    f = np.array(vals, dtype=np.uint32).view(np.float32)
+    f = np.concatenate([f, -f])
+    got = O.round_bf16(f)
+    for x, g in zip(f, got):
+        q = Fraction(float(x))
+        lo = np.array([np.float32(x)], dtype=np.float32).view(np.uint32)[0] >> 16
+        sign = 0x8000 if q < 0 else 0
+        cands = [int(lo), int(lo) + 1]
+        dist = [abs(_bf16_value(c) - q) for c in cands]
+        if dist[0] != dist[1]:
+            want = cands[int(dist[1] < dist[0])]
+        else:
+            want = [c for c in cands if c % 2 == 0][0]
+        assert int(g) == want, (float(x), hex(int(g)), hex(want), sign)
+
+
+def test_round_bf16_roundtrip_and_closed_forms():
+    b = np.arange(0, 0x7F80, 7, dtype=np.uint16)
+    f = (b.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(O.round_bf16(f), b)
+    # ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> even (1.0)
+    assert O.round_bf16(np.float32(1 + 2 ** -8)) == 0x3F80
+    assert O.round_bf16(np.float32(1 + 3 * 2 ** -8)) == 0x3F82   # halfway, upper is even
+
+
+def test_unfused_rmsnorm_is_the_rounded_fused_row():
+    inp = synth.layer_inputs("qkv", seed=3, M=4, with_weight=False)
+    got = O.rmsnorm_bf16(inp["x"], inp["gamma"], inp["eps"])
+    v = O.rmsnorm(inp["x"], inp["gamma"], inp["eps"])
+    back = (got.astype(np.uint32) << 16).view(np.float32)
+    # within half a bf16 ulp of v, and exactly v where v is already a bf16 value
+    ulp = np.exp2(np.floor(np.log2(np.abs(v.astype(np.float64)) + 1e-300)) - 7)
+    assert np.all(np.abs(back.astype(np.float64) - v) <= ulp / 2)
+    exact = (v.view(np.uint32) & 0xFFFF) == 0
+    assert np.array_equal(back[exact], v[exact])
+
+
+def test_paths_sum_to_the_fused_gemm():
+    inp = synth.layer_inputs("tiny", seed=0)
+    act = O.prepare(inp["x"], inp["gamma"], inp["eps"])
+    wc, ws = O.pack_weight(inp["w"])
+    ys, yr, b = O.linear_paths(act, wc, ws)
+    y, b2 = O.linear(act, wc, ws)
+    assert np.allclose(ys + yr, y, rtol=0, atol=1e-12 * b.max())
+    assert np.array_equal(b, b2)
+    # the backbone path alone is the plain FP4 GEMM of the dense backbone codes
+    dense_s = dict(r_codes=O.pack_nibbles(act["s_nib"]), r_scales=act["s_scales"])
+    ys2, _ = O.linear_dense(dense_s, wc, ws)
+    assert np.allclose(ys2, ys, rtol=0, atol=1e-12 * b.max())
