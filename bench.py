@@ -206,6 +206,9 @@ def main():
                     help="FP4 format (nvfp4: the decode workload only)")
     ap.add_argument("--mode", default="sharq", choices=["sharq", "dense"],
                     help="dense: the plain MXFP4 linear (no backbone), the baseline SharQ is compared against")
+    ap.add_argument("--ablation", default="none", choices=["none", "unfused_norm", "unfused_epilogue"],
+                    help="fusion ablations: a standalone RMSNorm writing bf16 before the preparation, or "
+                         "the two GEMM paths as separate launches and an add")
     ap.add_argument("--sets", type=int, default=0, help="rotating input/weight/output sets (0: enough for > 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -229,6 +232,11 @@ def main():
         sys.exit(2)
     if args.mode == "dense" and (args.fmt != "mxfp4" or args.workload == "moe"):
         print("the plain FP4 linear is built for MXFP4 dense layers", file=sys.stderr)
+        sys.exit(2)
+    if args.ablation != "none" and (args.fmt != "mxfp4" or args.mode != "sharq" or args.workload == "moe" or
+                                    (args.ablation == "unfused_norm" and not WORKLOADS[args.workload]["norm"])):
+        print("the fusion ablations run the MXFP4 SharQ layer (unfused_norm needs a workload with RMSNorm)",
+              file=sys.stderr)
         sys.exit(2)
     if args.workload == "moe":
         rec = run_moe(args)
@@ -270,31 +278,56 @@ def run_dense(args):
             inp = dict(x=x, gamma=synth.norm_weight(rng, K) if norm else None)
         xs.append(up(inp["x"]))
         gammas.append(up(inp["gamma"]) if norm else None)
+    ablation = args.ablation
     sets = []
     for s in range(nsets):
         w = sq.sharq_pack_weight(device_weight(gen, N, K), fmt=fmt)
-        sets.append((w, sq.SharqAct(M, K, torch.device("cuda"), n=pat_n, fmt=fmt),
-                     torch.empty(M, N, dtype=torch.float32, device="cuda")))
+        act = sq.SharqAct(M, K, torch.device("cuda"), n=pat_n, fmt=fmt)
+        y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+        extra = {}
+        if ablation == "unfused_norm":
+            extra["xb"] = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        if ablation == "unfused_epilogue":
+            extra["ys"] = torch.empty(M, N, dtype=torch.float32, device="cuda")
+            extra["yr"] = torch.empty(M, N, dtype=torch.float32, device="cuda")
+            extra["pb"], extra["pr"] = sq.path_act(act, "backbone"), sq.path_act(act, "residual")
+        sets.append((w, act, y, extra))
     torch.cuda.synchronize()
 
-    def step(i, ev=None, stream=None, part=None):
-        w, act, y = sets[i % nsets]
+    # the step as a list of launches; the first n_prep are the preparation side
+    def launches(i):
+        w, act, y, ex = sets[i % nsets]
         x, g = xs[i % nx], gammas[i % nx]
+        if ablation == "unfused_norm":
+            return [lambda: sq.sharq_rmsnorm(x, g, 1e-5, out=ex["xb"]),
+                    lambda: sq.sharq_prepare(ex["xb"], None, 1e-5, out=act),
+                    lambda: sq.sharq_linear(act, w, out=y)]
+        if ablation == "unfused_epilogue":
+            return [lambda: sq.sharq_prepare(x, g, 1e-5, out=act),
+                    lambda: sq.sharq_linear(ex["pb"], w, out=ex["ys"]),
+                    lambda: sq.sharq_linear(ex["pr"], w, out=ex["yr"]),
+                    lambda: sq.sharq_add_f32(ex["ys"], ex["yr"], out=y)]
+        return [lambda: sq.sharq_prepare(x, g, 1e-5, n=pat_n, fmt=fmt, out=act),
+                lambda: sq.sharq_linear(act, w, out=y)]
+    part_names = {"unfused_norm": ["rmsnorm", "prep", "gemm"],
+                  "unfused_epilogue": ["prep", "gemm_backbone", "gemm_residual", "add"]}.get(ablation, ["prep", "gemm"])
+    n_prep = 2 if ablation == "unfused_norm" else 1
+
+    def step(i, ev=None, stream=None, part=None):
+        fns = launches(i)
         if ev is not None:
             ev[0].record(stream)
-        if part in (None, 0):
-            sq.sharq_prepare(x, g, 1e-5, n=pat_n, fmt=fmt, out=act)
-        if ev is not None:
-            ev[1].record(stream)
-        if part in (None, 1):
-            sq.sharq_linear(act, w, out=y)
-        if ev is not None:
-            ev[2].record(stream)
-    step.parts = 2
+        for j, fn in enumerate(fns):
+            if part in (None, j):
+                fn()
+            if ev is not None:
+                ev[j + 1].record(stream)
+    step.parts = len(part_names)
 
     graph = args.workload == "decode"
     ms, parts = timed(step, args.steps, args.warmup, graph=graph)
-    prep_ms, gemm_ms = float(np.mean(parts[0])), float(np.mean(parts[1]))
+    part_ms = [float(np.mean(p)) for p in parts]
+    prep_ms, gemm_ms = sum(part_ms[:n_prep]), sum(part_ms[n_prep:])
     flops = gemm_flops(M, N, K) // (2 if dense else 1)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     gbytes = gemm_bytes(M, N, K, nv=nv, dense=dense)
@@ -309,11 +342,13 @@ def run_dense(args):
     else:
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak_mfma, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / peak_mfma, 4),
-                "traffic": read_traffic() if (args.workload == "qkv" and not dense) else None}
-    cpu = None if (args.no_cpu_baseline or args.workload != "qkv" or dense) else cpu_baseline()
+                "traffic": read_traffic() if (args.workload == "qkv" and not dense and ablation == "none") else None}
+    cpu = None if (args.no_cpu_baseline or args.workload != "qkv" or dense or ablation != "none") else cpu_baseline()
     wname = args.workload if args.workload != "decode" else f"decode{M}"
     if dense:
         wname += "-plainfp4"
+    if ablation != "none":
+        wname += "-" + ablation.replace("_", "-")
     return {
         "metric": ("plain MXFP4 linear TFLOPS (dense FP4 baseline, 2*M*N*K), Llama-8B shapes" if dense else
                    "SharQ linear TFLOPS + prep GB/s (fraction of peak), Llama-8B shapes M=2048"),
@@ -344,6 +379,7 @@ def run_dense(args):
                  "frac_hbm": round(gemm_gbs / PEAK_HBM_GBS, 4), "bytes": gbytes},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "parts_us": {k: round(v * 1e3, 3) for k, v in zip(part_names, part_ms)},
     }
 
 

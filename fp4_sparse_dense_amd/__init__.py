@@ -17,7 +17,8 @@ from ._lib import FMT_HIF4, FMT_MXFP4, FMT_NVFP4, OUT_BF16, OUT_F32, SharqError
 
 __all__ = [
     "SharqWeight", "SharqAct", "SharqError",
-    "sharq_pack_weight", "sharq_prepare", "sharq_linear",
+    "sharq_pack_weight", "sharq_prepare", "sharq_linear", "sharq_linear_grouped",
+    "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -172,3 +173,66 @@ def sharq_linear_grouped(act: SharqAct, weight: SharqWeight, seg_offsets, expert
                                         _ptr(workspace), workspace.numel(), _stream_ptr(stream)),
                "sharq_linear_grouped")
     return out
+
+
+def sharq_rmsnorm(x, gamma, eps: float = 1e-5, out=None, stream=None):
+    """Unfused RMSNorm (fusion ablation): bf16 [M, K] of the binary32 row the
+    fused preparation computes, rounded to nearest even."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit inner stride")
+    if gamma is None or gamma.dtype != torch.bfloat16 or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous bf16 tensor")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty(M, K, dtype=torch.bfloat16, device=x.device)
+    lib = _lib.load()
+    _lib.check(lib.sharq_rmsnorm(_ptr(x), M, K, x.stride(0), _ptr(gamma), eps, _ptr(out), out.stride(0),
+                                 _stream_ptr(stream)), "sharq_rmsnorm")
+    return out
+
+
+def sharq_add_f32(a, b, out=None, stream=None):
+    """out = a + b for contiguous fp32 device tensors of one size (the unfused epilogue's add)."""
+    torch = _torch()
+    if a.dtype != torch.float32 or b.dtype != torch.float32 or a.numel() != b.numel():
+        raise ValueError("a and b must be fp32 tensors of one size")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous")
+    if out is None:
+        out = torch.empty_like(a)
+    lib = _lib.load()
+    _lib.check(lib.sharq_add_f32(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream_ptr(stream)), "sharq_add_f32")
+    return out
+
+
+class _PathAct:
+    """One GEMM path of a prepared activation as a descriptor of pattern 0:4
+    (the plain FP4 operand): the backbone's or the residual's codes and scales."""
+
+    def __init__(self, act: SharqAct, path: str):
+        codes, scales = (act.s_codes, act.s_scales) if path == "backbone" else (act.r_codes, act.r_scales)
+        self.M, self.K, self.n, self.m, self.fmt = act.M, act.K, 0, 4, act.fmt
+        self.s_codes = codes
+        self._act = act
+        self._desc = _lib.ActDesc()
+        self._desc.struct_size = C.sizeof(_lib.ActDesc)
+        self._desc.M, self._desc.K, self._desc.n, self._desc.m, self._desc.fmt = act.M, act.K, 0, 4, act.fmt
+        self._desc.r_codes = codes.data_ptr()
+        self._desc.r_scales = scales.data_ptr()
+
+    @property
+    def desc(self):
+        # valid once the activation has been prepared by the library
+        self._desc.layout_version = self._act.desc.layout_version
+        return self._desc
+
+
+def path_act(act: SharqAct, path: str):
+    """Descriptor running one path of the dual GEMM alone (unfused epilogue):
+    path is "backbone" or "residual"; pass it to sharq_linear."""
+    if path not in ("backbone", "residual"):
+        raise ValueError("path is 'backbone' or 'residual'")
+    if act.n != 2 or act.fmt != FMT_MXFP4:
+        raise ValueError("paths are split for 2:4 MXFP4 activations")
+    return _PathAct(act, path)

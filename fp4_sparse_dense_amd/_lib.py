@@ -62,6 +62,9 @@ PROTOTYPES = {
     "sharq_linear_grouped": (C.c_int, [C.POINTER(ActDesc), C.c_void_p, C.c_int64, C.c_void_p, C.c_int32,
                                        C.POINTER(WeightDesc), C.c_void_p, C.c_int64, C.c_int32,
                                        C.c_void_p, C.c_size_t, C.c_void_p]),
+    "sharq_rmsnorm": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_float,
+                                C.c_void_p, C.c_int64, C.c_void_p]),
+    "sharq_add_f32": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
 }
 
 _LIB = None

@@ -288,6 +288,39 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   return SHARQ_OK;
 }
 
+sharq_status sharq_rmsnorm(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx, const void* gamma_bf16_dev,
+                           float eps, void* y_bf16_dev, int64_t ldy, void* stream) {
+  g_err[0] = 0;
+  if (M < 0 || K <= 0 || K % 32 || K > 32768)
+    return fail(SHARQ_ERR_INVALID_ARG, "bad shape M=%lld K=%lld (K%%32 == 0, K <= 32768)", (long long)M, (long long)K);
+  if (M == 0) return SHARQ_OK;
+  if (!x_bf16_dev || !gamma_bf16_dev || !y_bf16_dev) return fail(SHARQ_ERR_INVALID_ARG, "null pointer");
+  if (ldx < K || ldx % 8 || ldy < K || ldy % 8 || ldx > (int64_t(1) << 26) || ldy > (int64_t(1) << 26))
+    return fail(SHARQ_ERR_INVALID_ARG, "ldx=%lld / ldy=%lld must be >= K, multiples of 8, <= 2^26", (long long)ldx, (long long)ldy);
+  if (!aligned(x_bf16_dev, 16) || !aligned(gamma_bf16_dev, 16) || !aligned(y_bf16_dev, 16))
+    return fail(SHARQ_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  sharq_status s = check_device();
+  if (s) return s;
+  hipError_t e = sharq::launch_rmsnorm_bf16(static_cast<const uint16_t*>(x_bf16_dev), M, (int)K, ldx,
+                                            static_cast<const uint16_t*>(gamma_bf16_dev), eps,
+                                            static_cast<uint16_t*>(y_bf16_dev), ldy, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+  return SHARQ_OK;
+}
+
+sharq_status sharq_add_f32(const float* a_dev, const float* b_dev, float* y_dev, int64_t n, void* stream) {
+  g_err[0] = 0;
+  if (n < 0) return fail(SHARQ_ERR_INVALID_ARG, "n=%lld", (long long)n);
+  if (n == 0) return SHARQ_OK;
+  if (!a_dev || !b_dev || !y_dev) return fail(SHARQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(a_dev, 4) || !aligned(b_dev, 4) || !aligned(y_dev, 4)) return fail(SHARQ_ERR_INVALID_ARG, "misaligned");
+  sharq_status s = check_device();
+  if (s) return s;
+  hipError_t e = sharq::launch_add_f32(a_dev, b_dev, y_dev, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "add launch");
+  return SHARQ_OK;
+}
+
 sharq_status sharq_grouped_workspace_bytes(int64_t rows, int32_t E, int64_t K, size_t* bytes) {
   g_err[0] = 0;
   if (!bytes) return fail(SHARQ_ERR_INVALID_ARG, "null output");

@@ -84,6 +84,94 @@ __device__ __forceinline__ float rms_inverse(float ss, int K, float eps) {
   return (float)(1.0 / (double)root);
 }
 
+// ---------------------------------------------------------------- row helpers
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// max over the workgroup of non-negative v (all threads must call)
+template <int NWAVES>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < NWAVES; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+// 32 bf16 of one row -> binary32
+__device__ __forceinline__ void load32(const uint16_t* p, float (&v)[32]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 d = *reinterpret_cast<const uint4*>(p + 8 * q);
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[8 * q + 2 * h] = bf16_lo(w[h]);
+      v[8 * q + 2 * h + 1] = bf16_hi(w[h]);
+    }
+  }
+}
+
+// v = (x * inv) * gamma, elementwise, two roundings
+__device__ __forceinline__ void apply_norm(float (&v)[32], const uint16_t* gamma, float inv) {
+  float g[32];
+  load32(gamma, g);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = (v[i] * inv) * g[i];
+}
+
+// Pairwise tree of squares over 32 consecutive elements: leaves x0^2 + x1^2
+// (squares of bf16 values are exact), then halving in index order.
+__device__ __forceinline__ float chunk_sumsq(const float (&v)[32]) {
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = v[2 * i] * v[2 * i] + v[2 * i + 1] * v[2 * i + 1];
+#pragma unroll
+  for (int n = 8; n >= 1; n >>= 1)
+#pragma unroll
+    for (int i = 0; i < n; ++i) p[i] = p[2 * i] + p[2 * i + 1];
+  return p[0];
+}
+
+// 1/rms of one row of K bf16 values (K % 32 == 0, K <= 32768), computed by a
+// whole workgroup of 256 threads (all must call): the sum of squares is the
+// balanced pairwise tree over the row zero-padded to a power of two -- aligned
+// 32-element chunks are subtrees (chunk_sumsq), their sums are combined
+// pairwise in LDS (cs: 1024 floats).
+__device__ __forceinline__ float row_inv_rms(const uint16_t* xr, int K, float eps, float* cs) {
+  const int t = threadIdx.x;
+  const int KC = K / 32;
+  int P = 1;
+  while (P < KC) P *= 2;
+  for (int c = t; c < P; c += 256) {
+    float s = 0.0f;
+    if (c < KC) {
+      float v[32];
+      load32(xr + 32 * c, v);
+      s = chunk_sumsq(v);
+    }
+    cs[c] = s;
+  }
+  __syncthreads();
+  for (int n = P; n > 1; n >>= 1) {
+    const int h = n >> 1;
+    const float s0 = t < h ? cs[2 * t] + cs[2 * t + 1] : 0.0f;
+    const float s1 = t + 256 < h ? cs[2 * (t + 256)] + cs[2 * (t + 256) + 1] : 0.0f;
+    __syncthreads();
+    if (t < h) cs[t] = s0;
+    if (t + 256 < h) cs[t + 256] = s1;
+    __syncthreads();
+  }
+  return rms_inverse(cs[0], K, eps);
+}
+
 // ---------------------------------------------------------------- E2M1
 // Two binary32 values -> two E2M1 nibbles placed in byte SEL of `old`.
 // v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to nearest, ties to even,

@@ -56,6 +56,11 @@ hipError_t launch_prepare_dense(const uint16_t* x, int64_t M, int K, int64_t ldx
                                 float eps, PrepOut out, hipStream_t stream);
 hipError_t launch_linear_dense(const GemmArgs& a, hipStream_t stream);
 
+// Fusion ablations: standalone RMSNorm writing bf16; fp32 elementwise add.
+hipError_t launch_rmsnorm_bf16(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma, float eps,
+                               uint16_t* y, int64_t ldy, hipStream_t stream);
+hipError_t launch_add_f32(const float* a, const float* b, float* y, int64_t n, hipStream_t stream);
+
 // Grouped expert layer: rows of a prepared activation gathered (or taken in
 // order) into expert segments padded to whole 16-row blocks, then one tiled
 // dual GEMM over every (expert, tile).  See sharq_linear_grouped.

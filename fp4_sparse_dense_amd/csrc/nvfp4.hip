@@ -61,61 +61,6 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// max over the workgroup of non-negative v (all threads must call)
-template <int NWAVES>
-__device__ __forceinline__ float block_max(float v, float* red) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float m = red[0];
-#pragma unroll
-  for (int i = 1; i < NWAVES; ++i) m = fmaxf(m, red[i]);
-  return m;
-}
-
-// 32 bf16 of one row -> binary32
-__device__ __forceinline__ void load32(const uint16_t* p, float (&v)[32]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint4 d = *reinterpret_cast<const uint4*>(p + 8 * q);
-    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      v[8 * q + 2 * h] = bf16_lo(w[h]);
-      v[8 * q + 2 * h + 1] = bf16_hi(w[h]);
-    }
-  }
-}
-
-// v = (x * inv) * gamma, elementwise, two roundings
-__device__ __forceinline__ void apply_norm(float (&v)[32], const uint16_t* gamma, float inv) {
-  float g[32];
-  load32(gamma, g);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = (v[i] * inv) * g[i];
-}
-
-// Pairwise tree of squares over 32 consecutive elements: leaves x0^2 + x1^2
-// (squares of bf16 values are exact), then halving in index order.
-__device__ __forceinline__ float chunk_sumsq(const float (&v)[32]) {
-  float p[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) p[i] = v[2 * i] * v[2 * i] + v[2 * i + 1] * v[2 * i + 1];
-#pragma unroll
-  for (int n = 8; n >= 1; n >>= 1)
-#pragma unroll
-    for (int i = 0; i < n; ++i) p[i] = p[2 * i] + p[2 * i + 1];
-  return p[0];
-}
-
 // E2M1 nibble of binary32 q (round to nearest even, saturating at 6, sign of
 // zero kept): the convert instruction with unit scale.
 __device__ __forceinline__ uint32_t e2m1_pair(float lo, float hi) { return fp4_pack2<0>(0u, lo, hi) & 0xFFu; }
@@ -158,31 +103,7 @@ __global__ __launch_bounds__(256) void nv_rowstats_kernel(NvPrepArgs a) {
   const int64_t row = blockIdx.x;
   const uint16_t* xr = a.x + row * a.ldx;
   const int KC = a.K / 32;
-  float inv = 1.0f;
-  if (NORM) {
-    int P = 1;
-    while (P < KC) P *= 2;
-    for (int c = t; c < P; c += 256) {
-      float s = 0.0f;
-      if (c < KC) {
-        float v[32];
-        load32(xr + 32 * c, v);
-        s = chunk_sumsq(v);
-      }
-      cs[c] = s;
-    }
-    __syncthreads();
-    for (int n = P; n > 1; n >>= 1) {
-      const int h = n >> 1;
-      const float s0 = t < h ? cs[2 * t] + cs[2 * t + 1] : 0.0f;
-      const float s1 = t + 256 < h ? cs[2 * (t + 256)] + cs[2 * (t + 256) + 1] : 0.0f;
-      __syncthreads();
-      if (t < h) cs[t] = s0;
-      if (t + 256 < h) cs[t + 256] = s1;
-      __syncthreads();
-    }
-    inv = rms_inverse(cs[0], a.K, a.eps);
-  }
+  const float inv = NORM ? row_inv_rms(xr, a.K, a.eps, cs) : 1.0f;
   float am = 0.0f;
   for (int c = t; c < KC; c += 256) {
     float v[32];

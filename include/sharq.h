@@ -233,6 +233,26 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
 sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w,
                           void* y_dev, int64_t ldy, int32_t out_dtype, void* stream);
 
+/* Fusion ablations (README page of the SharQ repository, "Benchmarks": the
+ * RMSNorm fusion and the epilogue fusion can each be switched off).
+ *
+ * sharq_rmsnorm: unfused RMSNorm of X[M,K] (bf16, row stride ldx) into
+ * Y[M,K] (bf16, row stride ldy): the binary32 v of sharq_prepare (same
+ * pairwise tree, same rounding steps) rounded to bf16 (nearest, ties to even).
+ * Preparing Y with gamma NULL is the unfused preparation.
+ * Errors: INVALID_ARG (null, M<0, K<=0, K%32, K>32768, ldx/ldy < K or not
+ * multiples of 8 or > 2^26, buffers not 16-B aligned), UNSUPPORTED (not
+ * gfx950), HIP. */
+sharq_status sharq_rmsnorm(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx, const void* gamma_bf16_dev,
+                           float eps, void* y_bf16_dev, int64_t ldy, void* stream);
+
+/* y[i] = a[i] + b[i] for n fp32 elements (device pointers; y may alias a or b):
+ * the add of the unfused epilogue, whose two paths are two sharq_linear calls
+ * on descriptors with pattern 0:4 whose r_codes / r_scales point at the
+ * backbone's (s_codes / s_scales) or the residual's buffers.
+ * Errors: INVALID_ARG (null, n<0, misaligned), UNSUPPORTED (not gfx950), HIP. */
+sharq_status sharq_add_f32(const float* a_dev, const float* b_dev, float* y_dev, int64_t n, void* stream);
+
 /* Workspace bytes sharq_linear_grouped needs for `rows` routed rows, E
  * experts and reduction length K (the routed activation rows gathered into
  * expert order, each expert padded to whole 16-row blocks, plus small tables).

@@ -209,3 +209,16 @@ def test_grouped_rejects_before_launch(lib):
     a.fmt = w.fmt = 0
     a.n = 0
     assert call(64, 8) == _lib.ERR_UNSUPPORTED                   # and 2:4 only
+
+
+def test_ablation_entry_points_reject_before_launch(lib):
+    x, g, y = C.c_void_p(0x100000), C.c_void_p(0x200000), C.c_void_p(0x300000)
+    assert lib.sharq_rmsnorm(x, 16, 250, 256, g, 1e-5, y, 256, None) == _lib.ERR_INVALID_ARG   # K % 32
+    assert lib.sharq_rmsnorm(x, 16, 65536, 65536, g, 1e-5, y, 65536, None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_rmsnorm(x, 16, 256, 256, None, 1e-5, y, 256, None) == _lib.ERR_INVALID_ARG  # gamma needed
+    assert lib.sharq_rmsnorm(x, 16, 256, 256, g, 1e-5, y, 128, None) == _lib.ERR_INVALID_ARG     # ldy < K
+    assert lib.sharq_rmsnorm(None, 0, 256, 256, None, 1e-5, None, 256, None) == _lib.OK          # M == 0
+    assert lib.sharq_add_f32(x, g, y, -1, None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_add_f32(None, g, y, 8, None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_add_f32(C.c_void_p(0x100002), g, y, 8, None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_add_f32(None, None, None, 0, None) == _lib.OK
