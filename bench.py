@@ -206,6 +206,8 @@ def main():
                     help="FP4 format (nvfp4: the decode workload only)")
     ap.add_argument("--mode", default="sharq", choices=["sharq", "dense"],
                     help="dense: the plain MXFP4 linear (no backbone), the baseline SharQ is compared against")
+    ap.add_argument("--fused", action="store_true",
+                    help="decode with M <= 16: the whole layer in one launch (sharq_linear_fused)")
     ap.add_argument("--ablation", default="none", choices=["none", "unfused_norm", "unfused_epilogue"],
                     help="fusion ablations: a standalone RMSNorm writing bf16 before the preparation, or "
                          "the two GEMM paths as separate launches and an add")
@@ -232,6 +234,10 @@ def main():
         sys.exit(2)
     if args.mode == "dense" and (args.fmt != "mxfp4" or args.workload == "moe"):
         print("the plain FP4 linear is built for MXFP4 dense layers", file=sys.stderr)
+        sys.exit(2)
+    if args.fused and (args.workload != "decode" or args.m > 16 or args.fmt != "mxfp4" or args.mode != "sharq"
+                       or args.ablation != "none"):
+        print("--fused is the one-launch MXFP4 layer for the decode workload with --m <= 16", file=sys.stderr)
         sys.exit(2)
     if args.ablation != "none" and (args.fmt != "mxfp4" or args.mode != "sharq" or args.workload == "moe" or
                                     (args.ablation == "unfused_norm" and not WORKLOADS[args.workload]["norm"])):
@@ -307,11 +313,13 @@ def run_dense(args):
                     lambda: sq.sharq_linear(ex["pb"], w, out=ex["ys"]),
                     lambda: sq.sharq_linear(ex["pr"], w, out=ex["yr"]),
                     lambda: sq.sharq_add_f32(ex["ys"], ex["yr"], out=y)]
+        if args.fused:
+            return [lambda: sq.sharq_linear_fused(x, w, g, 1e-5, out=y)]
         return [lambda: sq.sharq_prepare(x, g, 1e-5, n=pat_n, fmt=fmt, out=act),
                 lambda: sq.sharq_linear(act, w, out=y)]
-    part_names = {"unfused_norm": ["rmsnorm", "prep", "gemm"],
+    part_names = ["layer"] if args.fused else {"unfused_norm": ["rmsnorm", "prep", "gemm"],
                   "unfused_epilogue": ["prep", "gemm_backbone", "gemm_residual", "add"]}.get(ablation, ["prep", "gemm"])
-    n_prep = 2 if ablation == "unfused_norm" else 1
+    n_prep = 0 if args.fused else (2 if ablation == "unfused_norm" else 1)
 
     def step(i, ev=None, stream=None, part=None):
         fns = launches(i)
@@ -330,10 +338,11 @@ def run_dense(args):
     prep_ms, gemm_ms = sum(part_ms[:n_prep]), sum(part_ms[n_prep:])
     flops = gemm_flops(M, N, K) // (2 if dense else 1)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    gbytes = gemm_bytes(M, N, K, nv=nv, dense=dense)
+    # the one-launch layer reads X (bf16) instead of the prepared activation
+    gbytes = (M * K * 2 + N * K * 17 // 32 + 4 * M * N) if args.fused else gemm_bytes(M, N, K, nv=nv, dense=dense)
     gemm_gbs = gbytes / (gemm_ms * 1e-3) / 1e9
     pbytes = prep_bytes(M, K, norm, nv=nv, dense=dense)
-    prep_gbs = pbytes / (prep_ms * 1e-3) / 1e9
+    prep_gbs = pbytes / (prep_ms * 1e-3) / 1e9 if prep_ms > 0 else 0.0
     peak_mfma = PEAK_BF16_TFLOPS if nv else PEAK_FP4_TFLOPS
     hbm_bound = gbytes / (PEAK_HBM_GBS * 1e9) > flops / (peak_mfma * 1e12)
     if hbm_bound:
@@ -347,6 +356,8 @@ def run_dense(args):
     wname = args.workload if args.workload != "decode" else f"decode{M}"
     if dense:
         wname += "-plainfp4"
+    if args.fused:
+        wname += "-fused"
     if ablation != "none":
         wname += "-" + ablation.replace("_", "-")
     return {
@@ -372,8 +383,8 @@ def run_dense(args):
                    "M": M, "K": K, "N": N, "pattern": "0:4" if dense else "2:4",
                    "format": "NVFP4-style" if nv else "MXFP4",
                    "rotating_sets": nsets},
-        "prep": {"us": round(prep_ms * 1e3, 3), "GB/s": round(prep_gbs, 1),
-                 "frac_hbm": round(prep_gbs / PEAK_HBM_GBS, 4), "bytes": pbytes},
+        "prep": None if args.fused else {"us": round(prep_ms * 1e3, 3), "GB/s": round(prep_gbs, 1),
+                                         "frac_hbm": round(prep_gbs / PEAK_HBM_GBS, 4), "bytes": pbytes},
         "gemm": {"us": round(gemm_ms * 1e3, 3), "TFLOP/s": round(gemm_tflops, 1),
                  "frac_mfma": round(gemm_tflops / peak_mfma, 4), "GB/s": round(gemm_gbs, 1),
                  "frac_hbm": round(gemm_gbs / PEAK_HBM_GBS, 4), "bytes": gbytes},

@@ -18,7 +18,7 @@ from ._lib import FMT_HIF4, FMT_MXFP4, FMT_NVFP4, OUT_BF16, OUT_F32, SharqError
 __all__ = [
     "SharqWeight", "SharqAct", "SharqError",
     "sharq_pack_weight", "sharq_prepare", "sharq_linear", "sharq_linear_grouped",
-    "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes",
+    "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -236,3 +236,25 @@ def path_act(act: SharqAct, path: str):
     if act.n != 2 or act.fmt != FMT_MXFP4:
         raise ValueError("paths are split for 2:4 MXFP4 activations")
     return _PathAct(act, path)
+
+
+def sharq_linear_fused(x, weight: SharqWeight, gamma=None, eps: float = 1e-5, out=None, out_dtype: int = OUT_F32,
+                       stream=None):
+    """The whole layer in one launch for M <= 16 (decode): the result of
+    sharq_prepare + sharq_linear, bit for bit, without the prepared activation."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit inner stride")
+    if gamma is not None and (gamma.dtype != torch.bfloat16 or not gamma.is_contiguous()):
+        raise ValueError("gamma must be a contiguous bf16 tensor")
+    M, K = x.shape
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty(M, weight.N, dtype=dt, device=x.device)
+    if out.dtype != dt or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be 2-D with unit inner stride and the requested dtype")
+    lib = _lib.load()
+    _lib.check(lib.sharq_linear_fused(_ptr(x), M, K, x.stride(0), _ptr(gamma), eps, 2, 4, FMT_MXFP4,
+                                      C.byref(weight.desc), _ptr(out), out.stride(0), out_dtype,
+                                      _stream_ptr(stream)), "sharq_linear_fused")
+    return out

@@ -288,6 +288,60 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   return SHARQ_OK;
 }
 
+sharq_status sharq_linear_fused(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx,
+                                const void* gamma_bf16_dev, float eps, int32_t n, int32_t m, int32_t fmt,
+                                const sharq_weight* w, void* y_dev, int64_t ldy, int32_t out_dtype, void* stream) {
+  g_err[0] = 0;
+  if (!w) return fail(SHARQ_ERR_INVALID_ARG, "null weight descriptor");
+  if (w->struct_size != sizeof(sharq_weight)) return fail(SHARQ_ERR_INVALID_ARG, "descriptor struct_size mismatch");
+  if (w->layout_version != SHARQ_ABI_VERSION)
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor layout_version mismatch (not produced by this library?)");
+  if (M < 0 || K <= 0 || K % 32) return fail(SHARQ_ERR_INVALID_ARG, "bad shape M=%lld K=%lld (K%%32 must be 0)", (long long)M, (long long)K);
+  if (K != w->K) return fail(SHARQ_ERR_INVALID_ARG, "K mismatch: activation %lld, weight %lld", (long long)K, (long long)w->K);
+  if (out_dtype != SHARQ_OUT_F32 && out_dtype != SHARQ_OUT_BF16) return fail(SHARQ_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
+  sharq_status s = check_fmt(fmt);
+  if (s) return s;
+  if (fmt != w->fmt) return fail(SHARQ_ERR_INVALID_ARG, "activation and weight formats differ");
+  if (fmt != SHARQ_FMT_MXFP4 || n != 2 || m != 4)
+    return fail(SHARQ_ERR_UNSUPPORTED, "the one-launch layer is built for 2:4 MXFP4");
+  if (M > 16 || K > 8192 || sharq::fused_layer_lds_bytes((int)K, gamma_bf16_dev != nullptr) > 160 * 1024)
+    return fail(SHARQ_ERR_UNSUPPORTED, "the one-launch layer takes M <= 16 and K <= 8192 (use sharq_prepare + sharq_linear)");
+  if (M == 0) return SHARQ_OK;
+  if (!x_bf16_dev || !y_dev) return fail(SHARQ_ERR_INVALID_ARG, "null pointer");
+  if (ldx < K || ldx % 8 || ldx > (int64_t(1) << 26)) return fail(SHARQ_ERR_INVALID_ARG, "ldx=%lld must be >= K, a multiple of 8, <= 2^26", (long long)ldx);
+  if (!aligned(x_bf16_dev, 16) || (gamma_bf16_dev && !aligned(gamma_bf16_dev, 16)))
+    return fail(SHARQ_ERR_INVALID_ARG, "activation or gamma not 16-byte aligned");
+  if (ldy < w->N) return fail(SHARQ_ERR_INVALID_ARG, "ldy=%lld < N=%lld", (long long)ldy, (long long)w->N);
+  if (!aligned(y_dev, out_dtype == SHARQ_OUT_F32 ? 4 : 2)) return fail(SHARQ_ERR_INVALID_ARG, "output misaligned");
+  if (!w->codes || !aligned(w->codes, 16)) return fail(SHARQ_ERR_INVALID_ARG, "weight codes null or misaligned");
+  const sharq_scale_view& vs = w->view[SHARQ_PATH_SPARSE];
+  const sharq_scale_view& vd = w->view[SHARQ_PATH_DENSE];
+  const int64_t nb64 = (w->N + 15) / 16 * 64;
+  if (!vs.base || !vd.base || vs.block != 32 || vd.block != 32 || vs.ld != nb64 || vd.ld != nb64)
+    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be tiled MX views (block 32, K-tile stride NB*64)");
+  if (vs.base != vd.base)
+    return fail(SHARQ_ERR_UNSUPPORTED, "the two paths must view the same packed scale array");
+  s = check_device();
+  if (s) return s;
+  sharq::GemmArgs g{};
+  g.w_codes = w->codes;
+  g.w_scales_sparse = vs.base;
+  g.w_scales_dense = vd.base;
+  g.w_scales_ld = vs.ld;
+  g.y = y_dev;
+  g.ldy = ldy;
+  g.M = M;
+  g.N = w->N;
+  g.K = (int)K;
+  g.out_bf16 = out_dtype == SHARQ_OUT_BF16;
+  g.a_blocks = 1;
+  hipError_t e = sharq::launch_linear_fused(static_cast<const uint16_t*>(x_bf16_dev), (int)M, (int)K, ldx,
+                                            static_cast<const uint16_t*>(gamma_bf16_dev), eps, g,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fused layer launch");
+  return SHARQ_OK;
+}
+
 sharq_status sharq_rmsnorm(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx, const void* gamma_bf16_dev,
                            float eps, void* y_bf16_dev, int64_t ldy, void* stream) {
   g_err[0] = 0;

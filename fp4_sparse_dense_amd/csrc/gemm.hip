@@ -19,30 +19,10 @@
 #include <atomic>
 
 #include "device_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace sharq {
-
-__device__ __forceinline__ v8i as_operand(uint4 q) {
-  v8i r;
-  r[0] = (int)q.x; r[1] = (int)q.y; r[2] = (int)q.z; r[3] = (int)q.w;
-  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
-  return r;
-}
-
-__device__ __forceinline__ v4f mfma_fp4(v8i a, v8i b, v4f c, uint32_t sa, uint32_t sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, (int)sa, 0, (int)sb);
-}
-
-__device__ __forceinline__ void store_out(const GemmArgs& g, int64_t row, int64_t col, float v) {
-  if (g.out_bf16) {
-    uint32_t u = __float_as_uint(v);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    reinterpret_cast<uint16_t*>(g.y)[row * g.ldy + col] = (uint16_t)(u >> 16);
-  } else {
-    reinterpret_cast<float*>(g.y)[row * g.ldy + col] = v;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Small-M kernel (decode, M <= 64): the weight is streamed once and the work

@@ -56,6 +56,12 @@ hipError_t launch_prepare_dense(const uint16_t* x, int64_t M, int K, int64_t ldx
                                 float eps, PrepOut out, hipStream_t stream);
 hipError_t launch_linear_dense(const GemmArgs& a, hipStream_t stream);
 
+// The whole layer in one launch for M <= 16 (every workgroup prepares the rows
+// into LDS); fused_layer_lds_bytes must be <= 160 KiB.
+size_t fused_layer_lds_bytes(int K, bool norm);
+hipError_t launch_linear_fused(const uint16_t* x, int M, int K, int64_t ldx, const uint16_t* gamma, float eps,
+                               const GemmArgs& g, hipStream_t stream);
+
 // Fusion ablations: standalone RMSNorm writing bf16; fp32 elementwise add.
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma, float eps,
                                uint16_t* y, int64_t ldy, hipStream_t stream);

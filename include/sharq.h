@@ -253,6 +253,21 @@ sharq_status sharq_rmsnorm(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
  * Errors: INVALID_ARG (null, n<0, misaligned), UNSUPPORTED (not gfx950), HIP. */
 sharq_status sharq_add_f32(const float* a_dev, const float* b_dev, float* y_dev, int64_t n, void* stream);
 
+/* The whole layer in one launch for small M (decode): Y[M,N] of the bf16
+ * activation X[M,K] (row stride ldx) and the packed weight, exactly
+ * sharq_prepare followed by sharq_linear -- the same arithmetic, identical
+ * outputs bit for bit -- without materialising the prepared activation: each
+ * workgroup of the weight-streaming GEMM prepares the rows into LDS.  SharQ
+ * abstract: the preparation is one fused operator feeding both GEMMs.
+ * Limits: M <= 16, K <= 8192, 2:4, MXFP4 (others: UNSUPPORTED; use the
+ * two-call path).  It is faster than the two calls up to M = 8 only.  gamma NULL skips RMSNorm.  y: fp32 or bf16 per out_dtype,
+ * row stride ldy >= N.
+ * Errors: INVALID_ARG (null, shapes, K mismatch, ldx/ldy, misaligned buffers,
+ * weight views), UNSUPPORTED (limits, format, pattern, not gfx950), HIP. */
+sharq_status sharq_linear_fused(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx,
+                                const void* gamma_bf16_dev, float eps, int32_t n, int32_t m, int32_t fmt,
+                                const sharq_weight* w, void* y_dev, int64_t ldy, int32_t out_dtype, void* stream);
+
 /* Workspace bytes sharq_linear_grouped needs for `rows` routed rows, E
  * experts and reduction length K (the routed activation rows gathered into
  * expert order, each expert padded to whole 16-row blocks, plus small tables).

@@ -222,3 +222,25 @@ def test_ablation_entry_points_reject_before_launch(lib):
     assert lib.sharq_add_f32(None, g, y, 8, None) == _lib.ERR_INVALID_ARG
     assert lib.sharq_add_f32(C.c_void_p(0x100002), g, y, 8, None) == _lib.ERR_INVALID_ARG
     assert lib.sharq_add_f32(None, None, None, 0, None) == _lib.OK
+
+
+def test_fused_layer_rejects_before_launch(lib):
+    w = _lib.WeightDesc()
+    w.struct_size = C.sizeof(_lib.WeightDesc)
+    w.layout_version = _lib.SHARQ_ABI_VERSION
+    w.N, w.K, w.codes, w.scales = 64, 256, 0x100000, 0x200000
+    for p in (0, 1):
+        w.view[p].base, w.view[p].ld, w.view[p].block = 0x200000, 4 * 64, 32
+    x, y = C.c_void_p(0x300000), C.c_void_p(0x400000)
+    call = lambda M, K=256, n=2, fmt=0, ldy=64: lib.sharq_linear_fused(x, M, K, K, None, 1e-5, n, 4, fmt,
+                                                                       C.byref(w), y, ldy, 0, None)
+    assert call(17) == _lib.ERR_UNSUPPORTED                 # M <= 16
+    assert call(4, n=0) == _lib.ERR_UNSUPPORTED             # 2:4 only
+    assert call(4, fmt=1) == _lib.ERR_INVALID_ARG           # formats differ
+    assert call(4, K=512) == _lib.ERR_INVALID_ARG           # K mismatch
+    assert call(4, ldy=32) == _lib.ERR_INVALID_ARG          # ldy < N
+    w.K = 16384
+    assert call(4, K=16384) == _lib.ERR_UNSUPPORTED         # LDS limit
+    assert call(0, K=16384) == _lib.ERR_UNSUPPORTED
+    w.K = 256
+    assert call(0) == _lib.OK                               # nothing to do
