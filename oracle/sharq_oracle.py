@@ -345,6 +345,54 @@ def linear_paths(act: dict, w_codes, w_scales, rows=None):
 
 
 # --------------------------------------------------------------------------
+# Gate/up projection with the SwiGLU epilogue (a synthetic decoder layer's MLP
+# front half; the SharQ README benchmarks whole decoder layers): the packed
+# weight holds the gate and up rows in alternating 16-row blocks, and the
+# layer's output is SiLU(gate) * up of the two SharQ outputs.
+# --------------------------------------------------------------------------
+def interleave_gate_up(w_gate, w_up) -> np.ndarray:
+    """[2F, K] rows: block 2j = gate rows 16j..16j+15, block 2j+1 = the same up rows."""
+    w_gate, w_up = np.asarray(w_gate), np.asarray(w_up)
+    F, K = w_gate.shape
+    if F % 16 or w_up.shape != (F, K):
+        raise ValueError("gate and up must both be [F, K] with F % 16 == 0")
+    return np.stack([w_gate.reshape(F // 16, 16, K), w_up.reshape(F // 16, 16, K)], axis=1).reshape(2 * F, K)
+
+
+def silu(g) -> np.ndarray:
+    """g * sigmoid(g) = g / (1 + exp(-g)) in float64."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def split_gate_up(y) -> tuple:
+    """Columns of the interleaved layer output -> (gate [M, F], up [M, F])."""
+    y = np.asarray(y)
+    M, N2 = y.shape
+    b = y.reshape(M, N2 // 32, 2, 16)
+    return b[:, :, 0, :].reshape(M, N2 // 2), b[:, :, 1, :].reshape(M, N2 // 2)
+
+
+def linear_swiglu(act: dict, w_codes, w_scales, rows=None):
+    """SiLU(gate) * up (float64) of the interleaved gate/up SharQ layer, with the
+    gate's and up's bounds sum|terms|.  Returns (h, b_gate, b_up, gate, up)."""
+    y, b = linear(act, w_codes, w_scales, rows)
+    g, u = split_gate_up(y)
+    bg, bu = split_gate_up(b)
+    return silu(g) * u, bg, bu, g, u
+
+
+def swiglu_bound(g, u, bg, bu, rel: float = 1e-5, abs_: float = 1e-6) -> np.ndarray:
+    """Allowed |h_gpu - h| for h = SiLU(g) u in bf16: the GEMM tolerance of g and u
+    carried through (|SiLU'| <= 1.1), the binary32 evaluation (a few ulps), and
+    the bf16 rounding (half an ulp, 2^-9 relative)."""
+    eg, eu = rel * bg + abs_, rel * bu + abs_
+    h = np.abs(silu(g) * u)
+    return 1.1 * np.abs(u) * eg + np.abs(silu(g)) * eu + eg * eu + h * (2.0 ** -9 + 2.0 ** -20) + 1e-30
+
+
+# --------------------------------------------------------------------------
 # Plain FP4 linear: the comparator the SharQ README benchmarks against (its
 # dense FP4 baseline mode): no backbone, the whole normalised row quantised
 # once, one GEMM.  In the descriptors this is the N:M pattern 0:4.

@@ -68,3 +68,41 @@ def test_paths_sum_to_the_fused_gemm():
     dense_s = dict(r_codes=O.pack_nibbles(act["s_nib"]), r_scales=act["s_scales"])
     ys2, _ = O.linear_dense(dense_s, wc, ws)
     assert np.allclose(ys2, ys, rtol=0, atol=1e-12 * b.max())
+
+
+def test_gate_up_interleave_and_split():
+    rng = np.random.default_rng(6)
+    g = rng.standard_normal((32, 8))
+    u = rng.standard_normal((32, 8))
+    w = O.interleave_gate_up(g, u)
+    assert w.shape == (64, 8)
+    assert np.array_equal(w[0:16], g[0:16]) and np.array_equal(w[16:32], u[0:16])
+    assert np.array_equal(w[32:48], g[16:32]) and np.array_equal(w[48:64], u[16:32])
+    # a layer output's columns follow the weight rows: splitting inverts the interleave
+    y = w.T                                       # [8, 64]: column n is weight row n
+    gg, uu = O.split_gate_up(y)
+    assert np.array_equal(gg, g.T) and np.array_equal(uu, u.T)
+
+
+def test_silu_closed_forms():
+    assert O.silu(0.0) == 0.0
+    assert abs(O.silu(1.0) - 1.0 / (1.0 + np.exp(-1.0))) < 1e-15
+    assert O.silu(-800.0) == 0.0 and O.silu(800.0) == 800.0          # saturation both ways
+    x = np.linspace(-6, 6, 101)
+    assert np.allclose(O.silu(x) - O.silu(-x), x)                      # silu(x) - silu(-x) = x
+
+
+def test_swiglu_equals_split_layers():
+    inp = synth.layer_inputs("tiny", seed=1)
+    rng = np.random.default_rng(3)
+    wg = synth.linear_weight(rng, 32, inp["K"])
+    wu = synth.linear_weight(rng, 32, inp["K"])
+    act = O.prepare(inp["x"], inp["gamma"], inp["eps"])
+    wc, ws = O.pack_weight(O.interleave_gate_up(wg, wu))
+    h, bg, bu, g, u = O.linear_swiglu(act, wc, ws)
+    gc, gs = O.pack_weight(wg)
+    uc, us = O.pack_weight(wu)
+    g2, _ = O.linear(act, gc, gs)
+    u2, _ = O.linear(act, uc, us)
+    assert np.allclose(g, g2, rtol=0, atol=1e-12) and np.allclose(u, u2, rtol=0, atol=1e-12)
+    assert np.allclose(h, O.silu(g2) * u2, rtol=1e-12, atol=1e-15)
