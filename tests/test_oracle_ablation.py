@@ -106,3 +106,16 @@ def test_swiglu_equals_split_layers():
     u2, _ = O.linear(act, uc, us)
     assert np.allclose(g, g2, rtol=0, atol=1e-12) and np.allclose(u, u2, rtol=0, atol=1e-12)
     assert np.allclose(h, O.silu(g2) * u2, rtol=1e-12, atol=1e-15)
+
+
+def test_swiglu_bound_covers_bf16_rounding():
+    """The bound must admit the worst bf16 rounding: a value just above a power of
+    two rounds by up to 2^-8 relative (half an ulp of 8 significant bits)."""
+    h = np.float32(1 + 2 ** -8)                       # halfway between bf16 1 and 1 + 2^-7
+    got = (np.array([O.round_bf16(h)], dtype=np.uint32) << 16).view(np.float32)[0]
+    err = abs(float(got) - float(h))
+    assert err == 2 ** -8
+    g = np.array([30.0])                              # SiLU(30) = 30 to 1e-12
+    u = np.array([float(h) / 30.0])
+    b = O.swiglu_bound(g, u, np.zeros(1), np.zeros(1), rel=0.0, abs_=0.0)
+    assert b[0] >= err * (1 - 1e-9)
