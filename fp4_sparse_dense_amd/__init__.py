@@ -19,6 +19,7 @@ __all__ = [
     "SharqWeight", "SharqAct", "SharqError",
     "sharq_pack_weight", "sharq_prepare", "sharq_linear", "sharq_linear_grouped",
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
+    "sharq_linear_swiglu", "interleave_gate_up",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -257,4 +258,28 @@ def sharq_linear_fused(x, weight: SharqWeight, gamma=None, eps: float = 1e-5, ou
     _lib.check(lib.sharq_linear_fused(_ptr(x), M, K, x.stride(0), _ptr(gamma), eps, 2, 4, FMT_MXFP4,
                                       C.byref(weight.desc), _ptr(out), out.stride(0), out_dtype,
                                       _stream_ptr(stream)), "sharq_linear_fused")
+    return out
+
+
+def interleave_gate_up(w_gate, w_up):
+    """[F, K] gate and up weights -> the [2F, K] stack sharq_linear_swiglu expects
+    (16-row blocks alternating gate, up); pack it with sharq_pack_weight."""
+    torch = _torch()
+    F, K = w_gate.shape
+    if F % 16 or tuple(w_up.shape) != (F, K):
+        raise ValueError("gate and up must both be [F, K] with F % 16 == 0")
+    return torch.stack([w_gate.reshape(F // 16, 16, K), w_up.reshape(F // 16, 16, K)], dim=1).reshape(2 * F, K)
+
+
+def sharq_linear_swiglu(act: SharqAct, weight: SharqWeight, out=None, stream=None):
+    """H [M, N/2] bf16 = SiLU(gate) * up of the interleaved gate/up SharQ layer."""
+    torch = _torch()
+    F = weight.N // 2
+    if out is None:
+        out = torch.empty(act.M, F, dtype=torch.bfloat16, device=act.r_codes.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be a 2-D bf16 tensor with unit inner stride")
+    lib = _lib.load()
+    _lib.check(lib.sharq_linear_swiglu(C.byref(act.desc), C.byref(weight.desc), _ptr(out), out.stride(0),
+                                       _stream_ptr(stream)), "sharq_linear_swiglu")
     return out

@@ -251,7 +251,7 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
     return fail(SHARQ_ERR_UNSUPPORTED, "the two paths must view the same packed scale array (distinct per-path scale arrays are not built)");
   s = check_device();
   if (s) return s;
-  sharq::GemmArgs g;
+  sharq::GemmArgs g{};
   g.s_codes = a->s_codes;
   g.s_meta = a->s_meta;
   g.s_scales = a->s_scales;
@@ -285,6 +285,60 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
                  : a->n == 0 ? sharq::launch_linear_dense(g, static_cast<hipStream_t>(stream))
                              : sharq::launch_linear(g, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "linear launch");
+  return SHARQ_OK;
+}
+
+sharq_status sharq_linear_swiglu(const sharq_act* a, const sharq_weight* w, void* y_bf16_dev, int64_t ldy,
+                                 void* stream) {
+  g_err[0] = 0;
+  if (!a || !w) return fail(SHARQ_ERR_INVALID_ARG, "null descriptor");
+  if (a->struct_size != sizeof(sharq_act) || w->struct_size != sizeof(sharq_weight))
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor struct_size mismatch");
+  if (a->layout_version != SHARQ_ABI_VERSION || w->layout_version != SHARQ_ABI_VERSION)
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor layout_version mismatch (not produced by this library?)");
+  if (a->K != w->K) return fail(SHARQ_ERR_INVALID_ARG, "K mismatch: activation %lld, weight %lld", (long long)a->K, (long long)w->K);
+  if (a->M < 0 || w->N <= 0 || a->K <= 0 || a->K % 32 || a->K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "bad shapes");
+  if (w->N % 32) return fail(SHARQ_ERR_INVALID_ARG, "the gate/up weight needs N %% 32 == 0 (pairs of 16-row blocks), got %lld", (long long)w->N);
+  if (a->fmt != w->fmt) return fail(SHARQ_ERR_INVALID_ARG, "activation and weight formats differ");
+  sharq_status s = check_fmt(a->fmt);
+  if (s) return s;
+  if (a->fmt != SHARQ_FMT_MXFP4 || a->n != 2 || a->m != 4)
+    return fail(SHARQ_ERR_UNSUPPORTED, "the SwiGLU epilogue is built for the 2:4 MXFP4 layer");
+  if (a->M == 0) return SHARQ_OK;
+  if (!y_bf16_dev || !aligned(y_bf16_dev, 2)) return fail(SHARQ_ERR_INVALID_ARG, "output null or misaligned");
+  if (ldy < w->N / 2) return fail(SHARQ_ERR_INVALID_ARG, "ldy=%lld < N/2=%lld", (long long)ldy, (long long)(w->N / 2));
+  if (!a->r_codes || !a->r_scales || !w->codes || !backbone_ok(a, a->n) || !aligned(a->r_codes, 16) ||
+      !aligned(a->r_scales, 16) || !aligned(w->codes, 16))
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor buffers not set or not 16-byte aligned");
+  const sharq_scale_view& vs = w->view[SHARQ_PATH_SPARSE];
+  const sharq_scale_view& vd = w->view[SHARQ_PATH_DENSE];
+  const int64_t nb64 = (w->N + 15) / 16 * 64;
+  if (!vs.base || !vd.base || vs.block != 32 || vd.block != 32 || vs.ld != nb64 || vd.ld != nb64 ||
+      !aligned(vs.base, 16) || !aligned(vd.base, 16))
+    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be tiled MX views (block 32, K-tile stride NB*64)");
+  if (vs.base != vd.base)
+    return fail(SHARQ_ERR_UNSUPPORTED, "the two paths must view the same packed scale array");
+  s = check_device();
+  if (s) return s;
+  sharq::GemmArgs g{};
+  g.s_codes = a->s_codes;
+  g.s_meta = a->s_meta;
+  g.s_scales = a->s_scales;
+  g.r_codes = a->r_codes;
+  g.r_scales = a->r_scales;
+  g.w_codes = w->codes;
+  g.w_scales_sparse = vs.base;
+  g.w_scales_dense = vd.base;
+  g.w_scales_ld = vs.ld;
+  g.y = y_bf16_dev;
+  g.ldy = ldy;
+  g.M = a->M;
+  g.N = w->N;
+  g.K = (int)a->K;
+  g.out_bf16 = 1;
+  g.a_blocks = (a->M + 15) / 16;
+  hipError_t e = sharq::launch_linear_swiglu(g, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "swiglu linear launch");
   return SHARQ_OK;
 }
 
@@ -434,7 +488,7 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
     return fail(SHARQ_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", need, ws_bytes);
   s = check_device();
   if (s) return s;
-  sharq::GroupedArgs ga;
+  sharq::GroupedArgs ga{};
   sharq::GemmArgs& g = ga.gemm;
   g.s_codes = a->s_codes;
   g.s_meta = a->s_meta;

@@ -143,7 +143,7 @@ struct TileCfg {
   static_assert(kMB % NWM == 0 && kNB % NWN == 0, "wave split");
 };
 
-template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE>
+template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE, bool SWIGLU>
 __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
   extern __shared__ __align__(1024) uint8_t smem[];
@@ -447,6 +447,30 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
 
   // single epilogue store of Y_S + Y_R
+  if constexpr (SWIGLU) {
+    static_assert(!GROUPED && !DENSE, "the SwiGLU epilogue follows the 2:4 layer");
+    // the wave's column blocks pair up as (gate, up): the tile starts at an
+    // even block (BN/16 is even) and so does each wave's share
+    static_assert(C::kWNT % 2 == 0 && C::kNB % 2 == 0, "gate/up pairs inside a wave");
+#pragma unroll
+    for (int i = 0; i < C::kWMT; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kWNT; j += 2) {
+        const int64_t col = (nb0 + wn * C::kWNT + j) / 2 * 16 + r16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t row = (rb0 + wm * C::kWMT + i) * 16 + 4 * c4 + q;
+          const float gt = acc[i][j][q], up = acc[i][j + 1][q];
+          const float h = gt / (1.0f + expf(-gt)) * up;
+          if (row < y_rows && col < y_cols / 2) {
+            uint32_t u = __float_as_uint(h);
+            u += 0x7FFFu + ((u >> 16) & 1u);
+            reinterpret_cast<uint16_t*>(g.y)[row * g.ldy + col] = (uint16_t)(u >> 16);
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
@@ -460,10 +484,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     }
 }
 
-template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE>
+template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE, bool SWIGLU = false>
 static hipError_t launch_tiled(const GemmArgs& a, int64_t tiles, hipStream_t stream) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
-  auto kern = dual_gemm_tiled<BM, BN, NWM, NWN, NST, GROUPED, DENSE>;
+  auto kern = dual_gemm_tiled<BM, BN, NWM, NWN, NST, GROUPED, DENSE, SWIGLU>;
   constexpr int lds = C::kStages * C::kStage;
   // the LDS limit is a per-function attribute: set it once per device
   int dev = 0;
@@ -543,6 +567,17 @@ static hipError_t launch_linear_t(const GemmArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_linear(const GemmArgs& a, hipStream_t stream) { return launch_linear_t<false>(a, stream); }
+
+hipError_t launch_linear_swiglu(const GemmArgs& a, hipStream_t stream) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  const uint64_t kb = (a.K + 127) / 128;
+  if ((uint64_t)((a.M + 15) / 16) * kb * 1024 >= 0x7FFFFFFFull || (uint64_t)((a.N + 15) / 16) * kb * 1024 >= 0x7FFFFFFFull)
+    return hipErrorInvalidValue;
+  const int64_t tm = (a.M + kTileM - 1) / kTileM, tn = (a.N + kTileN - 1) / kTileN;
+  GemmArgs b = a;
+  b.xcd_bm = xcd_region_m(tm, tn, a.K);
+  return launch_tiled<kTileM, kTileN, 4, 2, 3, false, false, true>(b, tm * tn, stream);
+}
 
 hipError_t launch_linear_dense(const GemmArgs& a, hipStream_t stream) { return launch_linear_t<true>(a, stream); }
 

@@ -55,6 +55,10 @@ hipError_t launch_linear(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_prepare_dense(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
                                 float eps, PrepOut out, hipStream_t stream);
 hipError_t launch_linear_dense(const GemmArgs& a, hipStream_t stream);
+// SwiGLU epilogue: the weight's 16-row blocks alternate gate and up, and
+// y[m][16j + c] = bf16(SiLU(gate) * up) of the column pair (block 2j,
+// block 2j + 1), column c; y is bf16 with row stride ldy.  The tiled kernel.
+hipError_t launch_linear_swiglu(const GemmArgs& a, hipStream_t stream);
 
 // The whole layer in one launch for M <= 16 (every workgroup prepares the rows
 // into LDS); fused_layer_lds_bytes must be <= 160 KiB.

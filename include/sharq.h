@@ -253,6 +253,18 @@ sharq_status sharq_rmsnorm(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
  * Errors: INVALID_ARG (null, n<0, misaligned), UNSUPPORTED (not gfx950), HIP. */
 sharq_status sharq_add_f32(const float* a_dev, const float* b_dev, float* y_dev, int64_t n, void* stream);
 
+/* Gate/up projection of a gated MLP with the SwiGLU epilogue: the SharQ layer
+ * Y = X W_gu^T on the packed [2F, K] weight whose 16-row blocks alternate gate
+ * and up (block 2j = gate rows 16j..16j+15, block 2j+1 = up rows 16j..16j+15),
+ * and one epilogue writes H[M,F] = bf16(SiLU(gate) * up) (binary32 SiLU
+ * g / (1 + exp(-g)), then the product, rounded to nearest even) -- the bf16
+ * input of the down projection's preparation, never materialising Y.
+ * y: device bf16, row stride ldy >= F = N/2.  Runs the tiled kernel.
+ * Errors: INVALID_ARG (null, shapes, N % 32, K mismatch, ldy, misaligned),
+ * UNSUPPORTED (not 2:4 MXFP4, not gfx950), HIP. */
+sharq_status sharq_linear_swiglu(const sharq_act* a, const sharq_weight* w, void* y_bf16_dev, int64_t ldy,
+                                 void* stream);
+
 /* The whole layer in one launch for small M (decode): Y[M,N] of the bf16
  * activation X[M,K] (row stride ldx) and the packed weight, exactly
  * sharq_prepare followed by sharq_linear -- the same arithmetic, identical

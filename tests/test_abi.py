@@ -244,3 +244,25 @@ def test_fused_layer_rejects_before_launch(lib):
     assert call(0, K=16384) == _lib.ERR_UNSUPPORTED
     w.K = 256
     assert call(0) == _lib.OK                               # nothing to do
+
+
+def test_swiglu_rejects_before_launch(lib):
+    a = _act()
+    a.layout_version = _lib.SHARQ_ABI_VERSION
+    a.M, a.K, a.n, a.m = 64, 256, 2, 4
+    w = _lib.WeightDesc()
+    w.struct_size = C.sizeof(_lib.WeightDesc)
+    w.layout_version = _lib.SHARQ_ABI_VERSION
+    w.N, w.K, w.codes, w.scales = 48, 256, 0x100000, 0x200000
+    for p in (0, 1):
+        w.view[p].base, w.view[p].ld, w.view[p].block = 0x200000, 3 * 64, 32
+    y = C.c_void_p(0x600000)
+    assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 24, None) == _lib.ERR_INVALID_ARG   # N % 32
+    w.N = 64
+    for p in (0, 1):
+        w.view[p].ld = 4 * 64
+    assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 16, None) == _lib.ERR_INVALID_ARG   # ldy < N/2
+    a.n = 0
+    assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 32, None) == _lib.ERR_UNSUPPORTED   # 2:4 only
+    a.n, a.M = 2, 0
+    assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 32, None) == _lib.OK
