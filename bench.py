@@ -158,7 +158,7 @@ def timed(step, steps, warmup, graph=False):
         wall = time.perf_counter() - t0
         evs = []
         for i in range(steps):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(step.parts + 1)]
             step(i, ev, stream)
             evs.append(ev)
         torch.cuda.synchronize()
@@ -200,7 +200,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qkv", choices=sorted(list(WORKLOADS) + ["moe"]))
+    ap.add_argument("--workload", default="qkv", choices=sorted(list(WORKLOADS) + ["moe", "layer"]))
     ap.add_argument("--m", type=int, default=1, help="rows of the decode workload")
     ap.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "nvfp4"],
                     help="FP4 format (nvfp4: the decode workload only)")
@@ -232,6 +232,10 @@ def main():
     if args.fmt == "nvfp4" and args.workload != "decode":
         print("the NVFP4-style path is built for the decode workload (--workload decode)", file=sys.stderr)
         sys.exit(2)
+    special = args.workload in ("moe", "layer")
+    if special and (args.fmt != "mxfp4" or args.mode != "sharq" or args.fused or args.ablation != "none"):
+        print("the moe and layer workloads run the default MXFP4 SharQ layers", file=sys.stderr)
+        sys.exit(2)
     if args.mode == "dense" and (args.fmt != "mxfp4" or args.workload == "moe"):
         print("the plain FP4 linear is built for MXFP4 dense layers", file=sys.stderr)
         sys.exit(2)
@@ -246,6 +250,8 @@ def main():
         sys.exit(2)
     if args.workload == "moe":
         rec = run_moe(args)
+    elif args.workload == "layer":
+        rec = run_layer(args)
     else:
         rec = run_dense(args)
     print(json.dumps(rec), flush=True)
@@ -391,6 +397,110 @@ def run_dense(args):
         "roofline": roof,
         "cpu_baseline": cpu,
         "parts_us": {k: round(v * 1e3, 3) for k, v in zip(part_names, part_ms)},
+    }
+
+
+LAYER = dict(M=2048, d=4096, qkv=6144, ff=14336)
+
+
+def run_layer(args):
+    """A synthetic Llama-3.1-8B decoder layer of SharQ linears, batch 1 x 2048
+    tokens, random weights: prep(x, g1) -> QKV -> [attention stand-in: the Q
+    columns of the bf16 QKV output, a strided view] -> prep -> O -> residual ->
+    prep(h, g2) -> gate/up with the SwiGLU epilogue (bf16) -> prep -> down ->
+    residual.  Attention itself is not part of the SharQ hot path."""
+    import numpy as np
+    import torch
+
+    import fp4_sparse_dense_amd as sq
+    from fp4_sparse_dense_amd import synth
+
+    M, d, nq, ff = LAYER["M"], LAYER["d"], LAYER["qkv"], LAYER["ff"]
+    dev = torch.device("cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    inp = synth.layer_inputs("qkv", seed=300, with_weight=False)
+    x = up(inp["x"])
+    g1 = up(inp["gamma"])
+    g2 = up(synth.norm_weight(np.random.default_rng(301), d))
+    w_bytes = (nq * d + d * d + 2 * ff * d + d * ff) * 17 // 32
+    nsets = args.sets or max(2, -(-ROTATE_BYTES // w_bytes))
+    sets = []
+    for s_ in range(nsets):
+        wgu = sq.interleave_gate_up(device_weight(gen, ff, d), device_weight(gen, ff, d))
+        sets.append(dict(qkv=sq.sharq_pack_weight(device_weight(gen, nq, d)),
+                         o=sq.sharq_pack_weight(device_weight(gen, d, d)),
+                         gu=sq.sharq_pack_weight(wgu),
+                         down=sq.sharq_pack_weight(device_weight(gen, d, ff))))
+        del wgu
+    b = dict(a1=sq.SharqAct(M, d, dev), a2=sq.SharqAct(M, d, dev), a3=sq.SharqAct(M, d, dev),
+             a4=sq.SharqAct(M, ff, dev),
+             qkv=torch.empty(M, nq, dtype=torch.bfloat16, device=dev),
+             o=torch.empty(M, d, dtype=torch.float32, device=dev),
+             h=torch.empty(M, d, dtype=torch.bfloat16, device=dev),
+             mid=torch.empty(M, ff, dtype=torch.bfloat16, device=dev),
+             dn=torch.empty(M, d, dtype=torch.float32, device=dev),
+             out=torch.empty(M, d, dtype=torch.bfloat16, device=dev))
+    torch.cuda.synchronize()
+    names = ["prep_qkv", "gemm_qkv", "prep_o", "gemm_o", "residual_1", "prep_gateup", "gemm_gateup_swiglu",
+             "prep_down", "gemm_down", "residual_2"]
+
+    def launches(i):
+        w = sets[i % nsets]
+        return [lambda: sq.sharq_prepare(x, g1, 1e-5, out=b["a1"]),
+                lambda: sq.sharq_linear(b["a1"], w["qkv"], out=b["qkv"], out_dtype=sq.OUT_BF16),
+                lambda: sq.sharq_prepare(b["qkv"][:, :d], None, 1e-5, out=b["a2"]),
+                lambda: sq.sharq_linear(b["a2"], w["o"], out=b["o"]),
+                lambda: sq.sharq_add_bf16_f32(x, b["o"], out=b["h"]),
+                lambda: sq.sharq_prepare(b["h"], g2, 1e-5, out=b["a3"]),
+                lambda: sq.sharq_linear_swiglu(b["a3"], w["gu"], out=b["mid"]),
+                lambda: sq.sharq_prepare(b["mid"], None, 1e-5, out=b["a4"]),
+                lambda: sq.sharq_linear(b["a4"], w["down"], out=b["dn"]),
+                lambda: sq.sharq_add_bf16_f32(b["h"], b["dn"], out=b["out"])]
+
+    def step(i, ev=None, stream=None, part=None):
+        fns = launches(i)
+        if ev is not None:
+            ev[0].record(stream)
+        for j, fn in enumerate(fns):
+            if part in (None, j):
+                fn()
+            if ev is not None:
+                ev[j + 1].record(stream)
+    step.parts = len(names)
+
+    ms, parts = timed(step, args.steps, args.warmup)
+    part_ms = [float(np.mean(p)) for p in parts]
+    shapes = {"gemm_qkv": nq * d, "gemm_o": d * d, "gemm_gateup_swiglu": 2 * ff * d, "gemm_down": d * ff}
+    flops = sum(4 * M * nk for nk in shapes.values())
+    j = names.index("gemm_gateup_swiglu")
+    gu_tflops = 4 * M * 2 * ff * d / (part_ms[j] * 1e-3) / 1e12
+    return {
+        "metric": "SharQ decoder layer TFLOPS (4*M*N*K summed over the layer's four SharQ linears)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": f"layer: synthetic Llama-3.1-8B decoder layer of SharQ linears, batch 1 x {M} tokens "
+                               "(QKV 6144, O 4096, gate/up 2x14336 with the SwiGLU epilogue, down 4096); attention "
+                               "replaced by the Q columns of the QKV output; random weights; 2:4 mask; MXFP4",
+                   "M": M, "rotating_sets": nsets},
+        "roofline": {"bound": "mfma", "achieved": round(gu_tflops, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tflops / PEAK_FP4_TFLOPS, 4), "traffic": None,
+                     "kernel": "gate/up GEMM with the SwiGLU epilogue"},
+        "cpu_baseline": None,
+        "parts_us": {k: round(v * 1e3, 3) for k, v in zip(names, part_ms)},
     }
 
 

@@ -19,7 +19,7 @@ __all__ = [
     "SharqWeight", "SharqAct", "SharqError",
     "sharq_pack_weight", "sharq_prepare", "sharq_linear", "sharq_linear_grouped",
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
-    "sharq_linear_swiglu", "interleave_gate_up",
+    "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -282,4 +282,19 @@ def sharq_linear_swiglu(act: SharqAct, weight: SharqWeight, out=None, stream=Non
     lib = _lib.load()
     _lib.check(lib.sharq_linear_swiglu(C.byref(act.desc), C.byref(weight.desc), _ptr(out), out.stride(0),
                                        _stream_ptr(stream)), "sharq_linear_swiglu")
+    return out
+
+
+def sharq_add_bf16_f32(x, y, out=None, stream=None):
+    """out = bf16(x + y): x bf16, y fp32 (contiguous, same size); the residual add."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or y.dtype != torch.float32 or x.numel() != y.numel():
+        raise ValueError("x must be bf16 and y fp32, of one size")
+    if not (x.is_contiguous() and y.is_contiguous()):
+        raise ValueError("x and y must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    lib = _lib.load()
+    _lib.check(lib.sharq_add_bf16_f32(_ptr(x), _ptr(y), _ptr(out), x.numel(), _stream_ptr(stream)),
+               "sharq_add_bf16_f32")
     return out

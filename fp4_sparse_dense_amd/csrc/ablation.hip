@@ -5,6 +5,7 @@
 //   unfused RMSNorm: a standalone normalisation writes the normalised row in
 //     bf16 (round to nearest even); the preparation then runs without gamma on
 //     that row.  The bf16 rounding is the numerical price of not fusing.
+//   residual add (the synthetic decoder layer): bf16 + fp32 -> bf16.
 //   unfused epilogue: the two GEMM paths run as separate launches into two
 //     fp32 outputs, then one elementwise add.  (With the backbone stored as a
 //     masked dense operand, either path alone is the plain FP4 GEMM pointed at
@@ -58,6 +59,33 @@ __global__ __launch_bounds__(256) void add_f32_kernel(const float* __restrict__ 
   }
 }
 
+// out = bf16(x + y) (binary32 sum of a bf16 and an fp32 element, rounded to
+// nearest even): the residual add of a decoder layer.  Four elements per
+// thread when every pointer is 8-byte aligned for x/out and 16 for y.
+__global__ __launch_bounds__(256) void add_bf16_f32_kernel(const uint16_t* __restrict__ x, const float* __restrict__ y,
+                                                           uint16_t* __restrict__ out, int64_t n, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  auto one = [](uint16_t xb, float yv) -> uint16_t {
+    uint32_t u = __float_as_uint(__uint_as_float((uint32_t)xb << 16) + yv);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+  };
+  int64_t start = 0;
+  if (vec) {
+    const int64_t n4 = n / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+      const uint2 xv = reinterpret_cast<const uint2*>(x)[i];
+      const float4 yv = reinterpret_cast<const float4*>(y)[i];
+      uint2 o;
+      o.x = (uint32_t)one((uint16_t)xv.x, yv.x) | ((uint32_t)one((uint16_t)(xv.x >> 16), yv.y) << 16);
+      o.y = (uint32_t)one((uint16_t)xv.y, yv.z) | ((uint32_t)one((uint16_t)(xv.y >> 16), yv.w) << 16);
+      reinterpret_cast<uint2*>(out)[i] = o;
+    }
+    start = n4 * 4;
+  }
+  for (int64_t i = start + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) out[i] = one(x[i], y[i]);
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma, float eps,
@@ -65,6 +93,16 @@ hipError_t launch_rmsnorm_bf16(const uint16_t* x, int64_t M, int K, int64_t ldx,
   if (M == 0) return hipSuccess;
   if (M > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, ldx, K, gamma, eps, y, ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_bf16_f32(const uint16_t* x, const float* y, uint16_t* out, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out)) & 7) == 0 &&
+                  (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+  int64_t blocks = (n / (vec ? 4 : 1) + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 8192 ? 8192 : blocks);
+  hipLaunchKernelGGL(add_bf16_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, y, out, n, vec);
   return hipGetLastError();
 }
 

@@ -416,6 +416,21 @@ sharq_status sharq_rmsnorm(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
   return SHARQ_OK;
 }
 
+sharq_status sharq_add_bf16_f32(const void* x_bf16_dev, const float* y_dev, void* out_bf16_dev, int64_t n,
+                                void* stream) {
+  g_err[0] = 0;
+  if (n < 0) return fail(SHARQ_ERR_INVALID_ARG, "n=%lld", (long long)n);
+  if (n == 0) return SHARQ_OK;
+  if (!x_bf16_dev || !y_dev || !out_bf16_dev) return fail(SHARQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(x_bf16_dev, 2) || !aligned(y_dev, 4) || !aligned(out_bf16_dev, 2)) return fail(SHARQ_ERR_INVALID_ARG, "misaligned");
+  sharq_status s = check_device();
+  if (s) return s;
+  hipError_t e = sharq::launch_add_bf16_f32(static_cast<const uint16_t*>(x_bf16_dev), y_dev,
+                                            static_cast<uint16_t*>(out_bf16_dev), n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "add launch");
+  return SHARQ_OK;
+}
+
 sharq_status sharq_add_f32(const float* a_dev, const float* b_dev, float* y_dev, int64_t n, void* stream) {
   g_err[0] = 0;
   if (n < 0) return fail(SHARQ_ERR_INVALID_ARG, "n=%lld", (long long)n);

@@ -70,6 +70,7 @@ hipError_t launch_linear_fused(const uint16_t* x, int M, int K, int64_t ldx, con
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma, float eps,
                                uint16_t* y, int64_t ldy, hipStream_t stream);
 hipError_t launch_add_f32(const float* a, const float* b, float* y, int64_t n, hipStream_t stream);
+hipError_t launch_add_bf16_f32(const uint16_t* x, const float* y, uint16_t* out, int64_t n, hipStream_t stream);
 
 // Grouped expert layer: rows of a prepared activation gathered (or taken in
 // order) into expert segments padded to whole 16-row blocks, then one tiled

@@ -246,6 +246,13 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w,
 sharq_status sharq_rmsnorm(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx, const void* gamma_bf16_dev,
                            float eps, void* y_bf16_dev, int64_t ldy, void* stream);
 
+/* out[i] = bf16(x[i] + y[i]) for n elements: x bf16, y fp32, the binary32 sum
+ * rounded to nearest even (out may alias x): the residual add of the
+ * synthetic decoder layer built from SharQ layers.
+ * Errors: INVALID_ARG (null, n<0, misaligned), UNSUPPORTED (not gfx950), HIP. */
+sharq_status sharq_add_bf16_f32(const void* x_bf16_dev, const float* y_dev, void* out_bf16_dev, int64_t n,
+                                void* stream);
+
 /* y[i] = a[i] + b[i] for n fp32 elements (device pointers; y may alias a or b):
  * the add of the unfused epilogue, whose two paths are two sharq_linear calls
  * on descriptors with pattern 0:4 whose r_codes / r_scales point at the

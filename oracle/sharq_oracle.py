@@ -334,6 +334,11 @@ def rmsnorm_bf16(x_bits, gamma_bits, eps: float) -> np.ndarray:
     return round_bf16(rmsnorm(x_bits, gamma_bits, eps))
 
 
+def residual_add_bf16(x_bits, y) -> np.ndarray:
+    """The decoder layer's residual add: bf16 bits of (binary32 x + binary32 y)."""
+    return round_bf16(widen_bf16(x_bits) + np.asarray(y, dtype=F32))
+
+
 def linear_paths(act: dict, w_codes, w_scales, rows=None):
     """The two paths of the dual GEMM on their own (float64): (y_s, y_r, bound)."""
     K = 2 * np.asarray(w_codes).shape[1]

@@ -55,3 +55,18 @@ def test_unfused_epilogue(M, K, N):
     assert_linear_close(y.cpu().numpy(), rs + rr, b, f"unfused M={M}")
     # the add kernel is exact binary32 addition
     assert torch.equal(y, ys + yr)
+
+
+@pytest.mark.parametrize("n,off", [(1 << 20, 0), (1000003, 0), (4099, 1)])
+def test_residual_add_bit_exact(n, off):
+    import torch
+    print(f"residual add n={n} off={off}", flush=True)
+    rng = np.random.default_rng(n)
+    x = synth.bf16_bits_from_f32(rng.standard_normal(n + off).astype(np.float32) * 4)
+    y = (rng.standard_normal(n + off) * 3).astype(np.float32)
+    xd = dev_bf16(x)[off:]
+    yd = torch.from_numpy(y).cuda()[off:]
+    out = sq.sharq_add_bf16_f32(xd, yd)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, O.residual_add_bf16(x[off:], y[off:]))

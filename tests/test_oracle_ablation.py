@@ -119,3 +119,11 @@ def test_swiglu_bound_covers_bf16_rounding():
     u = np.array([float(h) / 30.0])
     b = O.swiglu_bound(g, u, np.zeros(1), np.zeros(1), rel=0.0, abs_=0.0)
     assert b[0] >= err * (1 - 1e-9)
+
+
+def test_residual_add_closed_forms():
+    x = np.array([0x3F80, 0xBF80, 0x4000, 0x0000], dtype=np.uint16)      # 1, -1, 2, 0
+    y = np.array([0.5, 1.0, 2 ** -8, -0.0], dtype=np.float32)
+    got = O.residual_add_bf16(x, y)
+    # 1.5 exact; -1 + 1 = +0; 2 + 2^-8 rounds to 2 (below half an ulp, 2^-7); 0 + -0 = +0
+    assert list(got) == [0x3FC0, 0x0000, 0x4000, 0x0000]
