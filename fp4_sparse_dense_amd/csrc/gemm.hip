@@ -507,14 +507,26 @@ static hipError_t launch_tiled(const GemmArgs& a, int64_t tiles, hipStream_t str
 }
 
 // tile shape of the tiled kernel (M tile also used to count grouped tiles)
-constexpr int kTileM = 256, kTileN = 192;
+constexpr int kTileM = 256, kTileN = 192, kTileNarrow = 128;
 int grouped_tile_m() { return kTileM; }
+
+// compute units of the current device (cached per device), <= 0 on error
+static int compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  static std::atomic<int> cached[64];
+  int n = cached[dev].load(std::memory_order_acquire);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+  cached[dev].store(n, std::memory_order_release);
+  return n;
+}
 
 // M tiles per XCD region for a tm x tn tile grid split into 8 equal regions of
 // bm x bn tiles: the shape that minimises the operand bytes one XCD reads
 // (bm activation tiles at 1.0625 B/elem, bn weight tiles at 0.53125 B/elem);
 // 0 when no such split exists.
-static int xcd_region_m(int64_t tm, int64_t tn, int K) {
+static int xcd_region_m(int64_t tm, int64_t tn, int bm_rows, int bn_cols) {
   const int64_t T = tm * tn;
   if (T % 8 != 0) return 0;
   const int64_t per = T / 8;
@@ -524,10 +536,9 @@ static int xcd_region_m(int64_t tm, int64_t tn, int K) {
     if (tm % bm || per % bm) continue;
     const int64_t bn = per / bm;
     if (tn % bn) continue;
-    const double cost = (double)bm * kTileM * 1.0625 + (double)bn * kTileN * 0.53125;
+    const double cost = (double)bm * bm_rows * 1.0625 + (double)bn * bn_cols * 0.53125;
     if (best == 0 || cost < best_cost) { best = (int)bm; best_cost = cost; }
   }
-  (void)K;
   return best;
 }
 
@@ -545,10 +556,23 @@ static hipError_t launch_linear_t(const GemmArgs& a, hipStream_t stream) {
   const bool fits = (uint64_t)((a.M + 15) / 16) * kb * 1024 < 0x7FFFFFFFull &&
                     (uint64_t)((a.N + 15) / 16) * kb * 1024 < 0x7FFFFFFFull;
   if (a.M > 64 && fits) {
-    const int64_t tm = (a.M + kTileM - 1) / kTileM, tn = (a.N + kTileN - 1) / kTileN;
+    // 256 x 192 tiles, or 256 x 128 ones when those need no more waves of one
+    // workgroup per compute unit: a grid that already fits in the waves the
+    // wider tile needs then runs the shorter tile (N = 4096 at M = 2048: 256
+    // tiles of 128 columns fill the chip once where 176 of 192 leave a third
+    // of it idle)
+    const int cus = compute_units();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const int64_t tm = (a.M + kTileM - 1) / kTileM;
+    const int64_t tn_wide = (a.N + kTileN - 1) / kTileN, tn_narrow = (a.N + kTileNarrow - 1) / kTileNarrow;
+    const bool narrow = (tm * tn_narrow + cus - 1) / cus <= (tm * tn_wide + cus - 1) / cus;
     GemmArgs b = a;
-    b.xcd_bm = xcd_region_m(tm, tn, a.K);
-    return launch_tiled<kTileM, kTileN, 4, 2, 3, false, DENSE>(b, tm * tn, stream);
+    if (narrow) {
+      b.xcd_bm = xcd_region_m(tm, tn_narrow, kTileM, kTileNarrow);
+      return launch_tiled<kTileM, kTileNarrow, 4, 2, 3, false, DENSE>(b, tm * tn_narrow, stream);
+    }
+    b.xcd_bm = xcd_region_m(tm, tn_wide, kTileM, kTileN);
+    return launch_tiled<kTileM, kTileN, 4, 2, 3, false, DENSE>(b, tm * tn_wide, stream);
   }
   // M <= 64 (or operands past 31-bit buffer offsets): split-K weight streaming;
   // eight waves per column block for one or two row blocks, four for more
@@ -575,7 +599,7 @@ hipError_t launch_linear_swiglu(const GemmArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
   const int64_t tm = (a.M + kTileM - 1) / kTileM, tn = (a.N + kTileN - 1) / kTileN;
   GemmArgs b = a;
-  b.xcd_bm = xcd_region_m(tm, tn, a.K);
+  b.xcd_bm = xcd_region_m(tm, tn, kTileM, kTileN);
   return launch_tiled<kTileM, kTileN, 4, 2, 3, false, false, true>(b, tm * tn, stream);
 }
 
