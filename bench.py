@@ -56,7 +56,9 @@ WORKLOADS = {
 MOE = dict(tokens=4096, experts=128, top_k=8, d_model=2048, d_ff=768)
 ROTATE_BYTES = 600 << 20       # rotating sets exceed the 256 MB MALL
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dual_gemm_qkv.txt")
-GEMM_SRC = os.path.join(ROOT, "fp4_sparse_dense_amd", "csrc", "gemm.hip")
+# the dual GEMM's source: its kernel file and the headers it compiles with
+GEMM_SRC = [os.path.join(ROOT, "fp4_sparse_dense_amd", "csrc", f)
+            for f in ("gemm.hip", "gemm_common.h", "device_common.h", "launch.h")]
 
 
 def prep_bytes(M, K, norm=True, nv=False, dense=False):
@@ -84,8 +86,11 @@ def gemm_bytes(M, N, K, out_bytes=4, nv=False, dense=False):
     return M * K * 17 // 16 + N * K * 17 // 32 + out_bytes * M * N
 
 
-def source_digest(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
