@@ -143,6 +143,15 @@ struct TileCfg {
   static_assert(kMB % NWM == 0 && kNB % NWN == 0, "wave split");
 };
 
+// One 16x16 output block of the tiled kernel, computed transposed: the weight
+// fragment is the MFMA's first operand and the activation fragment its second,
+// so lane (c4 = lane / 16, r16 = lane % 16) accumulates output row r16, columns
+// 4*c4 .. 4*c4+3 of the block -- four consecutive outputs of one row, stored
+// with one 16-byte (fp32) or 8-byte (bf16) write.
+__device__ __forceinline__ v4f mfma_yt(v8i act, v8i w, v4f c, uint32_t s_act, uint32_t s_w) {
+  return mfma_fp4(w, act, c, s_w, s_act);
+}
+
 template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE, bool SWIGLU>
 __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
-      for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
+      for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_yt(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     const uint32_t cst = lds0 + stage_off(ks);   // slot of step ks, free after the barrier
@@ -366,7 +375,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < C::kWNT; ++j) {
 #pragma unroll
-      for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
+      for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_yt(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
       __builtin_amdgcn_sched_barrier(0);   // keep the refill after the column's last use
       const int blk = wn * C::kWNT + j;
       fb[j] = frag(nx, C::kOffB, blk);
@@ -395,7 +404,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < JH; ++j)
 #pragma unroll
-      for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
+      for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_yt(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     const uint32_t cst = lds0 + stage_off(ks);
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     for (int j = 0; j < C::kWNT; ++j) {
       if (j >= JH) {
 #pragma unroll
-        for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
+        for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_yt(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
       }
       __builtin_amdgcn_sched_barrier(0);
       const int blk = wn * C::kWNT + j;
@@ -439,12 +448,12 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
-      for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_fp4(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
+      for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_yt(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
   }
 #pragma unroll
   for (int j = 0; j < C::kWNT; ++j)
 #pragma unroll
-    for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_fp4(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
+    for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_yt(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
 
   // single epilogue store of Y_S + Y_R
   if constexpr (SWIGLU) {
@@ -452,34 +461,51 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     // the wave's column blocks pair up as (gate, up): the tile starts at an
     // even block (BN/16 is even) and so does each wave's share
     static_assert(C::kWNT % 2 == 0 && C::kNB % 2 == 0, "gate/up pairs inside a wave");
+    const int64_t hcols = y_cols / 2;
+    const bool vec = ((uintptr_t)g.y & 7) == 0 && (g.ldy & 3) == 0;
 #pragma unroll
     for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
       for (int j = 0; j < C::kWNT; j += 2) {
-        const int64_t col = (nb0 + wn * C::kWNT + j) / 2 * 16 + r16;
+        const int64_t row = (rb0 + wm * C::kWMT + i) * 16 + r16;
+        const int64_t col = (nb0 + wn * C::kWNT + j) / 2 * 16 + 4 * c4;
+        uint32_t hb[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t row = (rb0 + wm * C::kWMT + i) * 16 + 4 * c4 + q;
           const float gt = acc[i][j][q], up = acc[i][j + 1][q];
-          const float h = gt / (1.0f + expf(-gt)) * up;
-          if (row < y_rows && col < y_cols / 2) {
-            uint32_t u = __float_as_uint(h);
-            u += 0x7FFFu + ((u >> 16) & 1u);
-            reinterpret_cast<uint16_t*>(g.y)[row * g.ldy + col] = (uint16_t)(u >> 16);
-          }
+          uint32_t u = __float_as_uint(gt / (1.0f + expf(-gt)) * up);
+          u += 0x7FFFu + ((u >> 16) & 1u);
+          hb[q] = u >> 16;
+        }
+        if (row >= y_rows) continue;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(g.y) + row * g.ldy + col;
+        if (vec && col + 3 < hcols) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (col + q < hcols) dst[q] = (uint16_t)hb[q];
         }
       }
     return;
   }
+  // four consecutive outputs per lane and block: one 16-byte (fp32) or 8-byte
+  // (bf16) store where the row stride and base allow it and all four columns
+  // exist, else element by element
+  const bool vec = ((uintptr_t)g.y & 15) == 0 && (g.ldy & 3) == 0;
 #pragma unroll
   for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll
     for (int j = 0; j < C::kWNT; ++j) {
-      const int64_t col = (nb0 - nb_first + wn * C::kWNT + j) * 16 + r16;
+      const int64_t row = (rb0 - rb_first + wm * C::kWMT + i) * 16 + r16;
+      const int64_t col = (nb0 - nb_first + wn * C::kWNT + j) * 16 + 4 * c4;
+      if (row >= y_rows) continue;
+      if (vec && col + 3 < y_cols) {
+        store_out4(g, y_row0 + row, col, acc[i][j]);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row = (rb0 - rb_first + wm * C::kWMT + i) * 16 + 4 * c4 + q;
-        if (row < y_rows && col < y_cols) store_out(g, y_row0 + row, col, acc[i][j][q]);
+        for (int q = 0; q < 4; ++q)
+          if (col + q < y_cols) store_out(g, y_row0 + row, col + q, acc[i][j][q]);
       }
     }
 }

@@ -31,4 +31,21 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, int64_t row, int64_
   }
 }
 
+// four consecutive outputs of one row (16-byte aligned for fp32, 8-byte for bf16)
+__device__ __forceinline__ void store_out4(const GemmArgs& g, int64_t row, int64_t col, v4f v) {
+  if (g.out_bf16) {
+    uint32_t h[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t u = __float_as_uint(v[q]);
+      u += 0x7FFFu + ((u >> 16) & 1u);
+      h[q] = u >> 16;
+    }
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.y) + row * g.ldy + col) =
+        make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.y) + row * g.ldy + col) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 }  // namespace sharq
