@@ -62,6 +62,10 @@ constexpr int kUnitK = 256;
 constexpr int kSlotBytes = kPrepRows * kUnitK * 2;
 constexpr uint32_t kPrepLdsMax = 160 * 1024;
 constexpr int kMaxSlots = 4;
+// gamma in LDS: each 32-element block padded to 36 binary32 (or 40 bf16)
+// words, so the 16-byte reads of the eight distinct blocks a wave touches at
+// once (two K tiles x four chunks) fall into eight different bank groups
+constexpr uint32_t kGammaBlockF32 = 36, kGammaBlockBf16 = 40;
 
 struct PrepPlan {
   int nunits;      // units of 256 along K
@@ -81,9 +85,9 @@ static PrepPlan prep_plan(int K, bool norm) {
   const uint32_t kp = (uint32_t)p.nunits * kUnitK;
   const uint32_t sums = norm ? (uint32_t)p.units_p2 * kPrepRows * 4 : 0;
   for (int f32 = norm ? 1 : 0; f32 >= 0; --f32) {
-    const uint32_t gbytes = norm ? kp * (f32 ? 4u : 2u) : 0;
-    const uint32_t avail = kPrepLdsMax - gbytes - sums;
-    int s = (int)(avail / (kPrepWaves * kSlotBytes));
+    const uint32_t gbytes = norm ? kp / 32u * (f32 ? kGammaBlockF32 * 4u : kGammaBlockBf16 * 2u) : 0;
+    const int64_t avail = (int64_t)kPrepLdsMax - gbytes - sums;
+    int s = avail > 0 ? (int)(avail / (kPrepWaves * kSlotBytes)) : 0;
     s = s < kMaxSlots ? s : kMaxSlots;
     p.gamma_f32 = f32;
     p.single = norm && per_wave <= s;
@@ -178,11 +182,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
     for (int e = tid * 8; e < kp; e += kPrepThreads * 8) {
       const uint4 q = e < K ? *reinterpret_cast<const uint4*>(gamma + e) : make_uint4(0, 0, 0, 0);
       if (GF32) {
-        float* gs = reinterpret_cast<float*>(smem + P.off_gamma);
-        *reinterpret_cast<float4*>(gs + e) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
-        *reinterpret_cast<float4*>(gs + e + 4) = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
+        float* gs = reinterpret_cast<float*>(smem + P.off_gamma) + e + (kGammaBlockF32 - 32) * (e / 32);
+        *reinterpret_cast<float4*>(gs) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+        *reinterpret_cast<float4*>(gs + 4) = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
       } else {
-        *reinterpret_cast<uint4*>(smem + P.off_gamma + e * 2) = q;
+        *reinterpret_cast<uint4*>(smem + P.off_gamma + (e + (kGammaBlockBf16 - 32) * (e / 32)) * 2) = q;
       }
     }
     for (int i = P.nunits * kPrepRows + tid; i < P.units_p2 * kPrepRows; i += kPrepThreads) sums[i] = 0.0f;
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
     const int kb = (2 * u + t2) * 128 + c4 * 32;   // first element of the block
     if (NORM) {
       if (GF32) {
-        const float* gs = reinterpret_cast<const float*>(smem + P.off_gamma) + kb;
+        const float* gs = reinterpret_cast<const float*>(smem + P.off_gamma) + kb / 32 * kGammaBlockF32;
 #pragma unroll
         for (int i = 0; i < 32; i += 4) {
           const float4 g = *reinterpret_cast<const float4*>(gs + i);
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
           v[i + 3] = (v[i + 3] * inv) * g.w;
         }
       } else {
-        const uint8_t* gb = smem + P.off_gamma + kb * 2;
+        const uint8_t* gb = smem + P.off_gamma + kb / 32 * kGammaBlockBf16 * 2;
 #pragma unroll
         for (int i = 0; i < 32; i += 8) {
           const uint4 g = *reinterpret_cast<const uint4*>(gb + i * 2);

@@ -31,19 +31,14 @@ struct Block32 {
 //    elements 1 and 2 are both dropped or both kept; if exactly one is, the
 //    other kept element is whichever of 1 and 2 beats the other
 //    (|a1| >= |a2| for element 1).
-// group_keep evaluates this with lane masks in one asm block (so no mask
-// outlives its group), selects the kept values in index order (s0 = first
-// kept, s1 = second) and shifts the group's metadata nibble i0 | i1 << 2 into
-// `meta` most significant bit first (v_addc doubles and adds the carry-in
-// mask).  Its masks go to group_residual, which replaces a kept a_i by
-// a_i - dq_i, dq the dequantised kept value (dlo for the first kept, dhi for
-// the second); dropped elements keep a_i.
-struct Keep { uint64_t k0, k1, k2, k3; };
-
-__device__ __forceinline__ Keep group_keep(float a0, float a1, float a2, float a3, float& s0, float& s1,
-                                           uint32_t& meta) {
-  Keep k;
-  uint64_t b12, e, n, c;
+// group_mask evaluates this with lane masks inside one asm block (no mask
+// outlives the group), writes the masked group -- kept elements in place, +0
+// at the dropped ones (a kept -0 stays -0) -- and shifts the group's metadata
+// nibble i0 | i1 << 2 (the kept offsets in order) into `meta` most
+// significant bit first (v_addc doubles and adds the carry-in mask).
+__device__ __forceinline__ void group_mask(float a0, float a1, float a2, float a3, float& s0, float& s1, float& s2,
+                                           float& s3, uint32_t& meta) {
+  uint64_t k0, k1, k2, k3, b12, e, n, c;
   float m;
   asm volatile(
       "v_med3_f32 %[m], |%[a1]|, |%[a2]|, |%[a3]|\n\t"
@@ -58,11 +53,10 @@ __device__ __forceinline__ Keep group_keep(float a0, float a1, float a2, float a
       "s_or_b64 %[k1], %[n], %[c]\n\t"
       "s_andn2_b64 %[c], %[e], %[b12]\n\t"
       "s_or_b64 %[k2], %[n], %[c]\n\t"
-      // s0 = k0 ? a0 : (k1 ? a1 : a2);  s1 = k3 ? a3 : (k2 ? a2 : a1)
-      "v_cndmask_b32_e64 %[s0], %[a2], %[a1], %[k1]\n\t"
-      "v_cndmask_b32_e64 %[s0], %[s0], %[a0], %[k0]\n\t"
-      "v_cndmask_b32_e64 %[s1], %[a1], %[a2], %[k2]\n\t"
-      "v_cndmask_b32_e64 %[s1], %[s1], %[a3], %[k3]\n\t"
+      "v_cndmask_b32_e64 %[s0], 0, %[a0], %[k0]\n\t"
+      "v_cndmask_b32_e64 %[s1], 0, %[a1], %[k1]\n\t"
+      "v_cndmask_b32_e64 %[s2], 0, %[a2], %[k2]\n\t"
+      "v_cndmask_b32_e64 %[s3], 0, %[a3], %[k3]\n\t"
       // nibble bits, high to low: i1 = k3 ? 3 : (k2 ? 2 : 1), i0 = k0 ? 0 : (k1 ? 1 : 2)
       "s_or_b64 %[c], %[k3], %[k2]\n\t"
       "v_addc_co_u32_e64 %[meta], %[e], %[meta], %[meta], %[c]\n\t"
@@ -72,29 +66,11 @@ __device__ __forceinline__ Keep group_keep(float a0, float a1, float a2, float a
       "v_addc_co_u32_e64 %[meta], %[e], %[meta], %[meta], %[c]\n\t"
       "s_andn2_b64 %[c], %[k1], %[k0]\n\t"
       "v_addc_co_u32_e64 %[meta], %[e], %[meta], %[meta], %[c]"
-      : [s0] "=&v"(s0), [s1] "=&v"(s1), [meta] "+v"(meta), [m] "=&v"(m), [k0] "=&s"(k.k0), [k1] "=&s"(k.k1),
-        [k2] "=&s"(k.k2), [k3] "=&s"(k.k3), [b12] "=&s"(b12), [e] "=&s"(e), [n] "=&s"(n), [c] "=&s"(c)
+      : [s0] "=&v"(s0), [s1] "=&v"(s1), [s2] "=&v"(s2), [s3] "=&v"(s3), [meta] "+v"(meta), [m] "=&v"(m),
+        [k0] "=&s"(k0), [k1] "=&s"(k1), [k2] "=&s"(k2), [k3] "=&s"(k3), [b12] "=&s"(b12), [e] "=&s"(e),
+        [n] "=&s"(n), [c] "=&s"(c)
       : [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
       : "scc");
-  return k;
-}
-
-__device__ __forceinline__ void group_residual(float& a0, float& a1, float& a2, float& a3, float dlo, float dhi,
-                                               const Keep& k) {
-  float t;
-  asm volatile(
-      "v_sub_f32_e32 %[t], %[a0], %[dlo]\n\t"
-      "v_cndmask_b32_e64 %[a0], %[a0], %[t], %[k0]\n\t"
-      "v_sub_f32_e32 %[t], %[a3], %[dhi]\n\t"
-      "v_cndmask_b32_e64 %[a3], %[a3], %[t], %[k3]\n\t"
-      "v_cndmask_b32_e64 %[t], %[dlo], %[dhi], %[k0]\n\t"
-      "v_sub_f32_e32 %[t], %[a1], %[t]\n\t"
-      "v_cndmask_b32_e64 %[a1], %[a1], %[t], %[k1]\n\t"
-      "v_cndmask_b32_e64 %[t], %[dhi], %[dlo], %[k3]\n\t"
-      "v_sub_f32_e32 %[t], %[a2], %[t]\n\t"
-      "v_cndmask_b32_e64 %[a2], %[a2], %[t], %[k2]"
-      : [a0] "+v"(a0), [a1] "+v"(a1), [a2] "+v"(a2), [a3] "+v"(a3), [t] "=&v"(t)
-      : [dlo] "v"(dlo), [dhi] "v"(dhi), [k0] "s"(k.k0), [k1] "s"(k.k1), [k2] "s"(k.k2), [k3] "s"(k.k3));
 }
 
 __device__ __forceinline__ float abs_max3(float m, float a, float b) {
@@ -117,23 +93,12 @@ __device__ __forceinline__ void fp4_dec(uint32_t packed, float scale, float& lo,
   hi = v[1];
 }
 
-// Group G of a block: mask, kept codes into byte G%4 of `codes`, metadata,
-// residual in place.
-template <int G>
-__device__ __forceinline__ void group4(float (&v)[32], float s_scale, uint32_t& codes, uint32_t& meta) {
-  float s0, s1, dlo, dhi;
-  const Keep k = group_keep(v[4 * G], v[4 * G + 1], v[4 * G + 2], v[4 * G + 3], s0, s1, meta);
-  codes = fp4_enc<G % 4>(codes, s0, s1, s_scale);
-  fp4_dec<G % 4>(codes, s_scale, dlo, dhi);
-  group_residual(v[4 * G], v[4 * G + 1], v[4 * G + 2], v[4 * G + 3], dlo, dhi, k);
-}
-
 // The whole decomposition of one MX block; v is replaced by the residual.
 // DENSE (the plain FP4 linear, no backbone): the residual is v itself and
 // only its MXFP4 codes are produced.
 template <bool DENSE>
 __device__ __forceinline__ Block32 decompose32(float (&v)[32]) {
-  uint32_t lo = 0, hi = 0, meta = 0;
+  uint32_t sc[4] = {0u, 0u, 0u, 0u}, meta = 0;
   int es = -127;
   if constexpr (!DENSE) {
     // S block scale: the block maximum of v is always kept, so amax(S) == amax(v)
@@ -143,15 +108,28 @@ __device__ __forceinline__ Block32 decompose32(float (&v)[32]) {
     es = mx_shared_exp(__float_as_uint(am));
     const float ss = pow2(es);
 
-    // groups last to first: the metadata nibbles enter most significant first
-    group4<7>(v, ss, hi, meta);
-    group4<6>(v, ss, hi, meta);
-    group4<5>(v, ss, hi, meta);
-    group4<4>(v, ss, hi, meta);
-    group4<3>(v, ss, lo, meta);
-    group4<2>(v, ss, lo, meta);
-    group4<1>(v, ss, lo, meta);
-    group4<0>(v, ss, lo, meta);
+    // eight elements (two groups, one code word) at a time, last to first: the
+    // metadata nibbles enter most significant first.  The masked group is
+    // encoded in place (a dropped +0 gets code 0), decoded, and the residual is
+    // v - deq(code): exact, and v itself where the element was dropped.
+#pragma unroll
+    for (int w = 3; w >= 0; --w) {
+      float s8[8];
+      group_mask(v[8 * w + 4], v[8 * w + 5], v[8 * w + 6], v[8 * w + 7], s8[4], s8[5], s8[6], s8[7], meta);
+      group_mask(v[8 * w], v[8 * w + 1], v[8 * w + 2], v[8 * w + 3], s8[0], s8[1], s8[2], s8[3], meta);
+      uint32_t c = fp4_enc<0>(0u, s8[0], s8[1], ss);
+      c = fp4_enc<1>(c, s8[2], s8[3], ss);
+      c = fp4_enc<2>(c, s8[4], s8[5], ss);
+      c = fp4_enc<3>(c, s8[6], s8[7], ss);
+      sc[w] = c;
+      float d[8];
+      fp4_dec<0>(c, ss, d[0], d[1]);
+      fp4_dec<1>(c, ss, d[2], d[3]);
+      fp4_dec<2>(c, ss, d[4], d[5]);
+      fp4_dec<3>(c, ss, d[6], d[7]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[8 * w + i] = v[8 * w + i] - d[i];
+    }
   }
 
   float ar = 0.0f;
@@ -170,7 +148,7 @@ __device__ __forceinline__ Block32 decompose32(float (&v)[32]) {
 
   Block32 o;
   o.r_codes = make_uint4(rc[0], rc[1], rc[2], rc[3]);
-  o.s_codes = DENSE ? make_uint4(0, 0, 0, 0) : expand_chunk(lo, hi, meta);
+  o.s_codes = make_uint4(sc[0], sc[1], sc[2], sc[3]);
   o.meta = meta;
   o.s_e8 = (uint32_t)(es + 127);
   o.r_e8 = (uint32_t)(er + 127);
