@@ -411,9 +411,10 @@ LAYER = dict(M=2048, d=4096, qkv=6144, ff=14336)
 def run_layer(args):
     """A synthetic Llama-3.1-8B decoder layer of SharQ linears, batch 1 x 2048
     tokens, random weights: prep(x, g1) -> QKV -> [attention stand-in: the Q
-    columns of the bf16 QKV output, a strided view] -> prep -> O -> residual ->
-    prep(h, g2) -> gate/up with the SwiGLU epilogue (bf16) -> prep -> down ->
-    residual.  Attention itself is not part of the SharQ hot path."""
+    columns of the bf16 QKV output, a strided view] -> prep -> O with the
+    residual add in its epilogue -> prep(h, g2) -> gate/up with the SwiGLU
+    epilogue (bf16) -> prep -> down with the residual add.  Attention itself is
+    not part of the SharQ hot path."""
     import numpy as np
     import torch
 
@@ -445,27 +446,23 @@ def run_layer(args):
     b = dict(a1=sq.SharqAct(M, d, dev), a2=sq.SharqAct(M, d, dev), a3=sq.SharqAct(M, d, dev),
              a4=sq.SharqAct(M, ff, dev),
              qkv=torch.empty(M, nq, dtype=torch.bfloat16, device=dev),
-             o=torch.empty(M, d, dtype=torch.float32, device=dev),
              h=torch.empty(M, d, dtype=torch.bfloat16, device=dev),
              mid=torch.empty(M, ff, dtype=torch.bfloat16, device=dev),
-             dn=torch.empty(M, d, dtype=torch.float32, device=dev),
              out=torch.empty(M, d, dtype=torch.bfloat16, device=dev))
     torch.cuda.synchronize()
-    names = ["prep_qkv", "gemm_qkv", "prep_o", "gemm_o", "residual_1", "prep_gateup", "gemm_gateup_swiglu",
-             "prep_down", "gemm_down", "residual_2"]
+    names = ["prep_qkv", "gemm_qkv", "prep_o", "gemm_o_residual", "prep_gateup", "gemm_gateup_swiglu",
+             "prep_down", "gemm_down_residual"]
 
     def launches(i):
         w = sets[i % nsets]
         return [lambda: sq.sharq_prepare(x, g1, 1e-5, out=b["a1"]),
                 lambda: sq.sharq_linear(b["a1"], w["qkv"], out=b["qkv"], out_dtype=sq.OUT_BF16),
                 lambda: sq.sharq_prepare(b["qkv"][:, :d], None, 1e-5, out=b["a2"]),
-                lambda: sq.sharq_linear(b["a2"], w["o"], out=b["o"]),
-                lambda: sq.sharq_add_bf16_f32(x, b["o"], out=b["h"]),
+                lambda: sq.sharq_linear_residual(b["a2"], w["o"], x, out=b["h"]),
                 lambda: sq.sharq_prepare(b["h"], g2, 1e-5, out=b["a3"]),
                 lambda: sq.sharq_linear_swiglu(b["a3"], w["gu"], out=b["mid"]),
                 lambda: sq.sharq_prepare(b["mid"], None, 1e-5, out=b["a4"]),
-                lambda: sq.sharq_linear(b["a4"], w["down"], out=b["dn"]),
-                lambda: sq.sharq_add_bf16_f32(b["h"], b["dn"], out=b["out"])]
+                lambda: sq.sharq_linear_residual(b["a4"], w["down"], b["h"], out=b["out"])]
 
     def step(i, ev=None, stream=None, part=None):
         fns = launches(i)
@@ -498,7 +495,8 @@ def run_layer(args):
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {"workload": f"layer: synthetic Llama-3.1-8B decoder layer of SharQ linears, batch 1 x {M} tokens "
-                               "(QKV 6144, O 4096, gate/up 2x14336 with the SwiGLU epilogue, down 4096); attention "
+                               "(QKV 6144, O 4096 and down 4096 with the residual adds in their epilogues, gate/up 2x14336 "
+                               "with the SwiGLU epilogue); attention "
                                "replaced by the Q columns of the QKV output; random weights; 2:4 mask; MXFP4",
                    "M": M, "rotating_sets": nsets},
         "roofline": {"bound": "mfma", "achieved": round(gu_tflops, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",

@@ -19,7 +19,7 @@ __all__ = [
     "SharqWeight", "SharqAct", "SharqError",
     "sharq_pack_weight", "sharq_prepare", "sharq_linear", "sharq_linear_grouped",
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
-    "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32",
+    "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32", "sharq_linear_residual",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -133,6 +133,22 @@ def sharq_linear(act: SharqAct, weight: SharqWeight, out=None, out_dtype: int = 
     lib = _lib.load()
     _lib.check(lib.sharq_linear(C.byref(act.desc), C.byref(weight.desc), _ptr(out), out.stride(0), out_dtype,
                                 _stream_ptr(stream)), "sharq_linear")
+    return out
+
+
+def sharq_linear_residual(act: SharqAct, weight: SharqWeight, x, out=None, stream=None):
+    """Y [M, N] bf16 = bf16(x + layer output): the layer with the residual add
+    in its epilogue (x: bf16 [M, N], unit inner stride; out may be x)."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1 or tuple(x.shape) != (act.M, weight.N):
+        raise ValueError("x must be a 2-D bf16 [M, N] tensor with unit inner stride")
+    if out is None:
+        out = torch.empty(act.M, weight.N, dtype=torch.bfloat16, device=act.r_codes.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be a 2-D bf16 tensor with unit inner stride")
+    lib = _lib.load()
+    _lib.check(lib.sharq_linear_residual(C.byref(act.desc), C.byref(weight.desc), _ptr(x), x.stride(0), _ptr(out),
+                                         out.stride(0), _stream_ptr(stream)), "sharq_linear_residual")
     return out
 
 

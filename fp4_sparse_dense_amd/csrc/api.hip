@@ -213,9 +213,9 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
   return SHARQ_OK;
 }
 
-sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev, int64_t ldy, int32_t out_dtype,
-                          void* stream) {
-  g_err[0] = 0;
+// sharq_linear and sharq_linear_residual: resid == nullptr for the plain layer
+static sharq_status linear_impl(const sharq_act* a, const sharq_weight* w, void* y_dev, int64_t ldy, int32_t out_dtype,
+                                const void* resid, int64_t ld_resid, void* stream) {
   if (!a || !w) return fail(SHARQ_ERR_INVALID_ARG, "null descriptor");
   if (a->struct_size != sizeof(sharq_act) || w->struct_size != sizeof(sharq_weight))
     return fail(SHARQ_ERR_INVALID_ARG, "descriptor struct_size mismatch");
@@ -267,6 +267,8 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
   g.N = w->N;
   g.K = (int)a->K;
   g.out_bf16 = out_dtype == SHARQ_OUT_BF16;
+  g.resid = static_cast<const uint16_t*>(resid);
+  g.ld_resid = ld_resid;
   g.a_blocks = (a->M + 15) / 16;
   g.xcd_bm = 0;
   g.seg = nullptr;
@@ -286,6 +288,28 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev
                              : sharq::launch_linear(g, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "linear launch");
   return SHARQ_OK;
+}
+
+sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, void* y_dev, int64_t ldy, int32_t out_dtype,
+                          void* stream) {
+  g_err[0] = 0;
+  return linear_impl(a, w, y_dev, ldy, out_dtype, nullptr, 0, stream);
+}
+
+sharq_status sharq_linear_residual(const sharq_act* a, const sharq_weight* w, const void* x_bf16_dev, int64_t ldx,
+                                   void* y_bf16_dev, int64_t ldy, void* stream) {
+  g_err[0] = 0;
+  if (!a || !w) return fail(SHARQ_ERR_INVALID_ARG, "null descriptor");
+  if (a->struct_size != sizeof(sharq_act) || w->struct_size != sizeof(sharq_weight))
+    return fail(SHARQ_ERR_INVALID_ARG, "descriptor struct_size mismatch");
+  if (a->fmt != SHARQ_FMT_MXFP4 || w->fmt != SHARQ_FMT_MXFP4)
+    return fail(SHARQ_ERR_UNSUPPORTED, "the residual epilogue is built for MXFP4 layers");
+  if (a->M > 0) {
+    if (!x_bf16_dev) return fail(SHARQ_ERR_INVALID_ARG, "null residual pointer");
+    if (ldx < w->N) return fail(SHARQ_ERR_INVALID_ARG, "ldx=%lld < N=%lld", (long long)ldx, (long long)w->N);
+    if (!aligned(x_bf16_dev, 2)) return fail(SHARQ_ERR_INVALID_ARG, "residual misaligned");
+  }
+  return linear_impl(a, w, y_bf16_dev, ldy, SHARQ_OUT_BF16, x_bf16_dev, ldx, stream);
 }
 
 sharq_status sharq_linear_swiglu(const sharq_act* a, const sharq_weight* w, void* y_bf16_dev, int64_t ldy,
@@ -520,6 +544,8 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
   g.N = w->N;
   g.K = (int)a->K;
   g.out_bf16 = out_dtype == SHARQ_OUT_BF16;
+  g.resid = nullptr;
+  g.ld_resid = 0;
   g.a_blocks = (a->M + 15) / 16;
   g.xcd_bm = 0;
   g.seg = nullptr;

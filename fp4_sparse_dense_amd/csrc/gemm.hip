@@ -492,7 +492,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   // four consecutive outputs per lane and block: one 16-byte (fp32) or 8-byte
   // (bf16) store where the row stride and base allow it and all four columns
   // exist, else element by element
-  const bool vec = ((uintptr_t)g.y & 15) == 0 && (g.ldy & 3) == 0;
+  const bool vec = ((uintptr_t)g.y & 15) == 0 && (g.ldy & 3) == 0 &&
+                   (!g.resid || (((uintptr_t)g.resid & 7) == 0 && (g.ld_resid & 3) == 0));
 #pragma unroll
   for (int i = 0; i < C::kWMT; ++i)
 #pragma unroll

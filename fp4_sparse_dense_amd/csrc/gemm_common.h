@@ -21,28 +21,36 @@ __device__ __forceinline__ v4f mfma_fp4(v8i a, v8i b, v4f c, uint32_t sa, uint32
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
+__device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// One output: fp32, or bf16 (nearest even) of the value -- plus the residual
+// stream's bf16 element first when the layer adds one (one binary32 add).
 __device__ __forceinline__ void store_out(const GemmArgs& g, int64_t row, int64_t col, float v) {
   if (g.out_bf16) {
-    uint32_t u = __float_as_uint(v);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    reinterpret_cast<uint16_t*>(g.y)[row * g.ldy + col] = (uint16_t)(u >> 16);
+    if (g.resid) v = __uint_as_float((uint32_t)g.resid[row * g.ld_resid + col] << 16) + v;
+    reinterpret_cast<uint16_t*>(g.y)[row * g.ldy + col] = (uint16_t)bf16_bits_rne(v);
   } else {
     reinterpret_cast<float*>(g.y)[row * g.ldy + col] = v;
   }
 }
 
-// four consecutive outputs of one row (16-byte aligned for fp32, 8-byte for bf16)
+// four consecutive outputs of one row (16-byte aligned for fp32, 8-byte for
+// bf16 and the residual)
 __device__ __forceinline__ void store_out4(const GemmArgs& g, int64_t row, int64_t col, v4f v) {
   if (g.out_bf16) {
-    uint32_t h[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t u = __float_as_uint(v[q]);
-      u += 0x7FFFu + ((u >> 16) & 1u);
-      h[q] = u >> 16;
+    if (g.resid) {
+      const uint2 x = *reinterpret_cast<const uint2*>(g.resid + row * g.ld_resid + col);
+      v[0] = __uint_as_float(x.x << 16) + v[0];
+      v[1] = __uint_as_float(x.x & 0xFFFF0000u) + v[1];
+      v[2] = __uint_as_float(x.y << 16) + v[2];
+      v[3] = __uint_as_float(x.y & 0xFFFF0000u) + v[3];
     }
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.y) + row * g.ldy + col) =
-        make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+        make_uint2(bf16_bits_rne(v[0]) | bf16_bits_rne(v[1]) << 16, bf16_bits_rne(v[2]) | bf16_bits_rne(v[3]) << 16);
   } else {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.y) + row * g.ldy + col) = make_float4(v[0], v[1], v[2], v[3]);
   }

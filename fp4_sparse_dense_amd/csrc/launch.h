@@ -35,6 +35,9 @@ struct GemmArgs {
   int64_t M, N;
   int K;
   int out_bf16;
+  // residual epilogue (bf16 output only): y = bf16(resid + Y); nullptr: none
+  const uint16_t* resid;
+  int64_t ld_resid;
   int64_t a_blocks;                // 16-row blocks of the activation buffers (scale stride)
   int xcd_bm;                      // tiled kernel: M tiles per XCD region (0: plain XCD order)
   // grouped expert layer; seg == nullptr for a single problem

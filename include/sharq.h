@@ -233,6 +233,19 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
 sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w,
                           void* y_dev, int64_t ldy, int32_t out_dtype, void* stream);
 
+/* sharq_linear with the residual add of a decoder layer in its epilogue:
+ * Y[m][n] = bf16(x[m][n] + y) for the layer's binary32 output y (one binary32
+ * add, then round to nearest even) -- exactly sharq_linear (fp32 out) followed
+ * by sharq_add_bf16_f32, without writing the fp32 output.
+ * x: device bf16, row stride ldx >= N; Y: device bf16, row stride ldy >= N.
+ * Y may be x itself (same pointer and stride; every element is read before it
+ * is written by the same thread); any other overlap is undefined.  MXFP4
+ * layers (2:4 or 0:4).
+ * Errors: as sharq_linear, plus INVALID_ARG (null or misaligned x, ldx < N),
+ * UNSUPPORTED (NVFP4-style). */
+sharq_status sharq_linear_residual(const sharq_act* a, const sharq_weight* w, const void* x_bf16_dev, int64_t ldx,
+                                   void* y_bf16_dev, int64_t ldy, void* stream);
+
 /* Fusion ablations (README page of the SharQ repository, "Benchmarks": the
  * RMSNorm fusion and the epilogue fusion can each be switched off).
  *

@@ -266,3 +266,26 @@ def test_swiglu_rejects_before_launch(lib):
     assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 32, None) == _lib.ERR_UNSUPPORTED   # 2:4 only
     a.n, a.M = 2, 0
     assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 32, None) == _lib.OK
+
+
+def test_residual_rejects_before_launch(lib):
+    a = _act()
+    a.layout_version = _lib.SHARQ_ABI_VERSION
+    a.M, a.K, a.n, a.m = 64, 256, 2, 4
+    w = _lib.WeightDesc()
+    w.struct_size = C.sizeof(_lib.WeightDesc)
+    w.layout_version = _lib.SHARQ_ABI_VERSION
+    w.N, w.K, w.codes, w.scales = 64, 256, 0x100000, 0x200000
+    for p in (0, 1):
+        w.view[p].base, w.view[p].ld, w.view[p].block = 0x200000, 4 * 64, 32
+    x, y = C.c_void_p(0x700000), C.c_void_p(0x600000)
+    assert lib.sharq_linear_residual(C.byref(a), C.byref(w), None, 64, y, 64, None) == _lib.ERR_INVALID_ARG  # null x
+    assert lib.sharq_linear_residual(C.byref(a), C.byref(w), x, 32, y, 64, None) == _lib.ERR_INVALID_ARG    # ldx < N
+    assert lib.sharq_linear_residual(C.byref(a), C.byref(w), C.c_void_p(0x700001), 64, y, 64,
+                                     None) == _lib.ERR_INVALID_ARG                                         # misaligned
+    assert lib.sharq_linear_residual(C.byref(a), C.byref(w), x, 64, y, 32, None) == _lib.ERR_INVALID_ARG    # ldy < N
+    a.fmt = w.fmt = 1
+    assert lib.sharq_linear_residual(C.byref(a), C.byref(w), x, 64, y, 64, None) == _lib.ERR_UNSUPPORTED    # NVFP4-style
+    a.fmt = w.fmt = 0
+    a.M = 0
+    assert lib.sharq_linear_residual(C.byref(a), C.byref(w), None, 64, None, 64, None) == _lib.OK
