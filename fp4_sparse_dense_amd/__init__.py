@@ -20,6 +20,7 @@ __all__ = [
     "sharq_pack_weight", "sharq_prepare", "sharq_linear", "sharq_linear_grouped",
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
     "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32", "sharq_linear_residual",
+    "sharq_linear_swiglu_prep",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -298,6 +299,21 @@ def sharq_linear_swiglu(act: SharqAct, weight: SharqWeight, out=None, stream=Non
     lib = _lib.load()
     _lib.check(lib.sharq_linear_swiglu(C.byref(act.desc), C.byref(weight.desc), _ptr(out), out.stride(0),
                                        _stream_ptr(stream)), "sharq_linear_swiglu")
+    return out
+
+
+def sharq_linear_swiglu_prep(act: SharqAct, weight: SharqWeight, out: SharqAct | None = None, stream=None):
+    """The gate/up layer whose SwiGLU epilogue prepares H = bf16(SiLU(gate) * up)
+    for the down projection (2:4, MXFP4, no RMSNorm) without storing H: the
+    same bytes as sharq_prepare(sharq_linear_swiglu(act, weight))."""
+    F = weight.N // 2
+    if out is None:
+        out = SharqAct(act.M, F, act.r_codes.device)
+    if (out.M, out.K, out.n, out.m, out.fmt) != (act.M, F, 2, 4, FMT_MXFP4):
+        raise ValueError("out must be a 2:4 MXFP4 SharqAct of shape [M, N/2]")
+    lib = _lib.load()
+    _lib.check(lib.sharq_linear_swiglu_prep(C.byref(act.desc), C.byref(weight.desc), C.byref(out.desc),
+                                            _stream_ptr(stream)), "sharq_linear_swiglu_prep")
     return out
 
 

@@ -66,6 +66,8 @@ PROTOTYPES = {
                                 C.c_void_p, C.c_int64, C.c_void_p]),
     "sharq_add_f32": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
     "sharq_add_bf16_f32": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
+    "sharq_linear_swiglu_prep": (C.c_int, [C.POINTER(ActDesc), C.POINTER(WeightDesc), C.POINTER(ActDesc),
+                                           C.c_void_p]),
     "sharq_linear_residual": (C.c_int, [C.POINTER(ActDesc), C.POINTER(WeightDesc), C.c_void_p, C.c_int64,
                                         C.c_void_p, C.c_int64, C.c_void_p]),
     "sharq_linear_swiglu": (C.c_int, [C.POINTER(ActDesc), C.POINTER(WeightDesc), C.c_void_p, C.c_int64,

@@ -312,9 +312,10 @@ sharq_status sharq_linear_residual(const sharq_act* a, const sharq_weight* w, co
   return linear_impl(a, w, y_bf16_dev, ldy, SHARQ_OUT_BF16, x_bf16_dev, ldx, stream);
 }
 
-sharq_status sharq_linear_swiglu(const sharq_act* a, const sharq_weight* w, void* y_bf16_dev, int64_t ldy,
-                                 void* stream) {
-  g_err[0] = 0;
+// sharq_linear_swiglu (H stored, next == nullptr) and sharq_linear_swiglu_prep
+// (H prepared into *next)
+static sharq_status swiglu_impl(const sharq_act* a, const sharq_weight* w, void* y_bf16_dev, int64_t ldy,
+                                sharq_act* next, void* stream) {
   if (!a || !w) return fail(SHARQ_ERR_INVALID_ARG, "null descriptor");
   if (a->struct_size != sizeof(sharq_act) || w->struct_size != sizeof(sharq_weight))
     return fail(SHARQ_ERR_INVALID_ARG, "descriptor struct_size mismatch");
@@ -328,9 +329,32 @@ sharq_status sharq_linear_swiglu(const sharq_act* a, const sharq_weight* w, void
   if (s) return s;
   if (a->fmt != SHARQ_FMT_MXFP4 || a->n != 2 || a->m != 4)
     return fail(SHARQ_ERR_UNSUPPORTED, "the SwiGLU epilogue is built for the 2:4 MXFP4 layer");
-  if (a->M == 0) return SHARQ_OK;
-  if (!y_bf16_dev || !aligned(y_bf16_dev, 2)) return fail(SHARQ_ERR_INVALID_ARG, "output null or misaligned");
-  if (ldy < w->N / 2) return fail(SHARQ_ERR_INVALID_ARG, "ldy=%lld < N/2=%lld", (long long)ldy, (long long)(w->N / 2));
+  const int64_t F = w->N / 2;
+  if (next) {
+    if (next->struct_size != sizeof(sharq_act)) return fail(SHARQ_ERR_INVALID_ARG, "output descriptor struct_size mismatch");
+    if (F % 128) return fail(SHARQ_ERR_UNSUPPORTED, "preparing H in the epilogue needs N/2 %% 128 == 0, got %lld", (long long)F);
+  }
+  if (a->M > 0) {
+    if (next) {
+      if (!next->r_codes || !next->r_scales || !backbone_ok(next, 2) || !aligned(next->r_codes, 16) ||
+          !aligned(next->r_scales, 16))
+        return fail(SHARQ_ERR_INVALID_ARG, "output activation buffers not set or not 16-byte aligned");
+    } else {
+      if (!y_bf16_dev || !aligned(y_bf16_dev, 2)) return fail(SHARQ_ERR_INVALID_ARG, "output null or misaligned");
+      if (ldy < F) return fail(SHARQ_ERR_INVALID_ARG, "ldy=%lld < N/2=%lld", (long long)ldy, (long long)F);
+    }
+  }
+  if (a->M == 0) {
+    if (next) {
+      next->layout_version = SHARQ_ABI_VERSION;
+      next->M = 0;
+      next->K = F;
+      next->n = 2;
+      next->m = 4;
+      next->fmt = SHARQ_FMT_MXFP4;
+    }
+    return SHARQ_OK;
+  }
   if (!a->r_codes || !a->r_scales || !w->codes || !backbone_ok(a, a->n) || !aligned(a->r_codes, 16) ||
       !aligned(a->r_scales, 16) || !aligned(w->codes, 16))
     return fail(SHARQ_ERR_INVALID_ARG, "descriptor buffers not set or not 16-byte aligned");
@@ -361,9 +385,30 @@ sharq_status sharq_linear_swiglu(const sharq_act* a, const sharq_weight* w, void
   g.K = (int)a->K;
   g.out_bf16 = 1;
   g.a_blocks = (a->M + 15) / 16;
+  if (next) g.next = sharq::PrepOut{next->s_codes, next->s_meta, next->s_scales, next->r_codes, next->r_scales};
   hipError_t e = sharq::launch_linear_swiglu(g, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "swiglu linear launch");
+  if (next) {
+    next->layout_version = SHARQ_ABI_VERSION;
+    next->M = a->M;
+    next->K = F;
+    next->n = 2;
+    next->m = 4;
+    next->fmt = SHARQ_FMT_MXFP4;
+  }
   return SHARQ_OK;
+}
+
+sharq_status sharq_linear_swiglu(const sharq_act* a, const sharq_weight* w, void* y_bf16_dev, int64_t ldy,
+                                 void* stream) {
+  g_err[0] = 0;
+  return swiglu_impl(a, w, y_bf16_dev, ldy, nullptr, stream);
+}
+
+sharq_status sharq_linear_swiglu_prep(const sharq_act* a, const sharq_weight* w, sharq_act* next, void* stream) {
+  g_err[0] = 0;
+  if (!next) return fail(SHARQ_ERR_INVALID_ARG, "null output descriptor");
+  return swiglu_impl(a, w, nullptr, 0, next, stream);
 }
 
 sharq_status sharq_linear_fused(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx,

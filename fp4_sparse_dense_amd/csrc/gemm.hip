@@ -21,6 +21,7 @@
 #include "device_common.h"
 #include "gemm_common.h"
 #include "launch.h"
+#include "prep_common.h"
 
 namespace sharq {
 
@@ -152,7 +153,10 @@ __device__ __forceinline__ v4f mfma_yt(v8i act, v8i w, v4f c, uint32_t s_act, ui
   return mfma_fp4(w, act, c, s_w, s_act);
 }
 
-template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE, bool SWIGLU>
+// SWIGLU: 0 = store Y; 1 = store H = bf16(SiLU(gate) * up) of the column
+// pairs; 2 = prepare H for the next layer (2:4, MXFP4, no RMSNorm) straight
+// from the tile, H never stored.
+template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE, int SWIGLU>
 __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
   extern __shared__ __align__(1024) uint8_t smem[];
@@ -456,37 +460,92 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_yt(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
 
   // single epilogue store of Y_S + Y_R
-  if constexpr (SWIGLU) {
+  if constexpr (SWIGLU != 0) {
     static_assert(!GROUPED && !DENSE, "the SwiGLU epilogue follows the 2:4 layer");
     // the wave's column blocks pair up as (gate, up): the tile starts at an
     // even block (BN/16 is even) and so does each wave's share
     static_assert(C::kWNT % 2 == 0 && C::kNB % 2 == 0, "gate/up pairs inside a wave");
     const int64_t hcols = y_cols / 2;
-    const bool vec = ((uintptr_t)g.y & 7) == 0 && (g.ldy & 3) == 0;
+    auto h_bits = [&](int i, int j, uint32_t (&hb)[4]) {
 #pragma unroll
-    for (int i = 0; i < C::kWMT; ++i)
+      for (int q = 0; q < 4; ++q) {
+        const float gt = acc[i][j][q], up = acc[i][j + 1][q];
+        hb[q] = bf16_bits_rne(gt / (1.0f + expf(-gt)) * up);
+      }
+    };
+    if constexpr (SWIGLU == 1) {
+      const bool vec = ((uintptr_t)g.y & 7) == 0 && (g.ldy & 3) == 0;
 #pragma unroll
-      for (int j = 0; j < C::kWNT; j += 2) {
-        const int64_t row = (rb0 + wm * C::kWMT + i) * 16 + r16;
-        const int64_t col = (nb0 + wn * C::kWNT + j) / 2 * 16 + 4 * c4;
-        uint32_t hb[4];
+      for (int i = 0; i < C::kWMT; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kWNT; j += 2) {
+          const int64_t row = (rb0 + wm * C::kWMT + i) * 16 + r16;
+          const int64_t col = (nb0 + wn * C::kWNT + j) / 2 * 16 + 4 * c4;
+          uint32_t hb[4];
+          h_bits(i, j, hb);
+          if (row >= y_rows) continue;
+          uint16_t* dst = reinterpret_cast<uint16_t*>(g.y) + row * g.ldy + col;
+          if (vec && col + 3 < hcols) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (col + q < hcols) dst[q] = (uint16_t)hb[q];
+          }
+        }
+    } else {
+      // H of the tile (BM rows x BN/2 columns, bf16) goes to LDS -- rows
+      // padded to an odd number of 16-byte units so the block reads below hit
+      // distinct banks -- then every thread prepares whole 32-column blocks of
+      // it as sharq_prepare does (no RMSNorm: v = H) and writes them into the
+      // next activation's tiled layout.  F = N/2 is a multiple of 128, so the
+      // next layer's K tiles hold no padding; its padding rows (past M, below
+      // the last 16-row block) come from zero activation rows and so hold the
+      // outputs of zero input, as the preparation writes them.
+      constexpr int kHCols = BN / 2, kHStride = kHCols + 8;       // bf16 elements per LDS row
+      static_assert(kHCols % 32 == 0 && ((kHStride * 2 / 16) & 1) == 1, "H staging layout");
+      static_assert(BM * kHStride * 2 <= C::kStages * C::kStage, "H fits the LDS ring");
+      __syncthreads();   // every wave has consumed its last fragments: the ring is free
+      uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+      for (int i = 0; i < C::kWMT; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kWNT; j += 2) {
+          uint32_t hb[4];
+          h_bits(i, j, hb);
+          const int lrow = (wm * C::kWMT + i) * 16 + r16, lcol = (wn * C::kWNT + j) / 2 * 16 + 4 * c4;
+          *reinterpret_cast<uint2*>(hs + lrow * kHStride + lcol) = make_uint2(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16);
+        }
+      __syncthreads();
+      const PrepOut& o = g.next;
+      const int64_t RBn = g.a_blocks, KTn = hcols / 128;
+      constexpr int kBlk = BM * kHCols / 32;
+      for (int t = tid; t < kBlk; t += C::kThreads) {
+        const int r = t & 15, rbl = (t >> 4) % C::kMB, b = t / (16 * C::kMB);
+        const int64_t rb = rb0 + rbl, kb = nb0 / 4 + b;          // nb0 / 4: the tile's first 32-column block
+        if (rb >= RBn || kb * 32 >= hcols) continue;
+        const uint4* src = reinterpret_cast<const uint4*>(hs + (rbl * 16 + r) * kHStride + b * 32);
+        float v[32];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float gt = acc[i][j][q], up = acc[i][j + 1][q];
-          uint32_t u = __float_as_uint(gt / (1.0f + expf(-gt)) * up);
-          u += 0x7FFFu + ((u >> 16) & 1u);
-          hb[q] = u >> 16;
-        }
-        if (row >= y_rows) continue;
-        uint16_t* dst = reinterpret_cast<uint16_t*>(g.y) + row * g.ldy + col;
-        if (vec && col + 3 < hcols) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16);
-        } else {
+          const uint4 w4 = src[q];
+          const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (col + q < hcols) dst[q] = (uint16_t)hb[q];
+          for (int e = 0; e < 4; ++e) {
+            v[8 * q + 2 * e] = __uint_as_float(wd[e] << 16);
+            v[8 * q + 2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+          }
         }
+        const Block32 d = decompose32<false>(v);
+        const int64_t kt = kb / 4, c = kb % 4, tile = rb * KTn + kt, tl = c * 16 + r;
+        *reinterpret_cast<uint4*>(o.r_codes + tile * 1024 + tl * 16) = d.r_codes;
+        *reinterpret_cast<uint4*>(o.s_codes + tile * 1024 + tl * 16) = d.s_codes;
+        *reinterpret_cast<uint32_t*>(o.s_meta + tile * 256 + tl * 4) = d.meta;
+        const int64_t sc = (kt * RBn + rb) * 64 + tl;
+        o.s_scales[sc] = (uint8_t)d.s_e8;
+        o.r_scales[sc] = (uint8_t)d.r_e8;
       }
+    }
     return;
   }
   // four consecutive outputs per lane and block: one 16-byte (fp32) or 8-byte
@@ -511,7 +570,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     }
 }
 
-template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE, bool SWIGLU = false>
+template <int BM, int BN, int NWM, int NWN, int NST, bool GROUPED, bool DENSE, int SWIGLU = 0>
 static hipError_t launch_tiled(const GemmArgs& a, int64_t tiles, hipStream_t stream) {
   using C = TileCfg<BM, BN, NWM, NWN, NST>;
   auto kern = dual_gemm_tiled<BM, BN, NWM, NWN, NST, GROUPED, DENSE, SWIGLU>;
@@ -627,7 +686,8 @@ hipError_t launch_linear_swiglu(const GemmArgs& a, hipStream_t stream) {
   const int64_t tm = (a.M + kTileM - 1) / kTileM, tn = (a.N + kTileN - 1) / kTileN;
   GemmArgs b = a;
   b.xcd_bm = xcd_region_m(tm, tn, kTileM, kTileN);
-  return launch_tiled<kTileM, kTileN, 4, 2, 3, false, false, true>(b, tm * tn, stream);
+  return b.next.r_codes ? launch_tiled<kTileM, kTileN, 4, 2, 3, false, false, 2>(b, tm * tn, stream)
+                        : launch_tiled<kTileM, kTileN, 4, 2, 3, false, false, 1>(b, tm * tn, stream);
 }
 
 hipError_t launch_linear_dense(const GemmArgs& a, hipStream_t stream) { return launch_linear_t<true>(a, stream); }

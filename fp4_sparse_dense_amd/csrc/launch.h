@@ -38,6 +38,8 @@ struct GemmArgs {
   // residual epilogue (bf16 output only): y = bf16(resid + Y); nullptr: none
   const uint16_t* resid;
   int64_t ld_resid;
+  // SwiGLU epilogue preparing H for the next layer (r_codes == nullptr: store H)
+  PrepOut next;
   int64_t a_blocks;                // 16-row blocks of the activation buffers (scale stride)
   int xcd_bm;                      // tiled kernel: M tiles per XCD region (0: plain XCD order)
   // grouped expert layer; seg == nullptr for a single problem

@@ -285,6 +285,19 @@ sharq_status sharq_add_f32(const float* a_dev, const float* b_dev, float* y_dev,
 sharq_status sharq_linear_swiglu(const sharq_act* a, const sharq_weight* w, void* y_bf16_dev, int64_t ldy,
                                  void* stream);
 
+/* The gate/up layer with the SwiGLU epilogue feeding the down projection's
+ * preparation directly: *next = the prepared activation of H (2:4 mask,
+ * MXFP4 of S and R, no RMSNorm) in the tiled layout, exactly what
+ * sharq_linear_swiglu followed by sharq_prepare(H, gamma NULL) writes -- the
+ * same bytes -- without storing H.  Each output tile of the GEMM stages its H
+ * block in LDS and prepares whole 32-column blocks of it.
+ * next: caller-owned buffers sized by sharq_act_bytes(M, N/2, 2, 4, MXFP4);
+ * on success its M, K = N/2, n = 2, m = 4, fmt and layout_version are set.
+ * Limits: 2:4 MXFP4, N/2 a multiple of 128 (others: UNSUPPORTED).
+ * Errors: as sharq_linear_swiglu, plus INVALID_ARG (null next, next buffers
+ * not set or not 16-byte aligned), UNSUPPORTED (N/2 % 128). */
+sharq_status sharq_linear_swiglu_prep(const sharq_act* a, const sharq_weight* w, sharq_act* next, void* stream);
+
 /* The whole layer in one launch for small M (decode): Y[M,N] of the bf16
  * activation X[M,K] (row stride ldx) and the packed weight, exactly
  * sharq_prepare followed by sharq_linear -- the same arithmetic, identical

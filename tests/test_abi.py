@@ -289,3 +289,26 @@ def test_residual_rejects_before_launch(lib):
     a.fmt = w.fmt = 0
     a.M = 0
     assert lib.sharq_linear_residual(C.byref(a), C.byref(w), None, 64, None, 64, None) == _lib.OK
+
+
+def test_swiglu_prep_rejects_before_launch(lib):
+    a = _act()
+    a.layout_version = _lib.SHARQ_ABI_VERSION
+    a.M, a.K, a.n, a.m = 64, 256, 2, 4
+    w = _lib.WeightDesc()
+    w.struct_size = C.sizeof(_lib.WeightDesc)
+    w.layout_version = _lib.SHARQ_ABI_VERSION
+    w.N, w.K, w.codes, w.scales = 192, 256, 0x100000, 0x200000
+    for p in (0, 1):
+        w.view[p].base, w.view[p].ld, w.view[p].block = 0x200000, 12 * 64, 32
+    nxt = _act()
+    assert lib.sharq_linear_swiglu_prep(C.byref(a), C.byref(w), None, None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_linear_swiglu_prep(C.byref(a), C.byref(w), C.byref(nxt), None) == _lib.ERR_UNSUPPORTED  # N/2 % 128
+    w.N = 256
+    for p in (0, 1):
+        w.view[p].ld = 16 * 64
+    nxt.r_codes = 0
+    assert lib.sharq_linear_swiglu_prep(C.byref(a), C.byref(w), C.byref(nxt), None) == _lib.ERR_INVALID_ARG  # buffers
+    a.M = 0
+    assert lib.sharq_linear_swiglu_prep(C.byref(a), C.byref(w), C.byref(nxt), None) == _lib.OK
+    assert (nxt.M, nxt.K, nxt.n, nxt.m) == (0, 128, 2, 4)
