@@ -143,7 +143,10 @@ def device_weight(gen, N, K):
 
 def timed(step, steps, warmup, graph=False):
     """Wall time per step over `steps` steps after `warmup`, bracketed by
-    synchronisations, then per-kernel HIP-event times over the same steps.
+    synchronisations, then per-kernel HIP-event times over the same steps: for
+    each part of the step, that part's launches of all the steps run back to
+    back between two events (an event between every kernel would add its own
+    dispatch gap to each), giving the average duration of one launch.
 
     graph=True (workloads whose kernels are shorter than a host launch): the
     steps are captured once in a HIP graph and replayed, so the timed region
@@ -161,13 +164,16 @@ def timed(step, steps, warmup, graph=False):
             step(i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        evs = []
-        for i in range(steps):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(step.parts + 1)]
-            step(i, ev, stream)
-            evs.append(ev)
-        torch.cuda.synchronize()
-        return wall * 1e3 / steps, [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(step.parts)]
+        parts = []
+        for j in range(step.parts):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                step(i, part=j)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            parts.append([e0.elapsed_time(e1) / steps])
+        return wall * 1e3 / steps, parts
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -332,15 +338,10 @@ def run_dense(args):
                   "unfused_epilogue": ["prep", "gemm_backbone", "gemm_residual", "add"]}.get(ablation, ["prep", "gemm"])
     n_prep = 0 if args.fused else (2 if ablation == "unfused_norm" else 1)
 
-    def step(i, ev=None, stream=None, part=None):
-        fns = launches(i)
-        if ev is not None:
-            ev[0].record(stream)
-        for j, fn in enumerate(fns):
+    def step(i, part=None):
+        for j, fn in enumerate(launches(i)):
             if part in (None, j):
                 fn()
-            if ev is not None:
-                ev[j + 1].record(stream)
     step.parts = len(part_names)
 
     graph = args.workload == "decode"
@@ -463,15 +464,10 @@ def run_layer(args):
                 lambda: sq.sharq_linear_swiglu_prep(b["a3"], w["gu"], out=b["a4"]),
                 lambda: sq.sharq_linear_residual(b["a4"], w["down"], b["h"], out=b["out"])]
 
-    def step(i, ev=None, stream=None, part=None):
-        fns = launches(i)
-        if ev is not None:
-            ev[0].record(stream)
-        for j, fn in enumerate(fns):
+    def step(i, part=None):
+        for j, fn in enumerate(launches(i)):
             if part in (None, j):
                 fn()
-            if ev is not None:
-                ev[j + 1].record(stream)
     step.parts = len(names)
 
     ms, parts = timed(step, args.steps, args.warmup)
@@ -541,18 +537,15 @@ def run_moe(args):
                      dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
-    def step(i, ev=None, stream=None, part=None):
+    def step(i, part=None):
         wgu, wd, ygu, yd = sets[i % nsets]
-        rec = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
-        rec(0)
-        sq.sharq_prepare(x_tok, None, out=a_tok)
-        rec(1)
-        sq.sharq_linear_grouped(a_tok, wgu, seg_d, E, row_index=ri, rows=rows, out=ygu, workspace=ws)
-        rec(2)
-        sq.sharq_prepare(x_down, None, out=a_down)
-        rec(3)
-        sq.sharq_linear_grouped(a_down, wd, seg_d, E, rows=rows, out=yd, workspace=ws)
-        rec(4)
+        fns = [lambda: sq.sharq_prepare(x_tok, None, out=a_tok),
+               lambda: sq.sharq_linear_grouped(a_tok, wgu, seg_d, E, row_index=ri, rows=rows, out=ygu, workspace=ws),
+               lambda: sq.sharq_prepare(x_down, None, out=a_down),
+               lambda: sq.sharq_linear_grouped(a_down, wd, seg_d, E, rows=rows, out=yd, workspace=ws)]
+        for j, fn in enumerate(fns):
+            if part in (None, j):
+                fn()
     step.parts = 4
 
     ms, parts = timed(step, args.steps, args.warmup)
