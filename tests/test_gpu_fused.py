@@ -12,8 +12,11 @@ from tests.gpu_helpers import assert_linear_close, dev_bf16
 pytestmark = pytest.mark.gpu
 
 
+# M * K / 32 <= 1024 takes the register-resident path; (16, 4096) and (12, 8192) the other
 @pytest.mark.parametrize("M,K,N,norm", [(1, 4096, 4096, False), (8, 4096, 4096, False), (16, 2048, 1536, True),
-                                        (5, 96, 53, True), (3, 8192, 200, True), (13, 1376, 100, False)])
+                                        (5, 96, 53, True), (3, 8192, 200, True), (13, 1376, 100, False),
+                                        (1, 4096, 4096, True), (16, 4096, 512, True), (12, 8192, 300, False),
+                                        (9, 4096, 100, True)])
 def test_fused_layer(M, K, N, norm):
     import torch
     print(f"fused M={M} K={K} N={N} norm={norm}", flush=True)
