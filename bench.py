@@ -231,15 +231,6 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
-    torch.cuda.set_device(0)
-    if args.copy_calibration:
-        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     if args.fmt == "nvfp4" and args.workload != "decode":
         print("the NVFP4-style path is built for the decode workload (--workload decode)", file=sys.stderr)
         sys.exit(2)
@@ -259,6 +250,19 @@ def main():
         print("the fusion ablations run the MXFP4 SharQ layer (unfused_norm needs a workload with RMSNorm)",
               file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.m < 1 or args.sets < 0:
+        print("--steps and --m must be >= 1, --warmup and --sets >= 0", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload == "moe":
         rec = run_moe(args)
     elif args.workload == "layer":
