@@ -218,7 +218,7 @@ def main():
     ap.add_argument("--mode", default="sharq", choices=["sharq", "dense"],
                     help="dense: the plain MXFP4 linear (no backbone), the baseline SharQ is compared against")
     ap.add_argument("--fused", action="store_true",
-                    help="decode with M <= 16: the whole layer in one launch (sharq_linear_fused)")
+                    help="decode with M <= 16: the whole layer in one launch (sharq_linear_fused; MXFP4 or --fmt nvfp4)")
     ap.add_argument("--ablation", default="none", choices=["none", "unfused_norm", "unfused_epilogue"],
                     help="fusion ablations: a standalone RMSNorm writing bf16 before the preparation, or "
                          "the two GEMM paths as separate launches and an add")
@@ -241,9 +241,9 @@ def main():
     if args.mode == "dense" and (args.fmt != "mxfp4" or args.workload == "moe"):
         print("the plain FP4 linear is built for MXFP4 dense layers", file=sys.stderr)
         sys.exit(2)
-    if args.fused and (args.workload != "decode" or args.m > 16 or args.fmt != "mxfp4" or args.mode != "sharq"
-                       or args.ablation != "none"):
-        print("--fused is the one-launch MXFP4 layer for the decode workload with --m <= 16", file=sys.stderr)
+    if args.fused and (args.workload != "decode" or args.m > 16 or args.mode != "sharq" or args.ablation != "none"):
+        print("--fused is the one-launch layer (MXFP4 or NVFP4-style) for the decode workload with --m <= 16",
+              file=sys.stderr)
         sys.exit(2)
     if args.ablation != "none" and (args.fmt != "mxfp4" or args.mode != "sharq" or args.workload == "moe" or
                                     (args.ablation == "unfused_norm" and not WORKLOADS[args.workload]["norm"])):
@@ -355,7 +355,9 @@ def run_dense(args):
     flops = gemm_flops(M, N, K) // (2 if dense else 1)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     # the one-launch layer reads X (bf16) instead of the prepared activation
-    gbytes = (M * K * 2 + N * K * 17 // 32 + 4 * M * N) if args.fused else gemm_bytes(M, N, K, nv=nv, dense=dense)
+    # (NVFP4-style weight: 0.5625 B/elem, MXFP4: 0.53125)
+    wbytes = N * K * 9 // 16 if nv else N * K * 17 // 32
+    gbytes = (M * K * 2 + wbytes + 4 * M * N) if args.fused else gemm_bytes(M, N, K, nv=nv, dense=dense)
     gemm_gbs = gbytes / (gemm_ms * 1e-3) / 1e9
     pbytes = prep_bytes(M, K, norm, nv=nv, dense=dense)
     prep_gbs = pbytes / (prep_ms * 1e-3) / 1e9 if prep_ms > 0 else 0.0

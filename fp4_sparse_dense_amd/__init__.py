@@ -259,7 +259,8 @@ def path_act(act: SharqAct, path: str):
 def sharq_linear_fused(x, weight: SharqWeight, gamma=None, eps: float = 1e-5, out=None, out_dtype: int = OUT_F32,
                        stream=None):
     """The whole layer in one launch for M <= 16 (decode): the result of
-    sharq_prepare + sharq_linear, bit for bit, without the prepared activation."""
+    sharq_prepare + sharq_linear, bit for bit, without the prepared activation.
+    The format is the weight's (MXFP4 or NVFP4-style)."""
     torch = _torch()
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D bf16 tensor with unit inner stride")
@@ -272,7 +273,7 @@ def sharq_linear_fused(x, weight: SharqWeight, gamma=None, eps: float = 1e-5, ou
     if out.dtype != dt or out.dim() != 2 or out.stride(1) != 1:
         raise ValueError("out must be 2-D with unit inner stride and the requested dtype")
     lib = _lib.load()
-    _lib.check(lib.sharq_linear_fused(_ptr(x), M, K, x.stride(0), _ptr(gamma), eps, 2, 4, FMT_MXFP4,
+    _lib.check(lib.sharq_linear_fused(_ptr(x), M, K, x.stride(0), _ptr(gamma), eps, 2, 4, weight.fmt,
                                       C.byref(weight.desc), _ptr(out), out.stride(0), out_dtype,
                                       _stream_ptr(stream)), "sharq_linear_fused")
     return out

@@ -425,9 +425,11 @@ sharq_status sharq_linear_fused(const void* x_bf16_dev, int64_t M, int64_t K, in
   sharq_status s = check_fmt(fmt);
   if (s) return s;
   if (fmt != w->fmt) return fail(SHARQ_ERR_INVALID_ARG, "activation and weight formats differ");
-  if (fmt != SHARQ_FMT_MXFP4 || n != 2 || m != 4)
-    return fail(SHARQ_ERR_UNSUPPORTED, "the one-launch layer is built for 2:4 MXFP4");
-  if (M > 16 || K > 8192 || sharq::fused_layer_lds_bytes((int)K, gamma_bf16_dev != nullptr) > 160 * 1024)
+  if ((fmt != SHARQ_FMT_MXFP4 && fmt != SHARQ_FMT_NVFP4) || n != 2 || m != 4)
+    return fail(SHARQ_ERR_UNSUPPORTED, "the one-launch layer is built for 2:4 MXFP4 and NVFP4-style layers");
+  const bool nv = fmt == SHARQ_FMT_NVFP4;
+  const size_t lds = nv ? sharq::nv_fused_layer_lds_bytes((int)K) : sharq::fused_layer_lds_bytes((int)K, gamma_bf16_dev != nullptr);
+  if (M > 16 || K > 8192 || lds > 160 * 1024)
     return fail(SHARQ_ERR_UNSUPPORTED, "the one-launch layer takes M <= 16 and K <= 8192 (use sharq_prepare + sharq_linear)");
   if (M == 0) return SHARQ_OK;
   if (!x_bf16_dev || !y_dev) return fail(SHARQ_ERR_INVALID_ARG, "null pointer");
@@ -439,14 +441,18 @@ sharq_status sharq_linear_fused(const void* x_bf16_dev, int64_t M, int64_t K, in
   if (!w->codes || !aligned(w->codes, 16)) return fail(SHARQ_ERR_INVALID_ARG, "weight codes null or misaligned");
   const sharq_scale_view& vs = w->view[SHARQ_PATH_SPARSE];
   const sharq_scale_view& vd = w->view[SHARQ_PATH_DENSE];
-  const int64_t nb64 = (w->N + 15) / 16 * 64;
-  if (!vs.base || !vd.base || vs.block != 32 || vd.block != 32 || vs.ld != nb64 || vd.ld != nb64)
-    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be tiled MX views (block 32, K-tile stride NB*64)");
+  const int blk = nv ? 16 : 32;
+  const int64_t nbld = (w->N + 15) / 16 * (nv ? 128 : 64);
+  if (!vs.base || !vd.base || vs.block != blk || vd.block != blk || vs.ld != nbld || vd.ld != nbld ||
+      !aligned(vs.base, 16) || !aligned(vd.base, 16))
+    return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be the tiled views of the weight's format (block %d, K-tile stride %lld)",
+                blk, (long long)nbld);
   if (vs.base != vd.base)
     return fail(SHARQ_ERR_UNSUPPORTED, "the two paths must view the same packed scale array");
   s = check_device();
   if (s) return s;
   sharq::GemmArgs g{};
+  if (nv) g.g_w = reinterpret_cast<const float*>(vs.base + sharq::nv_weight_layout(w->N, w->K).g);
   g.w_codes = w->codes;
   g.w_scales_sparse = vs.base;
   g.w_scales_dense = vd.base;
@@ -458,9 +464,12 @@ sharq_status sharq_linear_fused(const void* x_bf16_dev, int64_t M, int64_t K, in
   g.K = (int)K;
   g.out_bf16 = out_dtype == SHARQ_OUT_BF16;
   g.a_blocks = 1;
-  hipError_t e = sharq::launch_linear_fused(static_cast<const uint16_t*>(x_bf16_dev), (int)M, (int)K, ldx,
-                                            static_cast<const uint16_t*>(gamma_bf16_dev), eps, g,
-                                            static_cast<hipStream_t>(stream));
+  hipError_t e = nv ? sharq::launch_linear_fused_nv(static_cast<const uint16_t*>(x_bf16_dev), (int)M, (int)K, ldx,
+                                                   static_cast<const uint16_t*>(gamma_bf16_dev), eps, g,
+                                                   static_cast<hipStream_t>(stream))
+                    : sharq::launch_linear_fused(static_cast<const uint16_t*>(x_bf16_dev), (int)M, (int)K, ldx,
+                                                 static_cast<const uint16_t*>(gamma_bf16_dev), eps, g,
+                                                 static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fused layer launch");
   return SHARQ_OK;
 }

@@ -68,6 +68,11 @@ hipError_t launch_linear_swiglu(const GemmArgs& a, hipStream_t stream);
 // The whole layer in one launch for M <= 16 (every workgroup prepares the rows
 // into LDS); fused_layer_lds_bytes must be <= 160 KiB.
 size_t fused_layer_lds_bytes(int K, bool norm);
+// The NVFP4-style layer in one launch (M <= 16): g carries the NVFP4 weight
+// (codes, tiled E4M3 scales, g_w) and the output.
+size_t nv_fused_layer_lds_bytes(int K);
+hipError_t launch_linear_fused_nv(const uint16_t* x, int M, int K, int64_t ldx, const uint16_t* gamma, float eps,
+                                  const GemmArgs& g, hipStream_t stream);
 hipError_t launch_linear_fused(const uint16_t* x, int M, int K, int64_t ldx, const uint16_t* gamma, float eps,
                                const GemmArgs& g, hipStream_t stream);
 

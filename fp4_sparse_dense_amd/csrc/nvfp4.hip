@@ -19,6 +19,8 @@
 // val(code) * s -- at most 6 significant bits, so exact in bf16 -- and runs the
 // bf16 MFMA with one fp32 accumulator per path; the tensor scales enter once,
 // in the epilogue: y = g_S g_W acc_S + g_R g_W acc_R.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -147,6 +149,76 @@ __device__ __forceinline__ Keep24 keep24(float a0, float a1, float a2, float a3)
   return k;
 }
 
+// One lane's 32 elements (two 16-element blocks) of v: the 2:4 mask, the
+// E4M3 block scales and the kept codes of the backbone (tensor scale g_s); v
+// is replaced by the residual r = v - deq(Q(S)).
+__device__ __forceinline__ void nv_backbone(float (&v)[32], float g_s, uint32_t (&scodes)[2], uint32_t& meta,
+                                            uint32_t& sbytes) {
+  const float six_g = 6.0f * g_s;
+  scodes[0] = scodes[1] = 0u;
+  meta = 0u;
+  sbytes = 0u;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float bm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[16 * b + i]));
+    uint32_t byte;
+    const float s = e4m3_round(bm / six_g, byte);
+    sbytes |= byte << (8 * b);
+    const float tq = s * g_s;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int G = 4 * b + gq;
+      float& a0 = v[4 * G];
+      float& a1 = v[4 * G + 1];
+      float& a2 = v[4 * G + 2];
+      float& a3 = v[4 * G + 3];
+      const Keep24 k = keep24(a0, a1, a2, a3);
+      meta |= k.nib << (4 * G);
+      const float x0 = k.k0 ? a0 : (k.f1 ? a1 : a2);
+      const float x1 = k.k3 ? a3 : (k.s2 ? a2 : a1);
+      const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
+      const uint32_t c = e2m1_pair(q0, q1);
+      scodes[b] |= c << (8 * gq);
+      float d0, d1;
+      fp4_unpack2<0>(c, d0, d1);
+      d0 = (d0 * s) * g_s;
+      d1 = (d1 * s) * g_s;
+      const float r0 = x0 - d0, r1 = x1 - d1;
+      a0 = k.k0 ? r0 : a0;
+      a1 = k.f1 ? r0 : (k.s1 ? r1 : a1);
+      a2 = k.f2 ? r0 : (k.s2 ? r1 : a2);
+      a3 = k.k3 ? r1 : a3;
+    }
+  }
+}
+
+// The residual codes and E4M3 block scales of one lane's 32 elements
+// (tensor scale g_r).
+__device__ __forceinline__ void nv_residual(const float (&v)[32], float g_r, uint32_t (&rc)[4], uint32_t& rbytes) {
+  const float six_r = 6.0f * g_r;
+  rc[0] = rc[1] = rc[2] = rc[3] = 0u;
+  rbytes = 0u;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float bm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[16 * b + i]));
+    uint32_t byte;
+    const float s = e4m3_round(bm / six_r, byte);
+    rbytes |= byte << (8 * b);
+    const float tq = s * g_r;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float x0 = v[16 * b + i], x1 = v[16 * b + i + 1];
+      const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
+      const int e = 16 * b + i;                 // element index; 8 per dword
+      rc[e / 8] |= e2m1_pair(q0, q1) << (4 * (e % 8));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Phases 2 and 3: one wave per 16-row x 128-K tile, 4 tiles of one row block
 // per workgroup; lane l owns row 16 rb + l%16 and K [128 kb + 32 (l/16), +32),
@@ -186,42 +258,8 @@ __global__ __launch_bounds__(256) void nv_decompose_kernel(NvPrepArgs a) {
   }
 
   // backbone: mask, per-16 block scale, kept codes; residual in place
-  const float six_g = 6.0f * g_s;
-  uint32_t scodes[2] = {0u, 0u}, meta = 0u, sbytes = 0u;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    float bm = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[16 * b + i]));
-    uint32_t byte;
-    const float s = e4m3_round(bm / six_g, byte);
-    sbytes |= byte << (8 * b);
-    const float tq = s * g_s;
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int G = 4 * b + gq;
-      float& a0 = v[4 * G];
-      float& a1 = v[4 * G + 1];
-      float& a2 = v[4 * G + 2];
-      float& a3 = v[4 * G + 3];
-      const Keep24 k = keep24(a0, a1, a2, a3);
-      meta |= k.nib << (4 * G);
-      const float x0 = k.k0 ? a0 : (k.f1 ? a1 : a2);
-      const float x1 = k.k3 ? a3 : (k.s2 ? a2 : a1);
-      const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
-      const uint32_t c = e2m1_pair(q0, q1);
-      scodes[b] |= c << (8 * gq);
-      float d0, d1;
-      fp4_unpack2<0>(c, d0, d1);
-      d0 = (d0 * s) * g_s;
-      d1 = (d1 * s) * g_s;
-      const float r0 = x0 - d0, r1 = x1 - d1;
-      a0 = k.k0 ? r0 : a0;
-      a1 = k.f1 ? r0 : (k.s1 ? r1 : a1);
-      a2 = k.f2 ? r0 : (k.s2 ? r1 : a2);
-      a3 = k.k3 ? r1 : a3;
-    }
-  }
+  uint32_t scodes[2], meta, sbytes;
+  nv_backbone(v, g_s, scodes, meta, sbytes);
   const int64_t tile = rb * a.KB + kb;
   const int64_t sc = ((int64_t)kb * a.RB + rb) * 128 + 2 * lane;
 
@@ -238,25 +276,8 @@ __global__ __launch_bounds__(256) void nv_decompose_kernel(NvPrepArgs a) {
     if (t == 0) a.rparts[rb * a.WX + blockIdx.x] = ar;
     if (t == 0 && blockIdx.x == 0 && blockIdx.y == 0) *a.g_s = g_s;
   } else {
-    const float six_r = 6.0f * g_r;
-    uint32_t rc[4] = {0u, 0u, 0u, 0u}, rbytes = 0u;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float bm = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[16 * b + i]));
-      uint32_t byte;
-      const float s = e4m3_round(bm / six_r, byte);
-      rbytes |= byte << (8 * b);
-      const float tq = s * g_r;
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float x0 = v[16 * b + i], x1 = v[16 * b + i + 1];
-        const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
-        const int e = 16 * b + i;                 // element index; 8 per dword
-        rc[e / 8] |= e2m1_pair(q0, q1) << (4 * (e % 8));
-      }
-    }
+    uint32_t rc[4], rbytes;
+    nv_residual(v, g_r, rc, rbytes);
     if (kb < a.KB) {
       *reinterpret_cast<uint4*>(a.o.r_codes + tile * 1024 + lane * 16) = make_uint4(rc[0], rc[1], rc[2], rc[3]);
       *reinterpret_cast<uint16_t*>(a.o.r_scales + sc) = (uint16_t)rbytes;
@@ -478,6 +499,344 @@ __global__ __launch_bounds__(64 * NW) void nv_dual_gemm_kernel(GemmArgs g) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// The NVFP4-style layer in one launch for small M (decode: M <= 16).  The
+// activation tensor is the M rows, so every workgroup of the weight-streaming
+// GEMM can compute its tensor scales itself: it prepares the rows into LDS --
+// the RMSNorm tree, max |v| (g_S), the backbone and max |r| (g_R), the
+// residual codes, the three phases of the preparation above with the same
+// arithmetic -- and then runs the small-M GEMM's split-K loop (one row block,
+// eight waves) on those operands.  Outputs are identical to the preparation
+// followed by the GEMM.
+// ---------------------------------------------------------------------------
+constexpr int kNvFusedWaves = 8;
+constexpr int kNvFusedThreads = 64 * kNvFusedWaves;
+
+struct NvFusedArgs {
+  const uint16_t* x;
+  int64_t ldx;
+  int M, K;
+  const uint16_t* gamma;   // nullptr: no RMSNorm
+  float eps;
+  GemmArgs g;              // weight (codes, scales, g_w), output, N
+};
+
+struct NvFusedLds {
+  uint32_t s, r, ss, rs, inv, red, total;   // byte offsets (the RMSNorm tree uses the R region first)
+  int KT, KC, P;
+};
+
+__host__ __device__ inline NvFusedLds nv_fused_lds(int K) {
+  NvFusedLds L;
+  L.KT = (K + 127) / 128;
+  L.KC = K / 32;
+  L.P = 1;
+  while (L.P < L.KC) L.P *= 2;
+  L.s = 0;
+  L.r = L.s + (uint32_t)L.KT * 1024;
+  L.ss = L.r + (uint32_t)L.KT * 1024;
+  L.rs = L.ss + (uint32_t)L.KT * 128;
+  L.inv = L.rs + (uint32_t)L.KT * 128;
+  L.red = L.inv + 16 * 4;
+  L.total = L.red + kNvFusedWaves * 4;
+  // after the GEMM loop the waves' partial sums (8 x 64 x 16 B) reuse the LDS from offset 0
+  const uint32_t parts = (uint32_t)kNvFusedWaves * 64u * 16u;
+  if (L.total < parts) L.total = parts;
+  return L;
+}
+
+// SMALL (at most kNvSmallChunks 32-element chunks of the rows per thread):
+// each thread loads its chunks of X and gamma once, then requests the weight's
+// first split-K pass (loads retire in issue order: the rows first), and keeps
+// v and then the residual in registers across the phases; otherwise every
+// phase re-reads its chunks and rebuilds the backbone.  Same arithmetic.
+constexpr int kNvSmallChunks = 2;
+
+template <bool NORM, bool SMALL>
+__global__ __launch_bounds__(kNvFusedThreads) void nv_fused_layer_kernel(NvFusedArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const NvFusedLds L = nv_fused_lds(a.K);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6) & (kNvFusedWaves - 1);
+  float* inv = reinterpret_cast<float*>(smem + L.inv);
+  float* red = reinterpret_cast<float*>(smem + L.red);
+  const int nq = a.M * L.KC;   // 32-element chunks of the rows
+  const GemmArgs& g = a.g;
+  const int KT = L.KT;
+  const int64_t NB = (g.N + 15) / 16, nb = blockIdx.x;
+  constexpr int CH = 8 * 4 / kNvFusedWaves;
+  // weight fragments of one split-K pass (a tile past K gets zeros)
+  auto load_w = [&](int base, uint4 (&wq)[CH], uint32_t (&wsb)[CH]) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int kt = base + wave + kNvFusedWaves * c;
+      const int ktc = kt < KT ? kt : KT - 1;
+      wq[c] = *reinterpret_cast<const uint4*>(g.w_codes + (nb * KT + ktc) * 1024 + lane * 16);
+      wsb[c] = *reinterpret_cast<const uint16_t*>(g.w_scales_dense + ((int64_t)ktc * NB + nb) * 128 + 2 * lane);
+      if (kt >= KT) { wq[c] = make_uint4(0, 0, 0, 0); wsb[c] = 0u; }
+    }
+  };
+  uint4 wq0[CH];
+  uint32_t wsb0[CH];
+  float g_s, g_r;
+
+  if constexpr (SMALL) {
+    // ---- chunk q = t + kNvFusedThreads * i: X and gamma as loaded, then the weight
+    uint4 xr[kNvSmallChunks][4], gr[kNvSmallChunks][4];
+#pragma unroll
+    for (int i = 0; i < kNvSmallChunks; ++i) {
+      const int q = t + kNvFusedThreads * i;
+      if (q < nq) {
+        const int r = q / L.KC, c = q % L.KC;
+        const uint4* px = reinterpret_cast<const uint4*>(a.x + (int64_t)r * a.ldx + 32 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xr[i][e] = px[e];
+        if (NORM) {
+          const uint4* pg = reinterpret_cast<const uint4*>(a.gamma + 32 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gr[i][e] = pg[e];
+        }
+      }
+    }
+    load_w(0, wq0, wsb0);
+    auto widen32 = [&](const uint4 (&q4)[4], float (&v)[32]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w[4] = {q4[e].x, q4[e].y, q4[e].z, q4[e].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v[8 * e + 2 * h] = bf16_lo(w[h]);
+          v[8 * e + 2 * h + 1] = bf16_hi(w[h]);
+        }
+      }
+    };
+    float v[kNvSmallChunks][32];
+#pragma unroll
+    for (int i = 0; i < kNvSmallChunks; ++i) widen32(xr[i], v[i]);
+    if (NORM) {
+      float* cs = reinterpret_cast<float*>(smem + L.r);
+#pragma unroll
+      for (int i = 0; i < kNvSmallChunks; ++i) {
+        const int q = t + kNvFusedThreads * i;
+        if (q < nq) cs[(q / L.KC) * L.P + q % L.KC] = chunk_sumsq(v[i]);
+      }
+      for (int it = t; it < a.M * L.P; it += kNvFusedThreads)
+        if (it % L.P >= L.KC) cs[it] = 0.0f;   // the zero padding of the tree
+      __syncthreads();
+      for (int n = L.P; n > 1; n >>= 1) {
+        const int h = n >> 1;
+        float tmp[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int it = t + qq * kNvFusedThreads;
+          tmp[qq] = it < a.M * h ? cs[(it / h) * L.P + 2 * (it % h)] + cs[(it / h) * L.P + 2 * (it % h) + 1] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int it = t + qq * kNvFusedThreads;
+          if (it < a.M * h) cs[(it / h) * L.P + (it % h)] = tmp[qq];
+        }
+        __syncthreads();
+      }
+      if (t < a.M) inv[t] = rms_inverse(cs[t * L.P], a.K, a.eps);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kNvSmallChunks; ++i) {
+        const int q = t + kNvFusedThreads * i;
+        if (q < nq) {
+          float gm[32];
+          widen32(gr[i], gm);
+          const float iv = inv[q / L.KC];
+#pragma unroll
+          for (int e = 0; e < 32; ++e) v[i][e] = (v[i][e] * iv) * gm[e];
+        }
+      }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kNvSmallChunks; ++i)
+      if (t + kNvFusedThreads * i < nq) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(v[i][e]));
+      }
+    g_s = tensor_scale(block_max<kNvFusedWaves>(am, red));
+    float ar = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kNvSmallChunks; ++i) {
+      const int q = t + kNvFusedThreads * i;
+      if (q < nq) {
+        uint32_t scodes[2], meta, sbytes;
+        nv_backbone(v[i], g_s, scodes, meta, sbytes);   // v[i] becomes the residual
+        const int r = q / L.KC, c = q % L.KC, kt = c >> 2, tl = (c & 3) * 16 + r;
+        *reinterpret_cast<uint4*>(smem + L.s + kt * 1024 + tl * 16) = expand_chunk(scodes[0], scodes[1], meta);
+        *reinterpret_cast<uint16_t*>(smem + L.ss + kt * 128 + 2 * tl) = (uint16_t)sbytes;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ar = fmaxf(ar, fabsf(v[i][e]));
+      }
+    }
+    g_r = tensor_scale(block_max<kNvFusedWaves>(ar, red));   // its barriers also end the tree's use of R
+#pragma unroll
+    for (int i = 0; i < kNvSmallChunks; ++i) {
+      const int q = t + kNvFusedThreads * i;
+      if (q < nq) {
+        uint32_t rc[4], rbytes;
+        nv_residual(v[i], g_r, rc, rbytes);
+        const int r = q / L.KC, c = q % L.KC, kt = c >> 2, tl = (c & 3) * 16 + r;
+        *reinterpret_cast<uint4*>(smem + L.r + kt * 1024 + tl * 16) = make_uint4(rc[0], rc[1], rc[2], rc[3]);
+        *reinterpret_cast<uint16_t*>(smem + L.rs + kt * 128 + 2 * tl) = (uint16_t)rbytes;
+      }
+    }
+  } else {
+
+  // ---- RMSNorm: per row the pairwise tree over 32-element chunk subtrees
+  // (M * P * 4 <= 4K bytes fit the R region, written only later)
+  if (NORM) {
+    float* cs = reinterpret_cast<float*>(smem + L.r);
+    for (int it = t; it < a.M * L.P; it += kNvFusedThreads) {
+      const int r = it / L.P, c = it % L.P;
+      float s = 0.0f;
+      if (c < L.KC) {
+        float v[32];
+        load32(a.x + (int64_t)r * a.ldx + 32 * c, v);
+        s = chunk_sumsq(v);
+      }
+      cs[r * L.P + c] = s;
+    }
+    __syncthreads();
+    for (int n = L.P; n > 1; n >>= 1) {
+      const int h = n >> 1;
+      float tmp[4];   // a.M * h <= 16 * 128 = 4 * kNvFusedThreads items
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int it = t + q * kNvFusedThreads;
+        tmp[q] = it < a.M * h ? cs[(it / h) * L.P + 2 * (it % h)] + cs[(it / h) * L.P + 2 * (it % h) + 1] : 0.0f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int it = t + q * kNvFusedThreads;
+        if (it < a.M * h) cs[(it / h) * L.P + (it % h)] = tmp[q];
+      }
+      __syncthreads();
+    }
+    if (t < a.M) inv[t] = rms_inverse(cs[t * L.P], a.K, a.eps);
+    __syncthreads();
+  }
+  auto load_v = [&](int q, float (&v)[32]) {
+    const int r = q / L.KC, c = q % L.KC;
+    load32(a.x + (int64_t)r * a.ldx + 32 * c, v);
+    if (NORM) apply_norm(v, a.gamma + 32 * c, inv[r]);
+  };
+
+  // ---- g_S from max |v| (the mask keeps each group's largest magnitude)
+  float am = 0.0f;
+  for (int q = t; q < nq; q += kNvFusedThreads) {
+    float v[32];
+    load_v(q, v);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+  }
+  g_s = tensor_scale(block_max<kNvFusedWaves>(am, red));
+
+  // ---- backbone into LDS (tile c/4, lane (c%4)*16 + r), g_R from max |r|
+  float ar = 0.0f;
+  for (int q = t; q < nq; q += kNvFusedThreads) {
+    float v[32];
+    load_v(q, v);
+    uint32_t scodes[2], meta, sbytes;
+    nv_backbone(v, g_s, scodes, meta, sbytes);
+    const int r = q / L.KC, c = q % L.KC, kt = c >> 2, tl = (c & 3) * 16 + r;
+    *reinterpret_cast<uint4*>(smem + L.s + kt * 1024 + tl * 16) = expand_chunk(scodes[0], scodes[1], meta);
+    *reinterpret_cast<uint16_t*>(smem + L.ss + kt * 128 + 2 * tl) = (uint16_t)sbytes;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ar = fmaxf(ar, fabsf(v[i]));
+  }
+  g_r = tensor_scale(block_max<kNvFusedWaves>(ar, red));   // its barriers also end the tree's use of R
+
+  // ---- residual codes into LDS
+  for (int q = t; q < nq; q += kNvFusedThreads) {
+    float v[32];
+    load_v(q, v);
+    uint32_t scodes[2], meta, sbytes, rc[4], rbytes;
+    nv_backbone(v, g_s, scodes, meta, sbytes);
+    nv_residual(v, g_r, rc, rbytes);
+    const int r = q / L.KC, c = q % L.KC, kt = c >> 2, tl = (c & 3) * 16 + r;
+    *reinterpret_cast<uint4*>(smem + L.r + kt * 1024 + tl * 16) = make_uint4(rc[0], rc[1], rc[2], rc[3]);
+    *reinterpret_cast<uint16_t*>(smem + L.rs + kt * 128 + 2 * tl) = (uint16_t)rbytes;
+  }
+  }   // !SMALL
+
+  // rows past M and chunks past K: zero codes and scale bytes
+  for (int b = t; b < 16 * L.KT * 4; b += kNvFusedThreads) {
+    const int r = b / (L.KT * 4), c = b % (L.KT * 4);
+    if (r < a.M && c < L.KC) continue;
+    const int kt = c >> 2, tl = (c & 3) * 16 + r;
+    *reinterpret_cast<uint4*>(smem + L.s + kt * 1024 + tl * 16) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(smem + L.r + kt * 1024 + tl * 16) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint16_t*>(smem + L.ss + kt * 128 + 2 * tl) = 0;
+    *reinterpret_cast<uint16_t*>(smem + L.rs + kt * 128 + 2 * tl) = 0;
+  }
+  __syncthreads();
+
+  // ---- split-K GEMM: nv_dual_gemm_kernel<1, 8>'s loop with A from LDS
+  v4f acs = (v4f){0.f, 0.f, 0.f, 0.f}, acr = acs;
+  for (int base = 0; base < KT; base += kNvFusedWaves * CH) {
+    uint4 wq[CH], rq[CH], sq[CH];
+    uint32_t wsb[CH], ssb[CH], rsb[CH];
+    if (SMALL && base == 0) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) { wq[c] = wq0[c]; wsb[c] = wsb0[c]; }
+    } else {
+      load_w(base, wq, wsb);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int kt = base + wave + kNvFusedWaves * c;
+      const int ktc = kt < KT ? kt : KT - 1;
+      rq[c] = *reinterpret_cast<const uint4*>(smem + L.r + ktc * 1024 + lane * 16);
+      sq[c] = *reinterpret_cast<const uint4*>(smem + L.s + ktc * 1024 + lane * 16);
+      ssb[c] = *reinterpret_cast<const uint16_t*>(smem + L.ss + ktc * 128 + 2 * lane);
+      rsb[c] = *reinterpret_cast<const uint16_t*>(smem + L.rs + ktc * 128 + 2 * lane);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      bf16x8 b[4], x[4];
+      deq32(wq[c], wsb[c], b);
+      deq32(sq[c], ssb[c], x);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acs = mfma_bf16(x[j], b[j], acs);
+      deq32(rq[c], rsb[c], x);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acr = mfma_bf16(x[j], b[j], acr);
+    }
+  }
+
+  // tensor scales once per path, then the waves' partial sums in wave order
+  // (all LDS is free once every wave has left the loop)
+  const float gw = *g.g_w;
+  const float fs = g_s * gw, fr = g_r * gw;
+  __syncthreads();
+  v4f* part = reinterpret_cast<v4f*>(smem + L.s);
+  v4f p;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) p[q] = fs * acs[q] + fr * acr[q];
+  part[wave * 64 + lane] = p;
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t col = nb * 16 + (lane & 15);
+    v4f v = part[lane];
+#pragma unroll
+    for (int w = 1; w < kNvFusedWaves; ++w) v = v + part[w * 64 + lane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = 4 * (lane >> 4) + q;
+      if (row < a.M && col < g.N) store_y(g, row, col, v[q]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prepare_nv(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma, float eps,
@@ -548,6 +907,43 @@ hipError_t launch_linear_nv(const GemmArgs& a, hipStream_t stream) {
     if (groups > 65535) return hipErrorInvalidValue;
     hipLaunchKernelGGL((nv_dual_gemm_kernel<4, 4>), dim3((unsigned)NB, (unsigned)groups), dim3(256), 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+
+size_t nv_fused_layer_lds_bytes(int K) { return nv_fused_lds(K).total; }
+
+hipError_t launch_linear_fused_nv(const uint16_t* x, int M, int K, int64_t ldx, const uint16_t* gamma, float eps,
+                                  const GemmArgs& g, hipStream_t stream) {
+  if (M == 0 || g.N == 0) return hipSuccess;
+  const int64_t NB = (g.N + 15) / 16;
+  const NvFusedLds L = nv_fused_lds(K);
+  if (M > 16 || NB > 0x7FFFFFFF || L.total > 160 * 1024) return hipErrorInvalidValue;
+  NvFusedArgs a;
+  a.x = x;
+  a.ldx = ldx;
+  a.M = M;
+  a.K = K;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.g = g;
+  const bool norm = gamma != nullptr;
+  const bool small = (int64_t)M * (K / 32) <= (int64_t)kNvSmallChunks * kNvFusedThreads;
+  auto kern = norm ? (small ? nv_fused_layer_kernel<true, true> : nv_fused_layer_kernel<true, false>)
+                   : (small ? nv_fused_layer_kernel<false, true> : nv_fused_layer_kernel<false, false>);
+  // the LDS limit is a per-function attribute: set it once per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  static std::atomic<bool> attr_set[64][4];
+  const int which = (norm ? 2 : 0) + (small ? 1 : 0);
+  if (!attr_set[dev][which].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set[dev][which].store(true, std::memory_order_release);
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)NB), dim3(kNvFusedThreads), L.total, stream, a);
   return hipGetLastError();
 }
 

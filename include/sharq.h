@@ -304,9 +304,14 @@ sharq_status sharq_linear_swiglu_prep(const sharq_act* a, const sharq_weight* w,
  * outputs bit for bit -- without materialising the prepared activation: each
  * workgroup of the weight-streaming GEMM prepares the rows into LDS.  SharQ
  * abstract: the preparation is one fused operator feeding both GEMMs.
- * Limits: M <= 16, K <= 8192, 2:4, MXFP4 (others: UNSUPPORTED; use the
- * two-call path).  It is faster than the two calls up to M = 8 only.  gamma NULL skips RMSNorm.  y: fp32 or bf16 per out_dtype,
- * row stride ldy >= N.
+ * Limits: M <= 16, K <= 8192, 2:4, MXFP4 or NVFP4-style (others:
+ * UNSUPPORTED; use the two-call path).  In the NVFP4-style format the
+ * activation tensor is the M rows, so each workgroup also computes the two
+ * tensor scales (g_S from max |v|, g_R from max |r|) itself, with the
+ * preparation's arithmetic; the outputs equal sharq_prepare (fmt NVFP4)
+ * followed by sharq_linear.  The MXFP4 form is faster than the two calls up to
+ * M = 8 only.  gamma NULL skips RMSNorm.  y: fp32 or bf16 per out_dtype, row
+ * stride ldy >= N.
  * Errors: INVALID_ARG (null, shapes, K mismatch, ldx/ldy, misaligned buffers,
  * weight views), UNSUPPORTED (limits, format, pattern, not gfx950), HIP. */
 sharq_status sharq_linear_fused(const void* x_bf16_dev, int64_t M, int64_t K, int64_t ldx,
