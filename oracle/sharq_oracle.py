@@ -13,7 +13,7 @@ FP4 Quantization for LLM Inference", Abstract):
   taken against the *quantised* backbone -> FP4 quantisation of R; then
   Y = deq(Q(S)) deq(W)^T + deq(Q(R)) deq(W)^T over one FP4 weight payload.
 
-The pages print no formulas.  Readings used here (each listed in the design doc):
+The pages print no formulas.  The readings this oracle takes of them:
 
 * RMSNorm is evaluated in IEEE binary32 with the sum of squares taken as a
   balanced pairwise tree in index order over the row zero-padded to a power of
