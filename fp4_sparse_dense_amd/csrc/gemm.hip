@@ -548,6 +548,69 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     }
     return;
   }
+  // A tile wholly inside Y with 16-byte-aligned rows goes out through LDS: the
+  // lanes hold 64- (fp32) or 32-byte (bf16) pieces of rows, which the memory
+  // system writes at a fraction of its line rate, so each wave stages its
+  // block in LDS (two halves of 32 rows) and writes whole 16-byte pieces in row
+  // order, consecutive lanes along a row.  The residual add and the rounding
+  // are those of store_out.
+  if constexpr (!GROUPED) {
+    static_assert(C::kWMT % 2 == 0, "two halves per wave");
+    constexpr int kSt = C::kWNT * 16 + 4;                 // floats per staged row (+4: banks)
+    static_assert(C::kWaves * 32 * kSt * 4 <= C::kStages * C::kStage, "staging fits the LDS ring");
+    const int eb = g.out_bf16 ? 2 : 4;
+    const bool full = (rb0 + C::kMB) * 16 <= y_rows && (nb0 + C::kNB) * 16 <= y_cols;
+    const bool al = ((uintptr_t)g.y & 15) == 0 && ((g.ldy * eb) & 15) == 0 &&
+                    (!g.resid || (((uintptr_t)g.resid & 15) == 0 && (g.ld_resid & 7) == 0));
+    if (full && al) {
+      __syncthreads();   // every wave has consumed its last fragments: the ring is free
+      float* st = reinterpret_cast<float*>(smem) + wave * 32 * kSt;
+      const int64_t col0 = (nb0 + wn * C::kWNT) * 16;
+#pragma unroll
+      for (int h = 0; h < C::kWMT / 2; ++h) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < C::kWNT; ++j)
+            *reinterpret_cast<v4f*>(st + (ii * 16 + r16) * kSt + 16 * j + 4 * c4) = acc[2 * h + ii][j];
+        const int64_t row0 = (rb0 + wm * C::kWMT + 2 * h) * 16;
+        if (g.out_bf16) {
+          constexpr int kPpr = C::kWNT * 2;                 // 8-element pieces per row
+#pragma unroll
+          for (int k = 0; k < 32 * kPpr / 64; ++k) {
+            const int pc = lane + 64 * k, r = pc / kPpr, c = (pc % kPpr) * 8;
+            v4f a = *reinterpret_cast<const v4f*>(st + r * kSt + c);
+            v4f b = *reinterpret_cast<const v4f*>(st + r * kSt + c + 4);
+            const int64_t row = y_row0 + row0 + r, col = col0 + c;
+            if (g.resid) {
+              const uint4 x = *reinterpret_cast<const uint4*>(g.resid + row * g.ld_resid + col);
+              a[0] = __uint_as_float(x.x << 16) + a[0];
+              a[1] = __uint_as_float(x.x & 0xFFFF0000u) + a[1];
+              a[2] = __uint_as_float(x.y << 16) + a[2];
+              a[3] = __uint_as_float(x.y & 0xFFFF0000u) + a[3];
+              b[0] = __uint_as_float(x.z << 16) + b[0];
+              b[1] = __uint_as_float(x.z & 0xFFFF0000u) + b[1];
+              b[2] = __uint_as_float(x.w << 16) + b[2];
+              b[3] = __uint_as_float(x.w & 0xFFFF0000u) + b[3];
+            }
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.y) + row * g.ldy + col) =
+                make_uint4(bf16_bits_rne(a[0]) | bf16_bits_rne(a[1]) << 16, bf16_bits_rne(a[2]) | bf16_bits_rne(a[3]) << 16,
+                           bf16_bits_rne(b[0]) | bf16_bits_rne(b[1]) << 16, bf16_bits_rne(b[2]) | bf16_bits_rne(b[3]) << 16);
+          }
+        } else {
+          constexpr int kPpr = C::kWNT * 4;                 // 4-element pieces per row
+#pragma unroll
+          for (int k = 0; k < 32 * kPpr / 64; ++k) {
+            const int pc = lane + 64 * k, r = pc / kPpr, c = (pc % kPpr) * 4;
+            const v4f a = *reinterpret_cast<const v4f*>(st + r * kSt + c);
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.y) + (y_row0 + row0 + r) * g.ldy + col0 + c) =
+                make_float4(a[0], a[1], a[2], a[3]);
+          }
+        }
+      }
+      return;
+    }
+  }
   // four consecutive outputs per lane and block: one 16-byte (fp32) or 8-byte
   // (bf16) store where the row stride and base allow it and all four columns
   // exist, else element by element

@@ -105,3 +105,24 @@ def test_linear_deterministic_and_strided_output():
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     assert torch.all(big[:, :32] == 7.0) and torch.all(big[:, 32 + inp["N"]:] == 7.0)
+
+
+@pytest.mark.parametrize("M,K,N", [(512, 512, 384), (512, 1024, 6144), (300, 512, 200), (2048, 256, 4096)])
+def test_linear_tiled_bf16_equals_rounded_fp32(M, K, N):
+    """The tiled kernel's bf16 output (staged through LDS for whole tiles,
+    element-wise at ragged edges) is its fp32 output rounded to nearest even."""
+    import torch
+    print(f"tiled bf16 M={M} K={K} N={N}", flush=True)
+    rng = np.random.default_rng(M + K + N + 7)
+    x = synth.outlier_activations(rng, M, K)
+    w = synth.linear_weight(rng, N, K)
+    act = sq.sharq_prepare(dev_bf16(x), None, 1e-5)
+    wt = sq.sharq_pack_weight(dev_bf16(w))
+    y32 = sq.sharq_linear(act, wt)
+    y16 = sq.sharq_linear(act, wt, out_dtype=sq.OUT_BF16)
+    wide = torch.zeros(M, N + 8, dtype=torch.bfloat16, device="cuda")
+    sq.sharq_linear(act, wt, out=wide[:, :N], out_dtype=sq.OUT_BF16)   # row stride N + 8
+    torch.cuda.synchronize()
+    ref = y32.to(torch.bfloat16).view(torch.int16)
+    assert torch.equal(y16.view(torch.int16), ref)
+    assert torch.equal(wide[:, :N].contiguous().view(torch.int16), ref)
