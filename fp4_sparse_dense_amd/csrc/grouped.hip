@@ -10,7 +10,7 @@
 //   1. setup   (one workgroup): clamps the caller's segment offsets into a
 //      nondecreasing sequence in [0, rows], and tabulates, per expert, its
 //      first 16-row block in the gathered activation (segments padded to whole
-//      blocks) and the number of 256-row M tiles before it;
+//      blocks) and the number of M tiles (grouped_tile_m() rows) before it;
 //   2. gather  (one wave per gathered 16-row block and K tile): copies each
 //      routed row's backbone and residual codes and scales (the GEMM does not
 //      read the metadata) from the source activation (row row_index[i], or i)
