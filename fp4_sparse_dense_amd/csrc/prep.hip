@@ -76,18 +76,18 @@ struct PrepPlan {
   uint32_t off_gamma, off_sums, total;
 };
 
-static PrepPlan prep_plan(int K, bool norm) {
+static PrepPlan prep_plan(int K, bool norm, int waves) {
   PrepPlan p{};
   p.nunits = (K + kUnitK - 1) / kUnitK;
   p.units_p2 = 1;
   while (p.units_p2 < p.nunits) p.units_p2 *= 2;
-  const int per_wave = (p.nunits + kPrepWaves - 1) / kPrepWaves;
+  const int per_wave = (p.nunits + waves - 1) / waves;
   const uint32_t kp = (uint32_t)p.nunits * kUnitK;
   const uint32_t sums = norm ? (uint32_t)p.units_p2 * kPrepRows * 4 : 0;
   for (int f32 = norm ? 1 : 0; f32 >= 0; --f32) {
     const uint32_t gbytes = norm ? kp / 32u * (f32 ? kGammaBlockF32 * 4u : kGammaBlockBf16 * 2u) : 0;
     const int64_t avail = (int64_t)kPrepLdsMax - gbytes - sums;
-    int s = avail > 0 ? (int)(avail / (kPrepWaves * kSlotBytes)) : 0;
+    int s = avail > 0 ? (int)(avail / ((int64_t)waves * kSlotBytes)) : 0;
     s = s < kMaxSlots ? s : kMaxSlots;
     p.gamma_f32 = f32;
     p.single = norm && per_wave <= s;
@@ -95,7 +95,7 @@ static PrepPlan prep_plan(int K, bool norm) {
     // flight per slot and gains nothing past the wave's units
     const int want = per_wave > 0 ? per_wave : 1;
     p.slots = p.single ? (per_wave > 0 ? per_wave : 1) : (want < s ? want : s);
-    p.off_gamma = (uint32_t)p.slots * kPrepWaves * kSlotBytes;
+    p.off_gamma = (uint32_t)p.slots * (uint32_t)waves * kSlotBytes;
     p.off_sums = p.off_gamma + gbytes;
     p.total = p.off_sums + sums;
     if (!norm || p.single || f32 == 0) break;
@@ -111,8 +111,8 @@ __device__ __forceinline__ void wait_units(int n) {
   else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
 }
 
-template <bool NORM, bool GF32, bool DENSE>
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
+template <int W, bool NORM, bool GF32, bool DENSE>
+__global__ __launch_bounds__(W * 64) void prep_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
                                                             int64_t ldx, const uint16_t* __restrict__ gamma,
                                                             float eps, PrepPlan P, PrepOut o) {
   extern __shared__ __align__(1024) uint8_t smem[];
@@ -144,14 +144,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
 
   const uint32_t ring_off = (uint32_t)wave * P.slots * kSlotBytes;
   const uint32_t ring = lds_addr(smem) + ring_off;
-  const int nu_w = P.nunits > wave ? (P.nunits - wave + kPrepWaves - 1) / kPrepWaves : 0;
+  const int nu_w = P.nunits > wave ? (P.nunits - wave + W - 1) / W : 0;
   // streaming look-ahead: one unit per slot.  A slot is refilled as soon as
   // its block reads have returned (the copies need no registers), so all
   // slots can be in flight while a block is being decomposed.
   const int D = P.slots;
 
   auto issue = [&](int j) {
-    const int u = wave + kPrepWaves * j;
+    const int u = wave + W * j;
     const uint32_t slot = ring + (uint32_t)(j % P.slots) * kSlotBytes;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
     float* sums = reinterpret_cast<float*>(smem + P.off_sums);
     // gamma into LDS (binary32, or bf16 words for long rows), zero past K
     const int kp = P.nunits * kUnitK;
-    for (int e = tid * 8; e < kp; e += kPrepThreads * 8) {
+    for (int e = tid * 8; e < kp; e += (W * 64) * 8) {
       const uint4 q = e < K ? *reinterpret_cast<const uint4*>(gamma + e) : make_uint4(0, 0, 0, 0);
       if (GF32) {
         float* gs = reinterpret_cast<float*>(smem + P.off_gamma) + e + (kGammaBlockF32 - 32) * (e / 32);
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
         *reinterpret_cast<uint4*>(smem + P.off_gamma + (e + (kGammaBlockBf16 - 32) * (e / 32)) * 2) = q;
       }
     }
-    for (int i = P.nunits * kPrepRows + tid; i < P.units_p2 * kPrepRows; i += kPrepThreads) sums[i] = 0.0f;
+    for (int i = P.nunits * kPrepRows + tid; i < P.units_p2 * kPrepRows; i += (W * 64)) sums[i] = 0.0f;
 
     auto unit_ss = [&](const uint32_t (&xw)[16], int j) {
       float p[16];
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
       t = t + __shfl_xor(t, 8, 64);    // blocks of a tile, in K order
       t = t + __shfl_xor(t, 16, 64);
       t = t + __shfl_xor(t, 32, 64);   // the two tiles of the unit
-      if (lane < 8) sums[(wave + kPrepWaves * j) * kPrepRows + lane] = t;
+      if (lane < 8) sums[(wave + W * j) * kPrepRows + lane] = t;
     };
 
     if (P.single) {
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
     for (int s = 1; s < P.units_p2; s *= 2) {
       __syncthreads();
       const int pairs = P.units_p2 / (2 * s);
-      for (int i = tid; i < pairs * kPrepRows; i += kPrepThreads) {
+      for (int i = tid; i < pairs * kPrepRows; i += (W * 64)) {
         const int a = (i / kPrepRows) * 2 * s, r = i % kPrepRows;
         sums[a * kPrepRows + r] = sums[a * kPrepRows + r] + sums[(a + s) * kPrepRows + r];
       }
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
     float v[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) { v[2 * i] = bf16_lo(xw[i]); v[2 * i + 1] = bf16_hi(xw[i]); }
-    const int u = wave + kPrepWaves * j;
+    const int u = wave + W * j;
     const int kb = (2 * u + t2) * 128 + c4 * 32;   // first element of the block
     if (NORM) {
       if (GF32) {
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
 
   const int tl = c4 * 16 + (int)half * 8 + r8;
   auto store = [&](const Block32& b, int j) {
-    const int kt = 2 * (wave + kPrepWaves * j) + t2;
+    const int kt = 2 * (wave + W * j) + t2;
     if (kt < KB) {
       const int64_t tile = rb * KB + kt;
       *reinterpret_cast<uint4*>(o.r_codes + tile * 1024 + tl * 16) = b.r_codes;
@@ -368,24 +368,32 @@ template <bool DENSE>
 static hipError_t launch_prepare_t(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
                                    float eps, PrepOut out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const PrepPlan P = prep_plan(K, gamma != nullptr);
+  // Short rows without RMSNorm (at most eight 256-element units: K <= 2048,
+  // the expert layers) run 4- or 8-wave workgroups: with 16 waves most would
+  // have no unit, and the CU would hold only two workgroups' few busy waves.
+  const int units = (K + kUnitK - 1) / kUnitK;
+  const int waves = gamma ? kPrepWaves : (units <= 4 ? 4 : (units <= 8 ? 8 : kPrepWaves));
+  const PrepPlan P = prep_plan(K, gamma != nullptr, waves);
   if (P.slots < 1 || P.total > kPrepLdsMax) return hipErrorInvalidValue;
-  auto kn = !gamma ? prep_kernel<false, false, DENSE>
-                   : (P.gamma_f32 ? prep_kernel<true, true, DENSE> : prep_kernel<true, false, DENSE>);
+  auto kn = waves == 4 ? prep_kernel<4, false, false, DENSE>
+            : waves == 8 ? prep_kernel<8, false, false, DENSE>
+            : (!gamma ? prep_kernel<kPrepWaves, false, false, DENSE>
+                      : (P.gamma_f32 ? prep_kernel<kPrepWaves, true, true, DENSE>
+                                     : prep_kernel<kPrepWaves, true, false, DENSE>));
   // the LDS limit is a per-function attribute: set it once per device
-  const int which = !gamma ? 0 : (P.gamma_f32 ? 1 : 2);
+  const int which = waves == 4 ? 3 : (waves == 8 ? 4 : (!gamma ? 0 : (P.gamma_f32 ? 1 : 2)));
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  static std::atomic<bool> attr_set[64][3];
+  static std::atomic<bool> attr_set[64][5];
   if (!attr_set[dev][which].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute((const void*)kn, hipFuncAttributeMaxDynamicSharedMemorySize, kPrepLdsMax);
     if (e != hipSuccess) return e;
     attr_set[dev][which].store(true, std::memory_order_release);
   }
   const int64_t nwg = (M + 15) / 16 * 2;
-  hipLaunchKernelGGL(kn, dim3((unsigned)nwg), dim3(kPrepThreads), P.total, stream, x, M, K, ldx, gamma, eps, P, out);
+  hipLaunchKernelGGL(kn, dim3((unsigned)nwg), dim3(waves * 64), P.total, stream, x, M, K, ldx, gamma, eps, P, out);
   return hipGetLastError();
 }
 
