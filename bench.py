@@ -223,6 +223,8 @@ def main():
                     help="fusion ablations: a standalone RMSNorm writing bf16 before the preparation, or "
                          "the two GEMM paths as separate launches and an add")
     ap.add_argument("--sets", type=int, default=0, help="rotating input/weight/output sets (0: enough for > 512 MB)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps in a HIP graph and replay it (always on for decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration under rocprofv3)")
@@ -348,7 +350,7 @@ def run_dense(args):
                 fn()
     step.parts = len(part_names)
 
-    graph = args.workload == "decode"
+    graph = args.workload == "decode" or args.graph
     ms, parts = timed(step, args.steps, args.warmup, graph=graph)
     part_ms = [float(np.mean(p)) for p in parts]
     prep_ms, gemm_ms = sum(part_ms[:n_prep]), sum(part_ms[n_prep:])
