@@ -200,11 +200,22 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   } else {
     // (expert, M tile, N tile): M tiles of all experts are numbered through
     // tprefix; the weight holds the experts' column blocks one after another
+    // The T = (M tiles) x tiles_n units, numbered M tile major, are cut into 8
+    // contiguous runs of `per`, one per XCD (workgroup b runs on XCD b mod 8,
+    // as its b / 8-th): an M tile's N tiles then run side by side on one XCD
+    // and share its activation tile in that L2, and an expert's M tiles stay
+    // together, sharing its weight.  (Dealt in plain order, N tile j of every M
+    // tile went to one XCD and each XCD read the whole activation.)  The grid
+    // is a multiple of 8 holding at least T units; the rest return.
     const int64_t NBe = NB / g.E;
     const int tiles_n = (int)((NBe + C::kNB - 1) / C::kNB);
-    const int nt = (int)(blockIdx.x % tiles_n);
-    const int mtg = (int)(blockIdx.x / tiles_n);
-    if (mtg >= g.tprefix[g.E]) return;              // the whole workgroup: past the last tile
+    const int64_t T = (int64_t)g.tprefix[g.E] * tiles_n;
+    const int64_t per = (T + 7) / 8;
+    const int64_t i_x = blockIdx.x / 8;
+    const int64_t u = (int64_t)(blockIdx.x % 8) * per + i_x;
+    if (i_x >= per || u >= T) return;               // the whole workgroup: past the last unit
+    const int nt = (int)(u % tiles_n);
+    const int mtg = (int)(u / tiles_n);
     int lo = 0, hi = g.E;                            // expert e: tprefix[e] <= mtg < tprefix[e+1]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -554,6 +565,56 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   // block in LDS (two halves of 32 rows) and writes whole 16-byte pieces in row
   // order, consecutive lanes along a row.  The residual add and the rounding
   // are those of store_out.
+  // The grouped layer's ring (two stages) holds one 16-row block per wave at a
+  // time, and its tiles are ragged (an expert's last rows, a last N tile past
+  // N_e): each wave stages its blocks one by one and skips the pieces outside
+  // Y.  N_e is a multiple of 16, so a 16-byte piece is wholly in or out.
+  if constexpr (GROUPED) {
+    constexpr int kSt = C::kWNT * 16 + 4;                 // floats per staged row (+4: banks)
+    static_assert(C::kWaves * 16 * kSt * 4 <= C::kStages * C::kStage, "staging fits the LDS ring");
+    const int eb = g.out_bf16 ? 2 : 4;
+    const bool al = ((uintptr_t)g.y & 15) == 0 && ((g.ldy * eb) & 15) == 0 && y_cols % 8 == 0 && !g.resid;
+    if (al) {
+      __syncthreads();   // every wave has consumed its last fragments: the ring is free
+      float* st = reinterpret_cast<float*>(smem) + wave * 16 * kSt;
+      const int64_t col0 = (nb0 - nb_first + wn * C::kWNT) * 16;
+#pragma unroll
+      for (int i = 0; i < C::kWMT; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::kWNT; ++j)
+          *reinterpret_cast<v4f*>(st + r16 * kSt + 16 * j + 4 * c4) = acc[i][j];
+        const int64_t row0 = (rb0 - rb_first + wm * C::kWMT + i) * 16;
+        if (g.out_bf16) {
+          constexpr int kPpr = C::kWNT * 2;                 // 8-element pieces per row
+          static_assert(16 * kPpr % 64 == 0, "whole lanes per block");
+#pragma unroll
+          for (int k = 0; k < 16 * kPpr / 64; ++k) {
+            const int pc = lane + 64 * k, r = pc / kPpr, c = (pc % kPpr) * 8;
+            const v4f a = *reinterpret_cast<const v4f*>(st + r * kSt + c);
+            const v4f b = *reinterpret_cast<const v4f*>(st + r * kSt + c + 4);
+            const int64_t row = row0 + r, col = col0 + c;
+            if (row < y_rows && col < y_cols)
+              *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.y) + (y_row0 + row) * g.ldy + col) =
+                  make_uint4(bf16_bits_rne(a[0]) | bf16_bits_rne(a[1]) << 16, bf16_bits_rne(a[2]) | bf16_bits_rne(a[3]) << 16,
+                             bf16_bits_rne(b[0]) | bf16_bits_rne(b[1]) << 16, bf16_bits_rne(b[2]) | bf16_bits_rne(b[3]) << 16);
+          }
+        } else {
+          constexpr int kPpr = C::kWNT * 4;                 // 4-element pieces per row
+          static_assert(16 * kPpr % 64 == 0, "whole lanes per block");
+#pragma unroll
+          for (int k = 0; k < 16 * kPpr / 64; ++k) {
+            const int pc = lane + 64 * k, r = pc / kPpr, c = (pc % kPpr) * 4;
+            const v4f a = *reinterpret_cast<const v4f*>(st + r * kSt + c);
+            const int64_t row = row0 + r, col = col0 + c;
+            if (row < y_rows && col < y_cols)
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.y) + (y_row0 + row) * g.ldy + col) =
+                  make_float4(a[0], a[1], a[2], a[3]);
+          }
+        }
+      }
+      return;
+    }
+  }
   if constexpr (!GROUPED) {
     static_assert(C::kWMT % 2 == 0, "two halves per wave");
     constexpr int kSt = C::kWNT * 16 + 4;                 // floats per staged row (+4: banks)
@@ -701,7 +762,8 @@ static int xcd_region_m(int64_t tm, int64_t tn, int bm_rows, int bn_cols) {
 hipError_t launch_linear_grouped_gemm(const GemmArgs& a, int64_t max_mtiles, hipStream_t stream) {
   const int64_t NBe = (a.N / a.E + 15) / 16;
   const int64_t tiles_n = (NBe + kTileN / 16 - 1) / (kTileN / 16);
-  return launch_tiled<kGroupedTileM, kTileN, 4, 2, 2, true, false>(a, max_mtiles * tiles_n, stream);
+  // a multiple of 8 workgroups: each XCD's run of units fits its share of the grid
+  return launch_tiled<kGroupedTileM, kTileN, 4, 2, 2, true, false>(a, (max_mtiles * tiles_n + 7) / 8 * 8, stream);
 }
 
 template <bool DENSE>

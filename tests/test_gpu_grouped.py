@@ -2,7 +2,8 @@
 against the oracle's SharQ linear layer of that row with that expert's weight
 (|y_gpu - y_ref| <= 1e-5 * sum|terms| + 1e-6), for gathered token rows
 (gate/up) and expert-sorted rows (down), with empty experts, experts spanning
-several 256-row tiles and out-of-range row indices."""
+several M tiles, ragged N tiles, bf16 and strided outputs, and out-of-range
+row indices."""
 import numpy as np
 import pytest
 
@@ -93,3 +94,40 @@ def test_grouped_out_of_range_rows_read_zero():
     bad = (row_index < 0) | (row_index >= tokens)
     assert np.all(yg[bad] == 0.0)
     assert_linear_close(yg, yr, b, "out-of-range rows")
+
+
+def test_grouped_ragged_tiles_bf16_and_strided_outputs():
+    """N_e = 80 (a last N tile past N_e) and experts ending inside a 16-row block:
+    fp32 output against the oracle; the bf16 output is the fp32 one rounded to
+    nearest even; outputs with a padded row stride (16-byte rows: the LDS-staged
+    epilogue; odd stride: the element-wise one) equal the dense ones and leave
+    the padding untouched."""
+    import torch
+    print("grouped ragged tiles / bf16 / strided", flush=True)
+    rng = np.random.default_rng(21)
+    tokens, experts, top_k, d_model, n_e = 300, 6, 3, 384, 80
+    expert, token, seg = synth.zipf_router(rng, tokens, experts, top_k)
+    x = synth.outlier_activations(rng, tokens, d_model)
+    w = np.concatenate([synth.linear_weight(rng, n_e, d_model) for _ in range(experts)])
+    act = sq.sharq_prepare(dev_bf16(x), None)
+    wt = sq.sharq_pack_weight(dev_bf16(w))
+    seg_d = _dev(seg, torch.int64)
+    ri = _dev(token.astype(np.int32), torch.int32)
+    rows = int(seg[-1])
+    y32 = sq.sharq_linear_grouped(act, wt, seg_d, experts, row_index=ri, rows=rows)
+    y16 = sq.sharq_linear_grouped(act, wt, seg_d, experts, row_index=ri, rows=rows, out_dtype=sq.OUT_BF16)
+    outs = {}
+    for pad in (8, 1):
+        for dt, code in ((torch.float32, sq.OUT_F32), (torch.bfloat16, sq.OUT_BF16)):
+            big = torch.full((rows, n_e + pad), 3.0, dtype=dt, device="cuda")
+            sq.sharq_linear_grouped(act, wt, seg_d, experts, row_index=ri, rows=rows, out=big[:, :n_e], out_dtype=code)
+            outs[(pad, code)] = big
+    torch.cuda.synchronize()
+    ref = O.prepare(x, None)
+    yr, b = _reference(ref, token.astype(np.int64), seg, w, experts)
+    assert_linear_close(y32.cpu().numpy(), yr, b, "ragged grouped fp32")
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    for (pad, code), big in outs.items():
+        want = y32 if code == sq.OUT_F32 else y16
+        assert torch.equal(big[:, :n_e].contiguous(), want), (pad, code)
+        assert torch.all(big[:, n_e:] == 3.0), (pad, code)
