@@ -576,6 +576,16 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
     return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be tiled MX views (block 32, K-tile stride NB*64)");
   if (vs.base != vd.base)
     return fail(SHARQ_ERR_UNSUPPORTED, "the two paths must view the same packed scale array (distinct per-path scale arrays are not built)");
+  {
+    // the tiled kernel addresses the source activation, the gathered one and
+    // the weight with 31-bit buffer offsets
+    const uint64_t kb = (uint64_t)(a->K + 127) / 128, lim = 0x7FFFFFFFull;
+    const uint64_t src_blocks = (uint64_t)(a->M + 15) / 16, dst_blocks = (uint64_t)(rows + 15 * (int64_t)E + 15) / 16;
+    const uint64_t w_blocks = (uint64_t)(w->N + 15) / 16;
+    if (src_blocks * kb * 1024 >= lim || dst_blocks * kb * 1024 >= lim || w_blocks * kb * 1024 >= lim)
+      return fail(SHARQ_ERR_UNSUPPORTED, "grouped operands past 2 GiB of codes (M=%lld, rows=%lld, N=%lld, K=%lld)",
+                  (long long)a->M, (long long)rows, (long long)w->N, (long long)a->K);
+  }
   const size_t need = sharq::grouped_workspace_bytes(rows, E, (int)a->K);
   if (!ws_dev || ws_bytes < need || !aligned(ws_dev, 256))
     return fail(SHARQ_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", need, ws_bytes);

@@ -233,9 +233,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     y_cols = g.N / g.E;
   }
 
-  const u32x4 rs_sc = make_desc(g.s_codes, (uint64_t)RB * KT * 1024);
+  const int64_t RBc = GROUPED && g.gather ? g.src_blocks : RB;   // blocks of the code buffers
+  const u32x4 rs_sc = make_desc(g.s_codes, (uint64_t)RBc * KT * 1024);
   const u32x4 rs_ss = make_desc(g.s_scales, (uint64_t)RB * KT * 64);
-  const u32x4 rs_rc = make_desc(g.r_codes, (uint64_t)RB * KT * 1024);
+  const u32x4 rs_rc = make_desc(g.r_codes, (uint64_t)RBc * KT * 1024);
   const u32x4 rs_rs = make_desc(g.r_scales, (uint64_t)RB * KT * 64);
   const u32x4 rs_wc = make_desc(g.w_codes, (uint64_t)NB * KT * 1024);
   const u32x4 rs_ws = make_desc(g.w_scales_dense, (uint64_t)KT * (uint64_t)g.w_scales_ld);
@@ -263,6 +264,19 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
   for (int i = 0; i < kSB; ++i) {
     const int64_t rb = rb0 + wave + i * C::kWaves;
     offA[i] = rb < rb_end ? (uint32_t)(rb * KT) * 1024u + lane * 16 : kOOB;
+    if constexpr (GROUPED) {
+      if (g.gather) {
+        // this lane's piece (row r16, 32-element chunk c4) of routed row lr of
+        // the expert, taken from its source row's piece; rows past the expert
+        // or out of range read as zero
+        const int64_t lr = (rb - rb_first) * 16 + r16;
+        int64_t src = -1;
+        if (rb < rb_end && lr < y_rows) src = g.row_index ? (int64_t)g.row_index[y_row0 + lr] : y_row0 + lr;
+        offA[i] = src >= 0 && src < g.src_rows
+                      ? (uint32_t)((src >> 4) * KT) * 1024u + (uint32_t)(c4 * 16 + (int)(src & 15)) * 16u
+                      : kOOB;
+      }
+    }
   }
   int wblk[kWB];
   uint32_t offW[kWB];

@@ -11,10 +11,12 @@
 //      nondecreasing sequence in [0, rows], and tabulates, per expert, its
 //      first 16-row block in the gathered activation (segments padded to whole
 //      blocks) and the number of M tiles (grouped_tile_m() rows) before it;
-//   2. gather  (one wave per gathered 16-row block and K tile): copies each
-//      routed row's backbone and residual codes and scales (the GEMM does not
-//      read the metadata) from the source activation (row row_index[i], or i)
-//      into expert order, writing zero codes and scales for the padding rows;
+//   2. gather  (one wave per gathered 16-row block): copies each routed row's
+//      backbone and residual codes and scales (the GEMM does not read the
+//      metadata) from the source activation (row row_index[i]) into expert
+//      order, writing zero codes and scales for the padding rows.  Without a
+//      row index the rows are already in expert order and only the scales are
+//      copied: the GEMM reads the codes from the source rows itself;
 //   3. the tiled dual GEMM with one workgroup per (expert, M tile, N tile).
 #include "device_common.h"
 #include "launch.h"
@@ -164,6 +166,54 @@ __global__ __launch_bounds__(256) void grouped_gather_kernel(GatherArgs a) {
   a.g_r_scales[((int64_t)kt * a.dst_blocks + rbp) * 64 + lane] = (uint8_t)rsc;
 }
 
+
+// Scale bytes only, for rows already in expert order (the GEMM reads their
+// codes straight from the source rows): one wave per gathered 16-row block,
+// every K tile, kGatherChunk K tiles of loads in flight before their stores.
+constexpr int kGatherChunk = 4;
+
+__global__ __launch_bounds__(256) void grouped_gather_scales_kernel(GatherArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rbp = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rbp >= a.pseg[a.E]) return;                     // wave-uniform
+  int lo = 0, hi = a.E;                               // expert: pseg[e] <= rbp < pseg[e+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.pseg[mid] <= rbp) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int r = lane & 15, c4 = lane >> 4;
+  const int64_t lr = (rbp - a.pseg[e]) * 16 + r;      // row within the expert
+  const int64_t n = a.seg[e + 1] - a.seg[e];
+  int64_t src = -1;
+  if (lr < n) {
+    const int64_t i = a.seg[e] + lr;
+    src = a.row_index ? (int64_t)a.row_index[i] : i;
+    if (src >= a.src_rows) src = -1;                  // a row index out of range reads as zero input
+  }
+  const int64_t sb = src >= 0 ? src / 16 : 0;
+  const int sl = c4 * 16 + (src >= 0 ? (int)(src % 16) : 0);
+  for (int kt0 = 0; kt0 < a.KT; kt0 += kGatherChunk) {
+    uint32_t ssc[kGatherChunk], rsc[kGatherChunk];
+#pragma unroll
+    for (int q = 0; q < kGatherChunk; ++q) {
+      const int kt = kt0 + q;
+      ssc[q] = rsc[q] = 0;
+      if (kt < a.KT && src >= 0) {
+        ssc[q] = a.s_scales[((int64_t)kt * a.src_blocks + sb) * 64 + sl];
+        rsc[q] = a.r_scales[((int64_t)kt * a.src_blocks + sb) * 64 + sl];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kGatherChunk; ++q) {
+      const int kt = kt0 + q;
+      if (kt >= a.KT) break;
+      a.g_s_scales[((int64_t)kt * a.dst_blocks + rbp) * 64 + lane] = (uint8_t)ssc[q];
+      a.g_r_scales[((int64_t)kt * a.dst_blocks + rbp) * 64 + lane] = (uint8_t)rsc[q];
+    }
+  }
+}
+
 }  // namespace
 
 size_t grouped_workspace_bytes(int64_t rows, int E, int K) { return ws_layout(rows, E, K).total; }
@@ -182,6 +232,11 @@ hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
+  // Rows already in expert order (no row index) are read by the GEMM straight
+  // from the source: each 16-row block of an expert spans at most two source
+  // blocks, so its copies stay nearly contiguous.  Routed token rows are
+  // gathered (codes too) into expert order first.
+  const bool gather_in_gemm = a.row_index == nullptr;
   GatherArgs g;
   g.s_codes = a.gemm.s_codes; g.s_scales = a.gemm.s_scales;
   g.r_codes = a.gemm.r_codes; g.r_scales = a.gemm.r_scales;
@@ -191,18 +246,29 @@ hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   g.seg = seg; g.pseg = pseg;
   g.src_rows = a.gemm.M; g.src_blocks = a.src_blocks; g.dst_blocks = L.blocks;
   g.KT = KT; g.E = E;
-  const int64_t waves = L.blocks * KT;
-  if (waves > 0) {
-    const int64_t wgs = (waves + 3) / 4;
+  if (gather_in_gemm) {
+    const int64_t wgs = (L.blocks + 3) / 4;            // one wave per gathered block (upper bound)
+    if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(grouped_gather_scales_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, g);
+  } else {
+    const int64_t wgs = (L.blocks * KT + 3) / 4;       // one wave per gathered block and K tile
     if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(grouped_gather_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, g);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
   }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
 
   GemmArgs m = a.gemm;
-  m.s_codes = g.g_s_codes; m.s_meta = nullptr; m.s_scales = g.g_s_scales;
-  m.r_codes = g.g_r_codes; m.r_scales = g.g_r_scales;
+  m.s_meta = nullptr; m.s_scales = g.g_s_scales; m.r_scales = g.g_r_scales;
+  if (gather_in_gemm) {
+    m.gather = 1;
+    m.row_index = a.row_index;
+    m.src_rows = a.gemm.M;
+    m.src_blocks = a.src_blocks;
+  } else {
+    m.gather = 0;
+    m.s_codes = g.g_s_codes; m.r_codes = g.g_r_codes;
+  }
   m.a_blocks = L.blocks;
   m.M = a.rows;
   m.seg = seg; m.pseg = pseg; m.tprefix = tprefix;

@@ -47,6 +47,13 @@ struct GemmArgs {
   const int64_t* pseg;             // [E+1] first activation 16-row block of each expert
   const int32_t* tprefix;          // [E+1] M tiles of the experts before each expert
   int E;
+  // grouped, gather != 0: the backbone and residual codes are read straight
+  // from the source activation (src_blocks 16-row blocks, src_rows rows):
+  // routed row i is source row row_index[i] (or i); the scale fields hold
+  // the scales gathered into expert order (a_blocks blocks)
+  int gather;
+  const int32_t* row_index;
+  int64_t src_rows, src_blocks;
   // NVFP4-style operands: binary32 tensor scales of S, R and W (device)
   const float* g_s;
   const float* g_r;

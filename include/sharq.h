@@ -344,8 +344,9 @@ sharq_status sharq_grouped_workspace_bytes(int64_t rows, int32_t E, int64_t K, s
  *   ws:         device workspace of ws_bytes >= sharq_grouped_workspace_bytes,
  *               owned by the caller; calls that share it must not overlap.
  * Errors: INVALID_ARG (null, shapes, K mismatch, ldy < N_e, workspace too
- * small, misaligned buffers), UNSUPPORTED (any format but MXFP4, any pattern
- * but 2:4, not gfx950), HIP. */
+ * small, misaligned buffers), WORKSPACE, UNSUPPORTED (any format but MXFP4,
+ * any pattern but 2:4, source or gathered activation codes or weight codes of
+ * 2 GiB or more, not gfx950), HIP. */
 sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
                                   const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
                                   void* y_dev, int64_t ldy, int32_t out_dtype,

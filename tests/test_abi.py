@@ -203,6 +203,10 @@ def test_grouped_rejects_before_launch(lib):
     assert call(63, 8) == _lib.ERR_INVALID_ARG                   # rows != M without a row index
     assert call(64, 8, ldy=8) == _lib.ERR_INVALID_ARG            # ldy < N_e
     assert call(64, 8, wsb=100) == _lib.ERR_WORKSPACE            # workspace too small
+    assert call(1 << 25, 8, ri=C.c_void_p(0x800000)) == _lib.ERR_UNSUPPORTED   # gathered codes past 2 GiB
+    a.M = 1 << 25
+    assert call(64, 8, ri=C.c_void_p(0x800000)) == _lib.ERR_UNSUPPORTED        # source codes past 2 GiB
+    a.M = 64
     assert call(0, 8, ri=C.c_void_p(0x800000)) == _lib.OK        # nothing routed: no launch
     a.fmt = w.fmt = 1
     assert call(64, 8) == _lib.ERR_UNSUPPORTED                   # grouped layer is MXFP4 only
