@@ -573,12 +573,14 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     }
     return;
   }
-  // A tile wholly inside Y with 16-byte-aligned rows goes out through LDS: the
-  // lanes hold 64- (fp32) or 32-byte (bf16) pieces of rows, which the memory
-  // system writes at a fraction of its line rate, so each wave stages its
-  // block in LDS (two halves of 32 rows) and writes whole 16-byte pieces in row
-  // order, consecutive lanes along a row.  The residual add and the rounding
-  // are those of store_out.
+  // Staged epilogue.  The lanes hold 64- (fp32) or 32-byte (bf16) pieces of
+  // rows, which the memory system writes at a fraction of its line rate, so
+  // each wave stages its blocks in LDS and writes whole 16-byte pieces in row
+  // order, consecutive lanes along a row.  The pieces go out as non-temporal
+  // stores: nothing here reads Y back, and keeping it out of the caches leaves
+  // them to the operand tiles (QKV-shaped GEMM 53.9 -> 52.2 us, the grouped
+  // K = 768 expert layer 138 -> 117 us).
+  //
   // The grouped layer's ring (two stages) holds one 16-row block per wave at a
   // time, and its tiles are ragged (an expert's last rows, a last N tile past
   // N_e): each wave stages its blocks one by one and skips the pieces outside
@@ -608,9 +610,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
             const v4f b = *reinterpret_cast<const v4f*>(st + r * kSt + c + 4);
             const int64_t row = row0 + r, col = col0 + c;
             if (row < y_rows && col < y_cols)
-              *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.y) + (y_row0 + row) * g.ldy + col) =
-                  make_uint4(bf16_bits_rne(a[0]) | bf16_bits_rne(a[1]) << 16, bf16_bits_rne(a[2]) | bf16_bits_rne(a[3]) << 16,
-                             bf16_bits_rne(b[0]) | bf16_bits_rne(b[1]) << 16, bf16_bits_rne(b[2]) | bf16_bits_rne(b[3]) << 16);
+              __builtin_nontemporal_store(
+                  (u32x4){bf16_bits_rne(a[0]) | bf16_bits_rne(a[1]) << 16, bf16_bits_rne(a[2]) | bf16_bits_rne(a[3]) << 16,
+                        bf16_bits_rne(b[0]) | bf16_bits_rne(b[1]) << 16, bf16_bits_rne(b[2]) | bf16_bits_rne(b[3]) << 16},
+                  reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.y) + (y_row0 + row) * g.ldy + col));
           }
         } else {
           constexpr int kPpr = C::kWNT * 4;                 // 4-element pieces per row
@@ -621,14 +624,16 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
             const v4f a = *reinterpret_cast<const v4f*>(st + r * kSt + c);
             const int64_t row = row0 + r, col = col0 + c;
             if (row < y_rows && col < y_cols)
-              *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.y) + (y_row0 + row) * g.ldy + col) =
-                  make_float4(a[0], a[1], a[2], a[3]);
+              __builtin_nontemporal_store(a, reinterpret_cast<v4f*>(reinterpret_cast<float*>(g.y) + (y_row0 + row) * g.ldy + col));
           }
         }
       }
       return;
     }
   }
+  // A single problem's tile goes out this way when it lies wholly inside Y
+  // with 16-byte-aligned rows, in two halves of 32 rows per wave; the residual
+  // add and the rounding are those of store_out.
   if constexpr (!GROUPED) {
     static_assert(C::kWMT % 2 == 0, "two halves per wave");
     constexpr int kSt = C::kWNT * 16 + 4;                 // floats per staged row (+4: banks)
@@ -668,9 +673,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
               b[2] = __uint_as_float(x.w << 16) + b[2];
               b[3] = __uint_as_float(x.w & 0xFFFF0000u) + b[3];
             }
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.y) + row * g.ldy + col) =
-                make_uint4(bf16_bits_rne(a[0]) | bf16_bits_rne(a[1]) << 16, bf16_bits_rne(a[2]) | bf16_bits_rne(a[3]) << 16,
-                           bf16_bits_rne(b[0]) | bf16_bits_rne(b[1]) << 16, bf16_bits_rne(b[2]) | bf16_bits_rne(b[3]) << 16);
+            __builtin_nontemporal_store(
+                (u32x4){bf16_bits_rne(a[0]) | bf16_bits_rne(a[1]) << 16, bf16_bits_rne(a[2]) | bf16_bits_rne(a[3]) << 16,
+                      bf16_bits_rne(b[0]) | bf16_bits_rne(b[1]) << 16, bf16_bits_rne(b[2]) | bf16_bits_rne(b[3]) << 16},
+                reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.y) + row * g.ldy + col));
           }
         } else {
           constexpr int kPpr = C::kWNT * 4;                 // 4-element pieces per row
@@ -678,8 +684,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
           for (int k = 0; k < 32 * kPpr / 64; ++k) {
             const int pc = lane + 64 * k, r = pc / kPpr, c = (pc % kPpr) * 4;
             const v4f a = *reinterpret_cast<const v4f*>(st + r * kSt + c);
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.y) + (y_row0 + row0 + r) * g.ldy + col0 + c) =
-                make_float4(a[0], a[1], a[2], a[3]);
+            __builtin_nontemporal_store(a, reinterpret_cast<v4f*>(reinterpret_cast<float*>(g.y) + (y_row0 + row0 + r) * g.ldy + col0 + c));
           }
         }
       }
