@@ -30,8 +30,9 @@ constexpr int kRowsPerBlock = 4;
 
 // ---------------------------------------------------------------------------
 // Prep kernel.  A workgroup owns 8 rows (one half of a 16-row tile block) and
-// all of K.  K is cut into units of 256 elements (two K tiles); wave w of the
-// 16 owns units w, w+16, w+32, ... and streams them through a private ring of LDS
+// all of K, or one K slice of them without RMSNorm.  K is cut into units of
+// 256 elements (two K tiles); wave w of the 16 (or of 4 or 8 for short rows)
+// owns the slice's units w, w+16, w+32, ... and streams them through a private ring of LDS
 // slots (8 rows x 512 bytes = 4 KiB each) filled by its own global -> LDS
 // copies, so no other wave ever waits for them.  The one workgroup-wide step
 // is the RMSNorm sum of squares.
@@ -69,6 +70,7 @@ constexpr uint32_t kGammaBlockF32 = 36, kGammaBlockBf16 = 40;
 
 struct PrepPlan {
   int nunits;      // units of 256 along K
+  int ups;         // units per K slice (one slice per workgroup; all units with RMSNorm)
   int units_p2;    // next power of two (RMSNorm tree width)
   int slots;       // LDS slots per wave
   int single;      // RMSNorm rows staged once (every unit of the wave resident)
@@ -76,12 +78,13 @@ struct PrepPlan {
   uint32_t off_gamma, off_sums, total;
 };
 
-static PrepPlan prep_plan(int K, bool norm, int waves) {
+static PrepPlan prep_plan(int K, bool norm, int waves, int ksplit) {
   PrepPlan p{};
   p.nunits = (K + kUnitK - 1) / kUnitK;
+  p.ups = (p.nunits + ksplit - 1) / ksplit;
   p.units_p2 = 1;
   while (p.units_p2 < p.nunits) p.units_p2 *= 2;
-  const int per_wave = (p.nunits + waves - 1) / waves;
+  const int per_wave = (p.ups + waves - 1) / waves;
   const uint32_t kp = (uint32_t)p.nunits * kUnitK;
   const uint32_t sums = norm ? (uint32_t)p.units_p2 * kPrepRows * 4 : 0;
   for (int f32 = norm ? 1 : 0; f32 >= 0; --f32) {
@@ -119,9 +122,12 @@ __global__ __launch_bounds__(W * 64) void prep_kernel(const uint16_t* __restrict
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // workgroup -> (16-row block, half); the two halves of a block are 8 blocks
-  // apart in launch order, i.e. on the same XCD, so their L2 merges the writes
-  const int64_t RB = (M + 15) / 16, nwg = RB * 2, w = blockIdx.x;
+  // workgroup -> (K slice, 16-row block, half); the two halves of a block are
+  // 8 blocks apart in launch order, i.e. on the same XCD, so their L2 merges
+  // the writes.  Slice ks holds units [ks * ups, ks * ups + ups) of K.
+  const int64_t RB = (M + 15) / 16, nwg = RB * 2, w = blockIdx.x % nwg;
+  const int ubase = (int)(blockIdx.x / nwg) * P.ups;
+  const int nunits_here = P.nunits - ubase < P.ups ? P.nunits - ubase : P.ups;
   const int64_t full = nwg / 16 * 16;
   int64_t rb, half;
   if (w < full) { rb = (w / 16) * 8 + (w % 8); half = (w % 16) / 8; }
@@ -144,14 +150,14 @@ __global__ __launch_bounds__(W * 64) void prep_kernel(const uint16_t* __restrict
 
   const uint32_t ring_off = (uint32_t)wave * P.slots * kSlotBytes;
   const uint32_t ring = lds_addr(smem) + ring_off;
-  const int nu_w = P.nunits > wave ? (P.nunits - wave + W - 1) / W : 0;
+  const int nu_w = nunits_here > wave ? (nunits_here - wave + W - 1) / W : 0;
   // streaming look-ahead: one unit per slot.  A slot is refilled as soon as
   // its block reads have returned (the copies need no registers), so all
   // slots can be in flight while a block is being decomposed.
   const int D = P.slots;
 
   auto issue = [&](int j) {
-    const int u = wave + W * j;
+    const int u = ubase + wave + W * j;
     const uint32_t slot = ring + (uint32_t)(j % P.slots) * kSlotBytes;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(W * 64) void prep_kernel(const uint16_t* __restrict
       t = t + __shfl_xor(t, 8, 64);    // blocks of a tile, in K order
       t = t + __shfl_xor(t, 16, 64);
       t = t + __shfl_xor(t, 32, 64);   // the two tiles of the unit
-      if (lane < 8) sums[(wave + W * j) * kPrepRows + lane] = t;
+      if (lane < 8) sums[(ubase + wave + W * j) * kPrepRows + lane] = t;
     };
 
     if (P.single) {
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(W * 64) void prep_kernel(const uint16_t* __restrict
     float v[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) { v[2 * i] = bf16_lo(xw[i]); v[2 * i + 1] = bf16_hi(xw[i]); }
-    const int u = wave + W * j;
+    const int u = ubase + wave + W * j;
     const int kb = (2 * u + t2) * 128 + c4 * 32;   // first element of the block
     if (NORM) {
       if (GF32) {
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(W * 64) void prep_kernel(const uint16_t* __restrict
 
   const int tl = c4 * 16 + (int)half * 8 + r8;
   auto store = [&](const Block32& b, int j) {
-    const int kt = 2 * (wave + W * j) + t2;
+    const int kt = 2 * (ubase + wave + W * j) + t2;
     if (kt < KB) {
       const int64_t tile = rb * KB + kt;
       *reinterpret_cast<uint4*>(o.r_codes + tile * 1024 + tl * 16) = b.r_codes;
@@ -364,6 +370,17 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
   }
 }
 
+// K slices per row group: rows without RMSNorm need nothing across K, so long
+// rows of a short grid are cut into up to four slices, each its own
+// workgroup, until the grid reaches 1024 workgroups (2048 x 14336: 24.8 ->
+// 23.9 us; 2048 x 4096: 11.2 -> 10.2 us).  Rows of fewer than 16 units gain
+// nothing and stay whole.
+static int prep_ksplit(int64_t nwg, int units, bool norm) {
+  if (norm || units < 16 || nwg >= 1024) return 1;
+  const int64_t want = (1024 + nwg - 1) / nwg;
+  return (int)(want < 4 ? want : 4);
+}
+
 template <bool DENSE>
 static hipError_t launch_prepare_t(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
                                    float eps, PrepOut out, hipStream_t stream) {
@@ -372,8 +389,11 @@ static hipError_t launch_prepare_t(const uint16_t* x, int64_t M, int K, int64_t 
   // the expert layers) run 4- or 8-wave workgroups: with 16 waves most would
   // have no unit, and the CU would hold only two workgroups' few busy waves.
   const int units = (K + kUnitK - 1) / kUnitK;
-  const int waves = gamma ? kPrepWaves : (units <= 4 ? 4 : (units <= 8 ? 8 : kPrepWaves));
-  const PrepPlan P = prep_plan(K, gamma != nullptr, waves);
+  const int64_t nwg = (M + 15) / 16 * 2;
+  const int ksplit = prep_ksplit(nwg, units, gamma != nullptr);
+  const int sunits = (units + ksplit - 1) / ksplit;
+  const int waves = gamma ? kPrepWaves : (sunits <= 4 ? 4 : (sunits <= 8 ? 8 : kPrepWaves));
+  const PrepPlan P = prep_plan(K, gamma != nullptr, waves, ksplit);
   if (P.slots < 1 || P.total > kPrepLdsMax) return hipErrorInvalidValue;
   auto kn = waves == 4 ? prep_kernel<4, false, false, DENSE>
             : waves == 8 ? prep_kernel<8, false, false, DENSE>
@@ -392,8 +412,9 @@ static hipError_t launch_prepare_t(const uint16_t* x, int64_t M, int K, int64_t 
     if (e != hipSuccess) return e;
     attr_set[dev][which].store(true, std::memory_order_release);
   }
-  const int64_t nwg = (M + 15) / 16 * 2;
-  hipLaunchKernelGGL(kn, dim3((unsigned)nwg), dim3(waves * 64), P.total, stream, x, M, K, ldx, gamma, eps, P, out);
+  const int64_t grid = nwg * ((units + P.ups - 1) / P.ups);
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kn, dim3((unsigned)grid), dim3(waves * 64), P.total, stream, x, M, K, ldx, gamma, eps, P, out);
   return hipGetLastError();
 }
 

@@ -79,7 +79,9 @@ def test_prep_edge_rows(K, norm):
 
 @pytest.mark.parametrize("M,K,ldx,norm", [(1, 4096, 4096, True), (3, 32768, 32768, True),
                                           (5, 16384, 16384, True), (7, 2048, 2056, True),
-                                          (9, 768, 800, False), (130, 14336, 14336, False)])
+                                          (9, 768, 800, False), (130, 14336, 14336, False),
+                                          # K slices without RMSNorm with a ragged last slice and K tail
+                                          (40, 4128, 4136, False), (17, 6176, 6176, False)])
 def test_prep_shapes(M, K, ldx, norm):
     print(f"prep shape M={M} K={K} ldx={ldx} norm={norm}", flush=True)
     rng = np.random.default_rng(M * K)
