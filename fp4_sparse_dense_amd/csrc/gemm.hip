@@ -214,14 +214,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     const int64_t i_x = blockIdx.x / 8;
     const int64_t u = (int64_t)(blockIdx.x % 8) * per + i_x;
     if (i_x >= per || u >= T) return;               // the whole workgroup: past the last unit
-    const int nt = (int)(u % tiles_n);
-    const int mtg = (int)(u / tiles_n);
-    int lo = 0, hi = g.E;                            // expert e: tprefix[e] <= mtg < tprefix[e+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (g.tprefix[mid] <= mtg) lo = mid; else hi = mid;
-    }
-    const int e = lo;
+    const int nt = (int)((uint32_t)u % (uint32_t)tiles_n);     // u < 2^31: 32-bit division
+    const int mtg = (int)((uint32_t)u / (uint32_t)tiles_n);
+    const int e = g.texp[mtg];                       // tprefix[e] <= mtg < tprefix[e+1]
     rb_first = g.pseg[e];
     rb0 = rb_first + (int64_t)(mtg - g.tprefix[e]) * C::kMB;
     rb_end = g.pseg[e + 1];

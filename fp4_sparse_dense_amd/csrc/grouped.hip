@@ -7,7 +7,7 @@
 // to (the result is identical to preparing it per expert).
 //
 // Three launches on the caller's stream:
-//   1. setup   (one workgroup): clamps the caller's segment offsets into a
+//   1. setup   (one wave): clamps the caller's segment offsets into a
 //      nondecreasing sequence in [0, rows], and tabulates, per expert, its
 //      first 16-row block in the gathered activation (segments padded to whole
 //      blocks) and the number of M tiles (grouped_tile_m() rows) before it;
@@ -32,7 +32,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
   int64_t blocks;        // 16-row blocks of the gathered activation (upper bound)
-  size_t r_codes, s_codes, s_scales, r_scales, seg, pseg, tprefix, total;
+  int64_t tiles;         // M tiles (upper bound)
+  size_t r_codes, s_codes, s_scales, r_scales, seg, pseg, tprefix, bexp, texp, total;
 };
 
 WsLayout ws_layout(int64_t rows, int E, int K) {
@@ -47,77 +48,125 @@ WsLayout ws_layout(int64_t rows, int E, int K) {
   L.seg = o;      o = align_up(o + (size_t)(E + 1) * 8);
   L.pseg = o;     o = align_up(o + (size_t)(E + 1) * 8);
   L.tprefix = o;  o = align_up(o + (size_t)(E + 1) * 4);
+  L.tiles = (rows + grouped_tile_m() - 1) / grouped_tile_m() + E;
+  L.bexp = o;     o = align_up(o + (size_t)L.blocks * 4);
+  L.texp = o;     o = align_up(o + (size_t)L.tiles * 4);
   L.total = o;
   return L;
 }
 
-// Setup, one workgroup of kSetupThreads: thread t owns offsets t, t +
-// kSetupThreads, ...  The sanitised offsets are the running maximum of the
-// clamped inputs with seg[0] = 0 and seg[E] = rows; each expert's 16-row blocks
-// and M tiles are then summed exclusively.  Scans are Hillis-Steele in LDS.
+// Setup, one workgroup: wave 0's lane l owns the kSetupPer-or-fewer consecutive entries
+// [l * per, l * per + per) of the E + 1 offsets.  The sanitised offsets are
+// the running maximum of the clamped inputs with seg[0] = 0 and seg[E] = rows
+// (every value is <= rows, so the sequence ends at rows); each expert's
+// 16-row blocks and M tiles are then summed inclusively (entry e + 1 belongs
+// to expert e).  Both scans run inside each lane's entries and then across
+// the lanes by shuffles.  The block and tile prefixes also go to LDS; after
+// one barrier every thread of the workgroup fills the block -> expert and
+// tile -> expert maps by binary search there (empty experts own nothing: the
+// search finds the last expert whose range starts at or before the entry).
+constexpr int kSetupPer = (kMaxExperts + 1 + 63) / 64;   // entries per lane at most
 constexpr int kSetupThreads = 1024;
-constexpr int kSetupPer = (kMaxExperts + 1 + kSetupThreads - 1) / kSetupThreads;   // entries per thread
 
-__global__ __launch_bounds__(kSetupThreads) void grouped_setup_kernel(const int64_t* __restrict__ seg_in, int E,
-                                                                      int64_t rows, int tile_m,
-                                                                      int64_t* __restrict__ seg,
-                                                                      int64_t* __restrict__ pseg,
-                                                                      int32_t* __restrict__ tprefix) {
-  __shared__ int64_t a[kMaxExperts + 1], b[kMaxExperts + 1];
-  const int t = threadIdx.x;
+__device__ __forceinline__ int64_t shfl_up64(int64_t v, int d) {
+  const int lo = __shfl_up((int)(uint32_t)v, d, 64), hi = __shfl_up((int)(v >> 32), d, 64);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__global__ __launch_bounds__(kSetupThreads) void grouped_setup_kernel(const int64_t* __restrict__ seg_in, int E, int64_t rows,
+                                                           int tile_shift, int64_t* __restrict__ seg,
+                                                           int64_t* __restrict__ pseg, int32_t* __restrict__ tprefix,
+                                                           int32_t* __restrict__ bexp, int32_t* __restrict__ texp) {
+  __shared__ int64_t lb[kMaxExperts + 1];
+  __shared__ int32_t lt[kMaxExperts + 1];
+  const int lane = threadIdx.x & 63;
   const int n = E + 1;
-  for (int e = t; e < n; e += kSetupThreads) {
-    const int64_t v = seg_in[e];
-    a[e] = e == 0 ? 0 : (e == E ? rows : (v < 0 ? 0 : (v > rows ? rows : v)));
+  if (threadIdx.x < 64) {   // wave 0: the scans
+    const int per = (n + 63) / 64;
+    const int e0 = lane * per;
+    // clamped offsets, running maximum inside the lane (entries past n carry
+    // it); every load is issued before the first is used (in-range indices)
+    int64_t a[kSetupPer];
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) a[k] = seg_in[e0 + k < n ? e0 + k : n - 1];
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) {
+      const int e = e0 + k;
+      int64_t v = 0;
+      if (k < per && e < n) {
+        v = e == 0 ? 0 : (e == E ? rows : a[k]);
+        v = v < 0 ? 0 : (v > rows ? rows : v);
+      }
+      a[k] = k > 0 && a[k - 1] > v ? a[k - 1] : v;
+    }
+    // exclusive running maximum of the lanes before this one
+    int64_t m = a[kSetupPer - 1];
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+      const int64_t y = shfl_up64(m, d);
+      if (lane >= d && y > m) m = y;
+    }
+    int64_t before = shfl_up64(m, 1);
+    if (lane == 0) before = 0;
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) a[k] = a[k] > before ? a[k] : before;
+    // per entry e >= 1 (expert e - 1): blocks and tiles of its length
+    int64_t prev = before;   // the offset before this lane's first entry
+    int64_t nb[kSetupPer], nt[kSetupPer];
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) {
+      const int e = e0 + k;
+      const int64_t len = (k < per && e < n && e > 0) ? a[k] - prev : 0;
+      prev = a[k];
+      nb[k] = (len + 15) / 16 + (k > 0 ? nb[k - 1] : 0);
+      nt[k] = ((len + (1 << tile_shift) - 1) >> tile_shift) + (k > 0 ? nt[k - 1] : 0);   // M tiles of 2^shift rows
+    }
+    // exclusive sums of the lanes before this one
+    int64_t sb = nb[kSetupPer - 1], st = nt[kSetupPer - 1];
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+      const int64_t yb = shfl_up64(sb, d), yt = shfl_up64(st, d);
+      if (lane >= d) { sb += yb; st += yt; }
+    }
+    int64_t bb = shfl_up64(sb, 1), bt = shfl_up64(st, 1);
+    if (lane == 0) bb = bt = 0;
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) {
+      const int e = e0 + k;
+      if (k < per && e < n) {
+        seg[e] = a[k];
+        pseg[e] = bb + nb[k];
+        tprefix[e] = (int32_t)(bt + nt[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kSetupPer; ++k) {
+      const int e = e0 + k;
+      if (k < per && e < n) {
+        lb[e] = bb + nb[k];
+        lt[e] = (int32_t)(bt + nt[k]);
+      }
+    }
   }
   __syncthreads();
-  // inclusive running maximum: nondecreasing, ends at rows (every value <= rows)
-  for (int d = 1; d < n; d *= 2) {
-    int64_t tmp[kSetupPer];
-#pragma unroll
-    for (int k = 0; k < kSetupPer; ++k) {
-      const int e = t + k * kSetupThreads;
-      tmp[k] = e < n ? (e >= d && a[e - d] > a[e] ? a[e - d] : a[e]) : 0;
+  // the expert of every gathered 16-row block and of every M tile, so that the
+  // gather and the GEMM find theirs with one load instead of a search
+  const int64_t nblk = lb[E], ntil = lt[E];
+  for (int64_t b = threadIdx.x; b < nblk; b += kSetupThreads) {
+    int lo = 0, hi = E;                               // lb[lo] <= b < lb[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (lb[mid] <= b) lo = mid; else hi = mid;
     }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kSetupPer; ++k) {
-      const int e = t + k * kSetupThreads;
-      if (e < n) a[e] = tmp[k];
-    }
-    __syncthreads();
+    bexp[b] = lo;
   }
-  // per expert e (entry e + 1): blocks in the low 32 bits, tiles in the high 32
-  for (int e = t; e < n; e += kSetupThreads) {
-    seg[e] = a[e];
-    int64_t c = 0;
-    if (e > 0) {
-      const int64_t len = a[e] - a[e - 1];
-      c = ((len + 15) / 16) | (((len + tile_m - 1) / tile_m) << 32);
+  for (int64_t t = threadIdx.x; t < ntil; t += kSetupThreads) {
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (lt[mid] <= t) lo = mid; else hi = mid;
     }
-    b[e] = c;
-  }
-  __syncthreads();
-  // inclusive sums of the packed pairs (no carry across halves: each half stays
-  // below 2^32 -- blocks <= (rows + 15 E) / 16 and tiles <= blocks)
-  for (int d = 1; d < n; d *= 2) {
-    int64_t tmp[kSetupPer];
-#pragma unroll
-    for (int k = 0; k < kSetupPer; ++k) {
-      const int e = t + k * kSetupThreads;
-      tmp[k] = e < n ? (e >= d ? b[e - d] + b[e] : b[e]) : 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kSetupPer; ++k) {
-      const int e = t + k * kSetupThreads;
-      if (e < n) b[e] = tmp[k];
-    }
-    __syncthreads();
-  }
-  for (int e = t; e < n; e += kSetupThreads) {
-    pseg[e] = b[e] & 0xFFFFFFFFll;
-    tprefix[e] = (int32_t)(b[e] >> 32);
+    texp[t] = lo;
   }
 }
 
@@ -126,22 +175,19 @@ struct GatherArgs {
   uint8_t *g_s_codes, *g_s_scales, *g_r_codes, *g_r_scales;
   const int32_t* row_index;
   const int64_t *seg, *pseg;
+  const int32_t* bexp;
   int64_t src_rows, src_blocks, dst_blocks;
   int KT, E;
 };
 
 __global__ __launch_bounds__(256) void grouped_gather_kernel(GatherArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t rbp = w / a.KT;
-  const int kt = (int)(w % a.KT);
+  // blocks x K tiles < 2^21 (the GEMM's 31-bit offsets): 32-bit division
+  const uint32_t w = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const int64_t rbp = w / (uint32_t)a.KT;
+  const int kt = (int)(w % (uint32_t)a.KT);
   if (rbp >= a.pseg[a.E]) return;                     // wave-uniform
-  int lo = 0, hi = a.E;                               // expert: pseg[e] <= rbp < pseg[e+1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.pseg[mid] <= rbp) lo = mid; else hi = mid;
-  }
-  const int e = lo;
+  const int e = a.bexp[rbp];                          // pseg[e] <= rbp < pseg[e+1]
   const int r = lane & 15, c4 = lane >> 4;
   const int64_t lr = (rbp - a.pseg[e]) * 16 + r;      // row within the expert
   const int64_t n = a.seg[e + 1] - a.seg[e];
@@ -176,12 +222,7 @@ __global__ __launch_bounds__(256) void grouped_gather_scales_kernel(GatherArgs a
   const int lane = threadIdx.x & 63;
   const int64_t rbp = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rbp >= a.pseg[a.E]) return;                     // wave-uniform
-  int lo = 0, hi = a.E;                               // expert: pseg[e] <= rbp < pseg[e+1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.pseg[mid] <= rbp) lo = mid; else hi = mid;
-  }
-  const int e = lo;
+  const int e = a.bexp[rbp];                          // pseg[e] <= rbp < pseg[e+1]
   const int r = lane & 15, c4 = lane >> 4;
   const int64_t lr = (rbp - a.pseg[e]) * 16 + r;      // row within the expert
   const int64_t n = a.seg[e + 1] - a.seg[e];
@@ -226,9 +267,16 @@ hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   int64_t* seg = reinterpret_cast<int64_t*>(a.ws + L.seg);
   int64_t* pseg = reinterpret_cast<int64_t*>(a.ws + L.pseg);
   int32_t* tprefix = reinterpret_cast<int32_t*>(a.ws + L.tprefix);
+  int32_t* bexp = reinterpret_cast<int32_t*>(a.ws + L.bexp);
+  int32_t* texp = reinterpret_cast<int32_t*>(a.ws + L.texp);
 
+  // M tiles are a power of two of rows: the kernel shifts (a 64-bit division
+  // by a runtime value is a long software sequence per entry)
+  int tile_shift = 0;
+  while ((1 << tile_shift) < grouped_tile_m()) ++tile_shift;
+  if ((1 << tile_shift) != grouped_tile_m()) return hipErrorInvalidValue;
   hipLaunchKernelGGL(grouped_setup_kernel, dim3(1), dim3(kSetupThreads), 0, stream, a.seg_in, E, a.rows,
-                     grouped_tile_m(), seg, pseg, tprefix);
+                     tile_shift, seg, pseg, tprefix, bexp, texp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -243,7 +291,7 @@ hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   g.g_r_codes = a.ws + L.r_codes; g.g_s_codes = a.ws + L.s_codes;
   g.g_s_scales = a.ws + L.s_scales; g.g_r_scales = a.ws + L.r_scales;
   g.row_index = a.row_index;
-  g.seg = seg; g.pseg = pseg;
+  g.seg = seg; g.pseg = pseg; g.bexp = bexp;
   g.src_rows = a.gemm.M; g.src_blocks = a.src_blocks; g.dst_blocks = L.blocks;
   g.KT = KT; g.E = E;
   if (gather_in_gemm) {
@@ -271,9 +319,8 @@ hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   }
   m.a_blocks = L.blocks;
   m.M = a.rows;
-  m.seg = seg; m.pseg = pseg; m.tprefix = tprefix;
-  const int64_t max_mtiles = (a.rows + grouped_tile_m() - 1) / grouped_tile_m() + E;
-  return launch_linear_grouped_gemm(m, max_mtiles, stream);
+  m.seg = seg; m.pseg = pseg; m.tprefix = tprefix; m.texp = texp;
+  return launch_linear_grouped_gemm(m, L.tiles, stream);
 }
 
 }  // namespace sharq

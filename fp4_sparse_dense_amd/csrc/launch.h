@@ -46,6 +46,7 @@ struct GemmArgs {
   const int64_t* seg;              // [E+1] first output row of each expert (sanitised)
   const int64_t* pseg;             // [E+1] first activation 16-row block of each expert
   const int32_t* tprefix;          // [E+1] M tiles of the experts before each expert
+  const int32_t* texp;             // [M tiles] expert of each M tile
   int E;
   // grouped, gather != 0: the backbone and residual codes are read straight
   // from the source activation (src_blocks 16-row blocks, src_rows rows):

@@ -125,8 +125,9 @@ __global__ __launch_bounds__(W * 64) void prep_kernel(const uint16_t* __restrict
   // workgroup -> (K slice, 16-row block, half); the two halves of a block are
   // 8 blocks apart in launch order, i.e. on the same XCD, so their L2 merges
   // the writes.  Slice ks holds units [ks * ups, ks * ups + ups) of K.
-  const int64_t RB = (M + 15) / 16, nwg = RB * 2, w = blockIdx.x % nwg;
-  const int ubase = (int)(blockIdx.x / nwg) * P.ups;
+  const int64_t RB = (M + 15) / 16, nwg = RB * 2;
+  const int64_t w = blockIdx.x % (uint32_t)nwg;                  // the grid is < 2^31: 32-bit division
+  const int ubase = (int)(blockIdx.x / (uint32_t)nwg) * P.ups;
   const int nunits_here = P.nunits - ubase < P.ups ? P.nunits - ubase : P.ups;
   const int64_t full = nwg / 16 * 16;
   int64_t rb, half;

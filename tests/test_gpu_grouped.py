@@ -40,13 +40,13 @@ def _reference(ref_act, src_rows, seg, w_stack, experts):
     return y, b
 
 
-def _run(x, w_stack, experts, seg, row_index):
+def _run(x, w_stack, experts, seg, row_index, rows=None):
     import torch
     act = sq.sharq_prepare(dev_bf16(x), None)
     wt = sq.sharq_pack_weight(dev_bf16(w_stack))
     seg_d = _dev(seg, torch.int64)
     ri = None if row_index is None else _dev(row_index.astype(np.int32), torch.int32)
-    y = sq.sharq_linear_grouped(act, wt, seg_d, experts, row_index=ri, rows=int(seg[-1]))
+    y = sq.sharq_linear_grouped(act, wt, seg_d, experts, row_index=ri, rows=int(seg[-1]) if rows is None else rows)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -131,3 +131,31 @@ def test_grouped_ragged_tiles_bf16_and_strided_outputs():
         want = y32 if code == sq.OUT_F32 else y16
         assert torch.equal(big[:, :n_e].contiguous(), want), (pad, code)
         assert torch.all(big[:, n_e:] == 3.0), (pad, code)
+
+
+def test_grouped_malformed_offsets_are_clamped():
+    """Segment offsets outside the contract (seg[0] != 0, decreasing, negative,
+    past rows, seg[E] != rows, more experts than a wave has lanes) act as their
+    sanitised form: clamped into [0, rows], seg[0] = 0, seg[E] = rows, then the
+    running maximum.  The output equals the oracle's over those segments."""
+    print("grouped malformed offsets", flush=True)
+    rng = np.random.default_rng(31)
+    experts, d_model, n_e = 70, 128, 16
+    rows = 300
+    seg = np.sort(rng.integers(0, rows, experts + 1)).astype(np.int64)
+    seg[5] = seg[4] - 30          # decreasing
+    seg[9] = -7                   # negative
+    seg[40] = rows + 25           # past rows (clamps to rows: the experts after it are empty ...)
+    seg[41:60] = seg[41:60] - rows  # ... whatever follows it below
+    seg[0], seg[-1] = 17, rows - 40
+    clean = np.clip(seg, 0, rows)
+    clean[0], clean[-1] = 0, rows
+    clean = np.maximum.accumulate(clean)
+    x = synth.outlier_activations(rng, rows, d_model)
+    w = np.concatenate([synth.linear_weight(rng, n_e, d_model) for _ in range(experts)])
+    yg = _run(x, w, experts, seg, None, rows=rows)
+    yc = _run(x, w, experts, clean, None, rows=rows)
+    assert np.array_equal(yg, yc)
+    ref = O.prepare(x, None)
+    yr, b = _reference(ref, np.arange(rows), clean, w, experts)
+    assert_linear_close(yg, yr, b, "malformed offsets")
