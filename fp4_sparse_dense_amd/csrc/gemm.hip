@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     // together, sharing its weight.  (Dealt in plain order, N tile j of every M
     // tile went to one XCD and each XCD read the whole activation.)  The grid
     // is a multiple of 8 holding at least T units; the rest return.
-    const int64_t NBe = NB / g.E;
+    const int64_t NBe = (uint32_t)NB / (uint32_t)g.E;            // 32-bit division (NB < 2^31)
     const int tiles_n = (int)((NBe + C::kNB - 1) / C::kNB);
     const int64_t T = (int64_t)g.tprefix[g.E] * tiles_n;
     const int64_t per = (T + 7) / 8;
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     nb_end = nb_first + NBe;
     y_row0 = g.seg[e];
     y_rows = g.seg[e + 1] - g.seg[e];
-    y_cols = g.N / g.E;
+    y_cols = NBe * 16;                              // N_e (a multiple of 16)
   }
 
   const int64_t RBc = GROUPED && g.gather ? g.src_blocks : RB;   // blocks of the code buffers

@@ -152,70 +152,85 @@ __device__ __forceinline__ Keep24 keep24(float a0, float a1, float a2, float a3)
 // One lane's 32 elements (two 16-element blocks) of v: the 2:4 mask, the
 // E4M3 block scales and the kept codes of the backbone (tensor scale g_s); v
 // is replaced by the residual r = v - deq(Q(S)).
+// One 16-element block v[0..16) of the backbone: its E4M3 scale byte, the 8
+// kept codes (first kept element of group g in bits 8g..8g+3, second in
+// 8g+4..8g+7), the 4 groups' metadata nibbles (bits 4g..4g+3); v becomes the
+// residual.
+__device__ __forceinline__ void nv_backbone_block(float* v, float g_s, uint32_t& scode, uint32_t& meta16,
+                                                  uint32_t& sbyte) {
+  const float six_g = 6.0f * g_s;
+  float bm = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[i]));
+  const float s = e4m3_round(bm / six_g, sbyte);
+  const float tq = s * g_s;
+  scode = 0u;
+  meta16 = 0u;
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    float& a0 = v[4 * gq];
+    float& a1 = v[4 * gq + 1];
+    float& a2 = v[4 * gq + 2];
+    float& a3 = v[4 * gq + 3];
+    const Keep24 k = keep24(a0, a1, a2, a3);
+    meta16 |= k.nib << (4 * gq);
+    const float x0 = k.k0 ? a0 : (k.f1 ? a1 : a2);
+    const float x1 = k.k3 ? a3 : (k.s2 ? a2 : a1);
+    const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
+    const uint32_t c = e2m1_pair(q0, q1);
+    scode |= c << (8 * gq);
+    float d0, d1;
+    fp4_unpack2<0>(c, d0, d1);
+    d0 = (d0 * s) * g_s;
+    d1 = (d1 * s) * g_s;
+    const float r0 = x0 - d0, r1 = x1 - d1;
+    a0 = k.k0 ? r0 : a0;
+    a1 = k.f1 ? r0 : (k.s1 ? r1 : a1);
+    a2 = k.f2 ? r0 : (k.s2 ? r1 : a2);
+    a3 = k.k3 ? r1 : a3;
+  }
+}
+
+// The backbone of a 32-element chunk: its two 16-element blocks.
 __device__ __forceinline__ void nv_backbone(float (&v)[32], float g_s, uint32_t (&scodes)[2], uint32_t& meta,
                                             uint32_t& sbytes) {
-  const float six_g = 6.0f * g_s;
-  scodes[0] = scodes[1] = 0u;
   meta = 0u;
   sbytes = 0u;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    float bm = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[16 * b + i]));
-    uint32_t byte;
-    const float s = e4m3_round(bm / six_g, byte);
+    uint32_t m16, byte;
+    nv_backbone_block(v + 16 * b, g_s, scodes[b], m16, byte);
+    meta |= m16 << (16 * b);
     sbytes |= byte << (8 * b);
-    const float tq = s * g_s;
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int G = 4 * b + gq;
-      float& a0 = v[4 * G];
-      float& a1 = v[4 * G + 1];
-      float& a2 = v[4 * G + 2];
-      float& a3 = v[4 * G + 3];
-      const Keep24 k = keep24(a0, a1, a2, a3);
-      meta |= k.nib << (4 * G);
-      const float x0 = k.k0 ? a0 : (k.f1 ? a1 : a2);
-      const float x1 = k.k3 ? a3 : (k.s2 ? a2 : a1);
-      const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
-      const uint32_t c = e2m1_pair(q0, q1);
-      scodes[b] |= c << (8 * gq);
-      float d0, d1;
-      fp4_unpack2<0>(c, d0, d1);
-      d0 = (d0 * s) * g_s;
-      d1 = (d1 * s) * g_s;
-      const float r0 = x0 - d0, r1 = x1 - d1;
-      a0 = k.k0 ? r0 : a0;
-      a1 = k.f1 ? r0 : (k.s1 ? r1 : a1);
-      a2 = k.f2 ? r0 : (k.s2 ? r1 : a2);
-      a3 = k.k3 ? r1 : a3;
-    }
   }
 }
 
-// The residual codes and E4M3 block scales of one lane's 32 elements
-// (tensor scale g_r).
-__device__ __forceinline__ void nv_residual(const float (&v)[32], float g_r, uint32_t (&rc)[4], uint32_t& rbytes) {
+// One 16-element block of the residual: its E4M3 scale byte and 16 codes
+// (element i in bits 4(i % 8).. of word i / 8).
+__device__ __forceinline__ void nv_residual_block(const float* v, float g_r, uint32_t (&rc)[2], uint32_t& rbyte) {
   const float six_r = 6.0f * g_r;
-  rc[0] = rc[1] = rc[2] = rc[3] = 0u;
+  float bm = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[i]));
+  const float s = e4m3_round(bm / six_r, rbyte);
+  const float tq = s * g_r;
+  rc[0] = rc[1] = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const float q0 = nv_quot(v[i], tq, s), q1 = nv_quot(v[i + 1], tq, s);
+    rc[i / 8] |= e2m1_pair(q0, q1) << (4 * (i % 8));
+  }
+}
+
+__device__ __forceinline__ void nv_residual(const float (&v)[32], float g_r, uint32_t (&rc)[4], uint32_t& rbytes) {
   rbytes = 0u;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    float bm = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[16 * b + i]));
-    uint32_t byte;
-    const float s = e4m3_round(bm / six_r, byte);
+    uint32_t w[2], byte;
+    nv_residual_block(v + 16 * b, g_r, w, byte);
+    rc[2 * b] = w[0];
+    rc[2 * b + 1] = w[1];
     rbytes |= byte << (8 * b);
-    const float tq = s * g_r;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float x0 = v[16 * b + i], x1 = v[16 * b + i + 1];
-      const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
-      const int e = 16 * b + i;                 // element index; 8 per dword
-      rc[e / 8] |= e2m1_pair(q0, q1) << (4 * (e % 8));
-    }
   }
 }
 
