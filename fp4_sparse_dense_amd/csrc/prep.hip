@@ -58,7 +58,6 @@ constexpr int kRowsPerBlock = 4;
 // ---------------------------------------------------------------------------
 constexpr int kPrepRows = 8;
 constexpr int kPrepWaves = 16;
-constexpr int kPrepThreads = kPrepWaves * 64;
 constexpr int kUnitK = 256;
 constexpr int kSlotBytes = kPrepRows * kUnitK * 2;
 constexpr uint32_t kPrepLdsMax = 160 * 1024;
