@@ -159,3 +159,44 @@ def test_grouped_malformed_offsets_are_clamped():
     ref = O.prepare(x, None)
     yr, b = _reference(ref, np.arange(rows), clean, w, experts)
     assert_linear_close(yg, yr, b, "malformed offsets")
+
+
+def test_grouped_full_size_sampled():
+    """The Qwen3-30B-A3B-shaped expert layer at full size (4096 tokens, top-8 of
+    128 experts with Zipf(1.1) loads; gate/up K = 2048, N_e = 1536 over routed
+    token rows, down K = 768, N_e = 2048 over expert-sorted rows), the launch
+    configuration the benchmark times; the oracle recomputes sampled routed
+    rows (the largest and smallest experts, segment edges, random ones) at
+    sampled columns from each row's expert weight."""
+    import torch
+    print("grouped full size sampled", flush=True)
+    inp = synth.moe_inputs(seed=4)
+    E, seg, token = 128, inp["seg"], inp["token"]
+    rows = int(seg[-1])
+    sizes = np.diff(seg)
+    rng = np.random.default_rng(5)
+    big, small = int(np.argmax(sizes)), int(np.argmin(np.where(sizes > 0, sizes, 1 << 30)))
+    pick = [seg[big], seg[big + 1] - 1, seg[small], seg[small + 1] - 1, 0, rows - 1]
+    pick += list(rng.choice(rows, 18, replace=False))
+    pick = np.unique(np.array(pick, dtype=np.int64))
+    expert_of = np.searchsorted(seg, pick, side="right") - 1
+    seg_d = _dev(seg, torch.int64)
+    for name, x, w, src in (("gate/up", inp["x_tok"], inp["w_gu"], token.astype(np.int64)),
+                            ("down", inp["x_down"], inp["w_d"], np.arange(rows))):
+        ne = w.shape[1]
+        act = sq.sharq_prepare(dev_bf16(x), None)
+        wt = sq.sharq_pack_weight(dev_bf16(w.reshape(E * ne, -1)))
+        ri = _dev(token.astype(np.int32), torch.int32) if name == "gate/up" else None
+        y = sq.sharq_linear_grouped(act, wt, seg_d, E, row_index=ri, rows=rows)
+        torch.cuda.synchronize()
+        cols = np.unique(np.concatenate([np.arange(16), np.arange(ne - 16, ne), rng.choice(ne, 96, replace=False)]))
+        got = y.cpu().numpy()[np.ix_(pick, cols)]
+        ref = O.prepare(x[src[pick]], None)
+        yr = np.zeros_like(got, dtype=np.float64)
+        b = np.zeros_like(yr)
+        for j, e in enumerate(expert_of):
+            wc, ws = O.pack_weight(w[e][cols])
+            yj, bj = O.linear(ref, wc, ws, rows=np.array([j]))
+            yr[j], b[j] = yj[0], bj[0]
+        assert_linear_close(got, yr, b, f"full-size {name}")
+        del act, wt, y
