@@ -48,9 +48,9 @@ def test_linear_ragged_full(M, K, N, norm):
     assert_linear_close(y.cpu().numpy(), yr, b, f"M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("name", ["decode8", "decode32"])
+@pytest.mark.parametrize("name", ["decode1", "decode8", "decode32", "decode64"])
 def test_linear_decode_full(name):
-    """Decode shapes (M in {8, 32}, K = N = 4096): every output against the oracle."""
+    """Decode shapes (M in {1, 8, 32, 64}, K = N = 4096): every output against the oracle."""
     print(f"linear {name}", flush=True)
     inp = synth.layer_inputs(name, seed=0)
     act, wt, y = gpu_layer(inp["x"], inp["gamma"], inp["w"])
