@@ -230,7 +230,7 @@ def main():
                     help="also run a 256 MiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     if args.fmt == "nvfp4" and args.workload != "decode":

@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
   SHARQ_OK = 0,
   SHARQ_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad enum */
-  SHARQ_ERR_UNSUPPORTED = 2, /* valid request this build does not run (e.g. HiF4, N:M != 2:4, not gfx950) */
+  SHARQ_ERR_UNSUPPORTED = 2, /* valid request the library does not run (e.g. HiF4, N:M != 2:4, not gfx950) */
   SHARQ_ERR_WORKSPACE = 3,   /* workspace missing or too small */
   SHARQ_ERR_HIP = 4          /* a HIP runtime call or launch failed; detail in sharq_last_error() */
 } sharq_status;
