@@ -183,8 +183,10 @@ def test_grouped_rejects_before_launch(lib):
     assert lib.sharq_grouped_workspace_bytes(100, 1025, 256, C.byref(n)) == _lib.ERR_INVALID_ARG
     assert lib.sharq_grouped_workspace_bytes(100, 8, 250, C.byref(n)) == _lib.ERR_INVALID_ARG
     assert lib.sharq_grouped_workspace_bytes(100, 8, 256, C.byref(n)) == _lib.OK
-    # gathered rows of 8 experts padded to 16-row blocks: (100 + 8*15 + 15) // 16 blocks x 2 K tiles x 2176 B
-    assert n.value >= (100 + 8 * 15 + 15) // 16 * 2 * 2176
+    # gathered rows of 8 experts padded to 16-row blocks: (100 + 8*15 + 15) // 16 blocks x 2 K tiles x 2176 B,
+    # plus the segment tables and the block -> expert and tile -> expert maps (4 B per block and M tile)
+    blocks, tiles = (100 + 8 * 15 + 15) // 16, (100 + 127) // 128 + 8
+    assert n.value >= blocks * 2 * 2176 + 9 * (8 + 8 + 4) + 4 * (blocks + tiles)
     a = _act()
     a.layout_version = _lib.SHARQ_ABI_VERSION
     a.M, a.K, a.n, a.m = 64, 256, 2, 4
