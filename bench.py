@@ -25,7 +25,13 @@ an earlier one.
 Prints one JSON line.  value = layer TFLOP/s = 4*M*N*K (2*M*N*K per path) /
 (wall time per step); prep GB/s and the GEMM's fractions are reported beside
 it; ``roofline`` describes the dominant kernel (the dual GEMM), timed with HIP
-events on the stream it is launched on.
+events on the stream it is launched on.  Bytes are the method's algorithmic
+bytes (a compressed 2:4 backbone: 2.9375 B per activation element through the
+prep, 0.9375 B read by the GEMM); the layout's own bytes (the backbone stored
+masked dense) are reported beside them.  The GEMM's fraction is given on the
+metric's 4*M*N*K and on the method's useful 3*M*N*K, against the published
+peaks and against the peaks measured on the same device in the same run
+(``measured_peaks``; ``--no-peaks`` skips that).
 """
 from __future__ import annotations
 
@@ -62,27 +68,61 @@ GEMM_SRC = [os.path.join(ROOT, "fp4_sparse_dense_amd", "csrc", f)
 
 
 def prep_bytes(M, K, norm=True, nv=False, dense=False):
-    """Algorithmic HBM bytes of one prep: bf16 X in once; out 1.1875 B/elem
-    (backbone and residual codes 0.5 each -- the backbone is a masked dense
-    operand -- metadata 0.125, scales 1/32 each; NVFP4-style: scales 1/16 each,
-    1.25 B/elem; plain FP4: 0.53125), gamma once."""
+    """Algorithmic HBM bytes of one prep, as the method counts them: bf16 X in
+    once, gamma once, and out per activation element the compressed 2:4
+    backbone (K/2 kept codes: 0.25 B), its metadata (0.125 B), the residual's
+    codes (0.5 B) and both block-scale arrays (1/32 B each for MXFP4, 1/16 B
+    each for the NVFP4-style format): 2.9375 B per element in all for MXFP4
+    (3.0 for NVFP4-style).  Plain FP4 (no backbone): 2 + 0.53125 B."""
+    if dense:
+        out = M * K * 17 // 32
+    else:
+        out = M * K * 15 // 16 if not nv else M * K
+    return M * K * 2 + out + (2 * K if norm else 0)
+
+
+def prep_layout_bytes(M, K, norm=True, nv=False, dense=False):
+    """Bytes the preparation actually moves in this library's layout: the
+    backbone is stored masked dense (0.5 B per element instead of 0.25, gfx950
+    has no sparse FP4 MFMA to consume a compressed one), so MXFP4 writes
+    1.1875 B per element (NVFP4-style 1.25; plain FP4 0.53125)."""
     out = M * K * 5 // 4 if nv else (M * K * 17 // 32 if dense else M * K * 19 // 16)
     return M * K * 2 + out + (2 * K if norm else 0)
 
 
 def gemm_flops(M, N, K):
+    """The metric's count: 2*M*N*K per path, 4*M*N*K for the dual GEMM."""
     return 4 * M * N * K
 
 
+def gemm_useful_flops(M, N, K):
+    """The method's own work: the backbone keeps K/2 of every row, so the sparse
+    path is M*N*K and the dense path 2*M*N*K.  gfx950 has no sparse FP4 MFMA,
+    so 4*M*N*K execute and 0.75 of the MFMA peak is this count's ceiling."""
+    return 3 * M * N * K
+
+
 def gemm_bytes(M, N, K, out_bytes=4, nv=False, dense=False):
-    """Algorithmic HBM bytes of one dual GEMM: the prepared A it reads (backbone
-    and residual codes and scales, MXFP4 1.0625 B/elem; NVFP4-style 1.125 B/elem,
-    scales per 16; the metadata is not read), the packed weight read once for
-    both paths (MXFP4 0.53125 B/elem; NVFP4-style 0.5625), Y."""
-    if nv:
-        return M * K * 9 // 8 + N * K * 9 // 16 + out_bytes * M * N
+    """Algorithmic HBM bytes of one dual GEMM: the prepared A with a compressed
+    backbone (0.9375 B per element: backbone codes 0.25, metadata 0.125, residual
+    codes 0.5, scales 1/32 each; NVFP4-style 1.0), the packed weight read once
+    for both paths (MXFP4 0.53125 B/elem; NVFP4-style 0.5625), Y.  Plain FP4:
+    0.53125 B/elem on both sides."""
     if dense:
         return M * K * 17 // 32 + N * K * 17 // 32 + out_bytes * M * N
+    if nv:
+        return M * K + N * K * 9 // 16 + out_bytes * M * N
+    return M * K * 15 // 16 + N * K * 17 // 32 + out_bytes * M * N
+
+
+def gemm_layout_bytes(M, N, K, out_bytes=4, nv=False, dense=False):
+    """Bytes the GEMM actually reads in this library's layout: the masked dense
+    backbone (0.5 B per element) and no metadata, so 1.0625 B per activation
+    element for MXFP4 (NVFP4-style 1.125)."""
+    if dense:
+        return gemm_bytes(M, N, K, out_bytes, dense=True)
+    if nv:
+        return M * K * 9 // 8 + N * K * 9 // 16 + out_bytes * M * N
     return M * K * 17 // 16 + N * K * 17 // 32 + out_bytes * M * N
 
 
@@ -112,33 +152,103 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(rows: int = 2048, min_s: float = 10.0):
-    """The oracle as it stands, on a bounded sample of the same workload."""
+def cpu_threads():
+    """(nproc, affinity count, threads used by the all-core legs)."""
+    nproc = os.cpu_count() or 1
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - not Linux
+        aff = nproc
+    return nproc, aff, max(1, min(aff, 16))
+
+
+def cpu_baseline(prep_rows: int = 128, gemm_rows: int = 512, min_s: float = 3.0):
+    """The oracle as it stands, on bounded samples of the QKV workload, in
+    three legs: the preparation single-threaded, the preparation on all
+    allowed cores (row blocks on a thread pool: numpy releases the GIL inside
+    its array operations, and the preparation is row-local), and the float64
+    dual GEMM with the BLAS library's threads.  Each leg repeats whole passes
+    until min_s of wall time."""
+    import concurrent.futures as cf
+
     import numpy as np
     from fp4_sparse_dense_amd import synth
     from oracle import sharq_oracle as O
     try:
         from threadpoolctl import threadpool_info
-        cores = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
+        blas = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
     except Exception:  # noqa: BLE001
-        cores = 1
+        blas = 1
+    nproc, aff, threads = cpu_threads()
     inp = synth.layer_inputs("qkv", seed=0)
+    M, K, N = inp["M"], inp["K"], inp["N"]
     wc, ws = O.pack_weight(inp["w"])            # offline step, not timed
-    x = inp["x"][:rows]
-    # whole passes until at least min_s of CPU work (one pass of the full
-    # workload is shorter than that on a many-core host)
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        act = O.prepare(x, inp["gamma"], inp["eps"])
-        O.linear(act, wc, ws)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_s:
-            break
-    flops = gemm_flops(rows, inp["N"], inp["K"]) * passes
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{passes} pass(es) over {rows} of {inp['M']} token rows of the QKV workload: prep + "
-                      f"float64 dual GEMM over all {inp['N']} outputs ({dt:.1f} s)"}
+
+    def loop(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_s:
+                return n, dt
+
+    x1 = inp["x"][:prep_rows]
+    n1, t1 = loop(lambda: O.prepare(x1, inp["gamma"], inp["eps"]))
+    prep1 = prep_bytes(prep_rows, K) * n1 / t1 / 1e9
+    xa = inp["x"][:prep_rows * threads]
+    chunks = np.array_split(xa, threads)
+    with cf.ThreadPoolExecutor(threads) as ex:
+        na, ta = loop(lambda: list(ex.map(lambda c: O.prepare(c, inp["gamma"], inp["eps"]), chunks)))
+    prep_all = prep_bytes(xa.shape[0], K) * na / ta / 1e9
+    act = O.prepare(inp["x"][:gemm_rows], inp["gamma"], inp["eps"])
+    ng, tg = loop(lambda: O.linear(act, wc, ws))
+    gemm_tf = gemm_flops(gemm_rows, N, K) * ng / tg / 1e12
+    # the whole layer on all cores, per token row: prep (all cores) + GEMM
+    s_row = prep_bytes(1, K, norm=False) / (prep_all * 1e9) + gemm_flops(1, N, K) / (gemm_tf * 1e12)
+    return {"value": gemm_flops(1, N, K) / s_row / 1e12, "unit": "TFLOP/s", "cores": max(threads, blas),
+            "kind": "oracle",
+            "sample": f"QKV workload (K={K}, N={N}): prep of {prep_rows} rows single-threaded ({n1} passes, "
+                      f"{t1:.1f} s), prep of {xa.shape[0]} rows on {threads} threads ({na} passes, {ta:.1f} s), "
+                      f"float64 dual GEMM of {gemm_rows} rows x all {N} outputs with {blas} BLAS threads "
+                      f"({ng} passes, {tg:.1f} s); value = 4*N*K flops per row over the all-core prep time "
+                      f"plus the GEMM time per row",
+            "prep_1thread_GB/s": round(prep1, 4), "prep_allcores_GB/s": round(prep_all, 4),
+            "gemm_fp64_TFLOP/s": round(gemm_tf, 5), "nproc": nproc, "affinity": aff,
+            "prep_threads": threads, "blas_threads": blas}
+
+
+def measure_peaks(reps: int = 5):
+    """FP4 MFMA rate on random operand bytes and streaming read bandwidth over
+    1 GiB (past the 256 MB last-level cache), measured on this device with the
+    library's measurement kernels; HIP events on the stream they run on."""
+    import torch
+
+    import fp4_sparse_dense_amd as sq
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    ops = torch.randint(0, 256, (4096,), dtype=torch.uint8, device="cuda", generator=gen)
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    buf = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device="cuda", generator=gen)
+    stream = torch.cuda.current_stream()
+
+    def rate(launch):
+        launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        work = sum(launch() for _ in range(reps))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return work / (e0.elapsed_time(e1) * 1e-3)
+
+    fp4 = rate(lambda: sq.peak_fp4_mfma(ops, 4096, sink)) / 1e12
+    rd = rate(lambda: sq.peak_read(buf, sink)) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return {"fp4_mfma_TFLOP/s": round(fp4, 1), "hbm_read_GB/s": round(rd, 1),
+            "how": "back-to-back v_mfma_scale_f32_16x16x128_f8f6f4 on random E2M1 bytes, 16 waves per CU; "
+                   "16-byte loads streaming 1 GiB"}
 
 
 def device_weight(gen, N, K):
@@ -232,6 +342,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed steps in a HIP graph and replay it (always on for decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the FP4 MFMA rate and read bandwidth on this device")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -271,6 +383,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    args.measured_peaks = None if args.no_peaks else measure_peaks()
     if args.workload == "moe":
         rec = run_moe(args)
     elif args.workload == "layer":
@@ -366,18 +479,33 @@ def run_dense(args):
     # (NVFP4-style weight: 0.5625 B/elem, MXFP4: 0.53125)
     wbytes = N * K * 9 // 16 if nv else N * K * 17 // 32
     gbytes = (M * K * 2 + wbytes + 4 * M * N) if args.fused else gemm_bytes(M, N, K, nv=nv, dense=dense)
+    glayout = (M * K * 2 + wbytes + 4 * M * N) if args.fused else gemm_layout_bytes(M, N, K, nv=nv, dense=dense)
     gemm_gbs = gbytes / (gemm_ms * 1e-3) / 1e9
     pbytes = prep_bytes(M, K, norm, nv=nv, dense=dense)
+    playout = prep_layout_bytes(M, K, norm, nv=nv, dense=dense)
     prep_gbs = pbytes / (prep_ms * 1e-3) / 1e9 if prep_ms > 0 else 0.0
     peak_mfma = PEAK_BF16_TFLOPS if nv else PEAK_FP4_TFLOPS
+    useful = flops if dense else gemm_useful_flops(M, N, K)
+    useful_frac = useful / (gemm_ms * 1e-3) / 1e12 / peak_mfma
+    # fractions of the peaks measured on this device in the same run (FP4 MFMA
+    # rate; streaming read bandwidth for the HBM-bound kernels)
+    mp = getattr(args, "measured_peaks", None)
+    m_fp4 = mp["fp4_mfma_TFLOP/s"] if mp and not nv else None
+    m_hbm = mp["hbm_read_GB/s"] if mp else None
+
+    def frac(a, peak):
+        return round(a / peak, 4) if peak else None
     hbm_bound = gbytes / (PEAK_HBM_GBS * 1e9) > flops / (peak_mfma * 1e12)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "peak_measured": m_hbm, "frac_measured": frac(gemm_gbs, m_hbm)}
     else:
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak_mfma, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / peak_mfma, 4),
-                "traffic": read_traffic() if (args.workload == "qkv" and not dense and ablation == "none") else None}
+                "traffic": read_traffic() if (args.workload == "qkv" and not dense and ablation == "none") else None,
+                "frac_useful": round(useful_frac, 4), "peak_measured": m_fp4,
+                "frac_measured": frac(gemm_tflops, m_fp4)}
     cpu = None if (args.no_cpu_baseline or args.workload != "qkv" or dense or ablation != "none") else cpu_baseline()
     wname = args.workload if args.workload != "decode" else f"decode{M}"
     if dense:
@@ -410,11 +538,15 @@ def run_dense(args):
                    "format": "NVFP4-style" if nv else "MXFP4",
                    "rotating_sets": nsets},
         "prep": None if args.fused else {"us": round(prep_ms * 1e3, 3), "GB/s": round(prep_gbs, 1),
-                                         "frac_hbm": round(prep_gbs / PEAK_HBM_GBS, 4), "bytes": pbytes},
+                                         "frac_hbm": round(prep_gbs / PEAK_HBM_GBS, 4),
+                                         "frac_hbm_measured": frac(prep_gbs, m_hbm), "bytes": pbytes,
+                                         "layout_bytes": playout, "layout_overhead_bytes": playout - pbytes},
         "gemm": {"us": round(gemm_ms * 1e3, 3), "TFLOP/s": round(gemm_tflops, 1),
-                 "frac_mfma": round(gemm_tflops / peak_mfma, 4), "GB/s": round(gemm_gbs, 1),
-                 "frac_hbm": round(gemm_gbs / PEAK_HBM_GBS, 4), "bytes": gbytes},
+                 "frac_mfma": round(gemm_tflops / peak_mfma, 4), "frac_useful": round(useful_frac, 4),
+                 "frac_mfma_measured": frac(gemm_tflops, m_fp4), "GB/s": round(gemm_gbs, 1),
+                 "frac_hbm": round(gemm_gbs / PEAK_HBM_GBS, 4), "bytes": gbytes, "layout_bytes": glayout},
         "roofline": roof,
+        "measured_peaks": mp,
         "cpu_baseline": cpu,
         "parts_us": {k: round(v * 1e3, 3) for k, v in zip(part_names, part_ms)},
     }

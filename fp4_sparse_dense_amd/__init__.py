@@ -11,6 +11,8 @@ kernels behind the C ABI.  The names follow the C entry points:
 from __future__ import annotations
 
 import ctypes as C
+import functools
+import inspect
 
 from . import _lib
 from ._lib import FMT_HIF4, FMT_MXFP4, FMT_NVFP4, OUT_BF16, OUT_F32, SharqError
@@ -20,7 +22,7 @@ __all__ = [
     "sharq_pack_weight", "sharq_prepare", "sharq_linear", "sharq_linear_grouped",
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
     "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32", "sharq_linear_residual",
-    "sharq_linear_swiglu_prep",
+    "sharq_linear_swiglu_prep", "peak_fp4_mfma", "peak_read",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -29,6 +31,25 @@ __all__ = [
 def _torch():
     import torch
     return torch
+
+
+def _on_stream(fn):
+    """Run `fn` with torch's current stream set to its `stream` argument when
+    one is given, so that every buffer it allocates (outputs, descriptors'
+    buffers, the grouped workspace) belongs to the stream its kernels run on:
+    the caching allocator then hands a freed block only to later work ordered
+    on that stream, never to another stream while a kernel may still read it."""
+    names = list(inspect.signature(fn).parameters)
+    pos = names.index("stream")
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kw):
+        stream = kw.get("stream", args[pos] if len(args) > pos else None)
+        if stream is None:
+            return fn(*args, **kw)
+        with _torch().cuda.stream(stream):
+            return fn(*args, **kw)
+    return wrapper
 
 
 def _stream_ptr(stream):
@@ -94,6 +115,7 @@ class SharqAct:
         return {f: getattr(self, f).cpu().numpy() for f in self.FIELDS}
 
 
+@_on_stream
 def sharq_pack_weight(w, fmt: int = FMT_MXFP4, out: SharqWeight | None = None, stream=None) -> SharqWeight:
     """Pack a bf16 device weight [N, K] (row stride w.stride(0)) into the FP4 payload."""
     torch = _torch()
@@ -107,6 +129,7 @@ def sharq_pack_weight(w, fmt: int = FMT_MXFP4, out: SharqWeight | None = None, s
     return out
 
 
+@_on_stream
 def sharq_prepare(x, gamma=None, eps: float = 1e-5, n: int = 2, m: int = 4, fmt: int = FMT_MXFP4,
                   out: SharqAct | None = None, stream=None) -> SharqAct:
     """Fused preparation of bf16 device activations x [M, K]; gamma [K] bf16 or None (no RMSNorm)."""
@@ -123,6 +146,7 @@ def sharq_prepare(x, gamma=None, eps: float = 1e-5, n: int = 2, m: int = 4, fmt:
     return out
 
 
+@_on_stream
 def sharq_linear(act: SharqAct, weight: SharqWeight, out=None, out_dtype: int = OUT_F32, stream=None):
     """Y [M, N] = sparse FP4 GEMM + dense FP4 GEMM over the shared payload, one epilogue."""
     torch = _torch()
@@ -137,6 +161,7 @@ def sharq_linear(act: SharqAct, weight: SharqWeight, out=None, out_dtype: int = 
     return out
 
 
+@_on_stream
 def sharq_linear_residual(act: SharqAct, weight: SharqWeight, x, out=None, stream=None):
     """Y [M, N] bf16 = bf16(x + layer output): the layer with the residual add
     in its epilogue (x: bf16 [M, N], unit inner stride; out may be x)."""
@@ -160,6 +185,7 @@ def grouped_workspace_bytes(rows: int, experts: int, K: int) -> int:
     return n.value
 
 
+@_on_stream
 def sharq_linear_grouped(act: SharqAct, weight: SharqWeight, seg_offsets, experts: int, row_index=None,
                          rows: int | None = None, out=None, out_dtype: int = OUT_F32, workspace=None, stream=None):
     """Grouped expert layer: expert e computes the SharQ linear layer of routed rows
@@ -193,6 +219,7 @@ def sharq_linear_grouped(act: SharqAct, weight: SharqWeight, seg_offsets, expert
     return out
 
 
+@_on_stream
 def sharq_rmsnorm(x, gamma, eps: float = 1e-5, out=None, stream=None):
     """Unfused RMSNorm (fusion ablation): bf16 [M, K] of the binary32 row the
     fused preparation computes, rounded to nearest even."""
@@ -210,6 +237,7 @@ def sharq_rmsnorm(x, gamma, eps: float = 1e-5, out=None, stream=None):
     return out
 
 
+@_on_stream
 def sharq_add_f32(a, b, out=None, stream=None):
     """out = a + b for contiguous fp32 device tensors of one size (the unfused epilogue's add)."""
     torch = _torch()
@@ -256,6 +284,7 @@ def path_act(act: SharqAct, path: str):
     return _PathAct(act, path)
 
 
+@_on_stream
 def sharq_linear_fused(x, weight: SharqWeight, gamma=None, eps: float = 1e-5, out=None, out_dtype: int = OUT_F32,
                        stream=None):
     """The whole layer in one launch for M <= 16 (decode): the result of
@@ -289,6 +318,7 @@ def interleave_gate_up(w_gate, w_up):
     return torch.stack([w_gate.reshape(F // 16, 16, K), w_up.reshape(F // 16, 16, K)], dim=1).reshape(2 * F, K)
 
 
+@_on_stream
 def sharq_linear_swiglu(act: SharqAct, weight: SharqWeight, out=None, stream=None):
     """H [M, N/2] bf16 = SiLU(gate) * up of the interleaved gate/up SharQ layer."""
     torch = _torch()
@@ -303,6 +333,7 @@ def sharq_linear_swiglu(act: SharqAct, weight: SharqWeight, out=None, stream=Non
     return out
 
 
+@_on_stream
 def sharq_linear_swiglu_prep(act: SharqAct, weight: SharqWeight, out: SharqAct | None = None, stream=None):
     """The gate/up layer whose SwiGLU epilogue prepares H = bf16(SiLU(gate) * up)
     for the down projection (2:4, MXFP4, no RMSNorm) without storing H: the
@@ -318,6 +349,29 @@ def sharq_linear_swiglu_prep(act: SharqAct, weight: SharqWeight, out: SharqAct |
     return out
 
 
+def peak_fp4_mfma(operands, iters: int, sink, stream=None) -> float:
+    """Launch the FP4 MFMA rate measurement (include/sharq_peak.h) on `stream`;
+    returns the flops the launch executes.  operands: device uint8 tensor of
+    >= 4096 random bytes; sink: device float32 tensor of >= 1 element."""
+    lib = _lib.load()
+    flops = C.c_double()
+    _lib.check(lib.sharq_peak_fp4_mfma(_ptr(operands), operands.numel(), iters, _ptr(sink), C.byref(flops),
+                                       _stream_ptr(stream)), "sharq_peak_fp4_mfma")
+    return flops.value
+
+
+def peak_read(buf, sink, stream=None) -> float:
+    """Launch the streaming read measurement over the device uint8 tensor `buf`
+    (a multiple of 16 bytes, >= 1 MiB); returns the bytes the launch reads.
+    sink: device int32 tensor of >= 1 element."""
+    lib = _lib.load()
+    nbytes = C.c_double()
+    _lib.check(lib.sharq_peak_read(_ptr(buf), buf.numel(), _ptr(sink), C.byref(nbytes), _stream_ptr(stream)),
+               "sharq_peak_read")
+    return nbytes.value
+
+
+@_on_stream
 def sharq_add_bf16_f32(x, y, out=None, stream=None):
     """out = bf16(x + y): x bf16, y fp32 (contiguous, same size); the residual add."""
     torch = _torch()

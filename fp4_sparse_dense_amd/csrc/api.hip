@@ -75,6 +75,11 @@ bool backbone_ok(const sharq_act* a, int32_t n) {
 
 }  // namespace
 
+namespace sharq {
+// the thread-local detail string of sharq_last_error, for the other entry-point files
+sharq_status record_error(sharq_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace sharq
+
 extern "C" {
 
 int sharq_abi_version(void) { return SHARQ_ABI_VERSION; }

@@ -332,6 +332,197 @@ __global__ __launch_bounds__(W * 64) void prep_kernel(const uint16_t* __restrict
   if (nu_w > 0) store(prev, nu_w - 1);
 }
 
+// ---------------------------------------------------------------------------
+// Prep kernel for RMSNorm rows of at most 8192 elements.
+//
+// The streaming kernel above stages its 8-row group through per-wave LDS
+// rings, sums the squares with a workgroup-wide tree and only then starts
+// the arithmetic.  Here a workgroup (16 waves) still owns the 8 rows of half
+// a 16-row tile block, but each row belongs to two waves (one half of its
+// blocks each), which load their blocks straight into registers (buffer
+// loads: reads past K or past the last row return zeros) and meet only
+// through a pair of LDS slots for the row's sum of squares, so a row's
+// arithmetic starts as soon as its own two halves have arrived.  (QKV shape
+// 2048 x 4096: 12.1 -> 10.2 us.  Per-wave clock stamps put the loads at
+// about 3 us of the launch, the arithmetic of 16 waves at about 2.2 us once
+// their rows are in, and the stores of the codes at about 2 us more; issuing
+// the four row pairs' loads at staggered times, a wave per two rows with
+// 32-byte store runs, or all 8 rows per wave with whole-line stores were no
+// faster.)
+//
+// Lane l of wave (row r, half h) holds blocks h*64*NB + 64*j + l, j < NB (one
+// MX block of 32 elements each).  Its sum of squares is the balanced pairwise
+// tree of the row zero-padded to 4096*NB elements, which equals the tree over
+// the next power of two of K (the extra leaves are +0): per block the 32-leaf
+// tree (chunk_sumsq), across the 64 lanes the butterfly of wave_tree_sum
+// (blocks in lane order), then the NB slots, then the two halves, which meet
+// through a pair of LDS slots (each wave publishes its half and waits for the
+// other's; both always publish, and the wait is bounded).
+//
+// Codes go out as 16-byte stores straight from the registers; metadata and
+// scale bytes (4- and 1-byte pieces per lane) are collected in LDS and
+// written after the last block in runs of the 8 rows (32 and 8 bytes).
+// ---------------------------------------------------------------------------
+constexpr int kRowsWaves = 16;
+constexpr int kRowsMaxK = 8192;
+constexpr uint32_t kRowsSpinLimit = 1u << 20;   // bound of the pair wait (never reached)
+
+struct RowsPlan {
+  int KB;                                     // K tiles (K padded to 128)
+  uint32_t off_sync, off_meta, off_ssc, off_rsc, total;
+};
+
+static RowsPlan rows_plan(int K) {
+  RowsPlan p{};
+  p.KB = (K + 127) / 128;
+  p.off_sync = ((uint32_t)p.KB * 4u + 1u) * kGammaBlockF32 * 4u;   // gamma: binary32, 36 words per block, then a zero block
+  p.off_meta = p.off_sync + 8u * 2u * 8u;                     // 8 rows x 2 halves x {sum, flag}
+  p.off_ssc = p.off_meta + (uint32_t)p.KB * 128u;             // [kt][chunk][row] words
+  p.off_rsc = p.off_ssc + (uint32_t)p.KB * 32u;               // [kt][chunk][row] bytes
+  p.total = p.off_rsc + (uint32_t)p.KB * 32u;
+  return p;
+}
+
+template <int NB, bool DENSE>
+__global__ __launch_bounds__(kRowsWaves * 64) void prep_norm_rows_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                                         int K, int64_t ldx,
+                                                                         const uint16_t* __restrict__ gamma, float eps,
+                                                                         RowsPlan P, PrepOut o) {
+  extern __shared__ __align__(1024) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rl = wave >> 1;                        // row among the workgroup's 8
+  const int hf = wave & 1;                         // half of the row's blocks
+
+  // workgroup -> (16-row block, half): the two halves of a block are 8 apart
+  // in launch order, i.e. on one XCD, so their L2 merges the writes
+  const int64_t RB = (M + 15) / 16, nwg = RB * 2;
+  const int64_t w = blockIdx.x;
+  const int64_t full = nwg / 16 * 16;
+  int64_t rb, half;
+  if (w < full) { rb = (w / 16) * 8 + (w % 8); half = (w % 16) / 8; }
+  else { rb = w / 2; half = w % 2; }
+  const int64_t row = rb * 16 + half * 8 + rl;
+  const int r16 = (int)half * 8 + rl;
+  const bool row_ok = row < M;
+  const int KB = P.KB, nblk = KB * 4;
+
+  // gamma: one 16-byte piece per thread (K <= 8192), zeros past K
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void*)gamma, (short)0, K * 2, 0x00020000);
+  const int ge = tid * 8;
+  const u32x4 gq = __builtin_amdgcn_raw_buffer_load_b128(grs, ge * 2, 0, 0);
+
+  // this wave's blocks of the row
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(x + (row_ok ? row : 0) * ldx), (short)0, row_ok ? K * 2 : 0, 0x00020000);
+  const int b0 = hf * 64 * NB + lane;
+  u32x4 xq[NB][4];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xq[j][q] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (b0 + 64 * j) * 64 + 16 * q, 0, 0);
+
+  // gamma into LDS as binary32, blocks padded to 36 words (the 16-byte reads
+  // of 16 consecutive blocks then hit 16 distinct bank groups); pair slots cleared
+  float* gs = reinterpret_cast<float*>(smem);
+  if (ge < nblk * 32) {
+    float* d = gs + (ge / 32) * kGammaBlockF32 + (ge % 32);
+    *reinterpret_cast<float4*>(d) = make_float4(bf16_lo(gq[0]), bf16_hi(gq[0]), bf16_lo(gq[1]), bf16_hi(gq[1]));
+    *reinterpret_cast<float4*>(d + 4) = make_float4(bf16_lo(gq[2]), bf16_hi(gq[2]), bf16_lo(gq[3]), bf16_hi(gq[3]));
+  }
+  if (tid < 32) gs[nblk * kGammaBlockF32 + tid] = 0.0f;
+  uint2* slots = reinterpret_cast<uint2*>(smem + P.off_sync);
+  if (tid < 16) slots[tid] = make_uint2(0u, 0u);
+  __syncthreads();
+  // nothing that needs this wave's rows moves above the barrier (each wave
+  // reaches it before its own rows have arrived)
+  __builtin_amdgcn_sched_barrier(0);
+
+  // sum of squares of this half, then of the row
+  float xf[NB][32];
+  float th = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        xf[j][8 * i + 2 * h] = bf16_lo(xq[j][i][h]);
+        xf[j][8 * i + 2 * h + 1] = bf16_hi(xq[j][i][h]);
+      }
+    const float t = wave_tree_sum(chunk_sumsq(xf[j]));
+    th = j == 0 ? t : th + t;
+  }
+  if (lane == 0) slots[rl * 2 + hf] = make_uint2(__float_as_uint(th), 1u);
+  float tother = 0.0f;
+  {
+    volatile __attribute__((address_space(3))) uint32_t* other =
+        (volatile __attribute__((address_space(3))) uint32_t*)(slots + rl * 2 + (hf ^ 1));
+    for (uint32_t it = 0; it < kRowsSpinLimit; ++it) {
+      // the flag first, then the sum (LDS accesses of one wave are done in order)
+      if (__builtin_amdgcn_readfirstlane(other[1]) != 0u) {
+        tother = __uint_as_float(__builtin_amdgcn_readfirstlane(other[0]));
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  const float inv = rms_inverse(th + tother, K, eps);   // the halves' sum (x + y == y + x exactly)
+
+  // decomposition; codes stored now, metadata and scales staged
+  uint32_t* meta_st = reinterpret_cast<uint32_t*>(smem + P.off_meta);
+  uint8_t* ssc_st = smem + P.off_ssc;
+  uint8_t* rsc_st = smem + P.off_rsc;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int b = b0 + 64 * j;
+    if (b < nblk) {
+      // rows past M and blocks past K are zero input: x reads as +0 there; a
+      // factor +0 in place of inv (which may not be finite) and gamma +0 (the
+      // table is zero past K; rows past M read the zero block after it) keep
+      // v = +0 with its sign
+      const float invb = row_ok && 32 * b < K ? inv : 0.0f;
+      float v[32];
+      const float* gb = gs + (row_ok ? b : nblk) * kGammaBlockF32;
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const float4 g = *reinterpret_cast<const float4*>(gb + i);
+        v[i] = (xf[j][i] * invb) * g.x;
+        v[i + 1] = (xf[j][i + 1] * invb) * g.y;
+        v[i + 2] = (xf[j][i + 2] * invb) * g.z;
+        v[i + 3] = (xf[j][i + 3] * invb) * g.w;
+      }
+      const Block32 d = decompose32<DENSE>(v);
+      const int kt = b >> 2, c = b & 3;
+      const int64_t tile = rb * KB + kt;
+      const int tl = c * 16 + r16;
+      *reinterpret_cast<uint4*>(o.r_codes + tile * 1024 + tl * 16) = d.r_codes;
+      const int st = kt * 32 + c * 8 + rl;
+      rsc_st[st] = (uint8_t)d.r_e8;
+      if constexpr (!DENSE) {
+        *reinterpret_cast<uint4*>(o.s_codes + tile * 1024 + tl * 16) = d.s_codes;
+        meta_st[st] = d.meta;
+        ssc_st[st] = (uint8_t)d.s_e8;
+      }
+    }
+  }
+  __syncthreads();
+
+  // metadata and scales of the 8 rows: per (K tile, chunk) 32 contiguous
+  // bytes of metadata and 8 of each scale
+  for (int i = tid; i < nblk; i += kRowsWaves * 64) {
+    const int kt = i >> 2, c = i & 3, st = kt * 32 + c * 8;
+    const int64_t sc = ((int64_t)kt * RB + rb) * 64 + c * 16 + half * 8;
+    *reinterpret_cast<uint2*>(o.r_scales + sc) = *reinterpret_cast<const uint2*>(rsc_st + st);
+    if constexpr (!DENSE) {
+      *reinterpret_cast<uint2*>(o.s_scales + sc) = *reinterpret_cast<const uint2*>(ssc_st + st);
+      uint8_t* md = o.s_meta + (rb * KB + kt) * 256 + (c * 16 + half * 8) * 4;
+      *reinterpret_cast<uint4*>(md) = *reinterpret_cast<const uint4*>(meta_st + st);
+      *reinterpret_cast<uint4*>(md + 16) = *reinterpret_cast<const uint4*>(meta_st + st + 4);
+    }
+  }
+}
+
 // Weight payload: MXFP4 over each 32-block of a row of W, no mask, no norm.
 __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __restrict__ w, int64_t N, int K,
                                                           int64_t ldw, uint8_t* __restrict__ codes,
@@ -382,9 +573,26 @@ static int prep_ksplit(int64_t nwg, int units, bool norm) {
 }
 
 template <bool DENSE>
+static hipError_t launch_prepare_rows(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
+                                     float eps, PrepOut out, hipStream_t stream) {
+  const RowsPlan P = rows_plan(K);
+  const int64_t grid = (M + 15) / 16 * 2;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (K <= 4096)
+    hipLaunchKernelGGL((prep_norm_rows_kernel<1, DENSE>), dim3((unsigned)grid), dim3(kRowsWaves * 64), P.total,
+                       stream, x, M, K, ldx, gamma, eps, P, out);
+  else
+    hipLaunchKernelGGL((prep_norm_rows_kernel<2, DENSE>), dim3((unsigned)grid), dim3(kRowsWaves * 64), P.total,
+                       stream, x, M, K, ldx, gamma, eps, P, out);
+  return hipGetLastError();
+}
+
+template <bool DENSE>
 static hipError_t launch_prepare_t(const uint16_t* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma,
                                    float eps, PrepOut out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  if (gamma && K <= kRowsMaxK)
+    return launch_prepare_rows<DENSE>(x, M, K, ldx, gamma, eps, out, stream);
   // Short rows without RMSNorm (at most eight 256-element units: K <= 2048,
   // the expert layers) run 4- or 8-wave workgroups: with 16 waves most would
   // have no unit, and the CU would hold only two workgroups' few busy waves.

@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every function include/sharq.h declares,
+"""The C-ABI library loads, exports every function include/*.h declares,
 answers size queries, and rejects invalid requests on the host before any HIP
 call (CPU only: no compute call is made)."""
 import ctypes as C
@@ -11,13 +11,16 @@ import pytest
 from fp4_sparse_dense_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sharq.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sharq_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(sharq_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -318,3 +321,18 @@ def test_swiglu_prep_rejects_before_launch(lib):
     a.M = 0
     assert lib.sharq_linear_swiglu_prep(C.byref(a), C.byref(w), C.byref(nxt), None) == _lib.OK
     assert (nxt.M, nxt.K, nxt.n, nxt.m) == (0, 128, 2, 4)
+
+
+def test_peak_entry_points_reject_bad_arguments(lib):
+    """The measurement entry points check their arguments on the host."""
+    d = C.c_double()
+    buf = C.c_void_p(0x1000)
+    assert lib.sharq_peak_fp4_mfma(None, 4096, 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_fp4_mfma(buf, 1024, 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_fp4_mfma(C.c_void_p(0x1004), 4096, 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_fp4_mfma(buf, 4096, 0, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_fp4_mfma(buf, 4096, (1 << 20) + 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert b"iters" in lib.sharq_last_error()
+    assert lib.sharq_peak_read(buf, (1 << 20) - 16, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_read(buf, (1 << 20) + 8, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_read(None, 1 << 20, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG

@@ -48,15 +48,39 @@ def test_bad_flag_combinations_exit_before_device_work(args):
 
 
 def test_algorithmic_accounting():
+    """The byte and flop counts follow the method's own accounting: a
+    compressed 2:4 backbone, 2.9375 B per activation element through the prep
+    and 0.9375 B read by the GEMM (QKV: 24,649,728 and 71,565,312 B)."""
     b = _bench()
     # QKV: 2048 x 4096 prep with gamma; dual GEMM to 6144 with fp32 Y
-    assert b.prep_bytes(2048, 4096) == 2048 * 4096 * 2 + 2048 * 4096 * 19 // 16 + 2 * 4096 == 26_746_880
+    assert b.prep_bytes(2048, 4096) == 2048 * 4096 * 47 // 16 + 2 * 4096 == 24_649_728
+    assert b.gemm_bytes(2048, 6144, 4096) == 7_864_320 + 13_369_344 + 50_331_648 == 71_565_312
     assert b.gemm_flops(2048, 6144, 4096) == 206_158_430_208
-    assert b.gemm_bytes(2048, 6144, 4096) == 8_912_896 + 13_369_344 + 50_331_648
+    assert b.gemm_useful_flops(2048, 6144, 4096) * 4 == b.gemm_flops(2048, 6144, 4096) * 3
+    # the layout's own bytes: the backbone stored masked dense (0.5 B instead of 0.25)
+    assert b.prep_layout_bytes(2048, 4096) == 26_746_880
+    assert b.prep_layout_bytes(2048, 4096) - b.prep_bytes(2048, 4096) == 2048 * 4096 // 4
+    assert b.gemm_layout_bytes(2048, 6144, 4096) == 8_912_896 + 13_369_344 + 50_331_648
+    # down projection: no RMSNorm
+    assert b.prep_bytes(2048, 14336, norm=False) == 86_245_376
+    assert b.gemm_bytes(2048, 4096, 14336) == 92_274_688
+    # gate/up and the Qwen3 MoE rows
+    assert b.gemm_bytes(2048, 28672, 4096) == 305_135_616
+    assert b.prep_bytes(32768, 768, norm=False) == 73_924_608
     # decode M=1, K=N=4096: the weight read once for both paths
-    assert b.gemm_bytes(1, 4096, 4096) == 4352 + 8_912_896 + 16_384
-    # plain FP4: 0.53125 B/elem on both sides
+    assert b.gemm_bytes(1, 4096, 4096) == 3840 + 8_912_896 + 16_384
+    # plain FP4: 0.53125 B/elem on both sides, as stored
     assert b.gemm_bytes(2048, 6144, 4096, dense=True) == 4_456_448 + 13_369_344 + 50_331_648
+    assert b.prep_bytes(2048, 4096, dense=True) == b.prep_layout_bytes(2048, 4096, dense=True)
+    # NVFP4-style: 16-element scales
+    assert b.prep_bytes(64, 4096, norm=False, nv=True) == 64 * 4096 * 3
+    assert b.gemm_bytes(64, 4096, 4096, nv=True) == 64 * 4096 + 4096 * 4096 * 9 // 16 + 4 * 64 * 4096
+
+
+def test_cpu_thread_counts():
+    b = _bench()
+    nproc, aff, threads = b.cpu_threads()
+    assert nproc >= aff >= 1 and 1 <= threads <= min(aff, 16)
 
 
 def test_traffic_record_follows_the_source_digest(tmp_path, monkeypatch):

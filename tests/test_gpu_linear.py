@@ -107,7 +107,10 @@ def test_linear_deterministic_and_strided_output():
     assert torch.all(big[:, :32] == 7.0) and torch.all(big[:, 32 + inp["N"]:] == 7.0)
 
 
-@pytest.mark.parametrize("M,K,N", [(512, 512, 384), (512, 1024, 6144), (300, 512, 200), (2048, 256, 4096)])
+@pytest.mark.parametrize("M,K,N", [(512, 512, 384), (512, 1024, 6144), (300, 512, 200), (2048, 256, 4096),
+                                   # 256 x 192 tiles (fewer waves of workgroups than 128 x 256 ones): whole
+                                   # tiles in rounds of two 16-row blocks, and a ragged last M tile
+                                   (2048, 512, 6144), (2000, 256, 6144)])
 def test_linear_tiled_bf16_equals_rounded_fp32(M, K, N):
     """The tiled kernel's bf16 output (staged through LDS for whole tiles,
     element-wise at ragged edges) is its fp32 output rounded to nearest even."""

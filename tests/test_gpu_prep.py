@@ -92,6 +92,22 @@ def test_prep_shapes(M, K, ldx, norm):
     assert_prep_equal(got, ref, f"M={M} K={K}")
 
 
+@pytest.mark.parametrize("M,K,ldx", [(13, 4096, 4096), (21, 4160, 4168), (11, 6176, 6176), (3, 8192, 8200),
+                                     (29, 1056, 1056)])
+def test_prep_norm_signed_gamma(M, K, ldx):
+    """RMSNorm rows with gamma of both signs (a negative gamma must not turn the
+    padding rows' zero input into -0), a zero row among them, ragged M and K
+    tiles, one and two blocks per lane."""
+    print(f"prep signed gamma M={M} K={K}", flush=True)
+    rng = np.random.default_rng(M * 7 + K)
+    x = synth.outlier_activations(rng, M, K)
+    x[M // 2] = 0
+    g = synth.bf16_bits_from_f32((rng.uniform(0.5, 1.5, K) * rng.choice([-1.0, 1.0], K)).astype(np.float32))
+    ref = O.prepare(x, g, 1e-5)
+    got = run_prep(x, g, 1e-5, ldx=ldx)
+    assert_prep_equal(got, ref, f"signed gamma M={M} K={K}")
+
+
 def test_prep_eps_values():
     inp = synth.layer_inputs("tiny", seed=0, with_weight=False)
     for eps in (1e-6, 0.5, 0.0):

@@ -26,7 +26,9 @@ def _layer(M, K, N, norm, n=2, seed=0):
 
 @pytest.mark.parametrize("M,K,N,norm,n", [(37, 96, 53, True, 2), (5, 1376, 100, False, 2), (130, 768, 200, False, 2),
                                           (300, 2048, 1536, True, 2), (2048, 4096, 4096, False, 2),
-                                          (257, 512, 384, True, 0)])
+                                          (257, 512, 384, True, 0),
+                                          # 256 x 192 tiles: whole and ragged M tiles
+                                          (2048, 256, 6144, False, 2), (2000, 512, 6144, True, 2)])
 def test_residual_layer_equals_two_calls(M, K, N, norm, n):
     import torch
     print(f"residual M={M} K={K} N={N} n={n}", flush=True)

@@ -74,3 +74,38 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for k, (a, b) in enumerate(zip(outs, ref)):
             assert torch.equal(a, b), (it, k)
+
+
+def _segment_stream(t):
+    """The stream torch's caching allocator attached to the block holding t."""
+    import torch
+    p = t.data_ptr()
+    for seg in torch.cuda.memory_snapshot():
+        if seg["address"] <= p < seg["address"] + seg["total_size"]:
+            return seg["stream"]
+    raise AssertionError("block not found in the allocator snapshot")
+
+
+def test_binding_allocates_on_the_callers_stream():
+    """Buffers the binding allocates for a call on an explicit stream belong to
+    that stream, so a block freed when the call returns (the grouped layer's
+    workspace) is handed only to later work ordered on that stream."""
+    import torch
+    print("binding allocation stream", flush=True)
+    x, g, w = _inputs(4, M=64, K=512, N=256)
+    xd, gd, wt = dev_bf16(x), dev_bf16(g), sq.sharq_pack_weight(dev_bf16(w))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    act = sq.sharq_prepare(xd, gd, 1e-5, stream=s)
+    y = sq.sharq_linear(act, wt, stream=s)
+    seg = torch.tensor([0, 20, 64], dtype=torch.int64, device="cuda")
+    s.wait_stream(torch.cuda.current_stream())
+    yg = sq.sharq_linear_grouped(act, sq.sharq_pack_weight(dev_bf16(np.concatenate([w[:128], w[128:]]))), seg, 2,
+                                 stream=s)
+    assert torch.cuda.current_stream() == torch.cuda.default_stream()
+    for t in (act.r_codes, act.s_codes, y, yg):
+        assert _segment_stream(t) == s.cuda_stream
+    torch.cuda.synchronize()
+    y0 = sq.sharq_linear(sq.sharq_prepare(xd, gd, 1e-5), wt)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
