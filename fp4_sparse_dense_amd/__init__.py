@@ -23,6 +23,7 @@ __all__ = [
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
     "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32", "sharq_linear_residual",
     "sharq_linear_swiglu_prep", "peak_fp4_mfma", "peak_read",
+    "sharq_linear_grouped_noalloc", "noalloc_scratch_bytes",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -217,6 +218,38 @@ def sharq_linear_grouped(act: SharqAct, weight: SharqWeight, seg_offsets, expert
                                         _ptr(workspace), workspace.numel(), _stream_ptr(stream)),
                "sharq_linear_grouped")
     return out
+
+
+@_on_stream
+def sharq_linear_grouped_noalloc(act: SharqAct, weight: SharqWeight, seg_offsets, experts: int, row_index=None,
+                                 rows: int | None = None, out=None, out_dtype: int = OUT_F32, stream=None):
+    """sharq_linear_grouped with the library's own per-GPU scratch as the
+    workspace (include/sharq.h): the C entry point allocates nothing.  Pass
+    `out` to allocate nothing here either.  Calls overlapping on one GPU race."""
+    torch = _torch()
+    dev = act.s_codes.device
+    if rows is None:
+        rows = int(row_index.numel()) if row_index is not None else act.M
+    if seg_offsets.dtype != torch.int64 or not seg_offsets.is_contiguous() or seg_offsets.numel() != experts + 1:
+        raise ValueError("seg_offsets must be a contiguous int64 tensor of E+1 entries")
+    if row_index is not None and (row_index.dtype != torch.int32 or not row_index.is_contiguous()):
+        raise ValueError("row_index must be a contiguous int32 tensor")
+    ne = weight.N // experts
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty(rows, ne, dtype=dt, device=dev)
+    if out.dtype != dt or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be 2-D with unit inner stride and the requested dtype")
+    lib = _lib.load()
+    _lib.check(lib.sharq_linear_grouped_noalloc(C.byref(act.desc), _ptr(row_index), rows, _ptr(seg_offsets), experts,
+                                                C.byref(weight.desc), _ptr(out), out.stride(0), out_dtype,
+                                                _stream_ptr(stream)), "sharq_linear_grouped_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the per-GPU scratch sharq_linear_grouped_noalloc uses."""
+    return int(_lib.load().sharq_noalloc_scratch_bytes())
 
 
 @_on_stream

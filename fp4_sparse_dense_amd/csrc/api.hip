@@ -536,10 +536,16 @@ sharq_status sharq_grouped_workspace_bytes(int64_t rows, int32_t E, int64_t K, s
   return SHARQ_OK;
 }
 
-sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
-                                  const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
-                                  void* y_dev, int64_t ldy, int32_t out_dtype,
-                                  void* ws_dev, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The grouped layer behind both entry points: with noalloc the workspace is
+// the library's per-GPU scratch (ws_dev and ws_bytes unused).
+sharq_status linear_grouped_impl(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
+                                 const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w, void* y_dev,
+                                 int64_t ldy, int32_t out_dtype, void* ws_dev, size_t ws_bytes, bool noalloc,
+                                 void* stream) {
   g_err[0] = 0;
   if (!a || !w) return fail(SHARQ_ERR_INVALID_ARG, "null descriptor");
   if (a->struct_size != sizeof(sharq_act) || w->struct_size != sizeof(sharq_weight))
@@ -592,10 +598,20 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
                   (long long)a->M, (long long)rows, (long long)w->N, (long long)a->K);
   }
   const size_t need = sharq::grouped_workspace_bytes(rows, E, (int)a->K);
-  if (!ws_dev || ws_bytes < need || !aligned(ws_dev, 256))
+  if (noalloc) {
+    if (need > sharq::kNoAllocScratchBytes)
+      return fail(SHARQ_ERR_WORKSPACE, "this layer needs %zu bytes of workspace; the library's scratch holds %zu "
+                  "(use sharq_linear_grouped with a caller workspace)", need, sharq::kNoAllocScratchBytes);
+  } else if (!ws_dev || ws_bytes < need || !aligned(ws_dev, 256)) {
     return fail(SHARQ_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", need, ws_bytes);
+  }
   s = check_device();
   if (s) return s;
+  if (noalloc) {
+    hipError_t e = hipSuccess;
+    ws_dev = sharq::noalloc_scratch(&e);
+    if (!ws_dev) return hip_fail(e, "address of the library's scratch (hipGetSymbolAddress)");
+  }
   sharq::GroupedArgs ga{};
   sharq::GemmArgs& g = ga.gemm;
   g.s_codes = a->s_codes;
@@ -631,5 +647,26 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
   if (e != hipSuccess) return hip_fail(e, "grouped linear launch");
   return SHARQ_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
+                                  const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
+                                  void* y_dev, int64_t ldy, int32_t out_dtype,
+                                  void* ws_dev, size_t ws_bytes, void* stream) {
+  return linear_grouped_impl(a, row_index_dev, rows, seg_offsets_dev, E, w, y_dev, ldy, out_dtype, ws_dev, ws_bytes,
+                             false, stream);
+}
+
+sharq_status sharq_linear_grouped_noalloc(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
+                                          const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
+                                          void* y_dev, int64_t ldy, int32_t out_dtype, void* stream) {
+  return linear_grouped_impl(a, row_index_dev, rows, seg_offsets_dev, E, w, y_dev, ldy, out_dtype, nullptr, 0, true,
+                             stream);
+}
+
+size_t sharq_noalloc_scratch_bytes(void) { return sharq::kNoAllocScratchBytes; }
 
 }  // extern "C"

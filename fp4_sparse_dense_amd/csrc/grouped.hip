@@ -18,6 +18,8 @@
 //      row index the rows are already in expert order and only the scales are
 //      copied: the GEMM reads the codes from the source rows itself;
 //   3. the tiled dual GEMM with one workgroup per (expert, M tile, N tile).
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -258,6 +260,33 @@ __global__ __launch_bounds__(256) void grouped_gather_scales_kernel(GatherArgs a
 }  // namespace
 
 size_t grouped_workspace_bytes(int64_t rows, int E, int K) { return ws_layout(rows, E, K).total; }
+
+// Library-owned scratch of sharq_linear_grouped_noalloc: one copy per GPU,
+// allocated when the code object is loaded there and held until the process
+// ends.  Host code never uses the array's name as an address (it is a
+// host-side stand-in): noalloc_scratch() asks the runtime for this device's
+// address once and keeps it.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+uint8_t* noalloc_scratch(hipError_t* err) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<uint8_t*> ptr[kMaxDev];
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDev) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  uint8_t* p = ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  *err = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess) return nullptr;
+  p = static_cast<uint8_t*>(q);
+  ptr[dev].store(p, std::memory_order_release);   // the same value for every thread that gets here
+  return p;
+}
 
 hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   const int E = a.gemm.E;

@@ -102,6 +102,11 @@ struct GroupedArgs {
   uint8_t* ws;                     // workspace (sharq_grouped_workspace_bytes)
 };
 size_t grouped_workspace_bytes(int64_t rows, int E, int K);
+// the grouped layer's workspace for callers that cannot allocate: a
+// library-owned device array per GPU (its address on the current device, or
+// nullptr with *err set)
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+uint8_t* noalloc_scratch(hipError_t* err);
 int grouped_tile_m();
 hipError_t launch_linear_grouped_gemm(const GemmArgs& a, int64_t max_mtiles, hipStream_t stream);
 hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream);

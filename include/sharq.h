@@ -12,9 +12,11 @@
  *
  * Conventions for every entry point:
  *  - Ownership: the caller allocates every buffer (sizes from the *_bytes
- *    queries).  The library never allocates, frees or keeps device memory and
- *    holds no mutable global state other than a thread-local error string and
- *    a per-device architecture check, so it is reentrant.
+ *    queries).  The library never allocates or frees device memory and holds
+ *    no mutable global state other than a thread-local error string, a
+ *    per-device architecture check, and the one device array per GPU that
+ *    sharq_linear_grouped_noalloc uses as its workspace (see there), so every
+ *    other entry point is reentrant.
  *  - Pointers named *_dev are device pointers; struct fields are device
  *    pointers unless stated.  `stream` is a hipStream_t (NULL = the null stream).
  *  - Ordering: every call is asynchronous on `stream`; nothing synchronises
@@ -351,6 +353,30 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
                                   const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
                                   void* y_dev, int64_t ldy, int32_t out_dtype,
                                   void* ws_dev, size_t ws_bytes, void* stream);
+
+/* sharq_linear_grouped for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same layer, the same kernels and the same outputs, with the
+ * workspace taken from a library-owned device array instead of an argument.
+ * Each GPU the library runs on holds one such array of
+ * sharq_noalloc_scratch_bytes() bytes (32 MiB) from the first use of the
+ * library's code there until the process ends; the first call on a device
+ * looks up its address once.  Nothing is allocated or freed per call.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on different streams, or from several host threads onto streams
+ * that are not ordered) race and give undefined results.  Nothing in the array
+ * needs to start at zero: every launch writes the parts it later reads.
+ * Arguments as sharq_linear_grouped, without ws/ws_bytes.
+ * Errors: as sharq_linear_grouped; WORKSPACE when the layer needs more than
+ * the array holds (sharq_grouped_workspace_bytes(rows, E, K) >
+ * sharq_noalloc_scratch_bytes()): use sharq_linear_grouped with a caller
+ * workspace then. */
+sharq_status sharq_linear_grouped_noalloc(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
+                                          const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
+                                          void* y_dev, int64_t ldy, int32_t out_dtype, void* stream);
+
+/* Bytes of the library-owned scratch sharq_linear_grouped_noalloc uses on each GPU. */
+size_t sharq_noalloc_scratch_bytes(void);
 
 #ifdef __cplusplus
 }

@@ -213,6 +213,15 @@ def test_grouped_rejects_before_launch(lib):
     assert call(64, 8, ri=C.c_void_p(0x800000)) == _lib.ERR_UNSUPPORTED        # source codes past 2 GiB
     a.M = 64
     assert call(0, 8, ri=C.c_void_p(0x800000)) == _lib.OK        # nothing routed: no launch
+    # the allocation-free form: the same checks, and a layer larger than the library's scratch
+    na = lambda rows, E, ri=None, ldy=32: lib.sharq_linear_grouped_noalloc(
+        C.byref(a), ri, rows, seg, E, C.byref(w), y, ldy, 0, None)
+    assert lib.sharq_noalloc_scratch_bytes() == 32 << 20
+    assert na(64, 3) == _lib.ERR_INVALID_ARG
+    assert na(64, 8, ldy=8) == _lib.ERR_INVALID_ARG
+    assert na(1 << 20, 8, ri=C.c_void_p(0x800000)) == _lib.ERR_WORKSPACE
+    assert b"scratch" in lib.sharq_last_error()
+    assert na(0, 8, ri=C.c_void_p(0x800000)) == _lib.OK           # nothing routed: no launch
     a.fmt = w.fmt = 1
     assert call(64, 8) == _lib.ERR_UNSUPPORTED                   # grouped layer is MXFP4 only
     a.fmt = w.fmt = 0
