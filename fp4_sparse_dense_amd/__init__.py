@@ -23,7 +23,7 @@ __all__ = [
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
     "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32", "sharq_linear_residual",
     "sharq_linear_swiglu_prep", "peak_fp4_mfma", "peak_read",
-    "sharq_linear_grouped_noalloc", "noalloc_scratch_bytes",
+    "sharq_linear_grouped_noalloc", "noalloc_scratch_bytes", "check_e2m1",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -245,6 +245,29 @@ def sharq_linear_grouped_noalloc(act: SharqAct, weight: SharqWeight, seg_offsets
                                                 C.byref(weight.desc), _ptr(out), out.stride(0), out_dtype,
                                                 _stream_ptr(stream)), "sharq_linear_grouped_noalloc")
     return out
+
+
+def check_e2m1(x, exps, stream=None):
+    """The kernels' E2M1 converts on device values (include/sharq_check.h):
+    x float32 [S, n] (n % 8 == 0), exps int32 [S] (-127..125).  Returns
+    (enc, pack, dec, unpack): uint32 [S, n/8] code words (value j of a group
+    of eight in nibble j) of x / 2^e converted with the scale inside the
+    convert and of the binary32 x * 2^-e converted with scale 1, and float32
+    [S, n] values of those codes (times 2^e, and plain)."""
+    torch = _torch()
+    if x.dtype != torch.float32 or x.dim() != 2 or not x.is_contiguous() or x.shape[1] % 8:
+        raise ValueError("x must be a contiguous float32 [S, n] tensor with n % 8 == 0")
+    if exps.dtype != torch.int32 or not exps.is_contiguous() or exps.numel() != x.shape[0]:
+        raise ValueError("exps must be a contiguous int32 tensor of S entries")
+    S, n = x.shape
+    enc = torch.empty(S, n // 8, dtype=torch.int32, device=x.device)
+    pack = torch.empty_like(enc)
+    dec = torch.empty_like(x)
+    unpack = torch.empty_like(x)
+    lib = _lib.load()
+    _lib.check(lib.sharq_check_e2m1(_ptr(x), _ptr(exps), n, S, _ptr(enc), _ptr(pack), _ptr(dec), _ptr(unpack),
+                                    _stream_ptr(stream)), "sharq_check_e2m1")
+    return enc, pack, dec, unpack
 
 
 def noalloc_scratch_bytes() -> int:

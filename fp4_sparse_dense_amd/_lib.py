@@ -43,7 +43,7 @@ class ActDesc(C.Structure):
     ]
 
 
-# name -> (restype, argtypes); mirrors include/sharq.h and include/sharq_peak.h
+# name -> (restype, argtypes); mirrors include/sharq.h, sharq_peak.h and sharq_check.h
 PROTOTYPES = {
     "sharq_abi_version": (C.c_int, []),
     "sharq_status_str": (C.c_char_p, [C.c_int]),
@@ -79,6 +79,8 @@ PROTOTYPES = {
     "sharq_peak_fp4_mfma": (C.c_int, [C.c_void_p, C.c_size_t, C.c_int32, C.c_void_p, C.POINTER(C.c_double),
                                       C.c_void_p]),
     "sharq_peak_read": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.POINTER(C.c_double), C.c_void_p]),
+    "sharq_check_e2m1": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_void_p]),
     "sharq_linear_fused": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_float,
                                      C.c_int32, C.c_int32, C.c_int32, C.POINTER(WeightDesc), C.c_void_p,
                                      C.c_int64, C.c_int32, C.c_void_p]),

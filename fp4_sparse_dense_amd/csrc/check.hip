@@ -1,0 +1,90 @@
+// The E2M1 converts of the SharQ kernels on caller-supplied values, used exactly
+// as the preparation (fp4_enc / fp4_dec with the block scale inside the
+// convert), the weight pack (a binary32 product by 2^-e, then fp4_pack2 with
+// scale 1) and the NVFP4-style path (fp4_pack2 / fp4_unpack2 with scale 1) use
+// them, so a test can compare every code and value with the rounding rule.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "sharq_check.h"
+#include "device_common.h"
+#include "prep_common.h"
+
+namespace sharq {
+
+sharq_status record_error(sharq_status s, const char* msg);   // api.hip
+
+__global__ __launch_bounds__(256) void check_e2m1_kernel(const float* __restrict__ x, const int32_t* __restrict__ exps,
+                                                         int64_t n, int64_t groups, uint32_t* __restrict__ enc,
+                                                         uint32_t* __restrict__ pack, float* __restrict__ dec,
+                                                         float* __restrict__ unpack) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;   // group of 8 values
+  if (gi >= groups) return;
+  const int64_t per = n / 8;
+  const int s = (int)(gi / per);
+  const int e = exps[s];
+  const float* xs = x + gi * 8;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = xs[i];
+  // the preparation's way
+  const float sc = pow2(e);
+  uint32_t c = fp4_enc<0>(0u, v[0], v[1], sc);
+  c = fp4_enc<1>(c, v[2], v[3], sc);
+  c = fp4_enc<2>(c, v[4], v[5], sc);
+  c = fp4_enc<3>(c, v[6], v[7], sc);
+  float d[8];
+  fp4_dec<0>(c, sc, d[0], d[1]);
+  fp4_dec<1>(c, sc, d[2], d[3]);
+  fp4_dec<2>(c, sc, d[4], d[5]);
+  fp4_dec<3>(c, sc, d[6], d[7]);
+  // the pack's way
+  const float qs = pow2_neg(e);
+  uint32_t p = fp4_pack2<0>(0u, v[0] * qs, v[1] * qs);
+  p = fp4_pack2<1>(p, v[2] * qs, v[3] * qs);
+  p = fp4_pack2<2>(p, v[4] * qs, v[5] * qs);
+  p = fp4_pack2<3>(p, v[6] * qs, v[7] * qs);
+  float u[8];
+  fp4_unpack2<0>(p, u[0], u[1]);
+  fp4_unpack2<1>(p, u[2], u[3]);
+  fp4_unpack2<2>(p, u[4], u[5]);
+  fp4_unpack2<3>(p, u[6], u[7]);
+  enc[gi] = c;
+  pack[gi] = p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    dec[gi * 8 + i] = d[i];
+    unpack[gi * 8 + i] = u[i];
+  }
+}
+
+}  // namespace sharq
+
+extern "C" {
+
+sharq_status sharq_check_e2m1(const float* x_dev, const int32_t* exps_dev, int64_t n, int32_t n_scales,
+                              uint32_t* enc_dev, uint32_t* pack_dev, float* dec_dev, float* unpack_dev, void* stream) {
+  if (!x_dev || !exps_dev || !enc_dev || !pack_dev || !dec_dev || !unpack_dev)
+    return sharq::record_error(SHARQ_ERR_INVALID_ARG, "null argument");
+  if (n <= 0 || n % 8 || n_scales < 1 || (int64_t)n_scales * n >= ((int64_t)1 << 31))
+    return sharq::record_error(SHARQ_ERR_INVALID_ARG, "n must be a positive multiple of 8, n_scales >= 1, n_scales*n < 2^31");
+  if ((reinterpret_cast<uintptr_t>(x_dev) | reinterpret_cast<uintptr_t>(exps_dev) | reinterpret_cast<uintptr_t>(enc_dev) |
+       reinterpret_cast<uintptr_t>(pack_dev) | reinterpret_cast<uintptr_t>(dec_dev) |
+       reinterpret_cast<uintptr_t>(unpack_dev)) & 3)
+    return sharq::record_error(SHARQ_ERR_INVALID_ARG, "buffers must be 4-byte aligned");
+  int dev = 0;
+  hipDeviceProp_t p;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess)
+    return sharq::record_error(SHARQ_ERR_HIP, "device query failed");
+  if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) return sharq::record_error(SHARQ_ERR_UNSUPPORTED, "not gfx950");
+  const int64_t groups = (int64_t)n_scales * n / 8;
+  hipLaunchKernelGGL(sharq::check_e2m1_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), x_dev, exps_dev, n, groups, enc_dev, pack_dev, dec_dev,
+                     unpack_dev);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return sharq::record_error(SHARQ_ERR_HIP, hipGetErrorString(e));
+  return SHARQ_OK;
+}
+
+}  // extern "C"

@@ -175,8 +175,10 @@ __device__ __forceinline__ float row_inv_rms(const uint16_t* xr, int K, float ep
 // ---------------------------------------------------------------- E2M1
 // Two binary32 values -> two E2M1 nibbles placed in byte SEL of `old`.
 // v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to nearest, ties to even,
-// saturates at 6 and keeps the sign of zero; it was checked equal to that rule
-// on every finite binary32 input.
+// saturates at 6 and keeps the sign of zero: tests/test_gpu_fp4_convert.py
+// checks it against that rule (through sharq_check_e2m1) on every finite bf16
+// value and the 64 binary32 neighbours of every grid point and midpoint, at
+// every power-of-two scale the kernels use.
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4_pack2(uint32_t old, float lo, float hi) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, 1.0f, SEL);

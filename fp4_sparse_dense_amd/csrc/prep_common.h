@@ -79,9 +79,11 @@ __device__ __forceinline__ float abs_max3(float m, float a, float b) {
 
 // Encode two values as E2M1 into byte SEL of `old`, dividing by the power of
 // two `scale` inside the convert, and decode byte SEL of `packed` multiplied
-// by `scale`.  Both were checked exact against the rounding rule (encode:
-// every binary32 in a 2^17 window around each scale, scales 2^-127..2^125;
-// decode: every code byte at the same scales).
+// by `scale`.  tests/test_gpu_fp4_convert.py checks both against the rounding
+// rule and the exact values (through sharq_check_e2m1, which uses them as
+// decompose32 does): every finite bf16 value and the 64 binary32 neighbours
+// of every E2M1 grid point and midpoint times the scale, for every scale
+// 2^-127 .. 2^125.
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4_enc(uint32_t old, float lo, float hi, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, scale, SEL);

@@ -1,0 +1,47 @@
+/*
+ * sharq_check.h -- the FP4 (E2M1) conversions of the SharQ kernels, exposed so
+ * that their rounding can be checked against its definition on the device.
+ *
+ * Every E2M1 code the preparation, the weight pack and the NVFP4-style path
+ * write comes from the hardware converts behind this entry point, used exactly
+ * as those kernels use them; it computes nothing the layer needs.
+ * Conventions as in sharq.h (device pointers, caller-owned buffers,
+ * asynchronous on `stream`, host-side checks before any launch).
+ */
+#ifndef SHARQ_CHECK_H
+#define SHARQ_CHECK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sharq.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* For scale s (0 <= s < n_scales) with exponent e = exps[s] (-127..125) and
+ * the n values x[s][0..n) (binary32, n a multiple of 8), in groups of eight
+ * consecutive values packed into one 32-bit word (value 2i in nibble 2i mod 8,
+ * the lower value of a pair in the low nibble):
+ *   enc[s][i]   = the codes of x / 2^e, converted with the scale 2^e inside
+ *                 the convert (the preparation's way: SharQ abstract, backbone
+ *                 and residual quantised to FP4 with an MX block scale);
+ *   pack[s][i]  = the codes of the binary32 product x * 2^-e converted with
+ *                 scale 1 (the weight pack's way, and the NVFP4-style path's);
+ *   dec[s][j]   = the value of code j of enc[s] times 2^e (the residual's
+ *                 dequantisation);
+ *   unpack[s][j] = the value of code j of pack[s] (scale 1).
+ * x_dev: float[n_scales][n]; exps_dev: int32[n_scales]; enc_dev, pack_dev:
+ * uint32[n_scales][n/8]; dec_dev, unpack_dev: float[n_scales][n].
+ * Errors: INVALID_ARG (null, n <= 0 or n % 8, n_scales < 1, n_scales * n >=
+ * 2^31, misaligned), UNSUPPORTED (not gfx950), HIP.  Exponents outside
+ * -127..125 give unspecified results. */
+sharq_status sharq_check_e2m1(const float* x_dev, const int32_t* exps_dev, int64_t n, int32_t n_scales,
+                              uint32_t* enc_dev, uint32_t* pack_dev, float* dec_dev, float* unpack_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHARQ_CHECK_H */
