@@ -52,10 +52,11 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_splitk(GemmArgs g) {
   for (int r = 0; r < RBG; ++r) acs[r] = acr[r] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   // K tiles in chunks of CH per wave, all loads of a chunk issued before its
-  // MFMAs.  Indices are clamped into range: a tile past K gets a zero weight
-  // fragment (it adds exactly zero) and a row block past the padding only feeds
-  // output rows that are never stored.
-  constexpr int CH = (RBG == 1 ? 8 : (RBG == 2 ? 4 : 2)) * 4 / NW;
+  // MFMAs (K = 4096 with eight waves: every K tile of a wave in one chunk, one
+  // memory round trip).  Indices are clamped into range: a tile past K gets a
+  // zero weight fragment (it adds exactly zero) and a row block past the
+  // padding only feeds output rows that are never stored.
+  constexpr int CH = 32 / NW;
   for (int base = 0; base < KT; base += NW * CH) {
     v8i b[CH], as[CH][RBG], ar[CH][RBG];
     uint32_t sw[CH], ss[CH][RBG], sr[CH][RBG];
@@ -809,18 +810,19 @@ static hipError_t launch_linear_t(const GemmArgs& a, hipStream_t stream) {
     b.xcd_bm = xcd_region_m(tm, tn_wide, kTileM, kTileN);
     return launch_tiled<kTileM, kTileN, 4, 2, 3, false, DENSE>(b, tm * tn_wide, stream);
   }
-  // M <= 64 (or operands past 31-bit buffer offsets): split-K weight streaming;
-  // eight waves per column block for one or two row blocks, four for more
   const int64_t RB = (a.M + 15) / 16, NB = (a.N + 15) / 16;
   if (NB > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // M <= 64 (or operands past 31-bit buffer offsets): split-K weight streaming,
+  // eight waves per 16 weight columns and per one or two 16-row blocks, so M =
+  // 64 runs 2 x 256 workgroups of two row blocks each (with one workgroup of
+  // four row blocks per column block: 10.4 -> 8.7 us), and a wave issues all
+  // its K tiles of a K = 4096 row in one chunk (M = 32: 6.8 -> 6.4 us)
   if (RB == 1) {
     hipLaunchKernelGGL((dual_gemm_splitk<1, 8, DENSE>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
-  } else if (RB == 2) {
-    hipLaunchKernelGGL((dual_gemm_splitk<2, 8, DENSE>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
   } else {
-    const int64_t groups = (RB + 3) / 4;
+    const int64_t groups = (RB + 1) / 2;
     if (groups > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dual_gemm_splitk<4, 4, DENSE>), dim3((unsigned)NB, (unsigned)groups), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((dual_gemm_splitk<2, 8, DENSE>), dim3((unsigned)NB, (unsigned)groups), dim3(512), 0, stream, a);
   }
   return hipGetLastError();
 }
