@@ -408,7 +408,8 @@ def sharq_linear_swiglu_prep(act: SharqAct, weight: SharqWeight, out: SharqAct |
 def peak_fp4_mfma(operands, iters: int, sink, stream=None) -> float:
     """Launch the FP4 MFMA rate measurement (include/sharq_peak.h) on `stream`;
     returns the flops the launch executes.  operands: device uint8 tensor of
-    >= 4096 random bytes; sink: device float32 tensor of >= 1 element."""
+    >= 6144 bytes (0..4095 the first operands, 4096..6143 the second); sink:
+    device float32 tensor of >= 1 element."""
     lib = _lib.load()
     flops = C.c_double()
     _lib.check(lib.sharq_peak_fp4_mfma(_ptr(operands), operands.numel(), iters, _ptr(sink), C.byref(flops),

@@ -628,8 +628,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
     }
   }
   // A single problem's tile goes out this way when it lies wholly inside Y
-  // with 16-byte-aligned rows, in two halves of 32 rows per wave; the residual
-  // add and the rounding are those of store_out.
+  // with 16-byte-aligned rows, in rounds of kRB 16-row blocks per wave; the
+  // residual add and the rounding are those of store_out.
   if constexpr (!GROUPED) {
     constexpr int kSt = C::kWNT * 16 + 4;                 // floats per staged row (+4: banks)
     // rounds of kRB 16-row blocks per wave: two where 32 rows fit the ring, else one

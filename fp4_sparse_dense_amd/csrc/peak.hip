@@ -18,16 +18,17 @@ constexpr int kPeakGroupsPerCu = 4;    // 16 waves per compute unit
 __global__ __launch_bounds__(kPeakWaves * 64) void peak_fp4_kernel(const uint8_t* __restrict__ ops, int iters,
                                                                    float* sink) {
   const int lane = threadIdx.x & 63;
-  // four A and two B operands of 16 bytes per lane from the 4 KiB of bytes
+  // four A operands (bytes 0 .. 4095) and two B operands (4096 .. 6143),
+  // 16 bytes per lane each
   v8i a[4], b[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 q = *reinterpret_cast<const uint4*>(ops + (size_t)(i * 64 + lane) * 16 % 4096);
+    const uint4 q = *reinterpret_cast<const uint4*>(ops + (size_t)(i * 64 + lane) * 16);
     a[i] = (v8i){(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const uint4 q = *reinterpret_cast<const uint4*>(ops + (size_t)((4 + i) * 64 + lane) * 16 % 4096);
+    const uint4 q = *reinterpret_cast<const uint4*>(ops + (size_t)((4 + i) * 64 + lane) * 16);
     b[i] = (v8i){(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
   }
   const uint32_t sa = 120u + ops[lane] % 15u, sb = 120u + ops[64 - 1 - lane] % 15u;
@@ -105,8 +106,8 @@ extern "C" {
 sharq_status sharq_peak_fp4_mfma(const void* operands_dev, size_t operand_bytes, int32_t iters, float* sink_dev,
                                  double* flops_out, void* stream) {
   if (!operands_dev || !sink_dev || !flops_out) return peak_fail(SHARQ_ERR_INVALID_ARG, "null argument");
-  if (operand_bytes < 4096 || (reinterpret_cast<uintptr_t>(operands_dev) & 15))
-    return peak_fail(SHARQ_ERR_INVALID_ARG, "operands must be >= 4096 bytes, 16-byte aligned");
+  if (operand_bytes < 6144 || (reinterpret_cast<uintptr_t>(operands_dev) & 15))
+    return peak_fail(SHARQ_ERR_INVALID_ARG, "operands must be >= 6144 bytes, 16-byte aligned");
   if (iters < 1 || iters > (1 << 20)) return peak_fail(SHARQ_ERR_INVALID_ARG, "iters out of range");
   int cus = 0;
   sharq_status st = peak_device(&cus);

@@ -26,10 +26,14 @@ extern "C" {
 /* Back-to-back block-scaled FP4 MFMAs (v_mfma_scale_f32_16x16x128_f8f6f4,
  * both operands E2M1, E8M0 scales), eight independent accumulators per
  * wave, sixteen waves per compute unit, on operand bytes the caller supplies
- * (random bytes give the data-dependent power draw of real work).
- *   operands_dev: device, >= 4096 bytes, 16-byte aligned: E2M1 operand bytes;
- *                 its first 64 bytes also give the scale bytes (clamped to
- *                 E8M0 120..134);
+ * (the chip is power-limited, so the rate depends on the data: random bytes
+ * give the draw of a dense operand, bytes with two zero codes in every four
+ * that of a 2:4 backbone).
+ *   operands_dev: device, >= 6144 bytes, 16-byte aligned: E2M1 operand bytes,
+ *                 bytes 0..4095 the four first operands (1 KiB each, 16 bytes
+ *                 per lane), 4096..6143 the two second operands; its first
+ *                 64 bytes also give the scale bytes (clamped to E8M0
+ *                 120..134);
  *   iters:        loop trips per wave (1 .. 1<<20), eight MFMAs each;
  *   sink_dev:     device float[1], written only if the accumulators happen to
  *                 sum to an impossible sentinel (keeps the work alive);

@@ -336,11 +336,11 @@ def test_peak_entry_points_reject_bad_arguments(lib):
     """The measurement entry points check their arguments on the host."""
     d = C.c_double()
     buf = C.c_void_p(0x1000)
-    assert lib.sharq_peak_fp4_mfma(None, 4096, 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
-    assert lib.sharq_peak_fp4_mfma(buf, 1024, 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
-    assert lib.sharq_peak_fp4_mfma(C.c_void_p(0x1004), 4096, 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
-    assert lib.sharq_peak_fp4_mfma(buf, 4096, 0, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
-    assert lib.sharq_peak_fp4_mfma(buf, 4096, (1 << 20) + 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_fp4_mfma(None, 6144, 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_fp4_mfma(buf, 6128, 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_fp4_mfma(C.c_void_p(0x1004), 6144, 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_fp4_mfma(buf, 6144, 0, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_peak_fp4_mfma(buf, 6144, (1 << 20) + 1, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
     assert b"iters" in lib.sharq_last_error()
     assert lib.sharq_peak_read(buf, (1 << 20) - 16, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
     assert lib.sharq_peak_read(buf, (1 << 20) + 8, buf, C.byref(d), None) == _lib.ERR_INVALID_ARG
