@@ -384,6 +384,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < C::kWNT; ++j) acc[i][j] = mfma_yt(fs[i], fb[j], acc[i][j], ss[i], sw[j]);
     __builtin_amdgcn_sched_barrier(0);
+    // the residual fragments of step ks were read from its slot at the end of
+    // the previous step: those reads must be complete before the barrier
+    // after which the slot is refilled (long done by now: no wait in practice)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
     const uint32_t cst = lds0 + stage_off(ks);   // slot of step ks, free after the barrier
     const uint8_t* nx = smem + stage_off(ks + 1);
@@ -431,6 +435,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < C::kWMT; ++i) acc[i][j] = mfma_yt(fr[i], fb[j], acc[i][j], sr[i], sw[j]);
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // every read of step ks's slot is complete
     __syncthreads();
     const uint32_t cst = lds0 + stage_off(ks);
     const uint8_t* nx = smem + stage_off(ks + 1);
