@@ -75,6 +75,47 @@ def test_nv_pack_weight(N, K):
     assert np.array_equal(codes, rc)
 
 
+def tie_tensor(rng, rows, K, k=-12):
+    """bf16 bits of a tensor whose every 16-block quotient u / (s g) is an E2M1
+    decision point (0.25, 0.75, ... 5: exact ties) or grid value: the tensor
+    maximum 2688 * 2^k makes g = 2^k, each block's maximum 6 * s0 * 2^k makes
+    its E4M3 scale s0, and its other elements are m * s0 * 2^k with random
+    signs (at most 7 significant bits: exact in bf16)."""
+    e4m3 = [0.5, 0.625, 0.75, 1.0, 1.125, 1.5, 2.0, 3.5, 7.0, 12.0, 40.0, 448.0]
+    ms = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 3.0, 4.0]
+    v = np.zeros((rows, K))
+    for r in range(rows):
+        for b in range(K // 16):
+            s0 = 448.0 if (r, b) == (0, 0) else e4m3[rng.integers(len(e4m3) - 1)]
+            t = s0 * 2.0 ** k
+            blk = rng.choice(ms, 16) * t * rng.choice([-1.0, 1.0], 16)
+            blk[rng.integers(16)] = 6.0 * t * rng.choice([-1.0, 1.0])
+            v[r, 16 * b:16 * b + 16] = blk
+    v[0, 0] = 2688.0 * 2.0 ** k
+    return synth.bf16_bits_from_f32(v.astype(np.float32))
+
+
+def test_nv_exact_quotient_ties():
+    """Block quotients exactly on the E2M1 decision points (ties to the even
+    code) for the backbone and the weight, every block; the residual's
+    quotients follow from them."""
+    import torch
+    print("nv ties", flush=True)
+    rng = np.random.default_rng(11)
+    x = tie_tensor(rng, 16, 512)
+    ref = O.prepare_nv(x, None)
+    assert ref["g_s"] == np.float32(2.0 ** -12)
+    check_prep(run_prep(x, None), ref, 16, 512, "ties")
+    w = tie_tensor(rng, 48, 256)
+    wt = sq.sharq_pack_weight(dev_bf16(w), fmt=NV)
+    torch.cuda.synchronize()
+    codes, scales, g = untile_weight_nv(wt.codes.cpu().numpy(), wt.scales.cpu().numpy(), 48, 256)
+    rc, rs, rg = O.pack_weight_nv(w)
+    assert g == rg == np.float32(2.0 ** -12)
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(codes, rc)
+
+
 def nv_layer(x, gamma, w, out_dtype=sq.OUT_F32):
     import torch
     act = sq.sharq_prepare(dev_bf16(x), dev_bf16(gamma) if gamma is not None else None, 1e-5, fmt=NV)
