@@ -27,29 +27,33 @@ namespace sharq {
 
 // ---------------------------------------------------------------------------
 // Small-M kernel (decode, M <= 64): the weight is streamed once and the work
-// is HBM-bound on it.  One workgroup per 16-column block of W (and per group
-// of RBG 16-row blocks); its NW waves split K (wave w takes K tiles w, w+NW,
-// ...) and read their fragments straight from global memory -- in the tiled
-// layout a fragment is 64 lanes x 16 contiguous bytes, so each read is one
-// contiguous KiB.  The NW partial
-// sums meet in LDS and are added in wave order.  Both paths read the weight
-// scales through one load: the API admits only views of one scale array.
+// is HBM-bound on it.  One workgroup per CBG 16-column blocks of W and RBG
+// 16-row blocks; its NW waves split K (wave w takes K tiles w, w+NW, ...) and
+// read their fragments straight from global memory -- in the tiled layout a
+// fragment is 64 lanes x 16 contiguous bytes, so each read is one contiguous
+// KiB.  With MASK, lanes of rows past M load no codes (zeros instead).  The
+// NW partial sums meet in LDS and are added in wave order.  Both paths read
+// the weight scales through one load: the API admits only views of one scale
+// array.
 // ---------------------------------------------------------------------------
-template <int RBG, int NW, bool DENSE>
+template <int RBG, int NW, bool DENSE, int CBG = 1, bool MASK = false>
 __global__ __launch_bounds__(64 * NW) void dual_gemm_splitk(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1);
   const int64_t RB = (g.M + 15) / 16;
+  const int64_t NBt = (g.N + 15) / 16;
   const int KT = (g.K + 127) / 128;
-  const int64_t nb = blockIdx.x;                      // 16-column block
+  const int64_t nb0 = (int64_t)blockIdx.x * CBG;      // first 16-column block
   const int64_t rb0 = (int64_t)blockIdx.y * RBG;      // first 16-row block
   const int r16 = lane & 15, c4 = lane >> 4;
 
   // one accumulator per path (shorter dependent MFMA chains); Y_S + Y_R is
   // formed once, before the cross-wave sum
-  v4f acs[RBG], acr[RBG];
+  v4f acs[CBG][RBG], acr[CBG][RBG];
 #pragma unroll
-  for (int r = 0; r < RBG; ++r) acs[r] = acr[r] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < CBG; ++n)
+#pragma unroll
+    for (int r = 0; r < RBG; ++r) acs[n][r] = acr[n][r] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   // K tiles in chunks of CH per wave, all loads of a chunk issued before its
   // MFMAs (K = 4096 with eight waves: every K tile of a wave in one chunk, one
@@ -58,25 +62,32 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_splitk(GemmArgs g) {
   // padding only feeds output rows that are never stored.
   constexpr int CH = 32 / NW;
   for (int base = 0; base < KT; base += NW * CH) {
-    v8i b[CH], as[CH][RBG], ar[CH][RBG];
-    uint32_t sw[CH], ss[CH][RBG], sr[CH][RBG];
+    v8i b[CH][CBG], as[CH][RBG], ar[CH][RBG];
+    uint32_t sw[CH][CBG], ss[CH][RBG], sr[CH][RBG];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int kt = base + wave + NW * c;
       const int ktc = kt < KT ? kt : KT - 1;
-      uint4 wq = *reinterpret_cast<const uint4*>(g.w_codes + (nb * KT + ktc) * 1024 + lane * 16);
-      if (kt >= KT) wq = make_uint4(0, 0, 0, 0);
-      b[c] = as_operand(wq);
-      sw[c] = g.w_scales_dense[(int64_t)ktc * g.w_scales_ld + nb * 64 + lane];   // both views (one array)
+#pragma unroll
+      for (int n = 0; n < CBG; ++n) {
+        const int64_t nb = nb0 + n < NBt ? nb0 + n : NBt - 1;   // past N: only feeds columns never stored
+        uint4 wq = *reinterpret_cast<const uint4*>(g.w_codes + (nb * KT + ktc) * 1024 + lane * 16);
+        if (kt >= KT) wq = make_uint4(0, 0, 0, 0);
+        b[c][n] = as_operand(wq);
+        sw[c][n] = g.w_scales_dense[(int64_t)ktc * g.w_scales_ld + nb * 64 + lane];   // both views (one array)
+      }
 #pragma unroll
       for (int r = 0; r < RBG; ++r) {
         const int64_t rb = rb0 + r < RB ? rb0 + r : RB - 1;
         const int64_t tile = rb * KT + ktc;
-        const uint4 rq = *reinterpret_cast<const uint4*>(g.r_codes + tile * 1024 + lane * 16);
+        const bool live = !MASK || (rb * 16 + r16 < g.M);
+        uint4 rq = make_uint4(0, 0, 0, 0);
+        if (live) rq = *reinterpret_cast<const uint4*>(g.r_codes + tile * 1024 + lane * 16);
         sr[c][r] = g.r_scales[((int64_t)ktc * RB + rb) * 64 + lane];
         ar[c][r] = as_operand(rq);
         if constexpr (!DENSE) {
-          const uint4 sq = *reinterpret_cast<const uint4*>(g.s_codes + tile * 1024 + lane * 16);
+          uint4 sq = make_uint4(0, 0, 0, 0);
+          if (live) sq = *reinterpret_cast<const uint4*>(g.s_codes + tile * 1024 + lane * 16);
           ss[c][r] = g.s_scales[((int64_t)ktc * RB + rb) * 64 + lane];
           as[c][r] = as_operand(sq);
         }
@@ -85,24 +96,31 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_splitk(GemmArgs g) {
 #pragma unroll
     for (int c = 0; c < CH; ++c)
 #pragma unroll
-      for (int r = 0; r < RBG; ++r) {
-        if constexpr (!DENSE) acs[r] = mfma_fp4(as[c][r], b[c], acs[r], ss[c][r], sw[c]);
-        acr[r] = mfma_fp4(ar[c][r], b[c], acr[r], sr[c][r], sw[c]);
-      }
+      for (int n = 0; n < CBG; ++n)
+#pragma unroll
+        for (int r = 0; r < RBG; ++r) {
+          if constexpr (!DENSE) acs[n][r] = mfma_fp4(as[c][r], b[c][n], acs[n][r], ss[c][r], sw[c][n]);
+          acr[n][r] = mfma_fp4(ar[c][r], b[c][n], acr[n][r], sr[c][r], sw[c][n]);
+        }
   }
 
   // partial sums of the waves, added in wave order; one store of Y_S + Y_R
-  __shared__ v4f part[NW][RBG][64];
+  // (column block n of the group by wave n mod NW)
+  __shared__ v4f part[NW][CBG][RBG][64];
 #pragma unroll
-  for (int r = 0; r < RBG; ++r) part[wave][r][lane] = acs[r] + acr[r];
+  for (int n = 0; n < CBG; ++n)
+#pragma unroll
+    for (int r = 0; r < RBG; ++r) part[wave][n][r][lane] = acs[n][r] + acr[n][r];
   __syncthreads();
-  if (wave == 0) {
-    const int64_t col = nb * 16 + r16;
+#pragma unroll
+  for (int n = 0; n < CBG; ++n) {
+    if (wave != n % NW) continue;
+    const int64_t col = (nb0 + n) * 16 + r16;
 #pragma unroll
     for (int r = 0; r < RBG; ++r) {
-      v4f v = part[0][r][lane];
+      v4f v = part[0][n][r][lane];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) v = v + part[w][r][lane];
+      for (int w = 1; w < NW; ++w) v = v + part[w][n][r][lane];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = (rb0 + r) * 16 + 4 * c4 + q;
@@ -817,17 +835,35 @@ static hipError_t launch_linear_t(const GemmArgs& a, hipStream_t stream) {
   }
   const int64_t RB = (a.M + 15) / 16, NB = (a.N + 15) / 16;
   if (NB > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // M <= 64 (or operands past 31-bit buffer offsets): split-K weight streaming,
-  // eight waves per 16 weight columns and per one or two 16-row blocks, so M =
-  // 64 runs 2 x 256 workgroups of two row blocks each (with one workgroup of
-  // four row blocks per column block: 10.4 -> 8.7 us), and a wave issues all
-  // its K tiles of a K = 4096 row in one chunk (M = 32: 6.8 -> 6.4 us)
-  if (RB == 1) {
-    hipLaunchKernelGGL((dual_gemm_splitk<1, 8, DENSE>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
-  } else {
+  if (a.M > 64) {
+    // operands past 31-bit buffer offsets: two row blocks per workgroup
     const int64_t groups = (RB + 1) / 2;
     if (groups > 65535) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dual_gemm_splitk<2, 8, DENSE>), dim3((unsigned)NB, (unsigned)groups), dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
+  // M <= 64: split-K weight streaming, eight waves per workgroup of one 16-row
+  // block and CBG 16-column blocks, a wave issuing all its K tiles of a K =
+  // 4096 row in one chunk.  The kernel is bound by the bytes each compute unit
+  // pulls (every workgroup re-reads its row block's activation tiles), so CBG
+  // is the largest of 4, 2, 1 that still gives every compute unit a workgroup:
+  // K = N = 4096 at M = 32 runs CBG 2 (6.33 -> 5.50 us against one column
+  // block and two row blocks per workgroup), at M = 64 CBG 4 (8.46 -> 6.66 us).
+  // A partial row block loads only its live rows' codes (the padding rows feed
+  // outputs that are never stored), which halves the activation lines read at
+  // M <= 8 (M = 1: 4.82 -> 4.47 us); full blocks skip the per-lane test.
+  const int cus = compute_units();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const int cbg = (NB + 3) / 4 * RB >= cus ? 4 : (NB + 1) / 2 * RB >= cus ? 2 : 1;
+  const dim3 grid((unsigned)((NB + cbg - 1) / cbg), (unsigned)RB);
+  if (a.M % 16 != 0) {
+    if (cbg == 4) hipLaunchKernelGGL((dual_gemm_splitk<1, 8, DENSE, 4, true>), grid, dim3(512), 0, stream, a);
+    else if (cbg == 2) hipLaunchKernelGGL((dual_gemm_splitk<1, 8, DENSE, 2, true>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((dual_gemm_splitk<1, 8, DENSE, 1, true>), grid, dim3(512), 0, stream, a);
+  } else {
+    if (cbg == 4) hipLaunchKernelGGL((dual_gemm_splitk<1, 8, DENSE, 4>), grid, dim3(512), 0, stream, a);
+    else if (cbg == 2) hipLaunchKernelGGL((dual_gemm_splitk<1, 8, DENSE, 2>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((dual_gemm_splitk<1, 8, DENSE, 1>), grid, dim3(512), 0, stream, a);
   }
   return hipGetLastError();
 }

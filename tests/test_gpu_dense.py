@@ -32,7 +32,7 @@ def check_prep(act, ref, M, K, label):
 
 @pytest.mark.parametrize("M,K,N,norm", [(37, 96, 53, True), (130, 768, 200, False), (5, 1376, 100, False),
                                         (256, 256, 272, True), (1, 4096, 4096, False), (64, 4096, 4096, False),
-                                        (300, 16384, 64, True)])
+                                        (300, 16384, 64, True), (63, 1056, 2025, False), (64, 1056, 4100, True)])
 def test_dense_linear_full(M, K, N, norm):
     print(f"dense M={M} K={K} N={N} norm={norm}", flush=True)
     rng = np.random.default_rng(M * 7 + K + N)

@@ -34,7 +34,8 @@ def test_linear_tiny_full():
 
 @pytest.mark.parametrize("M,K,N,norm", [(37, 96, 53, True), (1, 4096, 4096, False), (130, 768, 200, False),
                                         (64, 4096, 4096, False), (17, 2048, 1536, False), (256, 256, 272, True),
-                                        (5, 1376, 100, False), (3, 14336, 64, False), (49, 640, 48, True)])
+                                        (5, 1376, 100, False), (3, 14336, 64, False), (49, 640, 48, True),
+                                        (63, 1056, 2025, False), (64, 1056, 4100, True)])
 def test_linear_ragged_full(M, K, N, norm):
     print(f"linear M={M} K={K} N={N}", flush=True)
     rng = np.random.default_rng(M + K + N)
