@@ -95,13 +95,14 @@ def test_linear_bf16_output():
     assert_linear_close(yg, yr, b, "bf16 out", extra=half_ulp)
 
 
-def test_linear_deterministic_and_strided_output():
+@pytest.mark.parametrize("M", [256, 48])
+def test_linear_deterministic_and_strided_output(M):
     import torch
-    inp = synth.layer_inputs("qkv", seed=1, M=256)
+    inp = synth.layer_inputs("qkv", seed=1, M=M)
     act = sq.sharq_prepare(dev_bf16(inp["x"]), dev_bf16(inp["gamma"]))
     wt = sq.sharq_pack_weight(dev_bf16(inp["w"]))
     y1 = sq.sharq_linear(act, wt)
-    big = torch.full((256, inp["N"] + 64), 7.0, device="cuda")
+    big = torch.full((M, inp["N"] + 64), 7.0, device="cuda")
     y2 = sq.sharq_linear(act, wt, out=big[:, 32:32 + inp["N"]])
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
@@ -111,10 +112,13 @@ def test_linear_deterministic_and_strided_output():
 @pytest.mark.parametrize("M,K,N", [(512, 512, 384), (512, 1024, 6144), (300, 512, 200), (2048, 256, 4096),
                                    # 256 x 192 tiles (fewer waves of workgroups than 128 x 256 ones): whole
                                    # tiles in rounds of two 16-row blocks, and a ragged last M tile
-                                   (2048, 512, 6144), (2000, 256, 6144)])
+                                   (2048, 512, 6144), (2000, 256, 6144),
+                                   # split-K (M <= 64): one, two and four column blocks per workgroup
+                                   (1, 4096, 4096), (32, 1024, 4096), (63, 1056, 2025), (64, 512, 4100)])
 def test_linear_tiled_bf16_equals_rounded_fp32(M, K, N):
-    """The tiled kernel's bf16 output (staged through LDS for whole tiles,
-    element-wise at ragged edges) is its fp32 output rounded to nearest even."""
+    """The bf16 output (tiled kernel: staged through LDS for whole tiles,
+    element-wise at ragged edges; split-K kernel: element-wise) is the fp32
+    output rounded to nearest even."""
     import torch
     print(f"tiled bf16 M={M} K={K} N={N}", flush=True)
     rng = np.random.default_rng(M + K + N + 7)

@@ -28,7 +28,11 @@ def _layer(M, K, N, norm, n=2, seed=0):
                                           (300, 2048, 1536, True, 2), (2048, 4096, 4096, False, 2),
                                           (257, 512, 384, True, 0),
                                           # 256 x 192 tiles: whole and ragged M tiles
-                                          (2048, 256, 6144, False, 2), (2000, 512, 6144, True, 2)])
+                                          (2048, 256, 6144, False, 2), (2000, 512, 6144, True, 2),
+                                          # split-K (M <= 64): one, two and four column blocks per
+                                          # workgroup, partial row blocks
+                                          (1, 4096, 4096, False, 2), (32, 1024, 4096, False, 2),
+                                          (63, 1056, 2025, True, 2), (64, 512, 4100, False, 2)])
 def test_residual_layer_equals_two_calls(M, K, N, norm, n):
     import torch
     print(f"residual M={M} K={K} N={N} n={n}", flush=True)
