@@ -2,7 +2,7 @@
 //
 // SharQ paper page (mlsanity), Abstract: a sparse FP4 GEMM processes the
 // backbone, a dense FP4 GEMM compensates with the residual, both read one FP4
-// weight payload through path-specific scale views.  README page, section
+// weight payload, each through its own view of the scales.  README page, section
 // "Benchmarks": an epilogue fusion sums the two paths.
 //
 // gfx950 has block-scaled FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) but no

@@ -1,6 +1,6 @@
 // Fused SharQ preparation and weight packing for gfx950.
 //
-// SharQ paper page (mlsanity), Abstract: one preparation operator absorbs the
+// SharQ paper page (mlsanity), Abstract: one preparation operator computes the
 // normalisation, the input-adaptive N:M mask that extracts the sparse
 // backbone, the FP4 quantisation of that backbone, and the residual taken
 // against the *quantised* backbone; the residual is then quantised for the

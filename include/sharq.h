@@ -91,8 +91,8 @@ typedef enum { SHARQ_FMT_MXFP4 = 0, SHARQ_FMT_NVFP4 = 1, SHARQ_FMT_HIF4 = 2 } sh
 
 typedef enum { SHARQ_OUT_F32 = 0, SHARQ_OUT_BF16 = 1 } sharq_out_dtype;
 
-/* Which GEMM path a weight scale view serves (SharQ abstract: the two paths
- * share one FP4 weight payload through path-specific scale views). */
+/* Which GEMM path a weight scale view serves (SharQ paper page, Abstract:
+ * both paths read one FP4 weight payload, each through its own scale view). */
 typedef enum { SHARQ_PATH_SPARSE = 0, SHARQ_PATH_DENSE = 1 } sharq_path;
 
 /* A scale view: how one GEMM path reads the weight's block scales.
@@ -202,8 +202,8 @@ sharq_status sharq_pack_weight(const void* w_bf16_dev, int64_t N, int64_t K, int
  * positions; S's tensor scale from max|S|, R's from max|R|, so R's depends
  * on Q(S)); deq(Q(S)) = (val * s) * g in binary32.  This runs as three
  * dependent launches on `stream` (row statistics, backbone, residual).
- * SharQ abstract: one fused operator absorbs mask generation, residual
- * construction and the normalisation; the residual is relative to the
+ * SharQ paper page, Abstract: the normalisation, the mask and the residual
+ * come out of one fused operator; the residual is taken against the
  * quantised backbone.
  * `out` must have struct_size set and the five buffers allocated per
  * sharq_act_bytes; M, K, n, m, fmt are filled in.  M == 0 launches nothing.

@@ -95,8 +95,8 @@ def rmsnorm(x_bits, gamma_bits, eps: float) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# N:M input-adaptive mask  (SharQ abstract: an input-dependent N:M mask keeps
-# the outlier-dominated entries as the sparse backbone)
+# N:M input-adaptive mask  (SharQ paper page, Abstract: a mask chosen per input
+# keeps the largest-magnitude entries, the outliers, as the sparse backbone)
 # --------------------------------------------------------------------------
 def nm_mask(v: np.ndarray, n: int = 2, m: int = 4) -> np.ndarray:
     """Boolean keep-mask: in each aligned group of m along the last axis keep n.
