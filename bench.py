@@ -7,7 +7,7 @@ fused QKV projection (M=2048 tokens, K=4096, N=6144, RMSNorm).  Other
 workloads (``--workload``): gateup (N=28672, RMSNorm), down (K=14336, N=4096,
 SiLU-product inputs, no norm), decode (``--m`` in 1, 8, 32, 64; K=N=4096, no
 norm; ``--fmt nvfp4`` runs it in the NVFP4-style format: E4M3 scale per 16,
-binary32 tensor scales, bf16 MFMA on exactly expanded codes) and moe (Qwen3-30B-A3B-shaped expert layer: 4096 tokens routed top-8 of
+binary32 tensor scales, fp16 MFMA on exactly expanded codes) and moe (Qwen3-30B-A3B-shaped expert layer: 4096 tokens routed top-8 of
 128 experts with Zipf(1.1) loads; step = prep of the tokens + grouped gate/up
 (K=2048, N_e=1536) + prep of the 32768 expert-sorted down rows + grouped down
 (K=768, N_e=2048)).  ``--mode dense`` times the plain MXFP4 linear instead
@@ -48,7 +48,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (the NVFP4-style GEMM's instruction)
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16 / bf16 MFMA (the NVFP4-style GEMM runs the fp16 one)
 WORKLOADS = {
     "qkv": dict(M=2048, K=4096, N=6144, norm=True, law="outlier",
                 desc="Llama-3.1-8B fused QKV projection: M=2048 tokens, K=4096, N=6144; RMSNorm"),
@@ -497,7 +497,7 @@ def run_dense(args):
     pbytes = prep_bytes(M, K, norm, nv=nv, dense=dense)
     playout = prep_layout_bytes(M, K, norm, nv=nv, dense=dense)
     prep_gbs = pbytes / (prep_ms * 1e-3) / 1e9 if prep_ms > 0 else 0.0
-    peak_mfma = PEAK_BF16_TFLOPS if nv else PEAK_FP4_TFLOPS
+    peak_mfma = PEAK_F16_TFLOPS if nv else PEAK_FP4_TFLOPS
     useful = flops if dense else gemm_useful_flops(M, N, K)
     useful_frac = useful / (gemm_ms * 1e-3) / 1e12 / peak_mfma
     # fractions of the peaks measured on this device in the same run (the FP4
@@ -546,7 +546,7 @@ def run_dense(args):
         "config": {"workload": f"{wname}{'-nvfp4' if nv else ''}: " +
                                wl["desc"].split(": ", 1)[1].replace("M rows", f"M={M}") +
                                ("; 2:4 mask; NVFP4-style activations and weight (E4M3 scale per 16, binary32 tensor "
-                                "scales, bf16 MFMA on exactly expanded codes); fp32 output" if nv else
+                                "scales, fp16 MFMA on exactly expanded codes); fp32 output" if nv else
                                 "; no backbone (plain MXFP4 of the row), MXFP4 weight; fp32 output" if dense else
                                 "; 2:4 mask; MXFP4 activations and weight; fp32 output"),
                    "M": M, "K": K, "N": N, "pattern": "0:4" if dense else "2:4",

@@ -767,7 +767,7 @@ constexpr int kGroupedTileM = 128;
 int grouped_tile_m() { return kGroupedTileM; }
 
 // compute units of the current device (cached per device), <= 0 on error
-static int compute_units() {
+int compute_units() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
   static std::atomic<int> cached[64];

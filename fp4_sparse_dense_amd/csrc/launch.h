@@ -162,5 +162,7 @@ hipError_t launch_pack_weight_nv(const uint16_t* w, int64_t N, int K, int64_t ld
                                  uint8_t* scales, hipStream_t stream);
 // GemmArgs with the NVFP4-style tiled scales and g_s / g_r / g_w set
 hipError_t launch_linear_nv(const GemmArgs& a, hipStream_t stream);
+// compute units of the current device (cached per device), <= 0 on error
+int compute_units();
 
 }  // namespace sharq

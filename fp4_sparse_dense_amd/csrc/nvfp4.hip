@@ -16,9 +16,9 @@
 //
 // gfx950's block-scaled MFMA takes E8M0 scales per 32 elements, which cannot
 // carry an E4M3 scale per 16.  The GEMM therefore expands each code to
-// val(code) * s -- at most 6 significant bits, so exact in bf16 -- and runs the
-// bf16 MFMA with one fp32 accumulator per path; the tensor scales enter once,
-// in the epilogue: y = g_S g_W acc_S + g_R g_W acc_R.
+// val(code) * s -- at most 6 significant bits in [2^-10, 2688], so exact in
+// fp16 -- and runs the fp16 MFMA with one fp32 accumulator per path; the
+// tensor scales enter once, in the epilogue: y = g_S g_W acc_S + g_R g_W acc_R.
 #include <atomic>
 
 #include "device_common.h"
@@ -27,7 +27,8 @@
 namespace sharq {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr float kNvTensorDiv = 2688.0f;
@@ -383,44 +384,41 @@ __global__ __launch_bounds__(256) void nv_pack_weight_kernel(NvWeightArgs a) {
 
 // ---------------------------------------------------------------------------
 // Dual GEMM (small M: decode).  As the MXFP4 small-M kernel: one workgroup per
-// 16 weight rows (and per group of RBG 16-row activation blocks), NW waves
-// split K, operands read straight from the tiled layout.  Each lane's 32 codes
-// of a K tile are expanded to val * s in bf16 (exact) and feed four
-// 16x16x32 bf16 MFMAs; MFMA j takes elements [8j, 8j+8) of every lane for
-// both operands, so A and B see the same K order.
+// CBG 16-column blocks of the weight (and per group of RBG 16-row activation
+// blocks), NW waves split K, operands read straight from the tiled layout.
+// Each lane's 32 codes of a K tile are expanded to val * s in fp16 and feed
+// four 16x16x32 fp16 MFMAs; MFMA j takes elements [8j, 8j+8) of every lane
+// for both operands, so A and B see the same K order.  The expansion is
+// exact: val (E2M1) has at most 2 significant bits and s (E4M3) at most 4, so
+// val * s has at most 6 and lies in [2^-10, 2688] or is a signed zero -- all
+// fp16 normals.  The convert yields the fp16 pair of codes and one packed
+// fp16 multiply applies s.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  // upper halves: exact, the low 16 bits of val * s are zero
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
 template <int SEL>
-__device__ __forceinline__ uint32_t deq_pair(uint32_t codes, float s) {
-  float lo, hi;
-  fp4_unpack2<SEL>(codes, lo, hi);
-  return bf16_pair(lo * s, hi * s);
+__device__ __forceinline__ f16x2 deq_pair(uint32_t codes, f16x2 s) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, SEL) * s;
 }
 
-__device__ __forceinline__ bf16x8 deq8(uint32_t codes, float s) {
-  u32x4v r;
-  r[0] = deq_pair<0>(codes, s);
-  r[1] = deq_pair<1>(codes, s);
-  r[2] = deq_pair<2>(codes, s);
-  r[3] = deq_pair<3>(codes, s);
-  return __builtin_bit_cast(bf16x8, r);
+__device__ __forceinline__ f16x8 deq8(uint32_t codes, f16x2 s) {
+  const f16x2 p0 = deq_pair<0>(codes, s), p1 = deq_pair<1>(codes, s);
+  const f16x2 p2 = deq_pair<2>(codes, s), p3 = deq_pair<3>(codes, s);
+  const auto lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const auto hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // 32 codes (uint4) + two E4M3 bytes -> four MFMA operands
-__device__ __forceinline__ void deq32(uint4 q, uint32_t sb, bf16x8 (&o)[4]) {
-  const float s0 = e4m3_value(sb & 0xFFu), s1 = e4m3_value((sb >> 8) & 0xFFu);
+__device__ __forceinline__ void deq32(uint4 q, uint32_t sb, f16x8 (&o)[4]) {
+  const _Float16 h0 = (_Float16)e4m3_value(sb & 0xFFu), h1 = (_Float16)e4m3_value((sb >> 8) & 0xFFu);
+  const f16x2 s0 = {h0, h0}, s1 = {h1, h1};
   o[0] = deq8(q.x, s0);
   o[1] = deq8(q.y, s0);
   o[2] = deq8(q.z, s1);
   o[3] = deq8(q.w, s1);
 }
 
-__device__ __forceinline__ v4f mfma_bf16(bf16x8 a, bf16x8 b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ v4f mfma_f16(f16x8 a, f16x8 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ void store_y(const GemmArgs& g, int64_t row, int64_t col, float v) {
@@ -433,31 +431,37 @@ __device__ __forceinline__ void store_y(const GemmArgs& g, int64_t row, int64_t 
   }
 }
 
-template <int RBG, int NW>
+template <int RBG, int NW, int CBG = 1>
 __global__ __launch_bounds__(64 * NW) void nv_dual_gemm_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1);
   const int64_t RB = g.a_blocks, NB = (g.N + 15) / 16;
   const int KT = (g.K + 127) / 128;
-  const int64_t nb = blockIdx.x;
+  const int64_t nb0 = (int64_t)blockIdx.x * CBG;
   const int64_t rb0 = (int64_t)blockIdx.y * RBG;
 
-  v4f acs[RBG], acr[RBG];
+  v4f acs[CBG][RBG], acr[CBG][RBG];
 #pragma unroll
-  for (int r = 0; r < RBG; ++r) acs[r] = acr[r] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < CBG; ++n)
+#pragma unroll
+    for (int r = 0; r < RBG; ++r) acs[n][r] = acr[n][r] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   constexpr int CH = (RBG == 1 ? 8 : (RBG == 2 ? 4 : 2)) * 4 / NW;
   for (int base = 0; base < KT; base += NW * CH) {
-    uint4 wq[CH], rq[CH][RBG], sq[CH][RBG];
-    uint32_t wsb[CH], ssb[CH][RBG], rsb[CH][RBG];
+    uint4 wq[CH][CBG], rq[CH][RBG], sq[CH][RBG];
+    uint32_t wsb[CH][CBG], ssb[CH][RBG], rsb[CH][RBG];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       // clamped tile index; a tile past K gets a zero weight fragment
       const int kt = base + wave + NW * c;
       const int ktc = kt < KT ? kt : KT - 1;
-      wq[c] = *reinterpret_cast<const uint4*>(g.w_codes + (nb * KT + ktc) * 1024 + lane * 16);
-      wsb[c] = *reinterpret_cast<const uint16_t*>(g.w_scales_dense + ((int64_t)ktc * NB + nb) * 128 + 2 * lane);
-      if (kt >= KT) { wq[c] = make_uint4(0, 0, 0, 0); wsb[c] = 0u; }
+#pragma unroll
+      for (int n = 0; n < CBG; ++n) {
+        const int64_t nb = nb0 + n < NB ? nb0 + n : NB - 1;   // past N: only feeds columns never stored
+        wq[c][n] = *reinterpret_cast<const uint4*>(g.w_codes + (nb * KT + ktc) * 1024 + lane * 16);
+        wsb[c][n] = *reinterpret_cast<const uint16_t*>(g.w_scales_dense + ((int64_t)ktc * NB + nb) * 128 + 2 * lane);
+        if (kt >= KT) { wq[c][n] = make_uint4(0, 0, 0, 0); wsb[c][n] = 0u; }
+      }
 #pragma unroll
       for (int r = 0; r < RBG; ++r) {
         const int64_t rb = rb0 + r < RB ? rb0 + r : RB - 1;
@@ -471,40 +475,50 @@ __global__ __launch_bounds__(64 * NW) void nv_dual_gemm_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      bf16x8 b[4];
-      deq32(wq[c], wsb[c], b);
+      f16x8 b[CBG][4];
+#pragma unroll
+      for (int n = 0; n < CBG; ++n) deq32(wq[c][n], wsb[c][n], b[n]);
 #pragma unroll
       for (int r = 0; r < RBG; ++r) {
-        bf16x8 x[4];
+        f16x8 x[4];
         deq32(sq[c][r], ssb[c][r], x);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acs[r] = mfma_bf16(x[j], b[j], acs[r]);
+        for (int n = 0; n < CBG; ++n)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acs[n][r] = mfma_f16(x[j], b[n][j], acs[n][r]);
         deq32(rq[c][r], rsb[c][r], x);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acr[r] = mfma_bf16(x[j], b[j], acr[r]);
+        for (int n = 0; n < CBG; ++n)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acr[n][r] = mfma_f16(x[j], b[n][j], acr[n][r]);
       }
     }
   }
 
   // tensor scales once per path, then the waves' partial sums in wave order
+  // (column block n of the group by wave n mod NW)
   const float gw = *g.g_w;
   const float fs = *g.g_s * gw, fr = *g.g_r * gw;
-  __shared__ v4f part[NW][RBG][64];
+  __shared__ v4f part[NW][CBG][RBG][64];
 #pragma unroll
-  for (int r = 0; r < RBG; ++r) {
-    v4f p;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) p[q] = fs * acs[r][q] + fr * acr[r][q];
-    part[wave][r][lane] = p;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int64_t col = nb * 16 + (lane & 15);
+  for (int n = 0; n < CBG; ++n)
 #pragma unroll
     for (int r = 0; r < RBG; ++r) {
-      v4f v = part[0][r][lane];
+      v4f p;
 #pragma unroll
-      for (int w = 1; w < NW; ++w) v = v + part[w][r][lane];
+      for (int q = 0; q < 4; ++q) p[q] = fs * acs[n][r][q] + fr * acr[n][r][q];
+      part[wave][n][r][lane] = p;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < CBG; ++n) {
+    if (wave != n % NW) continue;
+    const int64_t col = (nb0 + n) * 16 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < RBG; ++r) {
+      v4f v = part[0][n][r][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v = v + part[w][n][r][lane];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = (rb0 + r) * 16 + 4 * (lane >> 4) + q;
@@ -817,14 +831,14 @@ __global__ __launch_bounds__(kNvFusedThreads) void nv_fused_layer_kernel(NvFused
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      bf16x8 b[4], x[4];
+      f16x8 b[4], x[4];
       deq32(wq[c], wsb[c], b);
       deq32(sq[c], ssb[c], x);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acs = mfma_bf16(x[j], b[j], acs);
+      for (int j = 0; j < 4; ++j) acs = mfma_f16(x[j], b[j], acs);
       deq32(rq[c], rsb[c], x);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acr = mfma_bf16(x[j], b[j], acr);
+      for (int j = 0; j < 4; ++j) acr = mfma_f16(x[j], b[j], acr);
     }
   }
 
@@ -913,15 +927,24 @@ hipError_t launch_pack_weight_nv(const uint16_t* w, int64_t N, int K, int64_t ld
 hipError_t launch_linear_nv(const GemmArgs& a, hipStream_t stream) {
   const int64_t NB = (a.N + 15) / 16, RB = a.a_blocks;
   if (NB > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (RB == 1) {
-    hipLaunchKernelGGL((nv_dual_gemm_kernel<1, 8>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
-  } else if (RB == 2) {
-    hipLaunchKernelGGL((nv_dual_gemm_kernel<2, 8>), dim3((unsigned)NB, 1), dim3(512), 0, stream, a);
-  } else {
+  if (RB > 4) {
+    // past the decode sizes: four row blocks per workgroup
     const int64_t groups = (RB + 3) / 4;
     if (groups > 65535) return hipErrorInvalidValue;
     hipLaunchKernelGGL((nv_dual_gemm_kernel<4, 4>), dim3((unsigned)NB, (unsigned)groups), dim3(256), 0, stream, a);
+    return hipGetLastError();
   }
+  // one row block and CBG 16-column blocks per workgroup, CBG the largest of
+  // 4, 2, 1 that still gives every compute unit a workgroup: each workgroup
+  // expands its row block's codes once for CBG weight blocks (K = N = 4096 at
+  // M = 64: CBG 4)
+  const int cus = compute_units();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const int cbg = (NB + 3) / 4 * RB >= cus ? 4 : (NB + 1) / 2 * RB >= cus ? 2 : 1;
+  const dim3 grid((unsigned)((NB + cbg - 1) / cbg), (unsigned)RB);
+  if (cbg == 4) hipLaunchKernelGGL((nv_dual_gemm_kernel<1, 8, 4>), grid, dim3(512), 0, stream, a);
+  else if (cbg == 2) hipLaunchKernelGGL((nv_dual_gemm_kernel<1, 8, 2>), grid, dim3(512), 0, stream, a);
+  else hipLaunchKernelGGL((nv_dual_gemm_kernel<1, 8, 1>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

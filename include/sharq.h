@@ -224,7 +224,7 @@ sharq_status sharq_prepare(const void* x_bf16_dev, int64_t M, int64_t K, int64_t
  * An activation prepared with pattern 0:4 runs the dense GEMM alone:
  * Y = deq(Q(v)) deq(W)^T (the plain FP4 linear).
  * NVFP4: the E4M3 scales cannot ride the MX MFMA, so each code is expanded
- * on chip to val * s (exact in bf16), the bf16 MFMA accumulates each path in
+ * on chip to val * s (exact in fp16), the fp16 MFMA accumulates each path in
  * fp32, and the epilogue applies the tensor scales:
  * y = g_S g_W acc_S + g_R g_W acc_R.  It is built for small M (decode); a
  * larger M reads the weight once per 64 rows.

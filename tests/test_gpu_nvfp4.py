@@ -126,7 +126,10 @@ def nv_layer(x, gamma, w, out_dtype=sq.OUT_F32):
 
 
 @pytest.mark.parametrize("M,K,N,norm", [(1, 4096, 4096, False), (37, 96, 53, True), (130, 768, 200, False),
-                                        (5, 1376, 100, False), (17, 2048, 272, True), (64, 256, 48, False)])
+                                        (5, 1376, 100, False), (17, 2048, 272, True), (64, 256, 48, False),
+                                        # two and four weight column blocks per workgroup, the last group
+                                        # partly past N
+                                        (63, 1056, 2025, False), (64, 512, 4100, True), (32, 1024, 4096, False)])
 def test_nv_linear_full(M, K, N, norm):
     print(f"nv linear M={M} K={K} N={N}", flush=True)
     rng = np.random.default_rng(M + K + N + 1)
