@@ -23,7 +23,7 @@ __all__ = [
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
     "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32", "sharq_linear_residual",
     "sharq_linear_swiglu_prep", "peak_fp4_mfma", "peak_read",
-    "sharq_linear_grouped_noalloc", "noalloc_scratch_bytes", "check_e2m1",
+    "sharq_linear_grouped_noalloc", "noalloc_scratch_bytes", "check_e2m1", "sharq_linear_grouped_swiglu_prep",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -247,6 +247,40 @@ def sharq_linear_grouped_noalloc(act: SharqAct, weight: SharqWeight, seg_offsets
     return out
 
 
+@_on_stream
+def sharq_linear_grouped_swiglu_prep(act: SharqAct, weight: SharqWeight, seg_offsets, experts: int, row_index=None,
+                                     rows: int | None = None, out: SharqAct | None = None, workspace=None,
+                                     stream=None):
+    """The grouped gate/up layer (each expert's gate and up rows interleaved as
+    interleave_gate_up(..., experts=E) lays them out) whose epilogue prepares
+    H = bf16(SiLU(gate) * up) for the down projection: returns the SharqAct of
+    the routed rows in order, [rows, F] with F = N_e / 2, the same bytes as
+    sharq_prepare of those rows of H.  Feed it to sharq_linear_grouped with
+    row_index=None and the same seg_offsets."""
+    torch = _torch()
+    dev = act.s_codes.device
+    if rows is None:
+        rows = int(row_index.numel()) if row_index is not None else act.M
+    if seg_offsets.dtype != torch.int64 or not seg_offsets.is_contiguous() or seg_offsets.numel() != experts + 1:
+        raise ValueError("seg_offsets must be a contiguous int64 tensor of E+1 entries")
+    if row_index is not None and (row_index.dtype != torch.int32 or not row_index.is_contiguous()):
+        raise ValueError("row_index must be a contiguous int32 tensor")
+    F = weight.N // experts // 2
+    if out is None:
+        out = SharqAct(rows, F, dev)
+    if (out.M, out.K, out.n, out.m, out.fmt) != (rows, F, 2, 4, FMT_MXFP4):
+        raise ValueError("out must be a 2:4 MXFP4 SharqAct of shape [rows, N_e/2]")
+    need = grouped_workspace_bytes(rows, experts, act.K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    _lib.check(lib.sharq_linear_grouped_swiglu_prep(C.byref(act.desc), _ptr(row_index), rows, _ptr(seg_offsets),
+                                                    experts, C.byref(weight.desc), C.byref(out.desc),
+                                                    _ptr(workspace), workspace.numel(), _stream_ptr(stream)),
+               "sharq_linear_grouped_swiglu_prep")
+    return out
+
+
 def check_e2m1(x, exps, stream=None):
     """The kernels' E2M1 converts on device values (include/sharq_check.h):
     x float32 [S, n] (n % 8 == 0), exps int32 [S] (-127..125).  Returns
@@ -364,14 +398,20 @@ def sharq_linear_fused(x, weight: SharqWeight, gamma=None, eps: float = 1e-5, ou
     return out
 
 
-def interleave_gate_up(w_gate, w_up):
+def interleave_gate_up(w_gate, w_up, experts: int = 1):
     """[F, K] gate and up weights -> the [2F, K] stack sharq_linear_swiglu expects
-    (16-row blocks alternating gate, up); pack it with sharq_pack_weight."""
+    (16-row blocks alternating gate, up); pack it with sharq_pack_weight.  With
+    experts=E the inputs are E experts' [F_e, K] weights stacked along rows
+    ([E F_e, K] each) and every expert's rows are interleaved in place (the
+    stack sharq_linear_grouped_swiglu_prep expects)."""
     torch = _torch()
-    F, K = w_gate.shape
-    if F % 16 or tuple(w_up.shape) != (F, K):
-        raise ValueError("gate and up must both be [F, K] with F % 16 == 0")
-    return torch.stack([w_gate.reshape(F // 16, 16, K), w_up.reshape(F // 16, 16, K)], dim=1).reshape(2 * F, K)
+    R, K = w_gate.shape
+    if experts < 1 or R % experts or (R // experts) % 16 or tuple(w_up.shape) != (R, K):
+        raise ValueError("gate and up must both be [E*F_e, K] with F_e % 16 == 0")
+    F = R // experts
+    g = w_gate.reshape(experts, F // 16, 16, K)
+    u = w_up.reshape(experts, F // 16, 16, K)
+    return torch.stack([g, u], dim=2).reshape(2 * R, K)
 
 
 @_on_stream

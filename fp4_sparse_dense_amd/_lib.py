@@ -65,6 +65,9 @@ PROTOTYPES = {
     "sharq_linear_grouped_noalloc": (C.c_int, [C.POINTER(ActDesc), C.c_void_p, C.c_int64, C.c_void_p, C.c_int32,
                                                C.POINTER(WeightDesc), C.c_void_p, C.c_int64, C.c_int32,
                                                C.c_void_p]),
+    "sharq_linear_grouped_swiglu_prep": (C.c_int, [C.POINTER(ActDesc), C.c_void_p, C.c_int64, C.c_void_p,
+                                                   C.c_int32, C.POINTER(WeightDesc), C.POINTER(ActDesc),
+                                                   C.c_void_p, C.c_size_t, C.c_void_p]),
     "sharq_noalloc_scratch_bytes": (C.c_size_t, []),
     "sharq_rmsnorm": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_float,
                                 C.c_void_p, C.c_int64, C.c_void_p]),

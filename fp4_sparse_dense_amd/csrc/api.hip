@@ -542,10 +542,12 @@ namespace {
 
 // The grouped layer behind both entry points: with noalloc the workspace is
 // the library's per-GPU scratch (ws_dev and ws_bytes unused).
+// With `next` (the SwiGLU-prep form) the layer writes the down projection's
+// prepared activation instead of Y (y_dev, ldy and out_dtype unused).
 sharq_status linear_grouped_impl(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
                                  const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w, void* y_dev,
                                  int64_t ldy, int32_t out_dtype, void* ws_dev, size_t ws_bytes, bool noalloc,
-                                 void* stream) {
+                                 sharq_act* next, void* stream) {
   g_err[0] = 0;
   if (!a || !w) return fail(SHARQ_ERR_INVALID_ARG, "null descriptor");
   if (a->struct_size != sizeof(sharq_act) || w->struct_size != sizeof(sharq_weight))
@@ -554,7 +556,7 @@ sharq_status linear_grouped_impl(const sharq_act* a, const int32_t* row_index_de
     return fail(SHARQ_ERR_INVALID_ARG, "descriptor layout_version mismatch (not produced by this library?)");
   if (a->K != w->K) return fail(SHARQ_ERR_INVALID_ARG, "K mismatch: activation %lld, weight %lld", (long long)a->K, (long long)w->K);
   if (a->M < 0 || w->N <= 0 || a->K <= 0 || a->K % 32 || a->K > (1 << 30)) return fail(SHARQ_ERR_INVALID_ARG, "bad shapes");
-  if (out_dtype != SHARQ_OUT_F32 && out_dtype != SHARQ_OUT_BF16) return fail(SHARQ_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
+  if (!next && out_dtype != SHARQ_OUT_F32 && out_dtype != SHARQ_OUT_BF16) return fail(SHARQ_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dtype);
   if (a->n != 2 || a->m != 4) return fail(SHARQ_ERR_UNSUPPORTED, "the grouped layer is built for the 2:4 pattern only");
   if (a->fmt != w->fmt) return fail(SHARQ_ERR_INVALID_ARG, "activation and weight formats differ");
   sharq_status s = check_fmt(a->fmt, false);
@@ -565,12 +567,36 @@ sharq_status linear_grouped_impl(const sharq_act* a, const int32_t* row_index_de
   const int64_t Ne = w->N / E;
   if (rows < 0) return fail(SHARQ_ERR_INVALID_ARG, "rows=%lld", (long long)rows);
   if (!row_index_dev && rows != a->M) return fail(SHARQ_ERR_INVALID_ARG, "without a row index the routed rows are the activation rows (rows=%lld, M=%lld)", (long long)rows, (long long)a->M);
-  if (rows == 0) return SHARQ_OK;
+  const int64_t F = Ne / 2;
+  if (next) {
+    if (next->struct_size != sizeof(sharq_act)) return fail(SHARQ_ERR_INVALID_ARG, "output descriptor struct_size mismatch");
+    if (a->fmt != SHARQ_FMT_MXFP4) return fail(SHARQ_ERR_UNSUPPORTED, "the SwiGLU epilogue is built for the 2:4 MXFP4 layer");
+    if (Ne % 32) return fail(SHARQ_ERR_INVALID_ARG, "each expert's gate/up rows need N_e %% 32 == 0 (pairs of 16-row blocks), got %lld", (long long)Ne);
+    if (F % 128) return fail(SHARQ_ERR_UNSUPPORTED, "preparing H in the epilogue needs N_e/2 %% 128 == 0, got %lld", (long long)F);
+  }
+  if (rows == 0) {
+    if (next) {
+      next->layout_version = SHARQ_ABI_VERSION;
+      next->M = 0;
+      next->K = F;
+      next->n = 2;
+      next->m = 4;
+      next->fmt = SHARQ_FMT_MXFP4;
+    }
+    return SHARQ_OK;
+  }
   if (!seg_offsets_dev || !aligned(seg_offsets_dev, 8)) return fail(SHARQ_ERR_INVALID_ARG, "segment offsets null or misaligned");
   if (row_index_dev && !aligned(row_index_dev, 4)) return fail(SHARQ_ERR_INVALID_ARG, "row index misaligned");
-  if (!y_dev) return fail(SHARQ_ERR_INVALID_ARG, "null output pointer");
-  if (ldy < Ne) return fail(SHARQ_ERR_INVALID_ARG, "ldy=%lld < N_e=%lld", (long long)ldy, (long long)Ne);
-  if (!aligned(y_dev, out_dtype == SHARQ_OUT_F32 ? 4 : 2)) return fail(SHARQ_ERR_INVALID_ARG, "output misaligned");
+  if (next) {
+    if (!next->r_codes || !next->r_scales || !next->s_codes || !next->s_meta || !next->s_scales ||
+        !aligned(next->r_codes, 16) || !aligned(next->r_scales, 16) || !aligned(next->s_codes, 16) ||
+        !aligned(next->s_meta, 16) || !aligned(next->s_scales, 16))
+      return fail(SHARQ_ERR_INVALID_ARG, "output activation buffers not set or not 16-byte aligned");
+  } else {
+    if (!y_dev) return fail(SHARQ_ERR_INVALID_ARG, "null output pointer");
+    if (ldy < Ne) return fail(SHARQ_ERR_INVALID_ARG, "ldy=%lld < N_e=%lld", (long long)ldy, (long long)Ne);
+    if (!aligned(y_dev, out_dtype == SHARQ_OUT_F32 ? 4 : 2)) return fail(SHARQ_ERR_INVALID_ARG, "output misaligned");
+  }
   if (a->M > 0) {
     if (!a->s_codes || !a->s_meta || !a->s_scales || !a->r_codes || !a->r_scales)
       return fail(SHARQ_ERR_INVALID_ARG, "activation buffers not set");
@@ -643,8 +669,17 @@ sharq_status linear_grouped_impl(const sharq_act* a, const int32_t* row_index_de
   ga.rows = rows;
   ga.src_blocks = (a->M + 15) / 16;
   ga.ws = static_cast<uint8_t*>(ws_dev);
+  if (next) g.next = sharq::PrepOut{next->s_codes, next->s_meta, next->s_scales, next->r_codes, next->r_scales};
   hipError_t e = sharq::launch_linear_grouped(ga, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "grouped linear launch");
+  if (next) {
+    next->layout_version = SHARQ_ABI_VERSION;
+    next->M = rows;
+    next->K = F;
+    next->n = 2;
+    next->m = 4;
+    next->fmt = SHARQ_FMT_MXFP4;
+  }
   return SHARQ_OK;
 }
 
@@ -657,14 +692,25 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
                                   void* y_dev, int64_t ldy, int32_t out_dtype,
                                   void* ws_dev, size_t ws_bytes, void* stream) {
   return linear_grouped_impl(a, row_index_dev, rows, seg_offsets_dev, E, w, y_dev, ldy, out_dtype, ws_dev, ws_bytes,
-                             false, stream);
+                             false, nullptr, stream);
+}
+
+sharq_status sharq_linear_grouped_swiglu_prep(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
+                                              const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
+                                              sharq_act* next, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!next) {
+    g_err[0] = 0;
+    return fail(SHARQ_ERR_INVALID_ARG, "null output descriptor");
+  }
+  return linear_grouped_impl(a, row_index_dev, rows, seg_offsets_dev, E, w, nullptr, 0, SHARQ_OUT_BF16, ws_dev,
+                             ws_bytes, false, next, stream);
 }
 
 sharq_status sharq_linear_grouped_noalloc(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
                                           const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
                                           void* y_dev, int64_t ldy, int32_t out_dtype, void* stream) {
   return linear_grouped_impl(a, row_index_dev, rows, seg_offsets_dev, E, w, y_dev, ldy, out_dtype, nullptr, 0, true,
-                             stream);
+                             nullptr, stream);
 }
 
 size_t sharq_noalloc_scratch_bytes(void) { return sharq::kNoAllocScratchBytes; }

@@ -505,7 +505,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
 
   // single epilogue store of Y_S + Y_R
   if constexpr (SWIGLU != 0) {
-    static_assert(!GROUPED && !DENSE, "the SwiGLU epilogue follows the 2:4 layer");
+    static_assert(!DENSE && (SWIGLU == 2 || !GROUPED), "the SwiGLU epilogue follows the 2:4 layer");
     // the wave's column blocks pair up as (gate, up): the tile starts at an
     // even block (BN/16 is even) and so does each wave's share
     static_assert(C::kWNT % 2 == 0 && C::kNB % 2 == 0, "gate/up pairs inside a wave");
@@ -561,14 +561,30 @@ __global__ __launch_bounds__(64 * NWM * NWN) void dual_gemm_tiled(GemmArgs g) {
           *reinterpret_cast<uint2*>(hs + lrow * kHStride + lcol) = make_uint2(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16);
         }
       __syncthreads();
+      //
+      // Grouped: the tile's rows are an expert's padded routed rows and H goes
+      // to routed row y_row0 + (row within the expert), so the next activation
+      // holds the routed rows in order, unpadded, as sharq_prepare lays out
+      // the rows of H.  The expert's padding rows are not written (that row
+      // of the next activation belongs to the next expert, or is its own
+      // padding, which the host fills).
       const PrepOut& o = g.next;
-      const int64_t RBn = g.a_blocks, KTn = hcols / 128;
+      const int64_t RBn = GROUPED ? (g.M + 15) / 16 : g.a_blocks, KTn = hcols / 128;
+      const int64_t kb0 = (nb0 - nb_first) / 4;                   // the tile's first 32-column block of H
       constexpr int kBlk = BM * kHCols / 32;
       for (int t = tid; t < kBlk; t += C::kThreads) {
-        const int r = t & 15, rbl = (t >> 4) % C::kMB, b = t / (16 * C::kMB);
-        const int64_t rb = rb0 + rbl, kb = nb0 / 4 + b;          // nb0 / 4: the tile's first 32-column block
+        const int rl = t & 15, rbl = (t >> 4) % C::kMB, b = t / (16 * C::kMB);
+        const int64_t kb = kb0 + b;
+        int64_t rb = rb0 + rbl;
+        int r = rl;
+        if constexpr (GROUPED) {
+          const int64_t lr = (rb0 - rb_first + rbl) * 16 + rl, yr = y_row0 + lr;
+          if (lr >= y_rows) continue;
+          rb = yr >> 4;
+          r = (int)(yr & 15);
+        }
         if (rb >= RBn || kb * 32 >= hcols) continue;
-        const uint4* src = reinterpret_cast<const uint4*>(hs + (rbl * 16 + r) * kHStride + b * 32);
+        const uint4* src = reinterpret_cast<const uint4*>(hs + (rbl * 16 + rl) * kHStride + b * 32);
         float v[32];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -802,7 +818,9 @@ hipError_t launch_linear_grouped_gemm(const GemmArgs& a, int64_t max_mtiles, hip
   const int64_t NBe = (a.N / a.E + 15) / 16;
   const int64_t tiles_n = (NBe + kTileN / 16 - 1) / (kTileN / 16);
   // a multiple of 8 workgroups: each XCD's run of units fits its share of the grid
-  return launch_tiled<kGroupedTileM, kTileN, 4, 2, 2, true, false>(a, (max_mtiles * tiles_n + 7) / 8 * 8, stream);
+  const int64_t grid = (max_mtiles * tiles_n + 7) / 8 * 8;
+  return a.next.r_codes ? launch_tiled<kGroupedTileM, kTileN, 4, 2, 2, true, false, 2>(a, grid, stream)
+                        : launch_tiled<kGroupedTileM, kTileN, 4, 2, 2, true, false>(a, grid, stream);
 }
 
 template <bool DENSE>

@@ -18,6 +18,11 @@
 //      row index the rows are already in expert order and only the scales are
 //      copied: the GEMM reads the codes from the source rows itself;
 //   3. the tiled dual GEMM with one workgroup per (expert, M tile, N tile).
+// The SwiGLU-prep form (gate and up rows of each expert interleaved in 16-row
+// blocks) replaces Y by the down projection's prepared activation: each tile
+// applies h = SiLU(gate) * up, rounds h to bf16 and prepares it in its
+// epilogue, writing the routed rows in order; a fourth small launch (before
+// the GEMM) fills that activation's padding rows.
 #include <atomic>
 
 #include "device_common.h"
@@ -257,6 +262,23 @@ __global__ __launch_bounds__(256) void grouped_gather_scales_kernel(GatherArgs a
   }
 }
 
+// The padding rows of the last 16-row block of an activation written by the
+// SwiGLU-prep epilogue (which writes routed rows only): the outputs of zero
+// input -- zero codes and scale bytes, metadata 0x4 per group (offsets 0 and
+// 1 kept).  One wave per K tile.
+__global__ __launch_bounds__(64) void grouped_act_tail_kernel(PrepOut o, int64_t rows, int KT) {
+  const int lane = threadIdx.x, r = lane & 15;
+  const int kt = blockIdx.x;
+  const int64_t rb = rows / 16, RB = (rows + 15) / 16;
+  if (r < (int)(rows % 16)) return;
+  const int64_t tile = rb * KT + kt;
+  *reinterpret_cast<uint4*>(o.r_codes + tile * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+  *reinterpret_cast<uint4*>(o.s_codes + tile * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+  *reinterpret_cast<uint32_t*>(o.s_meta + tile * 256 + lane * 4) = 0x44444444u;
+  o.s_scales[((int64_t)kt * RB + rb) * 64 + lane] = 0;
+  o.r_scales[((int64_t)kt * RB + rb) * 64 + lane] = 0;
+}
+
 }  // namespace
 
 size_t grouped_workspace_bytes(int64_t rows, int E, int K) { return ws_layout(rows, E, K).total; }
@@ -349,6 +371,14 @@ hipError_t launch_linear_grouped(const GroupedArgs& a, hipStream_t stream) {
   m.a_blocks = L.blocks;
   m.M = a.rows;
   m.seg = seg; m.pseg = pseg; m.tprefix = tprefix; m.texp = texp;
+  if (m.next.r_codes && a.rows % 16) {
+    // the next activation (K = N_e / 2) gets its padding rows before the GEMM
+    // writes the routed ones
+    const int KTn = (int)(a.gemm.N / E / 2 / 128);
+    hipLaunchKernelGGL(grouped_act_tail_kernel, dim3((unsigned)KTn), dim3(64), 0, stream, m.next, a.rows, KTn);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   return launch_linear_grouped_gemm(m, L.tiles, stream);
 }
 

@@ -354,6 +354,26 @@ sharq_status sharq_linear_grouped(const sharq_act* a, const int32_t* row_index_d
                                   void* y_dev, int64_t ldy, int32_t out_dtype,
                                   void* ws_dev, size_t ws_bytes, void* stream);
 
+/* The grouped gate/up layer of a mixture-of-experts MLP whose epilogue writes
+ * the down projection's prepared activation (README page, section
+ * "Benchmarks": epilogue fusion; the expert MLP as sharq_linear_swiglu_prep
+ * computes it for a dense layer).  Arguments as sharq_linear_grouped, with
+ * each expert's N_e = 2F weight rows interleaved in 16-row blocks (block 2j =
+ * gate rows 16j..16j+15, block 2j+1 = the same up rows) and, instead of Y,
+ *   next: output activation descriptor (struct_size set, all five buffers
+ *         allocated per sharq_act_bytes(rows, F, 2, 4, MXFP4)); routed row i
+ *         becomes row i of it: h = bf16(SiLU(gate) * up) of that row, then
+ *         sharq_prepare(h, gamma = NULL), its padding rows as sharq_prepare
+ *         writes them.  M, K = F, n, m, fmt are filled in.
+ * The down projection then runs as sharq_linear_grouped(next, NULL, rows,
+ * the same segment offsets, ...): its rows are already in expert order.
+ * Errors: as sharq_linear_grouped; INVALID_ARG also for N_e % 32 or unset
+ * output buffers; UNSUPPORTED for F % 128 (the K tiles of the next activation
+ * hold no padding) or a format other than MXFP4. */
+sharq_status sharq_linear_grouped_swiglu_prep(const sharq_act* a, const int32_t* row_index_dev, int64_t rows,
+                                              const int64_t* seg_offsets_dev, int32_t E, const sharq_weight* w,
+                                              sharq_act* next, void* ws_dev, size_t ws_bytes, void* stream);
+
 /* sharq_linear_grouped for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same layer, the same kernels and the same outputs, with the

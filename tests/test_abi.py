@@ -332,6 +332,38 @@ def test_swiglu_prep_rejects_before_launch(lib):
     assert (nxt.M, nxt.K, nxt.n, nxt.m) == (0, 128, 2, 4)
 
 
+def test_grouped_swiglu_prep_rejects_before_launch(lib):
+    a = _act()
+    a.layout_version = _lib.SHARQ_ABI_VERSION
+    a.M, a.K, a.n, a.m = 64, 256, 2, 4
+    w = _lib.WeightDesc()
+    w.struct_size = C.sizeof(_lib.WeightDesc)
+    w.layout_version = _lib.SHARQ_ABI_VERSION
+    w.K, w.codes, w.scales = 256, 0x100000, 0x200000
+
+    def weight(n):
+        w.N = n
+        for p in (0, 1):
+            w.view[p].base, w.view[p].ld, w.view[p].block = 0x200000, n // 16 * 64, 32
+
+    seg, ws, ri = C.c_void_p(0x500000), C.c_void_p(0x700000), C.c_void_p(0x800000)
+    nxt = _act()
+    call = lambda rows, E, nx=nxt, wsb=1 << 30: lib.sharq_linear_grouped_swiglu_prep(
+        C.byref(a), ri, rows, seg, E, C.byref(w), nx, ws, wsb, None)
+    weight(2 * 256)                                              # 2 experts, N_e = 256, F = 128
+    assert call(64, 2, nx=None) == _lib.ERR_INVALID_ARG          # no output descriptor
+    assert call(64, 2, wsb=100) == _lib.ERR_WORKSPACE            # workspace too small
+    weight(2 * 48)
+    assert call(64, 2) == _lib.ERR_INVALID_ARG                   # N_e = 48: not pairs of 16-row blocks
+    weight(2 * 64)
+    assert call(64, 2) == _lib.ERR_UNSUPPORTED                   # F = 32: not a multiple of 128
+    weight(2 * 256)
+    bad = _act(r_codes=0)
+    assert call(64, 2, nx=C.byref(bad)) == _lib.ERR_INVALID_ARG  # output buffers not set
+    assert call(0, 2, nx=C.byref(nxt)) == _lib.OK                # nothing routed: no launch
+    assert (nxt.M, nxt.K, nxt.n, nxt.m) == (0, 128, 2, 4)
+
+
 def test_peak_entry_points_reject_bad_arguments(lib):
     """The measurement entry points check their arguments on the host."""
     d = C.c_double()
