@@ -10,7 +10,9 @@ norm; ``--fmt nvfp4`` runs it in the NVFP4-style format: E4M3 scale per 16,
 binary32 tensor scales, fp16 MFMA on exactly expanded codes) and moe (Qwen3-30B-A3B-shaped expert layer: 4096 tokens routed top-8 of
 128 experts with Zipf(1.1) loads; step = prep of the tokens + grouped gate/up
 (K=2048, N_e=1536) + prep of the 32768 expert-sorted down rows + grouped down
-(K=768, N_e=2048)).  ``--mode dense`` times the plain MXFP4 linear instead
+(K=768, N_e=2048)) and moe_mlp (the same experts as one MLP: prep of the tokens
++ grouped gate/up whose SwiGLU epilogue prepares the down rows, h =
+SiLU(gate) * up never stored + grouped down on them).  ``--mode dense`` times the plain MXFP4 linear instead
 (pattern 0:4: no backbone, MXFP4 of the normalised row, one GEMM) -- the dense
 FP4 baseline SharQ is compared against; its flops are 2*M*N*K.  Weight payloads
 are packed once, outside the timed region (an offline step).
@@ -340,7 +342,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qkv", choices=sorted(list(WORKLOADS) + ["moe", "layer"]))
+    ap.add_argument("--workload", default="qkv", choices=sorted(list(WORKLOADS) + ["moe", "moe_mlp", "layer"]))
     ap.add_argument("--m", type=int, default=1, help="rows of the decode workload")
     ap.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "nvfp4"],
                     help="FP4 format (nvfp4: the decode workload only)")
@@ -367,18 +369,18 @@ def main():
     if args.fmt == "nvfp4" and args.workload != "decode":
         print("the NVFP4-style path is built for the decode workload (--workload decode)", file=sys.stderr)
         sys.exit(2)
-    special = args.workload in ("moe", "layer")
+    special = args.workload in ("moe", "moe_mlp", "layer")
     if special and (args.fmt != "mxfp4" or args.mode != "sharq" or args.fused or args.ablation != "none"):
-        print("the moe and layer workloads run the default MXFP4 SharQ layers", file=sys.stderr)
+        print("the moe, moe_mlp and layer workloads run the default MXFP4 SharQ layers", file=sys.stderr)
         sys.exit(2)
-    if args.mode == "dense" and (args.fmt != "mxfp4" or args.workload == "moe"):
+    if args.mode == "dense" and (args.fmt != "mxfp4" or args.workload in ("moe", "moe_mlp")):
         print("the plain FP4 linear is built for MXFP4 dense layers", file=sys.stderr)
         sys.exit(2)
     if args.fused and (args.workload != "decode" or args.m > 16 or args.mode != "sharq" or args.ablation != "none"):
         print("--fused is the one-launch layer (MXFP4 or NVFP4-style) for the decode workload with --m <= 16",
               file=sys.stderr)
         sys.exit(2)
-    if args.ablation != "none" and (args.fmt != "mxfp4" or args.mode != "sharq" or args.workload == "moe" or
+    if args.ablation != "none" and (args.fmt != "mxfp4" or args.mode != "sharq" or args.workload in ("moe", "moe_mlp") or
                                     (args.ablation == "unfused_norm" and not WORKLOADS[args.workload]["norm"])):
         print("the fusion ablations run the MXFP4 SharQ layer (unfused_norm needs a workload with RMSNorm)",
               file=sys.stderr)
@@ -397,7 +399,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     args.measured_peaks = None if args.no_peaks else measure_peaks()
-    if args.workload == "moe":
+    if args.workload in ("moe", "moe_mlp"):
         rec = run_moe(args)
     elif args.workload == "layer":
         rec = run_layer(args)
@@ -672,6 +674,7 @@ def run_moe(args):
 
     T, E, k, dm, dff = MOE["tokens"], MOE["experts"], MOE["top_k"], MOE["d_model"], MOE["d_ff"]
     rows = T * k
+    mlp = args.workload == "moe_mlp"
     rng = np.random.default_rng(300)
     expert, token, seg = synth.zipf_router(rng, T, E, k)
 
@@ -683,7 +686,9 @@ def run_moe(args):
     seg_d = torch.from_numpy(seg).cuda()
     ri = torch.from_numpy(token.astype(np.int32)).cuda()
     n_gu, n_d = 2 * dff, dm
-    per_set = (E * n_gu * dm + E * n_d * dff) * 17 // 32 + 4 * rows * (n_gu + n_d)
+    # moe_mlp: each expert's 2*dff gate/up rows are taken as gate and up rows
+    # interleaved in 16-row blocks (random weights either way)
+    per_set = (E * n_gu * dm + E * n_d * dff) * 17 // 32 + 4 * rows * n_d + (rows * dff * 19 // 16 if mlp else 4 * rows * n_gu)
     nsets = args.sets or max(2, -(-ROTATE_BYTES // per_set))
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4321)
@@ -691,7 +696,8 @@ def run_moe(args):
     for s in range(nsets):
         wgu = sq.sharq_pack_weight(device_weight(gen, E * n_gu, dm))
         wd = sq.sharq_pack_weight(device_weight(gen, E * n_d, dff))
-        sets.append((wgu, wd, torch.empty(rows, n_gu, device="cuda"), torch.empty(rows, n_d, device="cuda")))
+        mid = sq.SharqAct(rows, dff, torch.device("cuda")) if mlp else torch.empty(rows, n_gu, device="cuda")
+        sets.append((wgu, wd, mid, torch.empty(rows, n_d, device="cuda")))
     a_tok = sq.SharqAct(T, dm, torch.device("cuda"))
     a_down = sq.SharqAct(rows, dff, torch.device("cuda"))
     ws = torch.empty(max(sq.grouped_workspace_bytes(rows, E, dm), sq.grouped_workspace_bytes(rows, E, dff)),
@@ -699,26 +705,62 @@ def run_moe(args):
     torch.cuda.synchronize()
 
     def step(i, part=None):
-        wgu, wd, ygu, yd = sets[i % nsets]
-        fns = [lambda: sq.sharq_prepare(x_tok, None, out=a_tok),
-               lambda: sq.sharq_linear_grouped(a_tok, wgu, seg_d, E, row_index=ri, rows=rows, out=ygu, workspace=ws),
-               lambda: sq.sharq_prepare(x_down, None, out=a_down),
-               lambda: sq.sharq_linear_grouped(a_down, wd, seg_d, E, rows=rows, out=yd, workspace=ws)]
+        wgu, wd, mid, yd = sets[i % nsets]
+        if mlp:
+            fns = [lambda: sq.sharq_prepare(x_tok, None, out=a_tok),
+                   lambda: sq.sharq_linear_grouped_swiglu_prep(a_tok, wgu, seg_d, E, row_index=ri, rows=rows, out=mid,
+                                                               workspace=ws),
+                   lambda: sq.sharq_linear_grouped(mid, wd, seg_d, E, rows=rows, out=yd, workspace=ws)]
+        else:
+            fns = [lambda: sq.sharq_prepare(x_tok, None, out=a_tok),
+                   lambda: sq.sharq_linear_grouped(a_tok, wgu, seg_d, E, row_index=ri, rows=rows, out=mid,
+                                                   workspace=ws),
+                   lambda: sq.sharq_prepare(x_down, None, out=a_down),
+                   lambda: sq.sharq_linear_grouped(a_down, wd, seg_d, E, rows=rows, out=yd, workspace=ws)]
         for j, fn in enumerate(fns):
             if part in (None, j):
                 fn()
-    step.parts = 4
+    step.parts = 3 if mlp else 4
 
     ms, parts = timed(step, args.steps, args.warmup)
-    t = [float(np.mean(p)) for p in parts[:4]]
+    t = [float(np.mean(p)) for p in parts]
+    # moe_mlp parts: token prep, gate/up (+ SwiGLU + down prep), down
+    t_gu, t_d = t[1], (t[2] if mlp else t[3])
     f_gu, f_d = gemm_flops(rows, n_gu, dm), gemm_flops(rows, n_d, dff)
     # algorithmic bytes (the method's count, a compressed backbone: 0.9375 B per
     # activation element): prepared rows read once (distinct tokens for
-    # gate/up), all experts' weights once, Y once
-    b_gu = T * dm * 15 // 16 + E * n_gu * dm * 17 // 32 + 4 * rows * n_gu
+    # gate/up), all experts' weights once, Y (or, for moe_mlp, the prepared
+    # down rows) written once
+    b_gu = T * dm * 15 // 16 + E * n_gu * dm * 17 // 32 + (rows * dff * 15 // 16 if mlp else 4 * rows * n_gu)
     b_d = rows * dff * 15 // 16 + E * n_d * dff * 17 // 32 + 4 * rows * n_d
-    gbs_gu = b_gu / (t[1] * 1e-3) / 1e9
+    gbs_gu = b_gu / (t_gu * 1e-3) / 1e9
+    tf_gu = f_gu / (t_gu * 1e-3) / 1e12
+    hbm_bound = b_gu / (PEAK_HBM_GBS * 1e9) > f_gu / (PEAK_FP4_TFLOPS * 1e12)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbs_gu, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs_gu / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tf_gu, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf_gu / PEAK_FP4_TFLOPS, 4), "traffic": None,
+                "frac_useful": round(f_gu * 3 // 4 / (t_gu * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4)}
     loads = np.diff(seg)
+    if mlp:
+        desc = (f"moe_mlp: Qwen3-30B-A3B-shaped expert MLP, {T} tokens top-{k} of {E} experts "
+                f"(Zipf(1.1) loads, max {int(loads.max())} min {int(loads.min())} rows), gate/up K={dm} "
+                f"N_e={n_gu} with the SwiGLU epilogue preparing the down rows, down K={dff} N_e={n_d}; "
+                f"no norm; 2:4 mask; MXFP4; fp32 output")
+        prep = {"tokens_us": round(t[0] * 1e3, 3),
+                "GB/s": round(prep_bytes(T, dm, False) / (t[0] * 1e-3) / 1e9, 1)}
+        gemm = {"gate_up_swiglu_prep_us": round(t_gu * 1e3, 3), "down_us": round(t_d * 1e3, 3)}
+    else:
+        desc = (f"moe: Qwen3-30B-A3B-shaped expert layer, {T} tokens top-{k} of {E} experts "
+                f"(Zipf(1.1) loads, max {int(loads.max())} min {int(loads.min())} rows), "
+                f"gate/up K={dm} N_e={n_gu}, down K={dff} N_e={n_d}; no norm; 2:4 mask; MXFP4; fp32 output")
+        prep = {"tokens_us": round(t[0] * 1e3, 3), "down_rows_us": round(t[2] * 1e3, 3),
+                "GB/s": round((prep_bytes(T, dm, False) + prep_bytes(rows, dff, False)) / ((t[0] + t[2]) * 1e-3) / 1e9, 1)}
+        gemm = {"gate_up_us": round(t_gu * 1e3, 3), "down_us": round(t_d * 1e3, 3)}
+    gemm.update({"gate_up_TFLOP/s": round(tf_gu, 1), "down_TFLOP/s": round(f_d / (t_d * 1e-3) / 1e12, 1),
+                 "gate_up_GB/s": round(gbs_gu, 1), "down_GB/s": round(b_d / (t_d * 1e-3) / 1e9, 1)})
     return {
         "metric": "SharQ linear TFLOPS + prep GB/s (fraction of peak), Llama-8B shapes M=2048",
         "value": round((f_gu + f_d) / (ms * 1e-3) / 1e12, 2),
@@ -726,19 +768,14 @@ def run_moe(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
         "data": "synthetic",
-        "config": {"workload": f"moe: Qwen3-30B-A3B-shaped expert layer, {T} tokens top-{k} of {E} experts "
-                               f"(Zipf(1.1) loads, max {int(loads.max())} min {int(loads.min())} rows), "
-                               f"gate/up K={dm} N_e={n_gu}, down K={dff} N_e={n_d}; no norm; 2:4 mask; MXFP4; fp32 output",
-                   "rows": rows, "experts": E, "rotating_sets": nsets},
-        "prep": {"tokens_us": round(t[0] * 1e3, 3), "down_rows_us": round(t[2] * 1e3, 3),
-                 "GB/s": round((prep_bytes(T, dm, False) + prep_bytes(rows, dff, False)) / ((t[0] + t[2]) * 1e-3) / 1e9, 1)},
-        "gemm": {"gate_up_us": round(t[1] * 1e3, 3), "down_us": round(t[3] * 1e3, 3),
-                 "gate_up_TFLOP/s": round(f_gu / (t[1] * 1e-3) / 1e12, 1),
-                 "down_TFLOP/s": round(f_d / (t[3] * 1e-3) / 1e12, 1),
-                 "gate_up_GB/s": round(gbs_gu, 1), "down_GB/s": round(b_d / (t[3] * 1e-3) / 1e9, 1)},
-        "roofline": {"bound": "hbm", "achieved": round(gbs_gu, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs_gu / PEAK_HBM_GBS, 4), "traffic": None},
+        "config": {"workload": desc, "rows": rows, "experts": E, "rotating_sets": nsets},
+        "prep": prep,
+        "gemm": gemm,
+        "roofline": roof,
         "cpu_baseline": None,
+        "parts_us": {n: round(v * 1e3, 3) for n, v in zip(
+            ["prep_tokens", "gate_up_swiglu_prep", "down"] if mlp else ["prep_tokens", "gate_up", "prep_down", "down"],
+            t)},
     }
 
 
