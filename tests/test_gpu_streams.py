@@ -1,7 +1,7 @@
 """The library on the caller's stream and under HIP graph capture: results on a
 side stream (passed explicitly or current through torch.cuda.stream) equal the
 default stream's; a captured graph of the preparation, the layer, the grouped
-layer and the one-launch decode layer, replayed several times with new inputs
+layer, the grouped SwiGLU-prep layer and the one-launch decode layer, replayed several times with new inputs
 copied in and eager work in between, equals the eager result every time."""
 import numpy as np
 import pytest
@@ -46,16 +46,25 @@ def test_graph_replay_matches_eager():
     we = np.concatenate([synth.linear_weight(rng, 128, 1024) for _ in range(4)])
     wg = sq.sharq_pack_weight(dev_bf16(we))
     seg = torch.tensor([0, 40, 40, 201, 256], dtype=torch.int64, device="cuda")
+    # grouped gate/up with the SwiGLU-prep epilogue: 2 experts (F = 128) over 250
+    # routed rows (a ragged last block: the padding-row fill runs too)
+    wga = np.concatenate([synth.linear_weight(rng, 128, 1024) for _ in range(2)])
+    wua = np.concatenate([synth.linear_weight(rng, 128, 1024) for _ in range(2)])
+    wgu = sq.sharq_pack_weight(sq.interleave_gate_up(dev_bf16(wga), dev_bf16(wua), experts=2))
+    seg2 = torch.tensor([0, 90, 250], dtype=torch.int64, device="cuda")
+    ri = torch.arange(255, 5, -1, dtype=torch.int32, device="cuda")
     x_dec = dev_bf16(xs[0][:1])
 
     xd = dev_bf16(xs[0])                                   # static input of the graph
 
     def work(x, xdec):
         act = sq.sharq_prepare(x, gd, 1e-5)
+        h = sq.sharq_linear_grouped_swiglu_prep(act, wgu, seg2, 2, row_index=ri, rows=250)
         return (sq.sharq_linear(act, wt),
                 sq.sharq_linear_grouped(act, wg, seg, 4),
                 sq.sharq_linear_fused(xdec, wt, gd, 1e-5),
-                sq.sharq_linear_fused(xdec, wt_nv, gd, 1e-5))
+                sq.sharq_linear_fused(xdec, wt_nv, gd, 1e-5),
+                h.s_codes, h.s_meta, h.s_scales, h.r_codes, h.r_scales)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
