@@ -236,67 +236,159 @@ __device__ __forceinline__ void nv_residual(const float (&v)[32], float g_r, uin
 }
 
 // ---------------------------------------------------------------------------
-// Phases 2 and 3: one wave per 16-row x 128-K tile, 4 tiles of one row block
-// per workgroup; lane l owns row 16 rb + l%16 and K [128 kb + 32 (l/16), +32),
-// the lane order of the tiled layout.  Both phases rebuild v, the mask, Q(S)
-// and the residual; phase 2 stores the backbone and each workgroup's max |r|,
-// phase 3 quantises R with the tensor scale those maxima give.
+// Quarter-chunk forms of the two steps: one lane per 8 consecutive elements
+// of a 32-element chunk (half of a 16-element block; the chunk's quarters in
+// lanes 4j .. 4j+3 of one wave, so a block's two halves sit in lanes l and
+// l ^ 1).  The arithmetic is nv_backbone's and nv_residual's; a block maximum
+// is the larger of the two halves' maxima, exchanged between the two lanes,
+// and a lane's dependent chain is a quarter as long.  Every lane of a wave
+// must call them (the exchange).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float pair_max(float v) { return fmaxf(v, __shfl_xor(v, 1)); }
+
+// The backbone of a quarter: dense = its 8 S codes in the masked dense layout
+// (the kept codes in place, zero codes at the dropped positions; element i in
+// bits 4i..4i+3), meta8 = its two groups' metadata nibbles (group g in bits
+// 4g..4g+3), sbyte = the block's E4M3 scale byte; v becomes the residual.
+__device__ __forceinline__ void nv_backbone_q(float (&v)[8], float g_s, uint32_t& dense, uint32_t& meta8,
+                                              uint32_t& sbyte) {
+  const float six_g = 6.0f * g_s;
+  float bm = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bm = fmaxf(bm, fabsf(v[i]));
+  bm = pair_max(bm);
+  const float s = e4m3_round(bm / six_g, sbyte);
+  const float tq = s * g_s;
+  dense = 0u;
+  meta8 = 0u;
+#pragma unroll
+  for (int gq = 0; gq < 2; ++gq) {
+    float& a0 = v[4 * gq];
+    float& a1 = v[4 * gq + 1];
+    float& a2 = v[4 * gq + 2];
+    float& a3 = v[4 * gq + 3];
+    const Keep24 k = keep24(a0, a1, a2, a3);
+    meta8 |= k.nib << (4 * gq);
+    const float x0 = k.k0 ? a0 : (k.f1 ? a1 : a2);
+    const float x1 = k.k3 ? a3 : (k.s2 ? a2 : a1);
+    const float q0 = nv_quot(x0, tq, s), q1 = nv_quot(x1, tq, s);
+    const uint32_t c = e2m1_pair(q0, q1);
+    const uint32_t i0 = k.nib & 3u, i1 = k.nib >> 2;
+    dense |= ((c & 0xFu) << (16 * gq + 4 * i0)) | ((c >> 4) << (16 * gq + 4 * i1));
+    float d0, d1;
+    fp4_unpack2<0>(c, d0, d1);
+    d0 = (d0 * s) * g_s;
+    d1 = (d1 * s) * g_s;
+    const float r0 = x0 - d0, r1 = x1 - d1;
+    a0 = k.k0 ? r0 : a0;
+    a1 = k.f1 ? r0 : (k.s1 ? r1 : a1);
+    a2 = k.f2 ? r0 : (k.s2 ? r1 : a2);
+    a3 = k.k3 ? r1 : a3;
+  }
+}
+
+// The residual codes of a quarter (element i in bits 4i..4i+3) and its
+// block's E4M3 scale byte.
+__device__ __forceinline__ void nv_residual_q(const float (&v)[8], float g_r, uint32_t& rc, uint32_t& rbyte) {
+  const float six_r = 6.0f * g_r;
+  float bm = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bm = fmaxf(bm, fabsf(v[i]));
+  bm = pair_max(bm);
+  const float s = e4m3_round(bm / six_r, rbyte);
+  const float tq = s * g_r;
+  rc = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const float q0 = nv_quot(v[i], tq, s), q1 = nv_quot(v[i + 1], tq, s);
+    rc |= e2m1_pair(q0, q1) << (4 * i);
+  }
+}
+
+// 8 bf16 -> binary32
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    v[2 * h] = bf16_lo(w[h]);
+    v[2 * h + 1] = bf16_hi(w[h]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phases 2 and 3: one workgroup of 16 waves per 4 tiles (16 rows x 128 K
+// each) of one row block; the four quarters of a chunk in four consecutive
+// lanes, chunk lane l = (t % 256) / 4 owning row 16 rb + l%16 and K
+// [128 kb + 32 (l/16), +32) -- the lane order of the tiled layout.  Both
+// phases rebuild v, the mask, Q(S) and the residual; phase 2 stores the
+// backbone and each workgroup's max |r|, phase 3 quantises R with the tensor
+// scale those maxima give.
+// ---------------------------------------------------------------------------
+constexpr int kNvPrepThreads = 256 * kNvWaves;
+
 template <bool NORM, bool RESID>
-__global__ __launch_bounds__(256) void nv_decompose_kernel(NvPrepArgs a) {
-  __shared__ float red[4];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+__global__ __launch_bounds__(kNvPrepThreads) void nv_decompose_kernel(NvPrepArgs a) {
+  __shared__ float red[kNvPrepThreads / 64];
+  constexpr int NW = kNvPrepThreads / 64;
+  const int t = threadIdx.x, u = t & 255, l = u >> 2, h = u & 3;
   const int64_t rb = blockIdx.y;
-  const int kb = blockIdx.x * kNvWaves + wave;
+  const int kb = blockIdx.x * kNvWaves + (t >> 8);
 
   // tensor scales from the previous phases' maxima (max |S| = max |v|: the
   // mask keeps each group's largest magnitude)
   float am = 0.0f;
-  for (int64_t i = t; i < a.M; i += 256) am = fmaxf(am, a.rowamax[i]);
-  const float g_s = tensor_scale(block_max<4>(am, red));
+  for (int64_t i = t; i < a.M; i += kNvPrepThreads) am = fmaxf(am, a.rowamax[i]);
+  const float g_s = tensor_scale(block_max<NW>(am, red));
   float g_r = 1.0f;
   if (RESID) {
     float ar = 0.0f;
-    for (int64_t i = t; i < a.RB * a.WX; i += 256) ar = fmaxf(ar, a.rparts[i]);
-    g_r = tensor_scale(block_max<4>(ar, red));
+    for (int64_t i = t; i < a.RB * a.WX; i += kNvPrepThreads) ar = fmaxf(ar, a.rparts[i]);
+    g_r = tensor_scale(block_max<NW>(ar, red));
   }
 
-  const int64_t row = rb * 16 + (lane & 15);
-  const int k0 = kb * 128 + 32 * (lane >> 4);
+  const int64_t row = rb * 16 + (l & 15);
+  const int k0 = kb * 128 + 32 * (l >> 4) + 8 * h;
   const bool valid = kb < a.KB && row < a.M && k0 < a.K;
-  float v[32];
+  float v[8];
   if (valid) {
-    load32(a.x + row * a.ldx + k0, v);
-    if (NORM) apply_norm(v, a.gamma + k0, a.inv[row]);
+    load8(a.x + row * a.ldx + k0, v);
+    if (NORM) {
+      const float iv = a.inv[row];
+      float gm[8];
+      load8(a.gamma + k0, gm);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (v[i] * iv) * gm[i];
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
   }
 
   // backbone: mask, per-16 block scale, kept codes; residual in place
-  uint32_t scodes[2], meta, sbytes;
-  nv_backbone(v, g_s, scodes, meta, sbytes);
+  uint32_t dense, meta8, sbyte;
+  nv_backbone_q(v, g_s, dense, meta8, sbyte);
   const int64_t tile = rb * a.KB + kb;
-  const int64_t sc = ((int64_t)kb * a.RB + rb) * 128 + 2 * lane;
+  const int64_t sc = ((int64_t)kb * a.RB + rb) * 128 + 2 * l + (h >> 1);
 
   if (!RESID) {
     if (kb < a.KB) {
-      *reinterpret_cast<uint4*>(a.o.s_codes + tile * 1024 + lane * 16) = expand_chunk(scodes[0], scodes[1], meta);
-      *reinterpret_cast<uint32_t*>(a.o.s_meta + tile * 256 + lane * 4) = meta;
-      *reinterpret_cast<uint16_t*>(a.o.s_scales + sc) = (uint16_t)sbytes;
+      *reinterpret_cast<uint32_t*>(a.o.s_codes + tile * 1024 + l * 16 + h * 4) = dense;
+      a.o.s_meta[tile * 256 + l * 4 + h] = (uint8_t)meta8;
+      if (!(h & 1)) a.o.s_scales[sc] = (uint8_t)sbyte;
     }
     float ar = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) ar = fmaxf(ar, fabsf(v[i]));
-    ar = block_max<4>(ar, red);
+    for (int i = 0; i < 8; ++i) ar = fmaxf(ar, fabsf(v[i]));
+    ar = block_max<NW>(ar, red);
     if (t == 0) a.rparts[rb * a.WX + blockIdx.x] = ar;
     if (t == 0 && blockIdx.x == 0 && blockIdx.y == 0) *a.g_s = g_s;
   } else {
-    uint32_t rc[4], rbytes;
-    nv_residual(v, g_r, rc, rbytes);
+    uint32_t rc, rbyte;
+    nv_residual_q(v, g_r, rc, rbyte);
     if (kb < a.KB) {
-      *reinterpret_cast<uint4*>(a.o.r_codes + tile * 1024 + lane * 16) = make_uint4(rc[0], rc[1], rc[2], rc[3]);
-      *reinterpret_cast<uint16_t*>(a.o.r_scales + sc) = (uint16_t)rbytes;
+      *reinterpret_cast<uint32_t*>(a.o.r_codes + tile * 1024 + l * 16 + h * 4) = rc;
+      if (!(h & 1)) a.o.r_scales[sc] = (uint8_t)rbyte;
     }
     if (t == 0 && blockIdx.x == 0 && blockIdx.y == 0) *a.g_r = g_r;
   }
@@ -888,15 +980,15 @@ hipError_t launch_prepare_nv(const uint16_t* x, int64_t M, int K, int64_t ldx, c
   a.inv = reinterpret_cast<float*>(out.r_scales + L.inv);
   a.rparts = reinterpret_cast<float*>(out.r_scales + L.rparts);
   if (M > 0x7FFFFFFF || a.RB > 65535) return hipErrorInvalidValue;
-  const dim3 rows((unsigned)M), tiles((unsigned)a.WX, (unsigned)a.RB), blk(256);
+  const dim3 rows((unsigned)M), tiles((unsigned)a.WX, (unsigned)a.RB), blk(256), blk_q(kNvPrepThreads);
   if (gamma) {
     hipLaunchKernelGGL((nv_rowstats_kernel<true>), rows, blk, 0, stream, a);
-    hipLaunchKernelGGL((nv_decompose_kernel<true, false>), tiles, blk, 0, stream, a);
-    hipLaunchKernelGGL((nv_decompose_kernel<true, true>), tiles, blk, 0, stream, a);
+    hipLaunchKernelGGL((nv_decompose_kernel<true, false>), tiles, blk_q, 0, stream, a);
+    hipLaunchKernelGGL((nv_decompose_kernel<true, true>), tiles, blk_q, 0, stream, a);
   } else {
     hipLaunchKernelGGL((nv_rowstats_kernel<false>), rows, blk, 0, stream, a);
-    hipLaunchKernelGGL((nv_decompose_kernel<false, false>), tiles, blk, 0, stream, a);
-    hipLaunchKernelGGL((nv_decompose_kernel<false, true>), tiles, blk, 0, stream, a);
+    hipLaunchKernelGGL((nv_decompose_kernel<false, false>), tiles, blk_q, 0, stream, a);
+    hipLaunchKernelGGL((nv_decompose_kernel<false, true>), tiles, blk_q, 0, stream, a);
   }
   return hipGetLastError();
 }
