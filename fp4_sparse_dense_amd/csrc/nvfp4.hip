@@ -650,7 +650,7 @@ struct NvFusedLds {
   int KT, KC, P;
 };
 
-__host__ __device__ inline NvFusedLds nv_fused_lds(int K) {
+__host__ __device__ inline NvFusedLds nv_fused_lds(int K, int waves = kNvFusedWaves) {
   NvFusedLds L;
   L.KT = (K + 127) / 128;
   L.KC = K / 32;
@@ -662,7 +662,7 @@ __host__ __device__ inline NvFusedLds nv_fused_lds(int K) {
   L.rs = L.ss + (uint32_t)L.KT * 128;
   L.inv = L.rs + (uint32_t)L.KT * 128;
   L.red = L.inv + 16 * 4;
-  L.total = L.red + kNvFusedWaves * 4;
+  L.total = L.red + waves * 4;
   // after the GEMM loop the waves' partial sums (8 x 64 x 16 B) reuse the LDS from offset 0
   const uint32_t parts = (uint32_t)kNvFusedWaves * 64u * 16u;
   if (L.total < parts) L.total = parts;
@@ -679,10 +679,11 @@ constexpr int kNvSmallChunks = 2;
 // PREP: the preparation alone (one workgroup; M <= 16, so one row block): the
 // same three phases into LDS, then the tiles, the metadata and the tensor
 // scales go to the activation's buffers instead of feeding the GEMM.
-template <bool NORM, bool SMALL, bool PREP = false>
-__global__ __launch_bounds__(kNvFusedThreads) void nv_fused_layer_kernel(NvFusedArgs a) {
+template <bool NORM, bool SMALL, bool PREP = false, int NT = kNvFusedThreads>
+__global__ __launch_bounds__(NT) void nv_fused_layer_kernel(NvFusedArgs a) {
+  constexpr int kNvFusedThreads = NT, kNvFusedWaves = NT / 64;   // this instantiation's workgroup
   extern __shared__ __align__(16) uint8_t smem[];
-  const NvFusedLds L = nv_fused_lds(a.K);
+  const NvFusedLds L = nv_fused_lds(a.K, kNvFusedWaves);
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6) & (kNvFusedWaves - 1);
   float* inv = reinterpret_cast<float*>(smem + L.inv);
@@ -1004,11 +1005,16 @@ hipError_t launch_prepare_nv(const uint16_t* x, int64_t M, int K, int64_t ldx, c
   a.inv = reinterpret_cast<float*>(out.r_scales + L.inv);
   a.rparts = reinterpret_cast<float*>(out.r_scales + L.rparts);
   if (M > 0x7FFFFFFF || a.RB > 65535) return hipErrorInvalidValue;
-  if (M >= 1 && M <= 16 && M * (K / 32) <= kNvFusedThreads && nv_fused_lds(K).total <= 160 * 1024) {
-    // at most one 32-element chunk per thread of one workgroup: that workgroup
-    // runs the three phases (the one-launch layer's preparation) instead of
-    // three dependent launches (M = 1, K = 4096: 11.1 -> 6.8 us; with two
-    // chunks per thread, M = 8, it takes 14.3 against 11.6)
+  constexpr int kNvPrepOneWgThreads = kNvFusedThreads;
+  if (M >= 1 && M <= 16 && M * (K / 32) <= kNvPrepOneWgThreads &&
+      nv_fused_lds(K, kNvPrepOneWgThreads / 64).total <= 160 * 1024) {
+    // at most one 32-element chunk per thread of one 512-thread workgroup:
+    // that workgroup runs the three phases (the one-launch layer's
+    // preparation) instead of three dependent launches (K = 4096: M = 1
+    // 11.1 -> 6.9 us).  One compute unit's VALU then carries the whole
+    // preparation, which stops paying with more rows: at M = 8 it took
+    // 14.3 us with two chunks per thread and 13.5 us with 1024 threads,
+    // against 11.6 us for the three launches.
     NvFusedArgs f{};
     f.x = x;
     f.ldx = ldx;
@@ -1019,21 +1025,21 @@ hipError_t launch_prepare_nv(const uint16_t* x, int64_t M, int K, int64_t ldx, c
     f.out = out;
     f.g_s_out = a.g_s;
     f.g_r_out = a.g_r;
-    const bool small = M * (K / 32) <= (int64_t)kNvSmallChunks * kNvFusedThreads;
-    auto kern = gamma ? (small ? nv_fused_layer_kernel<true, true, true> : nv_fused_layer_kernel<true, false, true>)
-                      : (small ? nv_fused_layer_kernel<false, true, true> : nv_fused_layer_kernel<false, false, true>);
+    auto kern = gamma ? nv_fused_layer_kernel<true, true, true, kNvPrepOneWgThreads>
+                      : nv_fused_layer_kernel<false, true, true, kNvPrepOneWgThreads>;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    static std::atomic<bool> attr_set[64][4];
-    const int which = (gamma ? 2 : 0) + (small ? 1 : 0);
+    static std::atomic<bool> attr_set[64][2];
+    const int which = gamma ? 1 : 0;
     if (!attr_set[dev][which].load(std::memory_order_acquire)) {
       e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
       attr_set[dev][which].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(kern, dim3(1), dim3(kNvFusedThreads), nv_fused_lds(K).total, stream, f);
+    hipLaunchKernelGGL(kern, dim3(1), dim3(kNvPrepOneWgThreads), nv_fused_lds(K, kNvPrepOneWgThreads / 64).total,
+                       stream, f);
     return hipGetLastError();
   }
   const dim3 rows((unsigned)M), tiles((unsigned)a.WX, (unsigned)a.RB), blk(256), blk_q(kNvPrepThreads);
