@@ -326,20 +326,40 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
 // scale those maxima give.
 // ---------------------------------------------------------------------------
 constexpr int kNvPrepThreads = 256 * kNvWaves;
+constexpr int64_t kNvSelfScanElems = 65536;   // X small enough for every phase-2 workgroup to scan
 
-template <bool NORM, bool RESID>
+// SELF (phase 2 without RMSNorm, small tensors): max |v| = max |x| is taken
+// over the whole of X by every workgroup itself, with no per-row phase before.
+template <bool NORM, bool RESID, bool SELF = false>
 __global__ __launch_bounds__(kNvPrepThreads) void nv_decompose_kernel(NvPrepArgs a) {
+  static_assert(!SELF || (!NORM && !RESID), "the whole-tensor scan stands in for phase 1 without RMSNorm");
   __shared__ float red[kNvPrepThreads / 64];
   constexpr int NW = kNvPrepThreads / 64;
   const int t = threadIdx.x, u = t & 255, l = u >> 2, h = u & 3;
   const int64_t rb = blockIdx.y;
   const int kb = blockIdx.x * kNvWaves + (t >> 8);
 
-  // tensor scales from the previous phases' maxima (max |S| = max |v|: the
-  // mask keeps each group's largest magnitude)
-  float am = 0.0f;
-  for (int64_t i = t; i < a.M; i += kNvPrepThreads) am = fmaxf(am, a.rowamax[i]);
-  const float g_s = tensor_scale(block_max<NW>(am, red));
+  // tensor scales: g_S from max |v| (max |S| = max |v|: the mask keeps each
+  // group's largest magnitude) -- phase 2 reduces the rows' maxima (or scans
+  // X), phase 3 reads the g_S phase 2 stored -- and g_R from phase 2's maxima
+  float g_s;
+  if constexpr (RESID) {
+    g_s = *a.g_s;
+  } else {
+    float am = 0.0f;
+    if constexpr (SELF) {
+      const int k8 = a.K / 8;
+      for (int64_t j = t; j < a.M * k8; j += kNvPrepThreads) {
+        float v8[8];
+        load8(a.x + (j / k8) * a.ldx + 8 * (j % k8), v8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v8[i]));
+      }
+    } else {
+      for (int64_t i = t; i < a.M; i += kNvPrepThreads) am = fmaxf(am, a.rowamax[i]);
+    }
+    g_s = tensor_scale(block_max<NW>(am, red));
+  }
   float g_r = 1.0f;
   if (RESID) {
     float ar = 0.0f;
@@ -1047,6 +1067,11 @@ hipError_t launch_prepare_nv(const uint16_t* x, int64_t M, int K, int64_t ldx, c
     hipLaunchKernelGGL((nv_rowstats_kernel<true>), rows, blk, 0, stream, a);
     hipLaunchKernelGGL((nv_decompose_kernel<true, false>), tiles, blk_q, 0, stream, a);
     hipLaunchKernelGGL((nv_decompose_kernel<true, true>), tiles, blk_q, 0, stream, a);
+  } else if (M * (int64_t)K <= kNvSelfScanElems) {
+    // small tensors without RMSNorm: phase 2 scans X itself (two launches;
+    // M = 8, K = 4096: 11.4 -> 10.2 us)
+    hipLaunchKernelGGL((nv_decompose_kernel<false, false, true>), tiles, blk_q, 0, stream, a);
+    hipLaunchKernelGGL((nv_decompose_kernel<false, true>), tiles, blk_q, 0, stream, a);
   } else {
     hipLaunchKernelGGL((nv_rowstats_kernel<false>), rows, blk, 0, stream, a);
     hipLaunchKernelGGL((nv_decompose_kernel<false, false>), tiles, blk_q, 0, stream, a);

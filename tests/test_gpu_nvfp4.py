@@ -39,7 +39,9 @@ def check_prep(act, ref, M, K, label):
                                           (64, 4096, 4096, False), (130, 768, 768, True), (3, 1376, 1376, False),
                                           (5, 32768, 32768, True),
                                           # one workgroup for all three phases (at most 512 chunks of 32)
-                                          (4, 4096, 4104, True), (16, 1024, 1024, True), (13, 1056, 1056, False)])
+                                          (4, 4096, 4104, True), (16, 1024, 1024, True), (13, 1056, 1056, False),
+                                          # two launches: phase 2 scans X for max |x| (no RMSNorm, small X)
+                                          (9, 2080, 2088, False)])
 def test_nv_prep_shapes(M, K, ldx, norm):
     print(f"nv prep M={M} K={K} ldx={ldx} norm={norm}", flush=True)
     rng = np.random.default_rng(M * K + 7)
