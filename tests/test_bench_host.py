@@ -95,3 +95,12 @@ def test_traffic_record_follows_the_source_digest(tmp_path, monkeypatch):
     assert b.read_traffic() == 12345
     src.write_text("kernel v2")                              # the kernel changed since the counters
     assert b.read_traffic() is None
+
+
+def test_committed_traffic_record_matches_the_sources():
+    """The committed QKV counter summary carries the digest of the current GEMM
+    sources, so the bench line reports its HBM traffic (after a change to those
+    sources the counters are taken again, or the record re-stamped once the QKV
+    kernel's instructions are shown unchanged)."""
+    b = _bench()
+    assert b.read_traffic() is not None, "profiles/traffic_dual_gemm_qkv.txt does not match the GEMM sources"
