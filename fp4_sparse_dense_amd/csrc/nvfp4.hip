@@ -587,6 +587,25 @@ __global__ __launch_bounds__(64 * NW) void nv_dual_gemm_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
+      if constexpr (RBG == 1 && NW == 16) {
+        // one row block on 16 waves: both paths' operands expanded once, then
+        // each weight block in turn (fewer live registers than every weight
+        // block at once, for four waves per SIMD; every accumulator sees its
+        // MFMAs in the same order)
+        f16x8 xs[4], xr[4];
+        deq32(sq[c][0], ssb[c][0], xs);
+        deq32(rq[c][0], rsb[c][0], xr);
+#pragma unroll
+        for (int n = 0; n < CBG; ++n) {
+          f16x8 b[4];
+          deq32(wq[c][n], wsb[c][n], b);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acs[n][0] = mfma_f16(xs[j], b[j], acs[n][0]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acr[n][0] = mfma_f16(xr[j], b[j], acr[n][0]);
+        }
+        continue;
+      }
       f16x8 b[CBG][4];
 #pragma unroll
       for (int n = 0; n < CBG; ++n) deq32(wq[c][n], wsb[c][n], b[n]);
@@ -1121,8 +1140,12 @@ hipError_t launch_linear_nv(const GemmArgs& a, hipStream_t stream) {
   if (cus <= 0) return hipErrorInvalidDevice;
   const int cbg = (NB + 3) / 4 * RB >= cus ? 4 : (NB + 1) / 2 * RB >= cus ? 2 : 1;
   const dim3 grid((unsigned)((NB + cbg - 1) / cbg), (unsigned)RB);
+  // two column blocks: 16 waves, two K tiles each (M = 32: 8.25 -> 7.85 us);
+  // with four the 16-wave form spills or, at two blocks, doubles the
+  // activation's reads (M = 64: 11.8 against 14.8 and 13.1 us), and one
+  // block keeps 8 waves
   if (cbg == 4) hipLaunchKernelGGL((nv_dual_gemm_kernel<1, 8, 4>), grid, dim3(512), 0, stream, a);
-  else if (cbg == 2) hipLaunchKernelGGL((nv_dual_gemm_kernel<1, 8, 2>), grid, dim3(512), 0, stream, a);
+  else if (cbg == 2) hipLaunchKernelGGL((nv_dual_gemm_kernel<1, 16, 2>), grid, dim3(1024), 0, stream, a);
   else hipLaunchKernelGGL((nv_dual_gemm_kernel<1, 8, 1>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
