@@ -133,7 +133,9 @@ def nv_layer(x, gamma, w, out_dtype=sq.OUT_F32):
                                         (5, 1376, 100, False), (17, 2048, 272, True), (64, 256, 48, False),
                                         # two and four weight column blocks per workgroup, the last group
                                         # partly past N
-                                        (63, 1056, 2025, False), (64, 512, 4100, True), (32, 1024, 4096, False)])
+                                        (63, 1056, 2025, False), (64, 512, 4100, True), (32, 1024, 4096, False),
+                                        # two column blocks on 16 waves with a partial row block
+                                        (20, 512, 4096, True)])
 def test_nv_linear_full(M, K, N, norm):
     print(f"nv linear M={M} K={K} N={N}", flush=True)
     rng = np.random.default_rng(M + K + N + 1)
