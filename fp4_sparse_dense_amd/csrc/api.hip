@@ -371,6 +371,13 @@ static sharq_status swiglu_impl(const sharq_act* a, const sharq_weight* w, void*
     return fail(SHARQ_ERR_INVALID_ARG, "weight scale views must be tiled MX views (block 32, K-tile stride NB*64)");
   if (vs.base != vd.base)
     return fail(SHARQ_ERR_UNSUPPORTED, "the two paths must view the same packed scale array");
+  {
+    // the SwiGLU epilogues run on the tiled kernel only, whose buffer offsets are 31-bit
+    const uint64_t kb = (uint64_t)(a->K + 127) / 128, lim = 0x7FFFFFFFull;
+    if ((uint64_t)(a->M + 15) / 16 * kb * 1024 >= lim || (uint64_t)(w->N + 15) / 16 * kb * 1024 >= lim)
+      return fail(SHARQ_ERR_UNSUPPORTED, "the SwiGLU layer's operands past 2 GiB of codes (M=%lld, N=%lld, K=%lld)",
+                  (long long)a->M, (long long)w->N, (long long)a->K);
+  }
   s = check_device();
   if (s) return s;
   sharq::GemmArgs g{};

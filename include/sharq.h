@@ -283,7 +283,8 @@ sharq_status sharq_add_f32(const float* a_dev, const float* b_dev, float* y_dev,
  * input of the down projection's preparation, never materialising Y.
  * y: device bf16, row stride ldy >= F = N/2.  Runs the tiled kernel.
  * Errors: INVALID_ARG (null, shapes, N % 32, K mismatch, ldy, misaligned),
- * UNSUPPORTED (not 2:4 MXFP4, not gfx950), HIP. */
+ * UNSUPPORTED (not 2:4 MXFP4, either operand's codes past 2 GiB -- the tiled
+ * kernel's 31-bit offsets --, not gfx950), HIP. */
 sharq_status sharq_linear_swiglu(const sharq_act* a, const sharq_weight* w, void* y_bf16_dev, int64_t ldy,
                                  void* stream);
 

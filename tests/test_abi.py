@@ -282,7 +282,10 @@ def test_swiglu_rejects_before_launch(lib):
     assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 16, None) == _lib.ERR_INVALID_ARG   # ldy < N/2
     a.n = 0
     assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 32, None) == _lib.ERR_UNSUPPORTED   # 2:4 only
-    a.n, a.M = 2, 0
+    a.n, a.M = 2, 1 << 25
+    assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 32, None) == _lib.ERR_UNSUPPORTED   # codes past 2 GiB
+    assert b"2 GiB" in lib.sharq_last_error()
+    a.M = 0
     assert lib.sharq_linear_swiglu(C.byref(a), C.byref(w), y, 32, None) == _lib.OK
 
 
