@@ -161,6 +161,23 @@ def test_grouped_malformed_offsets_are_clamped():
     assert_linear_close(yg, yr, b, "malformed offsets")
 
 
+def test_grouped_most_experts():
+    """The largest expert count the layer takes (1024): the setup's scans then
+    hold 17 offsets per lane.  Zipf-routed token rows (most experts empty, a few
+    spanning several M tiles); every routed row against the oracle."""
+    print("grouped 1024 experts", flush=True)
+    rng = np.random.default_rng(41)
+    tokens, experts, top_k, d_model, n_e = 600, 1024, 4, 128, 16
+    expert, token, seg = synth.zipf_router(rng, tokens, experts, top_k)
+    assert (np.diff(seg) == 0).sum() > 100 and np.diff(seg).max() > 128
+    x = synth.outlier_activations(rng, tokens, d_model)
+    w = np.concatenate([synth.linear_weight(rng, n_e, d_model) for _ in range(experts)])
+    yg = _run(x, w, experts, seg, token)
+    ref = O.prepare(x, None)
+    yr, b = _reference(ref, token.astype(np.int64), seg, w, experts)
+    assert_linear_close(yg, yr, b, "1024 experts")
+
+
 def test_grouped_full_size_sampled():
     """The Qwen3-30B-A3B-shaped expert layer at full size (4096 tokens, top-8 of
     128 experts with Zipf(1.1) loads; gate/up K = 2048, N_e = 1536 over routed
