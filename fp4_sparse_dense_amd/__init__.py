@@ -23,7 +23,7 @@ __all__ = [
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
     "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32", "sharq_linear_residual",
     "sharq_linear_swiglu_prep", "peak_fp4_mfma", "peak_read",
-    "sharq_linear_grouped_noalloc", "noalloc_scratch_bytes", "check_e2m1", "sharq_linear_grouped_swiglu_prep",
+    "sharq_linear_grouped_noalloc", "noalloc_scratch_bytes", "check_e2m1", "check_mfma_fp4", "sharq_linear_grouped_swiglu_prep",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -302,6 +302,24 @@ def check_e2m1(x, exps, stream=None):
     _lib.check(lib.sharq_check_e2m1(_ptr(x), _ptr(exps), n, S, _ptr(enc), _ptr(pack), _ptr(dec), _ptr(unpack),
                                     _stream_ptr(stream)), "sharq_check_e2m1")
     return enc, pack, dec, unpack
+
+
+def check_mfma_fp4(a, sa, b, sb, stream=None):
+    """One FP4 MFMA per block as the GEMM kernels issue it (include/sharq_check.h):
+    a, b uint8 [B, 1024] codes and sa, sb uint8 [B, 64] scale bytes in the tiled
+    lane order.  Returns float32 [B, 16, 16], d[b][m][n]."""
+    torch = _torch()
+    for t, n in ((a, 1024), (b, 1024), (sa, 64), (sb, 64)):
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[1] != n or not t.is_contiguous():
+            raise ValueError("a, b must be contiguous uint8 [B, 1024] and sa, sb uint8 [B, 64]")
+    B = a.shape[0]
+    if not (b.shape[0] == sa.shape[0] == sb.shape[0] == B):
+        raise ValueError("operands hold different block counts")
+    d = torch.empty(B, 16, 16, dtype=torch.float32, device=a.device)
+    lib = _lib.load()
+    _lib.check(lib.sharq_check_mfma_fp4(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), B, _ptr(d), _stream_ptr(stream)),
+               "sharq_check_mfma_fp4")
+    return d
 
 
 def noalloc_scratch_bytes() -> int:

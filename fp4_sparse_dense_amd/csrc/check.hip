@@ -2,13 +2,16 @@
 // as the preparation (fp4_enc / fp4_dec with the block scale inside the
 // convert), the weight pack (a binary32 product by 2^-e, then fp4_pack2 with
 // scale 1) and the NVFP4-style path (fp4_pack2 / fp4_unpack2 with scale 1) use
-// them, so a test can compare every code and value with the rounding rule.
+// them, so a test can compare every code and value with the rounding rule; and
+// one block-scaled FP4 MFMA issued as the GEMM kernels issue it, so a test can
+// pin its operand, scale and accumulator lane layouts.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
 
 #include "sharq_check.h"
 #include "device_common.h"
+#include "gemm_common.h"
 #include "prep_common.h"
 
 namespace sharq {
@@ -59,6 +62,25 @@ __global__ __launch_bounds__(256) void check_e2m1_kernel(const float* __restrict
   }
 }
 
+// One block-scaled FP4 MFMA per wave on operands in the tiled layout, issued
+// through the GEMM kernels' own operand and MFMA helpers (as_operand,
+// mfma_fp4): lane l brings the 16 code bytes and the scale byte of row l % 16,
+// 32-element chunk l / 16, of each operand, and its accumulator holds
+// D[4 * (l / 16) + i][l % 16], i = 0..3.
+__global__ __launch_bounds__(256) void check_mfma_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
+                                                         const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
+                                                         int n_blocks, float* __restrict__ d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= n_blocks) return;   // wave-uniform
+  const uint4 qa = *reinterpret_cast<const uint4*>(a + blk * 1024 + lane * 16);
+  const uint4 qb = *reinterpret_cast<const uint4*>(b + blk * 1024 + lane * 16);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  acc = mfma_fp4(as_operand(qa), as_operand(qb), acc, sa[blk * 64 + lane], sb[blk * 64 + lane]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[blk * 256 + (4 * (lane >> 4) + i) * 16 + (lane & 15)] = acc[i];
+}
+
 }  // namespace sharq
 
 extern "C" {
@@ -82,6 +104,25 @@ sharq_status sharq_check_e2m1(const float* x_dev, const int32_t* exps_dev, int64
   hipLaunchKernelGGL(sharq::check_e2m1_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), x_dev, exps_dev, n, groups, enc_dev, pack_dev, dec_dev,
                      unpack_dev);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return sharq::record_error(SHARQ_ERR_HIP, hipGetErrorString(e));
+  return SHARQ_OK;
+}
+
+sharq_status sharq_check_mfma_fp4(const uint8_t* a_dev, const uint8_t* sa_dev, const uint8_t* b_dev,
+                                  const uint8_t* sb_dev, int32_t n_blocks, float* d_dev, void* stream) {
+  if (!a_dev || !sa_dev || !b_dev || !sb_dev || !d_dev) return sharq::record_error(SHARQ_ERR_INVALID_ARG, "null argument");
+  if (n_blocks < 1 || n_blocks > (1 << 20)) return sharq::record_error(SHARQ_ERR_INVALID_ARG, "n_blocks must be in 1 .. 2^20");
+  if ((reinterpret_cast<uintptr_t>(a_dev) | reinterpret_cast<uintptr_t>(b_dev)) & 15 ||
+      reinterpret_cast<uintptr_t>(d_dev) & 3)
+    return sharq::record_error(SHARQ_ERR_INVALID_ARG, "codes must be 16-byte aligned, outputs 4-byte aligned");
+  int dev = 0;
+  hipDeviceProp_t p;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess)
+    return sharq::record_error(SHARQ_ERR_HIP, "device query failed");
+  if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) return sharq::record_error(SHARQ_ERR_UNSUPPORTED, "not gfx950");
+  hipLaunchKernelGGL(sharq::check_mfma_kernel, dim3((unsigned)((n_blocks + 3) / 4)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a_dev, sa_dev, b_dev, sb_dev, n_blocks, d_dev);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sharq::record_error(SHARQ_ERR_HIP, hipGetErrorString(e));
   return SHARQ_OK;

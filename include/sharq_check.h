@@ -1,6 +1,7 @@
 /*
- * sharq_check.h -- the FP4 (E2M1) conversions of the SharQ kernels, exposed so
- * that their rounding can be checked against its definition on the device.
+ * sharq_check.h -- the FP4 (E2M1) conversions and the block-scaled FP4 MFMA of
+ * the SharQ kernels, exposed so that their rounding and lane layouts can be
+ * checked against their definitions on the device.
  *
  * Every E2M1 code the preparation, the weight pack and the NVFP4-style path
  * write comes from the hardware converts behind this entry point, used exactly
@@ -39,6 +40,23 @@ extern "C" {
  * -127..125 give unspecified results. */
 sharq_status sharq_check_e2m1(const float* x_dev, const int32_t* exps_dev, int64_t n, int32_t n_scales,
                               uint32_t* enc_dev, uint32_t* pack_dev, float* dec_dev, float* unpack_dev, void* stream);
+
+/* One block-scaled FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 operands,
+ * E8M0 scales) per block, issued exactly as the SharQ GEMM kernels issue it on
+ * operands in the tiled layout of sharq.h, so that a test can pin the operand,
+ * scale and accumulator lane layouts against the definition (SharQ abstract:
+ * both paths are FP4 GEMMs on block-scaled operands):
+ *   d[b][m][n] = sum over k < 128 of val(A_b[m][k]) * 2^(sa_b[m][k/32] - 127)
+ *                                  * val(B_b[n][k]) * 2^(sb_b[n][k/32] - 127),
+ * A_b, B_b: 16 x 128 E2M1 codes, 1 KiB each in the tiled lane order (lane
+ * l = row l%16 + 16 * (k/32): 16 bytes, the lower k in the low nibble);
+ * sa_b, sb_b: their 64 E8M0 scale bytes in the same lane order.
+ * a_dev, b_dev: uint8[n_blocks][1024] (16-byte aligned); sa_dev, sb_dev:
+ * uint8[n_blocks][64]; d_dev: float[n_blocks][16][16], m-major.
+ * Errors: INVALID_ARG (null, n_blocks outside 1 .. 2^20, misaligned),
+ * UNSUPPORTED (not gfx950), HIP. */
+sharq_status sharq_check_mfma_fp4(const uint8_t* a_dev, const uint8_t* sa_dev, const uint8_t* b_dev,
+                                  const uint8_t* sb_dev, int32_t n_blocks, float* d_dev, void* stream);
 
 #ifdef __cplusplus
 }
