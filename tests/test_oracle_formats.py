@@ -77,6 +77,38 @@ def test_e2m1_against_exact_bruteforce():
     assert np.all(got & 7 == O.e2m1_nearest(np.abs(allv)))
 
 
+@pytest.mark.slow
+def test_e2m1_exhaustive_over_binary32():
+    """Every non-negative finite binary32 value (2^31 - 2^23 bit patterns, about
+    80 s).  The exact-rational rule is monotone in the bit pattern of a
+    non-negative value, so its seven code boundaries -- the first pattern at or
+    above each code -- are found by bisection with brute_e2m1, and the expected
+    code of every pattern is the number of boundaries at or below it.  The
+    oracle's code must equal it for all of them; the sign bit adds 8 (checked
+    on every 64th pattern, and at -0)."""
+    bounds = []
+    for code in range(1, 8):
+        lo, hi = 0, 0x7F800000
+        while lo < hi:
+            mid = (lo + hi) // 2
+            if brute_e2m1(float(np.uint32(mid).view(np.float32))) >= code:
+                hi = mid
+            else:
+                lo = mid + 1
+        bounds.append(lo)
+    bounds = np.array(bounds, dtype=np.uint64)
+    chunk = 1 << 24
+    for start in range(0, 0x7F800000, chunk):
+        bits = np.arange(start, min(start + chunk, 0x7F800000), dtype=np.uint32)
+        got = O.e2m1_nearest(bits.view(np.float32))
+        want = np.searchsorted(bounds, bits.astype(np.uint64), side="right").astype(np.uint8)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"pattern {int(bits[bad[0]]):#010x}: {int(got[bad[0]])} != {int(want[bad[0]])}"
+        neg = bits[::64] | np.uint32(0x80000000)
+        assert np.array_equal(O.e2m1_nearest(neg.view(np.float32)), want[::64] | 8)
+    assert O.e2m1_nearest(np.float32(np.inf)) == 7                # beyond the grid: saturates
+
+
 def test_e2m1_value_roundtrip():
     for nib in range(16):
         v = O.e2m1_value(np.uint8(nib))

@@ -76,6 +76,42 @@ def test_e4m3_decode_and_roundtrip():
     assert np.array_equal(b, np.arange(127, dtype=np.uint8)) and np.array_equal(v, vals)
 
 
+@pytest.mark.slow
+def test_e4m3_exhaustive_over_binary32():
+    """Every binary32 value in [2^-11, 480] (about 1.7e8 patterns, where all the
+    rounding decisions lie), and every 4096th pattern from 0 to 2^-11 and from
+    480 to the largest finite value.  The nearest-value rule is monotone in the
+    bit pattern, so the first pattern at or above each byte is found by
+    bisection with brute_e4m3_byte, and the expected byte of every pattern is
+    the number of those boundaries at or below it (bytes 0..126 increase with
+    their values)."""
+    bounds = []
+    top = int(np.float32(2.0 ** 11).view(np.uint32))               # the brute force is exact up to 2^11
+    for byte in range(1, 127):
+        lo, hi = 0, top
+        while lo < hi:
+            mid = (lo + hi) // 2
+            if brute_e4m3_byte(np.array([np.uint32(mid)]).view(np.float32))[0] >= byte:
+                hi = mid
+            else:
+                lo = mid + 1
+        bounds.append(lo)
+    bounds = np.array(bounds, dtype=np.uint64)
+    lo_bits = int(np.float32(2.0 ** -11).view(np.uint32))
+    hi_bits = int(np.float32(480.0).view(np.uint32))
+    assert bounds[0] > lo_bits and bounds[-1] <= hi_bits          # every decision inside the dense range
+    ranges = [np.arange(0, lo_bits, 4096, dtype=np.uint32),
+              np.arange(hi_bits, 0x7F800000, 4096, dtype=np.uint32)]
+    chunk = 1 << 24
+    ranges += [np.arange(s0, min(s0 + chunk, hi_bits), dtype=np.uint32) for s0 in range(lo_bits, hi_bits, chunk)]
+    for bits in ranges:
+        v, b = O.e4m3_round(bits.view(np.float32))
+        want = np.searchsorted(bounds, bits.astype(np.uint64), side="right").astype(np.uint8)
+        bad = np.nonzero(b != want)[0]
+        assert bad.size == 0, f"pattern {int(bits[bad[0]]):#010x}: byte {int(b[bad[0]])} != {int(want[bad[0]])}"
+        assert np.array_equal(v, GRID_F[want])
+
+
 def test_e4m3_round_against_bruteforce():
     pts = []
     f = GRID_F
