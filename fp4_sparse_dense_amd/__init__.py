@@ -23,7 +23,7 @@ __all__ = [
     "sharq_rmsnorm", "sharq_add_f32", "path_act", "grouped_workspace_bytes", "sharq_linear_fused",
     "sharq_linear_swiglu", "interleave_gate_up", "sharq_add_bf16_f32", "sharq_linear_residual",
     "sharq_linear_swiglu_prep", "peak_fp4_mfma", "peak_read",
-    "sharq_linear_grouped_noalloc", "noalloc_scratch_bytes", "check_e2m1", "check_mfma_fp4", "sharq_linear_grouped_swiglu_prep",
+    "sharq_linear_grouped_noalloc", "noalloc_scratch_bytes", "check_e2m1", "check_e4m3", "check_mfma_fp4", "sharq_linear_grouped_swiglu_prep",
     "weight_bytes", "act_bytes",
     "FMT_MXFP4", "FMT_NVFP4", "FMT_HIF4", "OUT_F32", "OUT_BF16",
 ]
@@ -302,6 +302,22 @@ def check_e2m1(x, exps, stream=None):
     _lib.check(lib.sharq_check_e2m1(_ptr(x), _ptr(exps), n, S, _ptr(enc), _ptr(pack), _ptr(dec), _ptr(unpack),
                                     _stream_ptr(stream)), "sharq_check_e2m1")
     return enc, pack, dec, unpack
+
+
+def check_e4m3(x, stream=None):
+    """The NVFP4-style kernels' E4M3 block-scale rounding (include/sharq_check.h)
+    on a contiguous float32 device tensor of finite values >= 0.  Returns (byte
+    uint8, value float32, decoded float32), each shaped like x."""
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_contiguous() or x.numel() < 1:
+        raise ValueError("x must be a non-empty contiguous float32 tensor")
+    byte = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    value = torch.empty_like(x)
+    dec = torch.empty_like(x)
+    lib = _lib.load()
+    _lib.check(lib.sharq_check_e4m3(_ptr(x), x.numel(), _ptr(byte), _ptr(value), _ptr(dec), _stream_ptr(stream)),
+               "sharq_check_e4m3")
+    return byte, value, dec
 
 
 def check_mfma_fp4(a, sa, b, sb, stream=None):

@@ -2,15 +2,17 @@
 // as the preparation (fp4_enc / fp4_dec with the block scale inside the
 // convert), the weight pack (a binary32 product by 2^-e, then fp4_pack2 with
 // scale 1) and the NVFP4-style path (fp4_pack2 / fp4_unpack2 with scale 1) use
-// them, so a test can compare every code and value with the rounding rule; and
-// one block-scaled FP4 MFMA issued as the GEMM kernels issue it, so a test can
-// pin its operand, scale and accumulator lane layouts.
+// them, so a test can compare every code and value with the rounding rule; the
+// NVFP4-style path's E4M3 block-scale rounding and decoding; and one
+// block-scaled FP4 MFMA issued as the GEMM kernels issue it, so a test can pin
+// its operand, scale and accumulator lane layouts.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
 
 #include "sharq_check.h"
 #include "device_common.h"
+#include "e4m3.h"
 #include "gemm_common.h"
 #include "prep_common.h"
 
@@ -62,6 +64,19 @@ __global__ __launch_bounds__(256) void check_e2m1_kernel(const float* __restrict
   }
 }
 
+// E4M3 of each value as the NVFP4-style kernels round their block scales, and
+// the byte decoded back as their GEMM decodes it.
+__global__ __launch_bounds__(256) void check_e4m3_kernel(const float* __restrict__ x, int64_t n,
+                                                         uint8_t* __restrict__ byte, float* __restrict__ value,
+                                                         float* __restrict__ dec) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  uint32_t b = 0;
+  value[i] = e4m3_round(x[i], b);
+  byte[i] = (uint8_t)b;
+  dec[i] = e4m3_value(b);
+}
+
 // One block-scaled FP4 MFMA per wave on operands in the tiled layout, issued
 // through the GEMM kernels' own operand and MFMA helpers (as_operand,
 // mfma_fp4): lane l brings the 16 code bytes and the scale byte of row l % 16,
@@ -104,6 +119,24 @@ sharq_status sharq_check_e2m1(const float* x_dev, const int32_t* exps_dev, int64
   hipLaunchKernelGGL(sharq::check_e2m1_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), x_dev, exps_dev, n, groups, enc_dev, pack_dev, dec_dev,
                      unpack_dev);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return sharq::record_error(SHARQ_ERR_HIP, hipGetErrorString(e));
+  return SHARQ_OK;
+}
+
+sharq_status sharq_check_e4m3(const float* x_dev, int64_t n, uint8_t* byte_dev, float* value_dev, float* dec_dev,
+                              void* stream) {
+  if (!x_dev || !byte_dev || !value_dev || !dec_dev) return sharq::record_error(SHARQ_ERR_INVALID_ARG, "null argument");
+  if (n < 1 || n > ((int64_t)1 << 31)) return sharq::record_error(SHARQ_ERR_INVALID_ARG, "n must be in 1 .. 2^31");
+  if ((reinterpret_cast<uintptr_t>(x_dev) | reinterpret_cast<uintptr_t>(value_dev) | reinterpret_cast<uintptr_t>(dec_dev)) & 3)
+    return sharq::record_error(SHARQ_ERR_INVALID_ARG, "float buffers must be 4-byte aligned");
+  int dev = 0;
+  hipDeviceProp_t p;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess)
+    return sharq::record_error(SHARQ_ERR_HIP, "device query failed");
+  if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) return sharq::record_error(SHARQ_ERR_UNSUPPORTED, "not gfx950");
+  hipLaunchKernelGGL(sharq::check_e4m3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), x_dev, n, byte_dev, value_dev, dec_dev);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sharq::record_error(SHARQ_ERR_HIP, hipGetErrorString(e));
   return SHARQ_OK;

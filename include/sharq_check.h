@@ -1,7 +1,8 @@
 /*
- * sharq_check.h -- the FP4 (E2M1) conversions and the block-scaled FP4 MFMA of
- * the SharQ kernels, exposed so that their rounding and lane layouts can be
- * checked against their definitions on the device.
+ * sharq_check.h -- the FP4 (E2M1) conversions, the E4M3 block-scale rounding
+ * and the block-scaled FP4 MFMA of the SharQ kernels, exposed so that their
+ * rounding and lane layouts can be checked against their definitions on the
+ * device.
  *
  * Every E2M1 code the preparation, the weight pack and the NVFP4-style path
  * write comes from the hardware converts behind this entry point, used exactly
@@ -40,6 +41,17 @@ extern "C" {
  * -127..125 give unspecified results. */
 sharq_status sharq_check_e2m1(const float* x_dev, const int32_t* exps_dev, int64_t n, int32_t n_scales,
                               uint32_t* enc_dev, uint32_t* pack_dev, float* dec_dev, float* unpack_dev, void* stream);
+
+/* The E4M3 block-scale rounding of the NVFP4-style path (NVFP4 per the public
+ * description: an E4M3 scale per 16 values), as its kernels round the scales:
+ * byte[i] and value[i] = the E4M3 nearest to x[i] (ties to the even mantissa,
+ * saturating at 448), dec[i] = byte[i] decoded as their GEMM decodes it.
+ * x_dev: float[n], finite and >= 0 (others: unspecified); byte_dev: uint8[n];
+ * value_dev, dec_dev: float[n].
+ * Errors: INVALID_ARG (null, n outside 1 .. 2^31, misaligned), UNSUPPORTED
+ * (not gfx950), HIP. */
+sharq_status sharq_check_e4m3(const float* x_dev, int64_t n, uint8_t* byte_dev, float* value_dev, float* dec_dev,
+                              void* stream);
 
 /* One block-scaled FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 operands,
  * E8M0 scales) per block, issued exactly as the SharQ GEMM kernels issue it on

@@ -387,6 +387,9 @@ def test_check_entry_points_reject_before_launch(lib):
     assert lib.sharq_check_e2m1(None, buf, 8, 1, buf, buf, buf, buf, None) == _lib.ERR_INVALID_ARG
     assert lib.sharq_check_e2m1(buf, buf, 12, 1, buf, buf, buf, buf, None) == _lib.ERR_INVALID_ARG   # n % 8
     assert lib.sharq_check_e2m1(buf, buf, 8, 0, buf, buf, buf, buf, None) == _lib.ERR_INVALID_ARG    # no scales
+    assert lib.sharq_check_e4m3(None, 8, buf, buf, buf, None) == _lib.ERR_INVALID_ARG
+    assert lib.sharq_check_e4m3(buf, 0, buf, buf, buf, None) == _lib.ERR_INVALID_ARG               # empty
+    assert lib.sharq_check_e4m3(C.c_void_p(0x100002), 8, buf, buf, buf, None) == _lib.ERR_INVALID_ARG
     assert lib.sharq_check_mfma_fp4(None, buf, buf, buf, 1, buf, None) == _lib.ERR_INVALID_ARG
     assert lib.sharq_check_mfma_fp4(buf, buf, buf, buf, 0, buf, None) == _lib.ERR_INVALID_ARG        # no blocks
     assert lib.sharq_check_mfma_fp4(buf, buf, buf, buf, (1 << 20) + 1, buf, None) == _lib.ERR_INVALID_ARG
