@@ -1,6 +1,7 @@
 """The library on the caller's stream and under HIP graph capture: results on a
 side stream (passed explicitly or current through torch.cuda.stream) equal the
-default stream's; a captured graph of the preparation, the layer, the grouped
+default stream's; independent layers on two streams at once equal the same
+calls run alone; a captured graph of the preparation, the layer, the grouped
 layer, the grouped SwiGLU-prep layer and the one-launch decode layer, replayed several times with new inputs
 copied in and eager work in between, equals the eager result every time."""
 import numpy as np
@@ -32,6 +33,46 @@ def test_side_stream_equals_default():
         y2 = sq.sharq_linear(sq.sharq_prepare(xd, gd, 1e-5), wt)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1) and torch.equal(y0, y2)
+
+
+def test_two_streams_concurrently():
+    """Independent layers on two streams at once (default priority), nothing
+    ordering one stream's kernels against the other's: the 2:4 MXFP4 layer, the
+    NVFP4-style layer and the grouped layer on each, with different inputs,
+    four rounds; every output equals the same call run alone on the default
+    stream (the library keeps no state that calls share)."""
+    import torch
+    print("two streams", flush=True)
+    work = []
+    for seed in (11, 12):
+        x, g, w = _inputs(seed, M=384, K=768, N=640)
+        rng = np.random.default_rng(seed + 100)
+        expert, token, seg = synth.zipf_router(rng, 96, 5, 2)
+        we = np.concatenate([synth.linear_weight(rng, 64, 768) for _ in range(5)])
+        work.append(dict(x=dev_bf16(x), g=dev_bf16(g), wt=sq.sharq_pack_weight(dev_bf16(w)),
+                         wtn=sq.sharq_pack_weight(dev_bf16(w), fmt=sq.FMT_NVFP4),
+                         xe=dev_bf16(x[:96]), we=sq.sharq_pack_weight(dev_bf16(we)),
+                         seg=torch.from_numpy(seg).cuda(), ri=torch.from_numpy(token.astype(np.int32)).cuda()))
+
+    def run(d, stream=None):
+        y = sq.sharq_linear(sq.sharq_prepare(d["x"], d["g"], 1e-5, stream=stream), d["wt"], stream=stream)
+        yn = sq.sharq_linear(sq.sharq_prepare(d["x"], d["g"], 1e-5, fmt=sq.FMT_NVFP4, stream=stream), d["wtn"],
+                             stream=stream)
+        ye = sq.sharq_linear_grouped(sq.sharq_prepare(d["xe"], None, stream=stream), d["we"], d["seg"], 5,
+                                     row_index=d["ri"], rows=int(d["seg"][-1]), stream=stream)
+        return y, yn, ye
+
+    refs = [run(d) for d in work]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for rnd in range(4):
+        outs = [run(d, stream=st) for d, st in zip(work, streams)]
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, refs)):
+            for a, b in zip(o, r):
+                assert torch.equal(a, b), f"round {rnd}, stream {i}"
 
 
 def test_graph_replay_matches_eager():
