@@ -80,6 +80,25 @@ def test_grouped_down_sorted_rows_with_empty_experts():
     assert_linear_close(yg, yr, b, "down")
 
 
+def test_grouped_partial_k_tile():
+    """K = 160: the last 128-wide K tile holds 32 real columns and zero padding,
+    through the gather (token rows) and the in-place read (sorted rows)."""
+    print("grouped partial K tile", flush=True)
+    rng = np.random.default_rng(51)
+    tokens, experts, top_k, d_model, n_e = 140, 7, 3, 160, 48
+    expert, token, seg = synth.zipf_router(rng, tokens, experts, top_k)
+    x = synth.outlier_activations(rng, tokens, d_model)
+    w = np.concatenate([synth.linear_weight(rng, n_e, d_model) for _ in range(experts)])
+    ref = O.prepare(x, None)
+    yg = _run(x, w, experts, seg, token)
+    yr, b = _reference(ref, token.astype(np.int64), seg, w, experts)
+    assert_linear_close(yg, yr, b, "partial K tile, gathered")
+    xs = x[token]                                         # the same rows, already in expert order
+    ys = _run(xs, w, experts, seg, None)
+    yr2, b2 = _reference(O.prepare(xs, None), np.arange(len(xs)), seg, w, experts)
+    assert_linear_close(ys, yr2, b2, "partial K tile, in order")
+
+
 def test_grouped_out_of_range_rows_read_zero():
     print("grouped out-of-range rows", flush=True)
     rng = np.random.default_rng(11)
