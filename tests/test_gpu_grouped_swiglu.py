@@ -81,6 +81,7 @@ def _assert_same_act(a, b, label):
     (1, 512, 4, 2, 512, 256, False, False),     # experts spanning several 128-row tiles
     (2, 203, 6, 2, 256, 128, False, True),      # rows already in expert order
     (3, 64, 16, 1, 128, 384, False, False),     # empty experts, four N tiles per expert
+    (4, 100, 5, 2, 160, 128, True, False),      # K = 160: a partial last K tile
 ])
 def test_grouped_swiglu_prep_equals_per_expert_layers(seed, tokens, experts, top_k, K, F, holes, in_order):
     print(f"grouped swiglu_prep seed={seed} tokens={tokens} E={experts} K={K} F={F}", flush=True)
