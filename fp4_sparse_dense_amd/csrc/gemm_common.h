@@ -1,8 +1,9 @@
 // Operand, MFMA and output helpers shared by the GEMM kernels.
 //
-// MFMA 16x16x128 FP4 operand layout (measured): lane l holds row (or column)
-// l%16 and K range [32*(l/16), 32*(l/16)+32) as 16 bytes, lower k in the low
-// nibble; its scale byte is that row's E8M0 for the same 32-block; the
+// MFMA 16x16x128 FP4 operand layout (pinned on the device bit for bit by
+// tests/test_gpu_mfma.py through sharq_check_mfma_fp4): lane l holds row (or
+// column) l%16 and K range [32*(l/16), 32*(l/16)+32) as 16 bytes, lower k in
+// the low nibble; its scale byte is that row's E8M0 for the same 32-block; the
 // accumulator of lane l holds D[4*(l/16)+i][l%16], i = 0..3.
 #pragma once
 #include "device_common.h"
